@@ -1,0 +1,196 @@
+/*
+ * lowbit.h -- C ABI of liblowbit: matrix products over group-scaled binary
+ * {-1,+1} and ternary {-1,0,+1} weights on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources):
+ *   - Each weight is a sign (binary) or one of {-1,0,+1} (ternary), and every
+ *     group of weights shares one FP16 scale ("1-bit 嘅數學" section of the
+ *     richmindsetzone.com page "瀏覽器生圖技術內幕：1-bit diffusion 點樣將 3GB
+ *     模型塞入 WebGPU？"; effective widths 1.125 bits binary, 1.71 ternary).
+ *   - The group holds 128 weights, one FP16 scale each (method list of the
+ *     ainewscove.com OpenBonsai post).
+ *   - Multiplying by -1/0/+1 is an add or a sign flip ("精度保留了多少"
+ *     section of the kongchang.com Ternary Bonsai 2 article); a binary
+ *     product can be done with XOR + popcount (same section of the
+ *     richmindsetzone.com page, the paragraph comparing binary and ternary).
+ *   - Batch-1 decode streams every weight once per token and is bound by
+ *     memory bandwidth; prefill is a dense contraction (best.xiaohu.ai Bonsai
+ *     27B article, sections "ローカル27Bを阻む第一の壁" and "速度は二層").
+ *
+ * Dense (unpacked) meaning of the operands, shared by every entry point:
+ *   W       [N][K] weights, row n = output feature, k = reduction index.
+ *   codes   int8 [N][K] row-major: binary in {-1,+1}, ternary in {-1,0,+1}.
+ *   scales  IEEE binary16 bits, uint16 [N][G], G = K/128; group g of row n
+ *           covers k in [128g, 128g+128).  W[n][k] = scale[n][k/128]*code[n][k].
+ *           There is no zero point.  Scales must be finite (any sign, 0 ok).
+ *   X       [M][K] activations, row-major.  Y = X * W^T, Y is [M][N].
+ *   K must be a positive multiple of 128; N, M >= 1.
+ *
+ * Every pointer is caller-owned device memory unless stated.  Every call is
+ * asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
+ * stream).  Argument errors are returned synchronously before any HIP call.
+ * A launch failure returns LOWBIT_E_HIP.  No entry point synchronizes.
+ *
+ * =====================  PACKED LAYOUT (gfx950)  ===========================
+ * Rows are tiled in row-blocks of 16 (NB = ceil(N/16), rows >= N are padding
+ * with code 0 / +1 and scale 0).  Inside a row-block, row r = n % 16 and the
+ * 128 weights of a group are split over four quarters q = 0..3; the pair
+ * (r, q) is the lane L = r + 16q of a 64-wide wavefront.  Quarter q of a
+ * group holds 32 weights in slots i = 0..31; slot i of quarter q is the
+ * weight at k = 128g + KMAP(q, i) with
+ *     KMAP(q, i) = 64*(q & 1) + 16*(q >> 1) + 32*(i >> 4) + (i & 15).
+ * (This is the order in which the fp4 B operand of the gfx950
+ * 16x16x128 f8f6f4 MFMA consumes k, so one lane's 32 weights are one MFMA
+ * fragment.)
+ *
+ * LOWBIT_BINARY (1 bit / weight).  One 32-bit word per (row, group, quarter);
+ *   bit b of the word holds slot  i = 8*(3 - (b & 3)) + (b >> 2),  bit value
+ *   1 means -1 and 0 means +1.  Words are stored as
+ *     word[((rb * GQ + g/4) * 64 + L) * 4 + (g % 4)],   GQ = ceil(G/4),
+ *   so a wavefront reading one 16-byte vector per lane reads 1 KiB contiguous
+ *   (16 rows x 4 groups).  Code bytes: NB * GQ * 1024.
+ *
+ * LOWBIT_TERNARY_2BIT (2 bits / weight, bit-sliced).  Two words P0, P1 per
+ *   (row, group, quarter).  Each weight has a "nonzero" bit z and a "negative"
+ *   bit s (code = z * (1 - 2s); z = 0 with s = 1 is reserved and never
+ *   written).  For slot i = 8j + p (j = 0..3, p = 0..7):
+ *     j = 0: P0 bit 4p+1 = z, P0 bit 4p+3 = s      j = 1: P0 bit 4p = z, P0 bit 4p+2 = s
+ *     j = 2: P1 bit 4p+1 = z, P1 bit 4p+3 = s      j = 3: P1 bit 4p = z, P1 bit 4p+2 = s
+ *   Words are stored as
+ *     word[((rb * GP + g/2) * 64 + L) * 4 + 2*(g % 2) + t],  t = 0 (P0), 1 (P1),
+ *   GP = ceil(G/2).  Code bytes: NB * GP * 1024.
+ *
+ * LOWBIT_TERNARY_BASE3 (5 trits / byte, 1.625 bits / weight).  Trit
+ *   t = code + 1 in {0,1,2}; a byte holding trits t_0..t_{d-1} has value
+ *   sum t_e * 3^e (t_0 is the least-significant digit).  Groups are handled
+ *   in octets o = g/8 (GO = ceil(G/8)).  Lane L of octet o owns 52 bytes
+ *   B[0..51] covering the 8 groups j = 0..7 (g = 8o + j) of its quarter:
+ *     slots 0..29 of group j -> bytes 6j .. 6j+5, slot i in byte 6j + i/5,
+ *                                digit i % 5;
+ *     slots 30, 31 of group j -> byte 48 + j/2, digits 2*(j%2) + (i-30).
+ *   (Bytes 0..47 hold 5 trits, bytes 48..51 hold 4.)  An octet block of a
+ *   row-block is 3328 bytes: for s = 0..2 the 1024 bytes at 1024s hold
+ *   B[16s .. 16s+15] of lane L at offset 1024s + 16L, and the 256 bytes at
+ *   3072 hold B[48..51] of lane L at 3072 + 4L.  Block (rb, o) starts at
+ *   byte (rb * GO + o) * 3328.  Code bytes: NB * GO * 3328.  Byte values
+ *   >= 243 (>= 81 in bytes 48..51) are invalid.
+ *
+ * Scales, all formats: fp16 bits stored as
+ *     scale[((rb * GQ + g/4) * 16 + r) * 4 + (g % 4)],
+ *   i.e. 128 bytes per (row-block, 4 groups).  Scale bytes: NB * GQ * 128.
+ *   Padding groups (g >= G) and padding rows hold code 0 (+1 binary) and
+ *   scale 0.
+ *
+ * Bits per weight when N % 16 == 0 and G % 8 == 0: binary 1 + 0.125 = 1.125,
+ * ternary 2-bit 2.125, ternary base-3 1.625 + 0.125 = 1.75 (all at or above
+ * the information bound log2(3) + 0.125 = 1.70996 for ternary).
+ * ========================================================================= */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_ABI_VERSION 1
+
+enum lowbit_status {
+  LOWBIT_OK = 0,
+  LOWBIT_E_NULL = -1,        /* a required pointer is NULL                    */
+  LOWBIT_E_SHAPE = -2,       /* K % 128 != 0, N/M/K < 1, or size overflow     */
+  LOWBIT_E_ALIGN = -3,       /* pointer not aligned as documented             */
+  LOWBIT_E_UNSUPPORTED = -4, /* format / dtype combination not provided       */
+  LOWBIT_E_BADCODE = -5,     /* reserved for callers that check the flag     */
+  LOWBIT_E_HIP = -6,         /* a HIP runtime call or launch failed           */
+  LOWBIT_E_NOMEM = -7        /* the library could not allocate its workspace  */
+};
+
+enum lowbit_format {
+  LOWBIT_BINARY = 1,
+  LOWBIT_TERNARY_2BIT = 2,
+  LOWBIT_TERNARY_BASE3 = 3
+};
+
+enum lowbit_dtype {
+  LOWBIT_F32 = 1,   /* IEEE binary32                                          */
+  LOWBIT_BF16 = 2,  /* bfloat16 bits (uint16)                                 */
+  LOWBIT_I8 = 3,    /* int8 with a float scale: value = scale * q             */
+  LOWBIT_SIGN1 = 4, /* packed sign bits, K/8 bytes per row, bit k%8 of byte
+                       k/8 (LSB first); bit 1 means -alpha, 0 means +alpha     */
+  LOWBIT_I32 = 5    /* int32 output of the exact integer paths               */
+};
+
+/* ABI version of the loaded library (LOWBIT_ABI_VERSION). */
+int lowbit_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* lowbit_status_str(int status);
+
+/* Bytes of the packed code and scale buffers for an N x K matrix in `fmt`
+ * (layout above).  Host-only, no HIP call.  Errors: E_NULL, E_SHAPE,
+ * E_UNSUPPORTED. */
+int lowbit_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes,
+                        size_t* scale_bytes);
+
+/* Pack dense codes [N][K] (int8) and scales [N][G] (fp16 bits) into the
+ * layout above, writing every byte of pcodes/pscales (padding included).
+ * pcodes and pscales must be 16-byte aligned.  Codes outside the format's
+ * value set are counted into *bad_code_count (device int32, atomically
+ * added; pass NULL to skip); their packed value is unspecified.  The count is
+ * not cleared by the call. */
+int lowbit_pack(int fmt, int64_t N, int64_t K, const int8_t* codes,
+                const uint16_t* scales, void* pcodes, void* pscales,
+                int32_t* bad_code_count, void* stream);
+
+/* Inverse of lowbit_pack: writes codes [N][K] and scales [N][G].  A weight
+ * decoded from a reserved 2-bit pattern or an out-of-range base-3 byte is
+ * written as 0 and counted (one per weight) into *bad_code_count (device
+ * int32, atomically added, nullable). */
+int lowbit_unpack(int fmt, int64_t N, int64_t K, const void* pcodes,
+                  const void* pscales, int8_t* codes, uint16_t* scales,
+                  int32_t* bad_code_count, void* stream);
+
+/* Per-row absmax int8 quantization of bf16 X [M][K] (fp32 arithmetic, no
+ * fused operations): a = max_k |x|; if a == 0 then q = 0 and s_x = 0, else
+ * inv = 127.0f / a, q = clamp(rint(x * inv), -127, 127) with ties to even,
+ * s_x = a / 127.0f.  Writes Q [M][K] and s_x [M]. */
+int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
+                           int8_t* Q, float* s_x, void* stream);
+
+/* Batch-1 product y[n] = sum_k W[n][k] * x[k] for n < N.
+ *   x_dtype F32 / BF16: x holds K values.
+ *   x_dtype I8: x holds K int8 q; the result is multiplied by x_scale.
+ *   x_dtype SIGN1 (binary weights only): x holds K/8 bytes of sign bits;
+ *     the result is multiplied by x_scale (alpha).
+ *   y_dtype F32 or BF16 (round to nearest even).  y_dtype I32 is allowed
+ *   only for x_dtype I8 / SIGN1 with pscales == NULL: y = exact integer
+ *   sum_k code * q (or the signed bit agreement count), x_scale ignored.
+ * Alignment: pcodes, pscales, x 16 bytes; y 4 bytes.  Uses a per-stream
+ * device workspace owned by the library (allocated on first use on a stream;
+ * calls on one stream are ordered, calls on different streams do not share
+ * it). */
+int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
+                const void* pscales, int x_dtype, const void* x, float x_scale,
+                int y_dtype, void* y, void* stream);
+
+/* Product Y[m][n] = sum_k W[n][k] * X[m][k] for m < M, n < N.
+ *   x_dtype BF16: X bf16 [M][K], fp32 accumulation.
+ *   x_dtype I8: X int8 [M][K] (e.g. from lowbit_quantize_act_i8) with
+ *     x_scales[M] (device fp32); per 128-group integer sums are exact in int32
+ *     and Y[m][n] = x_scales[m] * sum_g scale[n][g] * A[m][n][g].
+ *     y_dtype I32 requires pscales == NULL and returns sum_g A[m][n][g].
+ *   y_dtype F32 or BF16 (or I32 as above).
+ * Alignment: pcodes, pscales, X, Y 16 bytes.  Uses the per-stream workspace
+ * described for lowbit_gemv. */
+int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
+                const void* pscales, int x_dtype, const void* X,
+                const float* x_scales, int y_dtype, void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */
