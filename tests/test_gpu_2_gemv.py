@@ -1,0 +1,177 @@
+"""lowbit_gemv / small-M lowbit_gemm on the GPU against the fp64 oracle.
+
+Float outputs must satisfy |y - y_ref| <= 1e-3 * sum_k |w x| per output
+(plus 2^-8 |y_ref| for bf16 outputs); integer outputs must be bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle as O
+from ultra_bit_dit_amd import lowbit as lb
+
+from helpers import SEED, assert_within, codes_for
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def make(fmt, N, K, seed=SEED, tid=1):
+    codes = codes_for(fmt, seed, tid, N, K)
+    scales = synth.group_scales(seed, tid + 1, N, K // 128)
+    pc, ps = lb.pack(fmt, dev(codes), dev(scales.view(np.int16)))
+    return codes, scales, pc, ps
+
+
+SHAPES = [(16, 128), (1, 128), (37, 384), (5, 1152), (33, 2048), (100, 640), (256, 1024), (48, 1664)]
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+def test_gemv_float_parity(fmt, N, K, xk):
+    print(f"gemv fmt={fmt} N={N} K={K} x={xk}", flush=True)
+    codes, scales, pc, ps = make(fmt, N, K)
+    if xk == "bf16":
+        x = synth.normal_bf16(SEED, 9, 1, K)
+        xt = dev(x.view(np.int16)).view(torch.bfloat16)[0]
+        kind = O.X_BF16
+    else:
+        x = synth.normal_f32(SEED, 9, 1, K)
+        xt = dev(x)[0]
+        kind = O.X_F32
+    yref, absY = O.matmul(codes, scales, kind, x)
+    y = lb.gemv(fmt, N, K, pc, ps, xt, y_dtype=lb.F32)
+    yb = lb.gemv(fmt, N, K, pc, ps, xt, y_dtype=lb.BF16)
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy()[None], yref, absY, what="f32 out")
+    assert_within(yb.float().cpu().numpy()[None], yref, absY, bf16_out=True, what="bf16 out")
+
+
+def test_c0_binary_256x1024_f32():
+    """Binary GEMV N=256, K=1024, fp32 activations N(0,1), scales U[0.01,0.1]."""
+    N, K = 256, 1024
+    codes, scales, pc, ps = make(1, N, K, seed=SEED, tid=1)
+    x = synth.normal_f32(SEED, 3, 1, K)
+    yref, absY = O.matmul(codes, scales, O.X_F32, x)
+    y = lb.gemv(1, N, K, pc, ps, dev(x)[0])
+    torch.cuda.synchronize()
+    worst = assert_within(y.cpu().numpy()[None], yref, absY, what="C0")
+    print(f"C0 worst err/tol = {worst:.3e}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("N,K", [(5120, 5120), (17408, 5120), (5120, 17408)])
+def test_full_size_shapes(fmt, N, K):
+    """27B-class layer shapes, weights generated on the device, full compare."""
+    print(f"gemv full fmt={fmt} N={N} K={K}", flush=True)
+    tern = fmt != 1
+    codes_t = synth.device_codes(tern, SEED + 1, 21, N, K, "cuda")
+    scales_t = synth.device_scales(SEED + 1, 22, N, K // 128, "cuda")
+    pc, ps = lb.pack(fmt, codes_t, scales_t)
+    del codes_t
+    x = synth.normal_bf16(SEED + 1, 23, 1, K)
+    y = lb.gemv(fmt, N, K, pc, ps, dev(x.view(np.int16)).view(torch.bfloat16)[0])
+    torch.cuda.synchronize()
+    codes = codes_for(fmt, SEED + 1, 21, N, K)
+    scales = synth.group_scales(SEED + 1, 22, N, K // 128)
+    yref, absY = O.matmul(codes, scales, O.X_BF16, x)
+    worst = assert_within(y.cpu().numpy()[None], yref, absY, what="full")
+    print(f"worst err/tol = {worst:.3e}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_dyadic_inputs_are_exact(fmt):
+    """Small-integer bf16 activations and power-of-two scales: the product is
+    exactly representable and the GPU result equals the oracle exactly."""
+    rng = np.random.default_rng(4)
+    N, K = 64, 1280
+    codes = codes_for(fmt, SEED, 31, N, K)
+    scales = np.asarray(2.0 ** rng.integers(-7, -2, size=(N, K // 128)), np.float16).view(np.uint16)
+    xv = rng.integers(-8, 9, size=(1, K)).astype(np.float32)
+    x = synth.f32_to_bf16_bits(xv)
+    pc, ps = lb.pack(fmt, dev(codes), dev(scales.view(np.int16)))
+    y = lb.gemv(fmt, N, K, pc, ps, dev(x.view(np.int16)).view(torch.bfloat16)[0])
+    yref = O.matmul(codes, scales, O.X_BF16, x, with_abs=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), yref[0])
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("N,K", [(37, 384), (5120, 5120)])
+def test_int8_activations(fmt, N, K):
+    codes, scales, pc, ps = make(fmt, N, K, tid=41)
+    xb = synth.normal_bf16(SEED, 43, 1, K)
+    q, sx = O.quantize_act_i8(xb)
+    qt = dev(q)[0]
+    # exact integer path: unit scales, int32 output
+    yi = lb.gemv(fmt, N, K, pc, None, qt, y_dtype=lb.I32, x_dtype=lb.I8)
+    A = O.group_int_sums(codes, q).sum(axis=2)[0]
+    # float path with the group scales and s_x
+    yf = lb.gemv(fmt, N, K, pc, ps, qt, x_scale=float(sx[0]), y_dtype=lb.F32, x_dtype=lb.I8)
+    torch.cuda.synchronize()
+    assert np.array_equal(yi.cpu().numpy().astype(np.int64), A)
+    yref, absY = O.matmul(codes, scales, O.X_I8, q, sx)
+    assert_within(yf.cpu().numpy()[None], yref, absY, what="i8 float")
+
+
+@pytest.mark.parametrize("N,K", [(37, 384), (256, 1024), (5120, 5120)])
+def test_sign_activations_xor_popcount(N, K):
+    codes, scales, pc, ps = make(1, N, K, tid=51)
+    xb = synth.sign_bits(SEED, 53, 1, K)
+    yi = lb.gemv(1, N, K, pc, None, dev(xb)[0], y_dtype=lb.I32, x_dtype=lb.SIGN1)
+    yf = lb.gemv(1, N, K, pc, ps, dev(xb)[0], x_scale=0.75, y_dtype=lb.F32, x_dtype=lb.SIGN1)
+    torch.cuda.synchronize()
+    Y, D = O.xor_popcount(codes, scales, xb, np.array([0.75], np.float32))
+    assert np.array_equal(yi.cpu().numpy().astype(np.int64), D[0])
+    _, absY = O.matmul(codes, scales, O.X_SIGN1, xb, np.array([0.75], np.float32))
+    assert_within(yf.cpu().numpy()[None], Y, absY, what="sign float")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_repeat_runs_bit_identical(fmt):
+    N, K = 5120, 5120
+    codes_t = synth.device_codes(fmt != 1, SEED, 61, N, K, "cuda")
+    pc, ps = lb.pack(fmt, codes_t, synth.device_scales(SEED, 62, N, K // 128, "cuda"))
+    x = dev(synth.normal_bf16(SEED, 63, 1, K).view(np.int16)).view(torch.bfloat16)[0]
+    y1 = lb.gemv(fmt, N, K, pc, ps, x)
+    y2 = lb.gemv(fmt, N, K, pc, ps, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_small_m_gemm_bf16(fmt, M):
+    """Small-M products (M = k+1 = 5 is a speculative-decoding verify pass)."""
+    N, K = 96, 1536
+    codes, scales, pc, ps = make(fmt, N, K, tid=71)
+    X = synth.normal_bf16(SEED, 73, M, K)
+    Xt = dev(X.view(np.int16)).view(torch.bfloat16)
+    Y = lb.gemm(fmt, M, N, K, pc, ps, Xt)
+    torch.cuda.synchronize()
+    yref, absY = O.matmul(codes, scales, O.X_BF16, X)
+    assert_within(Y.cpu().numpy(), yref, absY, what=f"M={M}")
+    if M == 1:
+        y = lb.gemv(fmt, N, K, pc, ps, Xt[0])
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0], y)
+
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_small_m_gemm_int8(M):
+    N, K = 80, 1024
+    codes, scales, pc, ps = make(2, N, K, tid=81)
+    Xb = synth.normal_bf16(SEED, 83, M, K)
+    Q, sx = lb.quantize_act_i8(dev(Xb.view(np.int16)).view(torch.bfloat16))
+    q_ref, sx_ref = O.quantize_act_i8(Xb)
+    Yi = lb.gemm(2, M, N, K, pc, None, Q, y_dtype=lb.I32)
+    Yf = lb.gemm(2, M, N, K, pc, ps, Q, x_scales=sx)
+    torch.cuda.synchronize()
+    assert np.array_equal(Q.cpu().numpy(), q_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(Yi.cpu().numpy().astype(np.int64), O.group_int_sums(codes, q_ref).sum(axis=2))
+    yref, absY = O.matmul(codes, scales, O.X_I8, q_ref, sx_ref)
+    assert_within(Yf.cpu().numpy(), yref, absY, what="i8 gemm")

@@ -1,0 +1,239 @@
+// C ABI of liblowbit: argument validation, dispatch and the per-stream
+// workspace.  Every check runs on the host before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/lowbit.h"
+#include "common.hpp"
+
+using namespace lowbit;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_fmt(int fmt) {
+  return fmt == LOWBIT_BINARY || fmt == LOWBIT_TERNARY_2BIT || fmt == LOWBIT_TERNARY_BASE3;
+}
+
+// N * K and derived sizes must stay far from int64 overflow
+bool shape_ok(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || K % kGroup != 0) return false;
+  if (N > (int64_t(1) << 40) || K > (int64_t(1) << 40)) return false;
+  if (N > (int64_t(1) << 62) / K) return false;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_E_HIP; }
+
+// ---- per-(device, stream) workspace, grown on demand.  Growing waits for the
+// stream (the old buffer may still be read by queued kernels), so a stream
+// being captured into a graph must already hold a large enough workspace.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int workspace(hipStream_t s, size_t need, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LOWBIT_E_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, s}];
+  if (w.bytes < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return LOWBIT_E_HIP;
+    if (cs != hipStreamCaptureStatusNone) return LOWBIT_E_NOMEM;
+    if (w.ptr) {
+      if (hipStreamSynchronize(s) != hipSuccess) return LOWBIT_E_HIP;
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    size_t sz = need < (1u << 20) ? (1u << 20) : need + need / 4;
+    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
+      w.ptr = nullptr;
+      return LOWBIT_E_NOMEM;
+    }
+    w.bytes = sz;
+  }
+  *out = w.ptr;
+  return LOWBIT_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int split_terms(int x_dtype) {
+  return x_dtype == LOWBIT_F32 ? kSplitF32 : x_dtype == LOWBIT_BF16 ? kSplitBF16 : kSplitI8;
+}
+
+// small-M product through the MFMA GEMV kernel (M * R <= 16 staged A rows)
+int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
+                  const void* pscales, int x_dtype, const void* x, float x_scale,
+                  const float* x_scales, int y_dtype, void* y, hipStream_t s) {
+  const int R = split_terms(x_dtype);
+  const int64_t G = K / kGroup, GQ = cdiv(G, 4);
+  // whole 4-group quads: the kernel reads a quad's 4 groups even past G
+  const size_t xa_bytes = align_up((size_t)GQ * 4 * kGroup * M * R, 256);
+  const size_t xe_bytes = (size_t)GQ * 4 * M * R * 4;
+  void* ws = nullptr;
+  int rc = workspace(s, xa_bytes + xe_bytes, &ws);
+  if (rc) return rc;
+  uint8_t* xa = (uint8_t*)ws;
+  uint32_t* xe = (uint32_t*)((uint8_t*)ws + xa_bytes);
+  hipError_t e = launch_stage_fp8(x_dtype, M, K, x, R, xa, xe, s);
+  if (e != hipSuccess) return LOWBIT_E_HIP;
+  GemvArgs g;
+  g.fmt = fmt;
+  g.N = N;
+  g.K = K;
+  g.M = M;
+  g.pcodes = pcodes;
+  g.pscales = (const uint16_t*)pscales;
+  g.xa = xa;
+  g.xe = xe;
+  g.R = R;
+  g.int_combine = x_dtype == LOWBIT_I8;
+  g.x_scale = (x_dtype == LOWBIT_I8) ? x_scale : 1.0f;
+  g.x_scales = x_scales;
+  g.ykind = y_dtype;
+  g.y = y;
+  return hip_status(launch_gemv_mfma(g, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_abi_version(void) { return LOWBIT_ABI_VERSION; }
+
+const char* lowbit_status_str(int status) {
+  switch (status) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_E_NULL: return "null pointer";
+    case LOWBIT_E_SHAPE: return "invalid shape (K must be a positive multiple of 128)";
+    case LOWBIT_E_ALIGN: return "misaligned pointer";
+    case LOWBIT_E_UNSUPPORTED: return "unsupported format / dtype combination";
+    case LOWBIT_E_BADCODE: return "invalid code";
+    case LOWBIT_E_HIP: return "HIP runtime error";
+    case LOWBIT_E_NOMEM: return "workspace allocation failed";
+  }
+  return "unknown status";
+}
+
+int lowbit_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
+  int64_t NB = cdiv(N, 16), G = K / kGroup;
+  int64_t c = fmt == LOWBIT_BINARY ? NB * cdiv(G, 4) * 1024
+              : fmt == LOWBIT_TERNARY_2BIT ? NB * cdiv(G, 2) * 1024
+                                           : NB * cdiv(G, 8) * 3328;
+  *code_bytes = (size_t)c;
+  *scale_bytes = (size_t)(NB * cdiv(G, 4) * 128);
+  return LOWBIT_OK;
+}
+
+int lowbit_pack(int fmt, int64_t N, int64_t K, const int8_t* codes, const uint16_t* scales,
+                void* pcodes, void* pscales, int32_t* bad_code_count, void* stream) {
+  if (!codes || !scales || !pcodes || !pscales) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
+  if (!aligned(pcodes, 16) || !aligned(pscales, 16) || !aligned(scales, 2) ||
+      (bad_code_count && !aligned(bad_code_count, 4)))
+    return LOWBIT_E_ALIGN;
+  return hip_status(launch_pack(fmt, N, K, codes, scales, pcodes, pscales, bad_code_count,
+                                (hipStream_t)stream));
+}
+
+int lowbit_unpack(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+                  int8_t* codes, uint16_t* scales, int32_t* bad_code_count, void* stream) {
+  if (!codes || !scales || !pcodes || !pscales) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
+  if (!aligned(pcodes, 16) || !aligned(pscales, 16) || !aligned(scales, 2) ||
+      (bad_code_count && !aligned(bad_code_count, 4)))
+    return LOWBIT_E_ALIGN;
+  return hip_status(launch_unpack(fmt, N, K, pcodes, pscales, codes, scales, bad_code_count,
+                                  (hipStream_t)stream));
+}
+
+int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16, int8_t* Q, float* s_x,
+                           void* stream) {
+  if (!X_bf16 || !Q || !s_x) return LOWBIT_E_NULL;
+  if (M < 1 || K < 1 || M > (int64_t(1) << 31) || K > (int64_t(1) << 40)) return LOWBIT_E_SHAPE;
+  if (!aligned(X_bf16, 2) || !aligned(s_x, 4)) return LOWBIT_E_ALIGN;
+  return hip_status(launch_quantize_i8(M, K, X_bf16, Q, s_x, (hipStream_t)stream));
+}
+
+int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+                int x_dtype, const void* x, float x_scale, int y_dtype, void* y, void* stream) {
+  if (!pcodes || !x || !y) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
+  const bool int_x = x_dtype == LOWBIT_I8 || x_dtype == LOWBIT_SIGN1;
+  if (x_dtype < LOWBIT_F32 || x_dtype > LOWBIT_SIGN1) return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_I32)
+    return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype == LOWBIT_I32 && !(int_x && pscales == nullptr)) return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype != LOWBIT_I32 && !pscales) return LOWBIT_E_NULL;
+  if (x_dtype == LOWBIT_SIGN1 && fmt != LOWBIT_BINARY) return LOWBIT_E_UNSUPPORTED;
+  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;  // packed format only for now
+  if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(x, 16) ||
+      !aligned(y, 4))
+    return LOWBIT_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (x_dtype == LOWBIT_SIGN1) {
+    const int64_t G = K / kGroup, GQ = cdiv(G, 4);
+    void* ws = nullptr;
+    int rc = workspace(s, (size_t)GQ * 16 * 4, &ws);
+    if (rc) return rc;
+    if (launch_stage_sign(1, K, (const uint8_t*)x, (uint32_t*)ws, s) != hipSuccess)
+      return LOWBIT_E_HIP;
+    SignArgs a;
+    a.N = N;
+    a.K = K;
+    a.M = 1;
+    a.pcodes = pcodes;
+    a.pscales = (const uint16_t*)pscales;
+    a.xw = (const uint32_t*)ws;
+    a.alpha = x_scale;
+    a.ykind = y_dtype;
+    a.y = y;
+    return hip_status(launch_gemv_sign(a, s));
+  }
+  return run_gemv_mfma(fmt, 1, N, K, pcodes, pscales, x_dtype, x, x_scale, nullptr, y_dtype, y,
+                       s);
+}
+
+int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+                int x_dtype, const void* X, const float* x_scales, int y_dtype, void* Y,
+                void* stream) {
+  if (!pcodes || !X || !Y) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K) || M < 1 || M > (int64_t(1) << 31)) return LOWBIT_E_SHAPE;
+  if (x_dtype != LOWBIT_BF16 && x_dtype != LOWBIT_I8) return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_I32)
+    return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype == LOWBIT_I32 && !(x_dtype == LOWBIT_I8 && pscales == nullptr))
+    return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype != LOWBIT_I32 && !pscales) return LOWBIT_E_NULL;
+  if (x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 && !x_scales) return LOWBIT_E_NULL;
+  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;
+  if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(X, 16) ||
+      !aligned(Y, 16) || (x_scales && !aligned(x_scales, 4)))
+    return LOWBIT_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int R = split_terms(x_dtype);
+  if (M * R <= 16)
+    return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
+                         x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
+                         y_dtype, Y, s);
+  return LOWBIT_E_UNSUPPORTED;  // large-M kernels are added in gemm.hip
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal definitions shared by the HIP sources of liblowbit (not part of
+// the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+constexpr int kGroup = 128;  // weights per FP16 scale
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// k offset inside a group of slot i (0..31) of quarter q (0..3): the order in
+// which the fp4 B operand of the 16x16x128 f8f6f4 MFMA consumes k relative
+// to the fp8 A operand (lane = row + 16 * quarter).
+__host__ __device__ inline int kmap(int q, int i) {
+  return 64 * (q & 1) + 16 * (q >> 1) + 32 * (i >> 4) + (i & 15);
+}
+
+// binary word: slot held by bit b (bit b lands in nibble b>>2 of fp4
+// register 3-(b&3) after the decode shift)
+__host__ __device__ inline int bin_slot(int b) { return 8 * (3 - (b & 3)) + (b >> 2); }
+
+// fp16 bit pattern (low 16 bits of h) -> fp32, exact
+__device__ inline float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
+// x staging parameters for the MFMA GEMV: number of fp8 split terms per
+// activation row and the exponent step between terms
+constexpr int kSplitBF16 = 2;
+constexpr int kSplitF32 = 4;
+constexpr int kSplitI8 = 2;
+constexpr int kSplitShift = 4;  // each term is scaled 2^-4 relative to the previous
+
+enum XKind { XK_F32 = 1, XK_BF16 = 2, XK_I8 = 3, XK_SIGN1 = 4 };
+enum YKind { YK_F32 = 1, YK_BF16 = 2, YK_I32 = 5 };
+
+// ------------------------------------------------------------ launchers
+// (host side, defined in the .hip files; every one returns a hipError_t)
+
+hipError_t launch_pack(int fmt, int64_t N, int64_t K, const int8_t* codes,
+                       const uint16_t* scales, void* pcodes, void* pscales,
+                       int32_t* bad, hipStream_t s);
+hipError_t launch_unpack(int fmt, int64_t N, int64_t K, const void* pcodes,
+                         const void* pscales, int8_t* codes, uint16_t* scales,
+                         int32_t* bad, hipStream_t s);
+hipError_t launch_quantize_i8(int64_t M, int64_t K, const uint16_t* X, int8_t* Q,
+                              float* sx, hipStream_t s);
+
+// fp8 split staging of M activation rows for the MFMA GEMV; writes
+// xa (K * M * R bytes) and xe (ceil(G/4) * 4 * M * R words)
+hipError_t launch_stage_fp8(int xkind, int64_t M, int64_t K, const void* X, int R,
+                            uint8_t* xa, uint32_t* xe, hipStream_t s);
+// sign bits permuted into the binary word order: M * G * 4 words
+hipError_t launch_stage_sign(int64_t M, int64_t K, const uint8_t* xbits, uint32_t* xw,
+                             hipStream_t s);
+
+struct GemvArgs {
+  int fmt;
+  int64_t N, K, M;       // M activation rows (1 for a GEMV)
+  const void* pcodes;
+  const uint16_t* pscales;  // NULL = unit scales
+  const uint8_t* xa;
+  const uint32_t* xe;
+  int R;                 // split terms per activation row
+  int int_combine;       // 1: the int8 path (terms recombine to an exact integer)
+  float x_scale;         // GEMV: multiply the result (I8 s_x); 1 otherwise
+  const float* x_scales; // per-row scales (small-M I8), or NULL
+  int ykind;
+  void* y;               // [M][N]
+};
+hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t s);
+
+struct SignArgs {
+  int64_t N, K, M;
+  const void* pcodes;
+  const uint16_t* pscales;
+  const uint32_t* xw;
+  float alpha;
+  int ykind;
+  void* y;
+};
+hipError_t launch_gemv_sign(const SignArgs& a, hipStream_t s);
+
+}  // namespace lowbit

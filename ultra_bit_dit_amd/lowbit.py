@@ -1,0 +1,149 @@
+"""Thin ctypes binding of liblowbit (include/lowbit.h).
+
+Argument marshalling only: torch tensors are passed as device pointers with
+the current HIP stream; every step runs in the library's HIP kernels.  The
+library must be built first (``python -m ultra_bit_dit_amd.build``); there is
+no fallback.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "liblowbit.so")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_BADCODE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+BINARY, TERNARY_2BIT, TERNARY_BASE3 = 1, 2, 3
+F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
+
+# every symbol the public header declares
+EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
+           "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm")
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"liblowbit is not built ({LIB_PATH} missing); "
+                               "run `python -m ultra_bit_dit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.lowbit_abi_version.restype = i32
+        L.lowbit_status_str.argtypes = [i32]
+        L.lowbit_status_str.restype = ctypes.c_char_p
+        L.lowbit_packed_bytes.argtypes = [i32, i64, i64, ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.lowbit_pack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.lowbit_unpack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.lowbit_quantize_act_i8.argtypes = [i64, i64, vp, vp, vp, vp]
+        L.lowbit_gemv.argtypes = [i32, i64, i64, vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
+        L.lowbit_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i32, vp, vp, i32, vp, vp]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().lowbit_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != OK:
+        raise LowbitError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def packed_bytes(fmt, N, K):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("lowbit_packed_bytes", lib().lowbit_packed_bytes(fmt, N, K, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def empty_packed(fmt, N, K, device="cuda"):
+    import torch
+    cb, sb = packed_bytes(fmt, N, K)
+    return (torch.empty(cb, dtype=torch.uint8, device=device),
+            torch.empty(sb // 2, dtype=torch.int16, device=device))
+
+
+def pack(fmt, codes, scales, pcodes=None, pscales=None, bad=None, stream=None):
+    """codes int8 [N][K], scales fp16 (or int16 bits) [N][K/128] -> packed tensors."""
+    N, K = codes.shape
+    if pcodes is None:
+        pcodes, pscales = empty_packed(fmt, N, K, codes.device)
+    _check("lowbit_pack", lib().lowbit_pack(fmt, N, K, _ptr(codes), _ptr(scales), _ptr(pcodes),
+                                            _ptr(pscales), _ptr(bad), _stream(stream)))
+    return pcodes, pscales
+
+
+def unpack(fmt, N, K, pcodes, pscales, bad=None, stream=None):
+    import torch
+    codes = torch.empty((N, K), dtype=torch.int8, device=pcodes.device)
+    scales = torch.empty((N, K // 128), dtype=torch.int16, device=pcodes.device)
+    _check("lowbit_unpack", lib().lowbit_unpack(fmt, N, K, _ptr(pcodes), _ptr(pscales), _ptr(codes),
+                                                _ptr(scales), _ptr(bad), _stream(stream)))
+    return codes, scales
+
+
+def quantize_act_i8(X, stream=None):
+    """bf16 X [M][K] -> (int8 Q [M][K], fp32 s_x [M])."""
+    import torch
+    M, K = X.shape
+    Q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check("lowbit_quantize_act_i8", lib().lowbit_quantize_act_i8(M, K, _ptr(X), _ptr(Q), _ptr(sx),
+                                                                  _stream(stream)))
+    return Q, sx
+
+
+def _xdt(x, x_dtype):
+    import torch
+    if x_dtype is not None:
+        return x_dtype
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: SIGN1}[x.dtype]
+
+
+def _ytorch(y_dtype):
+    import torch
+    return {F32: torch.float32, BF16: torch.bfloat16, I32: torch.int32}[y_dtype]
+
+
+def gemv(fmt, N, K, pcodes, pscales, x, x_scale=1.0, y_dtype=F32, y=None, x_dtype=None,
+         stream=None):
+    """y[n] = sum_k W[n][k] x[k] (see lowbit_gemv)."""
+    import torch
+    if y is None:
+        y = torch.empty(N, dtype=_ytorch(y_dtype), device=pcodes.device)
+    _check("lowbit_gemv", lib().lowbit_gemv(fmt, N, K, _ptr(pcodes), _ptr(pscales), _xdt(x, x_dtype),
+                                            _ptr(x), float(x_scale), y_dtype, _ptr(y), _stream(stream)))
+    return y
+
+
+def gemm(fmt, M, N, K, pcodes, pscales, X, x_scales=None, y_dtype=F32, Y=None, x_dtype=None,
+         stream=None):
+    """Y[m][n] = sum_k W[n][k] X[m][k] (see lowbit_gemm)."""
+    import torch
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_ytorch(y_dtype), device=pcodes.device)
+    _check("lowbit_gemm", lib().lowbit_gemm(fmt, M, N, K, _ptr(pcodes), _ptr(pscales), _xdt(X, x_dtype),
+                                            _ptr(X), _ptr(x_scales), y_dtype, _ptr(Y), _stream(stream)))
+    return Y
