@@ -32,6 +32,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_E_HIP
 // ---- per-(device, stream) workspace, grown on demand.  Growing waits for the
 // stream (the old buffer may still be read by queued kernels), so a stream
 // being captured into a graph must already hold a large enough workspace.
+// Its first kCounterBytes hold the fused GEMV's counters (zeroed here once;
+// every launch leaves them zero).
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -59,6 +61,8 @@ int workspace(hipStream_t s, size_t need, void** out) {
       w.ptr = nullptr;
       return LOWBIT_E_NOMEM;
     }
+    // the counter block must start at zero; kernels leave it zero
+    if (hipMemsetAsync(w.ptr, 0, kCounterBytes, s) != hipSuccess) return LOWBIT_E_HIP;
     w.bytes = sz;
   }
   *out = w.ptr;
@@ -67,26 +71,14 @@ int workspace(hipStream_t s, size_t need, void** out) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-int split_terms(int x_dtype) {
-  return x_dtype == LOWBIT_F32 ? kSplitF32 : x_dtype == LOWBIT_BF16 ? kSplitBF16 : kSplitI8;
-}
-
-// small-M product through the MFMA GEMV kernel (M * R <= 16 staged A rows)
+// small-M product through the fused MFMA GEMV kernel (M * R <= 16 rows of A)
 int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
                   const void* pscales, int x_dtype, const void* x, float x_scale,
                   const float* x_scales, int y_dtype, void* y, hipStream_t s) {
-  const int R = split_terms(x_dtype);
-  const int64_t G = K / kGroup, GQ = cdiv(G, 4);
-  // whole 4-group quads: the kernel reads a quad's 4 groups even past G
-  const size_t xa_bytes = align_up((size_t)GQ * 4 * kGroup * M * R, 256);
-  const size_t xe_bytes = (size_t)GQ * 4 * M * R * 4;
+  if (cdiv(N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
   void* ws = nullptr;
-  int rc = workspace(s, xa_bytes + xe_bytes, &ws);
+  int rc = workspace(s, gemv_workspace_bytes(fmt, N, K, M, x_dtype), &ws);
   if (rc) return rc;
-  uint8_t* xa = (uint8_t*)ws;
-  uint32_t* xe = (uint32_t*)((uint8_t*)ws + xa_bytes);
-  hipError_t e = launch_stage_fp8(x_dtype, M, K, x, R, xa, xe, s);
-  if (e != hipSuccess) return LOWBIT_E_HIP;
   GemvArgs g;
   g.fmt = fmt;
   g.N = N;
@@ -94,16 +86,17 @@ int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
   g.M = M;
   g.pcodes = pcodes;
   g.pscales = (const uint16_t*)pscales;
-  g.xa = xa;
-  g.xe = xe;
-  g.R = R;
-  g.int_combine = x_dtype == LOWBIT_I8;
+  g.xkind = x_dtype;
+  g.x = x;
   g.x_scale = (x_dtype == LOWBIT_I8) ? x_scale : 1.0f;
   g.x_scales = x_scales;
   g.ykind = y_dtype;
   g.y = y;
+  g.ws = ws;
   return hip_status(launch_gemv_mfma(g, s));
 }
+
+int max_small_m(int x_dtype) { return x_dtype == LOWBIT_F32 ? 16 / kSplitF32 : 16 / kSplitBF16; }
 
 }  // namespace
 
@@ -190,17 +183,17 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* p
   if (x_dtype == LOWBIT_SIGN1) {
     const int64_t G = K / kGroup, GQ = cdiv(G, 4);
     void* ws = nullptr;
-    int rc = workspace(s, (size_t)GQ * 16 * 4, &ws);
+    int rc = workspace(s, kCounterBytes + (size_t)GQ * 16 * 4, &ws);
     if (rc) return rc;
-    if (launch_stage_sign(1, K, (const uint8_t*)x, (uint32_t*)ws, s) != hipSuccess)
-      return LOWBIT_E_HIP;
+    uint32_t* xw = (uint32_t*)((uint8_t*)ws + kCounterBytes);
+    if (launch_stage_sign(1, K, (const uint8_t*)x, xw, s) != hipSuccess) return LOWBIT_E_HIP;
     SignArgs a;
     a.N = N;
     a.K = K;
     a.M = 1;
     a.pcodes = pcodes;
     a.pscales = (const uint16_t*)pscales;
-    a.xw = (const uint32_t*)ws;
+    a.xw = xw;
     a.alpha = x_scale;
     a.ykind = y_dtype;
     a.y = y;
@@ -228,8 +221,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
       !aligned(Y, 16) || (x_scales && !aligned(x_scales, 4)))
     return LOWBIT_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  const int R = split_terms(x_dtype);
-  if (M * R <= 16)
+  if (M <= max_small_m(x_dtype))
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);

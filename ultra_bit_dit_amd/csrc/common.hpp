@@ -56,28 +56,32 @@ hipError_t launch_unpack(int fmt, int64_t N, int64_t K, const void* pcodes,
 hipError_t launch_quantize_i8(int64_t M, int64_t K, const uint16_t* X, int8_t* Q,
                               float* sx, hipStream_t s);
 
-// fp8 split staging of M activation rows for the MFMA GEMV; writes
-// xa (K * M * R bytes) and xe (ceil(G/4) * 4 * M * R words)
-hipError_t launch_stage_fp8(int xkind, int64_t M, int64_t K, const void* X, int R,
-                            uint8_t* xa, uint32_t* xe, hipStream_t s);
 // sign bits permuted into the binary word order: M * G * 4 words
 hipError_t launch_stage_sign(int64_t M, int64_t K, const uint8_t* xbits, uint32_t* xw,
                              hipStream_t s);
 
+// Workspace of the fused GEMV: a fixed block of zero-initialised counters
+// (self-resetting: every launch leaves them zero) followed by the staged
+// activations and the split-K partial sums.
+constexpr int64_t kCounterWords = 65536;
+constexpr int64_t kCounterBytes = kCounterWords * 4;
+constexpr int64_t kMaxRowGroups = kCounterWords - 16;  // row groups of 64 rows
+
 struct GemvArgs {
   int fmt;
-  int64_t N, K, M;       // M activation rows (1 for a GEMV)
+  int64_t N, K, M;          // M activation rows (1 for a GEMV)
   const void* pcodes;
   const uint16_t* pscales;  // NULL = unit scales
-  const uint8_t* xa;
-  const uint32_t* xe;
-  int R;                 // split terms per activation row
-  int int_combine;       // 1: the int8 path (terms recombine to an exact integer)
-  float x_scale;         // GEMV: multiply the result (I8 s_x); 1 otherwise
-  const float* x_scales; // per-row scales (small-M I8), or NULL
+  int xkind;                // XK_F32 / XK_BF16 / XK_I8
+  const void* x;            // [M][K] activations
+  float x_scale;            // multiplies the result (I8 s_x of a GEMV); 1 otherwise
+  const float* x_scales;    // per-row result scales (small-M I8), or NULL
   int ykind;
-  void* y;               // [M][N]
+  void* y;                  // [M][N]
+  void* ws;                 // workspace (counters first)
 };
+// bytes of workspace the fused GEMV needs (counters included)
+size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind);
 hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t s);
 
 struct SignArgs {

@@ -21,12 +21,15 @@
 // one popcount give the exact signed agreement 32 - 2 * popcount(w ^ x)
 // (the XOR + popcount remark of the "1-bit 嘅數學" section of the
 // richmindsetzone.com 1-bit diffusion page).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace lowbit {
 namespace {
 
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = 16;  // waves per workgroup of the sign kernel
+constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
 
 template <int T>
 __device__ inline v4f mfma_group(const v8i& A, const v8i& B, int sa) {
@@ -41,138 +44,493 @@ __device__ inline uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-struct KArgs {
-  const void* pcodes;
-  const uint16_t* pscales;
-  const uint8_t* xa;
-  const uint32_t* xe;
-  const float* x_scales;
-  void* y;
-  int64_t N, G, GQ, GP, M, MA;
-  float x_scale;
-};
+// ------------------------------------------------------- activation staging
+// The MFMA multiplies fp4 weights (exactly +-1 / 0) by activations given as
+// fp8 e4m3 split terms.  For each 32-element hardware block, E is chosen so
+// the block maximum scaled by 2^-E lies in [128, 256); term 0 is
+// rne_e4m3(v), each next term is rne_e4m3 of 16 x the remaining residual,
+// and term r carries the E8M0 block exponent E - 4r, applied inside the
+// MFMA.  Two terms reproduce a bf16 value exactly for elements within 2^13 of
+// the block maximum (smaller ones keep an error below 2^-21 x the maximum);
+// four terms give fp32 inputs 16 significant bits.  int8 values q are split
+// exactly as 16 * (q >> 4) + (q & 15).  The conversions use the hardware
+// v_cvt_pk_fp8_f32 / v_cvt_f32_fp8 (OCP e4m3, round to nearest even).
+//
+// Hardware block b of a group covers MFMA positions h = 32b + i; position h
+// pairs with fp4 weight slot i of quarter b (activation k = 128g +
+// kmap(b, i)) and is fed by A byte e = 16(b>>1) + (i&15) of lane group
+// kb = 2(b&1) + (i>>4).  The scale of block b is read from lane group b.
+//
+// Each workgroup stages the quads of its K-slice into LDS (MA = M x R rows
+// of A, ql = quad index inside the slice):
+//   xa[((ql * 16 + t * 4 + kb) * MA + a) * 32 + e]   fp8 bytes (group t of the quad)
+//   xe[((ql * 4 + b) * MA + a) * 4 + t]             E8M0 exponents
 
-// FMT 1 binary, 2 ternary 2-bit.  R split terms per activation row (2 or 4).
-// INTC: terms recombine to an exact integer (int8 activations).
-template <int FMT, int R, bool INTC, int YK>
-__global__ __launch_bounds__(1024) void gemv_mfma(KArgs a) {
-  constexpr int NX = 4 / R;  // activation rows per lane group
-  __shared__ float red_f[kMaxWaves][64][NX];
-  __shared__ int red_i[kMaxWaves][64][NX];
-
-  const int L = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int S = blockDim.x >> 6;
-  const int r = L & 15, lg = L >> 4;
-  const int64_t rb = blockIdx.x;
-  const int64_t q0 = (a.GQ * w) / S, q1 = (a.GQ * (w + 1)) / S;
-  const bool arow = r < a.MA;
-
-  float acc[NX];
-  int iacc[NX];
+__device__ inline void load8(int xkind, const void* X, int64_t idx, float (&v)[8]) {
+  if (xkind == XK_BF16) {
+    const uint4 w = *(const uint4*)((const uint16_t*)X + idx);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int j = 0; j < NX; j++) {
-    acc[j] = 0.f;
-    iacc[j] = 0;
-  }
-
-  const uint4* pc4 = (const uint4*)a.pcodes;
-  const uint2* ps2 = (const uint2*)a.pscales;
-  const uint4* xa4 = (const uint4*)a.xa;
-
-  for (int64_t gq = q0; gq < q1; gq++) {
-    // ---- loads for 4 groups
-    uint4 cw0, cw1;
-    if (FMT == 1) {
-      cw0 = pc4[(rb * a.GQ + gq) * 64 + L];
-      cw1 = make_uint4(0, 0, 0, 0);
-    } else {
-      cw0 = pc4[(rb * a.GP + 2 * gq) * 64 + L];
-      cw1 = (2 * gq + 1 < a.GP) ? pc4[(rb * a.GP + 2 * gq + 1) * 64 + L] : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 4; j++) {
+      v[2 * j] = __uint_as_float(u[j] << 16);
+      v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
     }
-    uint2 sc = a.pscales ? ps2[(rb * a.GQ + gq) * 16 + r] : make_uint2(0x3C003C00u, 0x3C003C00u);
-    uint4 av[8];
-    uint32_t se = 127u * 0x01010101u;
-    if (arow) {
+  } else if (xkind == XK_F32) {
+    const float4 a = *(const float4*)((const float*)X + idx);
+    const float4 b = *(const float4*)((const float*)X + idx + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint2 w = *(const uint2*)((const int8_t*)X + idx);
 #pragma unroll
-      for (int t = 0; t < 4; t++) {
-        int64_t base = ((4 * gq + t) * 4 + lg) * a.MA + r;
-        av[2 * t] = xa4[base * 2];
-        av[2 * t + 1] = xa4[base * 2 + 1];
-      }
-      se = a.xe[(gq * 4 + lg) * a.MA + r];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; t++) av[t] = make_uint4(0, 0, 0, 0);
-    }
-    const int ng = (int)min<int64_t>(4, a.G - 4 * gq);
-
-    // ---- 4 groups: decode, MFMA, scale epilogue
-#define LOWBIT_GROUP(T)                                                                     \
-  if (T < ng) {                                                                             \
-    uint32_t d0, d1, d2, d3;                                                                \
-    if (FMT == 1) {                                                                         \
-      uint32_t wv = T == 0 ? cw0.x : T == 1 ? cw0.y : T == 2 ? cw0.z : cw0.w;               \
-      d0 = (wv & 0x88888888u) | 0x22222222u;                                                \
-      d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;                                         \
-      d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;                                         \
-      d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;                                         \
-    } else {                                                                                \
-      uint32_t p0 = T == 0 ? cw0.x : T == 1 ? cw0.z : T == 2 ? cw1.x : cw1.z;               \
-      uint32_t p1 = T == 0 ? cw0.y : T == 1 ? cw0.w : T == 2 ? cw1.y : cw1.w;               \
-      d0 = p0 & 0xAAAAAAAAu;                                                                \
-      d1 = (p0 << 1) & 0xAAAAAAAAu;                                                         \
-      d2 = p1 & 0xAAAAAAAAu;                                                                \
-      d3 = (p1 << 1) & 0xAAAAAAAAu;                                                         \
-    }                                                                                       \
-    v8i B = {(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};                               \
-    uint4 x0 = av[2 * T], x1 = av[2 * T + 1];                                               \
-    v8i A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,                                    \
-             (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};                                   \
-    v4f c = mfma_group<T>(A, B, (int)se);                                                   \
-    uint32_t sh = (T < 2 ? sc.x : sc.y) >> (16 * (T & 1));                                  \
-    float s = f16_bits_to_f32(sh);                       \
-    _Pragma("unroll") for (int j = 0; j < NX; j++) {                                        \
-      float t = c[R * j];                                                                   \
-      _Pragma("unroll") for (int i = 1; i < R; i++) t += c[R * j + i];                      \
-      acc[j] = fmaf(s, t, acc[j]);                                                          \
-      if (INTC) iacc[j] += __float2int_rn(t);                                               \
-    }                                                                                       \
-  }
-    LOWBIT_GROUP(0)
-    LOWBIT_GROUP(1)
-    LOWBIT_GROUP(2)
-    LOWBIT_GROUP(3)
-#undef LOWBIT_GROUP
-  }
-
-  // ---- split-K reduction over the waves, fixed order
-#pragma unroll
-  for (int j = 0; j < NX; j++) {
-    red_f[w][L][j] = acc[j];
-    red_i[w][L][j] = iacc[j];
-  }
-  __syncthreads();
-  if (w != 0) return;
-#pragma unroll
-  for (int j = 0; j < NX; j++) {
-    float f = red_f[0][L][j];
-    int iv = red_i[0][L][j];
-    for (int ww = 1; ww < S; ww++) {
-      f += red_f[ww][L][j];
-      iv += red_i[ww][L][j];
-    }
-    const int64_t m = (int64_t)lg * NX + j;  // activation row
-    const int64_t n = rb * 16 + r;
-    if (m < a.M && n < a.N) {
-      float sxm = a.x_scales ? a.x_scales[m] : a.x_scale;
-      if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = f * sxm;
-      else if (YK == YK_BF16) ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(f * sxm);
-      else ((int32_t*)a.y)[m * a.N + n] = iv;
-    }
+    for (int j = 0; j < 8; j++)
+      v[j] = (float)(int8_t)(((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFF);
   }
 }
 
+struct FArgs {
+  const uint8_t* pcodes;
+  const uint16_t* pscales;
+  const void* x;
+  const float* x_scales;
+  void* y;
+  float* part;    // split-K partial sums [KS][M][Npad]
+  uint32_t* cnt;  // [16 + rg]: arrivals of the row group's K-slices
+  int64_t N, K, G, GQ, GP, M, MA, NB, KS, Npad;
+  float x_scale;
+  int xkind;
+};
+
+// Staging of quads [q0, q1) of the M activation rows into LDS by all threads
+// of the workgroup.  Work unit = 8 consecutive elements of a hardware block
+// (the 4 units of a block sit in adjacent lanes); a thread handles units
+// c = threadIdx + round * blockDim.  The loads of the first kStageRounds
+// rounds are issued together (stage_load) so that they share one memory
+// round trip with the weight loads; stage_convert then writes the terms.
+constexpr int kStageRounds = 5;
+
+__device__ __attribute__((always_inline)) inline bool stage_unit(const FArgs& a, int64_t q0,
+                                                                 int64_t nq, int64_t c, int& ch,
+                                                                 int& b, int& t, int64_t& ql,
+                                                                 int64_t& m, int64_t& g) {
+  ch = (int)(c & 3);
+  b = (int)((c >> 2) & 3);
+  t = (int)((c >> 4) & 3);
+  const int64_t rest = c >> 6;
+  ql = rest % nq;
+  m = rest / nq;
+  g = 4 * (q0 + ql) + t;
+  return c < nq * 64 * a.M && g < a.G;
+}
+
+// raw activations of one unit: bf16 in ra, f32 in ra:rb, int8 in ra.xy.
+// The load is unconditional (a unit past the end reads element 0) so that
+// no control flow joins wait on it.
+template <int XK>
+__device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a, int64_t q0,
+                                                                  int64_t nq, int64_t rd,
+                                                                  uint4& ra, uint4& rb) {
+  const int64_t c = rd * blockDim.x + threadIdx.x;
+  int ch, b, t;
+  int64_t ql, m, g;
+  const bool valid = stage_unit(a, q0, nq, c, ch, b, t, ql, m, g);
+  const int64_t idx = valid ? m * a.K + g * kGroup + kmap(b, 8 * ch) : 0;
+  if constexpr (XK == XK_BF16) {
+    ra = *(const uint4*)((const uint16_t*)a.x + idx);
+    rb = ra;
+  } else if constexpr (XK == XK_F32) {
+    ra = *(const uint4*)((const float*)a.x + idx);
+    rb = *(const uint4*)((const float*)a.x + idx + 4);
+  } else {
+    const uint2 w = *(const uint2*)((const int8_t*)a.x + idx);
+    ra = make_uint4(w.x, w.y, w.x, w.y);
+    rb = ra;
+  }
+}
+
+// convert one round of units into fp8 terms and exponents in LDS
+template <int R, int XK>
+__device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs& a, int64_t q0,
+                                                                     int64_t nq, int64_t rd,
+                                                                     uint4 ra, uint4 rb,
+                                                                     uint8_t* xa, uint8_t* xe) {
+  if (rd * blockDim.x >= nq * 64 * a.M) return;  // uniform: round past the end
+  const int64_t c = rd * blockDim.x + threadIdx.x;
+  int ch, b, t;
+  int64_t ql, m, g;
+  const bool valid = stage_unit(a, q0, nq, c, ch, b, t, ql, m, g);
+  const bool inside = c < nq * 64 * a.M;  // a slot of the slice (padding groups get zeros)
+  float v[8];
+  if constexpr (XK == XK_BF16) {
+    const uint32_t u[4] = {ra.x, ra.y, ra.z, ra.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[2 * j] = __uint_as_float(u[j] << 16);
+      v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+    }
+  } else if constexpr (XK == XK_F32) {
+    v[0] = __uint_as_float(ra.x); v[1] = __uint_as_float(ra.y);
+    v[2] = __uint_as_float(ra.z); v[3] = __uint_as_float(ra.w);
+    v[4] = __uint_as_float(rb.x); v[5] = __uint_as_float(rb.y);
+    v[6] = __uint_as_float(rb.z); v[7] = __uint_as_float(rb.w);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      v[j] = (float)(int8_t)(((j < 4 ? ra.x : ra.y) >> (8 * (j & 3))) & 0xFF);
+  }
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));  // the 4 units of a block
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  if (!inside) return;
+  int E = 0;
+  if (XK != XK_I8 && amax != 0.0f) {
+    int ex;
+    frexpf(amax, &ex);
+    E = (ex - 1) - 7;
+    const int lo = -127 + kSplitShift * (R - 1);
+    if (E < lo) E = lo;
+  }
+  const int kb = 2 * (b & 1) + (ch >> 1), e = 16 * (b >> 1) + 8 * (ch & 1);
+  float tv[8];
+  if constexpr (XK == XK_I8) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) tv[j] = v[j];
+  } else {
+    // exact power of two: E is clamped to [-127 + 4(R-1), 120]
+    const float sc = ldexpf(1.0f, -E);
+#pragma unroll
+    for (int j = 0; j < 8; j++) tv[j] = v[j] * sc;
+  }
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    uint32_t w0, w1;
+    int Er;
+    if constexpr (XK == XK_I8) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int q = (int)tv[j];
+        p[j] = (float)(r == 0 ? (q >> 4) : (q & 15));
+      }
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w0, true);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], w1, true);
+      Er = r == 0 ? 4 : 0;
+    } else {
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[0], tv[1], 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[2], tv[3], w0, true);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[4], tv[5], 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[6], tv[7], w1, true);
+      if (r + 1 < R) {  // residual for the next term, exact in fp32
+        const float d[8] = {
+            __builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
+            __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3),
+            __builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
+            __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
+#pragma unroll
+        for (int j = 0; j < 8; j++) tv[j] = (tv[j] - d[j]) * 16.0f;
+      }
+      Er = E - kSplitShift * r;
+    }
+    const int64_t arow = m * R + r;
+    *(uint2*)(xa + ((ql * 16 + t * 4 + kb) * a.MA + arow) * 32 + e) = make_uint2(w0, w1);
+    if (ch == 0) xe[((ql * 4 + b) * a.MA + arow) * 4 + t] = (uint8_t)(127 + Er);
+  }
+}
+
+// --------------------------------------------------------------- MFMA GEMV
+// Workgroup = W waves, one row-block (16 rows) per wave, all on one K-slice of
+// up to QM whole 4-group quads.  Every wave issues the loads of all its codes
+// and scales at once, then the workgroup stages the slice's activations into
+// LDS while those loads are in flight; one staged group of activations feeds
+// the MFMAs of all W row-blocks.  With several K-slices, each workgroup
+// writes coherent partial sums and the last workgroup of the row group to
+// arrive adds them in slice order.
+template <int FMT, int XK, int MX, int YK, int QM>
+__global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr bool INTC = XK == XK_I8;
+  constexpr int NC = FMT == 1 ? 1 : 2;  // 16-byte code vectors per quad
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint32_t s_last;
+  const int W = blockDim.x >> 6;
+  const int L = threadIdx.x & 63, w = threadIdx.x >> 6, r = L & 15, lg = L >> 4;
+  const int64_t rg = blockIdx.x / a.KS, ks = blockIdx.x % a.KS;
+  const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
+  const int nq = (int)(q1 - q0);
+  const int64_t rb = (int64_t)W * rg + w;  // this wave's row-block
+  const bool live = rb < a.NB;
+  const bool arow = r < a.MA;
+  uint8_t* xa = smem;
+  uint8_t* xe = smem + (int64_t)nq * 16 * a.MA * 32;
+  // 32 zero bytes + one word of unit exponents, read by lanes that hold no
+  // activation row (their A operand is zero)
+  uint8_t* zblk = xe + (int64_t)nq * 16 * a.MA;
+  if (threadIdx.x < 9) ((uint32_t*)zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
+
+  // activation loads of the first staging rounds go out first
+  uint4 ra[kStageRounds], rbv[kStageRounds];
+#pragma unroll
+  for (int k = 0; k < kStageRounds; k++) stage_load1<XK>(a, q0, nq, k, ra[k], rbv[k]);
+
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4* pcv = (const u4*)a.pcodes;
+  const uint2* ps2 = (const uint2*)a.pscales;
+  u4 cw[QM][NC];
+  uint2 sc[QM];
+  // Every code and scale of the wave is requested before anything else.  The
+  // loads are unconditional (clamped to the last valid block, results of
+  // clamped loads are never used) so that none of them waits on another.
+  const bool unit_scales = a.pscales == nullptr;
+  const uint2* sbase = unit_scales ? (const uint2*)a.pcodes : ps2;  // any readable memory
+  const int64_t rbc = live ? rb : a.NB - 1;
+#pragma unroll
+  for (int q = 0; q < QM; q++) {
+    const int64_t gq = min<int64_t>(q0 + q, a.GQ - 1);
+    if constexpr (FMT == 1) {
+      cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GQ + gq) * 64 + L]);
+    } else {
+      const int64_t p0 = 2 * gq, p1 = min<int64_t>(2 * gq + 1, a.GP - 1);
+      cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p0) * 64 + L]);
+      cw[q][NC - 1] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p1) * 64 + L]);
+    }
+    sc[q] = sbase[(rbc * a.GQ + gq) * 16 + r];
+  }
+#pragma unroll
+  for (int k = 0; k < kStageRounds; k++) stage_convert1<R, XK>(a, q0, nq, k, ra[k], rbv[k], xa, xe);
+  // remaining rounds (small-M products with long slices), loaded and converted in turn
+  const int64_t rounds = cdiv(nq * 64 * a.M, (int64_t)blockDim.x);
+  for (int64_t rd = kStageRounds; rd < rounds; rd++) {
+    uint4 r0, r1;
+    stage_load1<XK>(a, q0, nq, rd, r0, r1);
+    stage_convert1<R, XK>(a, q0, nq, rd, r0, r1, xa, xe);
+  }
+  __syncthreads();
+
+  float acc[MX];
+  int iacc[MX];
+#pragma unroll
+  for (int j = 0; j < MX; j++) {
+    acc[j] = 0.f;
+    iacc[j] = 0;
+  }
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < QM; q++) {
+      if (q < nq) {
+        // the 4 groups of the quad: operands first, then 4 independent MFMAs,
+        // then the epilogues (padding groups have zero activations)
+        const uint32_t se = *(const uint32_t*)(arow ? xe + ((q * 4 + lg) * a.MA + r) * 4 : zblk + 32);
+        v8i A[4], B[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const uint4* src =
+              (const uint4*)(arow ? xa + ((q * 16 + t * 4 + lg) * a.MA + r) * 32 : zblk);
+          const uint4 x0 = src[0], x1 = src[1];
+          A[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          uint32_t d0, d1, d2, d3;
+          if constexpr (FMT == 1) {
+            const u4 c4 = cw[q][0];
+            const uint32_t wv = t == 0 ? c4.x : t == 1 ? c4.y : t == 2 ? c4.z : c4.w;
+            d0 = (wv & 0x88888888u) | 0x22222222u;
+            d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;
+            d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;
+            d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;
+          } else {
+            const u4 c4 = cw[q][(t >> 1) % NC];
+            const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
+            d0 = p0 & 0xAAAAAAAAu;
+            d1 = (p0 << 1) & 0xAAAAAAAAu;
+            d2 = p1 & 0xAAAAAAAAu;
+            d3 = (p1 << 1) & 0xAAAAAAAAu;
+          }
+          B[t] = v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
+        }
+        v4f c[4];
+        c[0] = mfma_group<0>(A[0], B[0], (int)se);
+        c[1] = mfma_group<1>(A[1], B[1], (int)se);
+        c[2] = mfma_group<2>(A[2], B[2], (int)se);
+        c[3] = mfma_group<3>(A[3], B[3], (int)se);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const float s = unit_scales
+                              ? 1.0f
+                              : f16_bits_to_f32((t < 2 ? sc[q].x : sc[q].y) >> (16 * (t & 1)));
+#pragma unroll
+          for (int j = 0; j < MX; j++) {
+            float tsum = c[t][R * j];
+#pragma unroll
+            for (int i = 1; i < R; i++) tsum += c[t][R * j + i];
+            acc[j] = fmaf(s, tsum, acc[j]);
+            if (INTC) iacc[j] += __float2int_rn(tsum);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- output
+  auto store = [&](int64_t m, int64_t n, float f, int iv) {
+    const float sxm = a.x_scales ? a.x_scales[m] : a.x_scale;
+    if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = f * sxm;
+    else if (YK == YK_BF16) ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(f * sxm);
+    else ((int32_t*)a.y)[m * a.N + n] = iv;
+  };
+  constexpr bool IPART = INTC && YK == YK_I32;
+  const int64_t n = 16 * rb + r;
+  if (a.KS == 1) {
+#pragma unroll
+    for (int j = 0; j < MX; j++) {
+      const int64_t m = (int64_t)lg * (4 / R) + j;
+      if (live && m < a.M && n < a.N) store(m, n, acc[j], iacc[j]);
+    }
+    return;
+  }
+  // partials: write-through (agent-coherent) stores, completed before the
+  // workgroup's arrival is counted
+#pragma unroll
+  for (int j = 0; j < MX; j++) {
+    const int64_t m = (int64_t)lg * (4 / R) + j;
+    if (live && m < a.M) {
+      float* dst = a.part + (ks * a.M + m) * a.Npad + n;
+      if (IPART) __hip_atomic_store((int*)dst, iacc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.cnt + 16 + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_last != (uint32_t)(a.KS - 1)) return;
+  // last arrival: add the slices in order (coherent loads) and store
+#pragma unroll
+  for (int j = 0; j < MX; j++) {
+    const int64_t m = (int64_t)lg * (4 / R) + j;
+    if (live && m < a.M && n < a.N) {
+      float f = 0.f;
+      int iv = 0;
+      for (int64_t k2 = 0; k2 < a.KS; k2++) {
+        float* src = a.part + (k2 * a.M + m) * a.Npad + n;
+        if (IPART) iv += __hip_atomic_load((int*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else f += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      store(m, n, f, iv);
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.cnt + 16 + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct Plan {
+  int64_t NB, NRG, G, GQ, GP, KS, Npad, MA;
+  int R, W, QM;
+  size_t lds, part_off, bytes;
+};
+
+int split_terms(int xkind) { return xkind == XK_F32 ? kSplitF32 : kSplitBF16; }
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
+constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
+
+Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
+  Plan p;
+  p.R = split_terms(xkind);
+  p.MA = M * p.R;
+  p.NB = cdiv(N, 16);
+  p.G = K / kGroup;
+  p.GQ = cdiv(p.G, 4);
+  p.GP = cdiv(p.G, 2);
+  p.QM = fmt == 1 ? kQuadsBinary : kQuadsTernary;
+  // staged activations of a slice stay within 48 KiB of LDS
+  const int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (48 * 1024) / (16 * p.MA * 33)));
+  p.KS = cdiv(p.GQ, qcap);
+  // 4 waves per workgroup: 64 rows share one staged slice, and the slice's
+  // activation loads fit in the hoisted staging rounds
+  p.W = kMaxW;
+  p.NRG = cdiv(p.NB, p.W);
+  const int64_t qmax = cdiv(p.GQ, p.KS);
+  p.lds = (size_t)qmax * 16 * p.MA * 32 + (size_t)qmax * 16 * p.MA + 48;
+  p.Npad = p.NRG * p.W * 16;
+  p.part_off = kCounterBytes;
+  p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
+  return p;
+}
+
+template <int FMT, int XK, int MX, int QM>
+hipError_t launch_y(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, size_t lds,
+                    hipStream_t s) {
+  if (g.ykind == YK_F32)
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_F32, QM>), grid, block, lds, s, k);
+  else if (g.ykind == YK_BF16)
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_BF16, QM>), grid, block, lds, s, k);
+  else
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_I32, QM>), grid, block, lds, s, k);
+  return hipGetLastError();
+}
+
+template <int FMT, int QM>
+hipError_t launch_x(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, size_t lds,
+                    hipStream_t s) {
+  if (g.xkind == XK_F32) return launch_y<FMT, XK_F32, 1, QM>(g, k, grid, block, lds, s);
+  if (g.xkind == XK_I8)
+    return g.M == 1 ? launch_y<FMT, XK_I8, 1, QM>(g, k, grid, block, lds, s)
+                    : launch_y<FMT, XK_I8, 2, QM>(g, k, grid, block, lds, s);
+  return g.M == 1 ? launch_y<FMT, XK_BF16, 1, QM>(g, k, grid, block, lds, s)
+                  : launch_y<FMT, XK_BF16, 2, QM>(g, k, grid, block, lds, s);
+}
+
+}  // namespace
+
+size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
+  return make_plan(fmt, N, K, M, xkind).bytes;
+}
+
+hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
+  const Plan p = make_plan(g.fmt, g.N, g.K, g.M, g.xkind);
+  if (p.NRG > kMaxRowGroups || p.lds > 64 * 1024) return hipErrorInvalidValue;
+  FArgs k;
+  k.pcodes = (const uint8_t*)g.pcodes;
+  k.pscales = g.pscales;
+  k.x = g.x;
+  k.x_scales = g.x_scales;
+  k.y = g.y;
+  k.part = (float*)((uint8_t*)g.ws + p.part_off);
+  k.cnt = (uint32_t*)g.ws;
+  k.N = g.N;
+  k.K = g.K;
+  k.G = p.G;
+  k.GQ = p.GQ;
+  k.GP = p.GP;
+  k.M = g.M;
+  k.MA = p.MA;
+  k.NB = p.NB;
+  k.KS = p.KS;
+  k.Npad = p.Npad;
+  k.x_scale = g.x_scale;
+  k.xkind = g.xkind;
+  const dim3 grid((unsigned)(p.NRG * p.KS)), block((unsigned)(64 * p.W));
+  if (g.fmt == 1) return launch_x<1, kQuadsBinary>(g, k, grid, block, p.lds, s);
+  if (g.fmt == 2) return launch_x<2, kQuadsTernary>(g, k, grid, block, p.lds, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_sign(const SignArgs& g, hipStream_t s);
+
+}  // namespace lowbit
+
+namespace lowbit {
+namespace {
 // ------------------------------------------------------------ sign path
 struct SArgs {
   const void* pcodes;
@@ -241,48 +599,7 @@ int pick_waves(int64_t NB, int64_t GQ) {
   return (int)S;
 }
 
-template <int FMT, int R, bool INTC>
-hipError_t dispatch_y(const GemvArgs& g, const KArgs& k, dim3 grid, dim3 block, hipStream_t s) {
-  if (g.ykind == YK_F32)
-    hipLaunchKernelGGL((gemv_mfma<FMT, R, INTC, YK_F32>), grid, block, 0, s, k);
-  else if (g.ykind == YK_BF16)
-    hipLaunchKernelGGL((gemv_mfma<FMT, R, INTC, YK_BF16>), grid, block, 0, s, k);
-  else
-    hipLaunchKernelGGL((gemv_mfma<FMT, R, INTC, YK_I32>), grid, block, 0, s, k);
-  return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t dispatch_r(const GemvArgs& g, const KArgs& k, dim3 grid, dim3 block, hipStream_t s) {
-  if (g.R == 4) return dispatch_y<FMT, 4, false>(g, k, grid, block, s);
-  if (g.int_combine) return dispatch_y<FMT, 2, true>(g, k, grid, block, s);
-  return dispatch_y<FMT, 2, false>(g, k, grid, block, s);
-}
-
 }  // namespace
-
-hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
-  KArgs k;
-  int64_t NB = cdiv(g.N, 16), G = g.K / kGroup;
-  k.pcodes = g.pcodes;
-  k.pscales = g.pscales;
-  k.xa = g.xa;
-  k.xe = g.xe;
-  k.x_scales = g.x_scales;
-  k.y = g.y;
-  k.N = g.N;
-  k.G = G;
-  k.GQ = cdiv(G, 4);
-  k.GP = cdiv(G, 2);
-  k.M = g.M;
-  k.MA = g.M * g.R;
-  k.x_scale = g.x_scale;
-  int S = pick_waves(NB, k.GQ);
-  dim3 grid((unsigned)NB), block(64 * S);
-  if (g.fmt == 1) return dispatch_r<1>(g, k, grid, block, s);
-  if (g.fmt == 2) return dispatch_r<2>(g, k, grid, block, s);
-  return hipErrorInvalidValue;
-}
 
 hipError_t launch_gemv_sign(const SignArgs& g, hipStream_t s) {
   SArgs k;
