@@ -96,6 +96,30 @@ int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
   return hip_status(launch_gemv_mfma(g, s));
 }
 
+// large-M product through the staged-tile MFMA GEMM
+int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+             int x_dtype, const void* X, const float* x_scales, int y_dtype, void* Y,
+             hipStream_t s) {
+  if (cdiv(N, 16) > (int64_t(1) << 40) / 16) return LOWBIT_E_SHAPE;
+  void* ws = nullptr;
+  int rc = workspace(s, gemm_workspace_bytes(M, N, K, x_dtype), &ws);
+  if (rc) return rc;
+  GemmArgs g;
+  g.fmt = fmt;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.pcodes = pcodes;
+  g.pscales = (const uint16_t*)pscales;
+  g.xkind = x_dtype;
+  g.x = X;
+  g.x_scales = x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr;
+  g.ykind = y_dtype;
+  g.y = Y;
+  g.ws = ws;
+  return hip_status(launch_gemm(g, s));
+}
+
 int max_small_m(int x_dtype) { return x_dtype == LOWBIT_F32 ? 16 / kSplitF32 : 16 / kSplitBF16; }
 
 }  // namespace
@@ -225,7 +249,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
-  return LOWBIT_E_UNSUPPORTED;  // large-M kernels are added in gemm.hip
+  return run_gemm(fmt, M, N, K, pcodes, pscales, x_dtype, X, x_scales, y_dtype, Y, s);
 }
 
 }  // extern "C"

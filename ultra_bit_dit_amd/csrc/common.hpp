@@ -95,4 +95,21 @@ struct SignArgs {
 };
 hipError_t launch_gemv_sign(const SignArgs& a, hipStream_t s);
 
+// Large-M GEMM (activations staged into per-(row tile, group) tiles in the
+// workspace, then MFMA over decoded weight registers)
+struct GemmArgs {
+  int fmt;
+  int64_t M, N, K;
+  const void* pcodes;
+  const uint16_t* pscales;  // NULL only for the exact int32 product
+  int xkind;                // XK_BF16 or XK_I8
+  const void* x;            // [M][K]
+  const float* x_scales;    // per-row scales of int8 activations (scaled outputs)
+  int ykind;
+  void* y;                  // [M][N]
+  void* ws;                 // workspace (counters first)
+};
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int xkind);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
 }  // namespace lowbit
