@@ -1,17 +1,25 @@
 #!/usr/bin/env python3
-"""Benchmark: batch-1 decode through a 27B-class stack of low-bit layers.
+"""Benchmark of the group-scaled binary / ternary matmul on one MI355X.
 
-One step = one token through 64 layers; each layer runs the batch-1 products
-of its projections in the order a decoder layer uses them: q/k/v (one fused
-15360 x 5120 matrix), o (5120 x 5120), gate/up (one fused 34816 x 5120
-matrix) and down (5120 x 17408), with group-128 fp16 scales and bf16
-activations.  All weights (3.35 GB binary, 6.33 GB ternary 2-bit) are
+Headline (``value``): batch-1 decode through a 27B-class stack of low-bit
+layers.  One step = one token through 64 layers; each layer runs the batch-1
+products of its projections in the order a decoder layer uses them: q/k/v
+(one fused 15360 x 5120 matrix), o (5120 x 5120), gate/up (one fused
+34816 x 5120 matrix) and down (5120 x 17408), with group-128 fp16 scales and
+bf16 activations.  All weights (3.35 GB binary, 6.33 GB ternary 2-bit) are
 resident in HBM; the step is captured once as a HIP graph and replayed.
+``value`` is packed-weight GB/s (weights + scales read per step / step time).
 
-Prints one JSON line (see --help for options).  The CPU-baseline leg times
-the fp64 oracle on one layer of the same workload.
+Also reported: the pp512 prefill pass (M = 512 tokens through the same four
+ternary layer products, bf16 activations and int8 activations) and the
+diffusion-transformer block GEMMs (binary, M = 4608 and 18432) in TFLOP/s;
+the roofline of the decode kernel (HBM) with its measured HBM traffic; and
+the fp64 oracle timed on the host as a CPU baseline.
+
+Prints one JSON line (see --help for options).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -20,34 +28,44 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_PEAK_F16_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA
+MFMA_PEAK_I8_TOPS = 5033.2     # dense int8 MFMA
 LAYERS = 64
 HIDDEN, FFN = 5120, 17408
 # (name, N, K) of the per-layer products, fused where the inputs are shared
 MATS = [("qkv", 3 * HIDDEN, HIDDEN), ("o", HIDDEN, HIDDEN), ("gateup", 2 * FFN, HIDDEN),
         ("down", HIDDEN, FFN)]
+# diffusion-transformer block: q, k, v, out (3072^2), FFN up 3072 -> 9216, down 9216 -> 3072
+DIT = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("out", 3072, 3072),
+       ("up", 9216, 3072), ("down", 3072, 9216)]
 FMT_NAMES = {1: "binary", 2: "ternary-2bit", 3: "ternary-base3"}
-SEED = 1002  # 1000 + config index of the decode-step workload
+SEED = 1002  # decode-step workload
+PP_SEED, DIT_SEED = 1003, 1004
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_decode_step_pmc.txt")
+GEMV_SOURCE = os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", "gemv.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def build_mats(lb, synth, fmt, seed, tid0, shapes, chunk_rows=2048):
+    out = []
+    for j, (name, N, K) in enumerate(shapes):
+        tid = tid0 + 2 * j
+        codes = synth.device_codes(fmt != 1, seed, tid, N, K, "cuda", chunk_rows=chunk_rows)
+        scales = synth.device_scales(seed, tid + 1, N, K // 128, "cuda")
+        out.append(lb.pack(fmt, codes, scales))
+        del codes, scales
+    return out
+
+
 def build_model(lb, synth, torch, fmt, layers):
-    tern = fmt != 1
     W = []
     t0 = time.time()
     for l in range(layers):
-        mats = []
-        for j, (name, N, K) in enumerate(MATS):
-            tid = 16 * l + 2 * j
-            codes = synth.device_codes(tern, SEED, tid, N, K, "cuda", chunk_rows=2048)
-            scales = synth.device_scales(SEED, tid + 1, N, K // 128, "cuda")
-            pc, ps = lb.pack(fmt, codes, scales)
-            del codes, scales
-            mats.append((pc, ps))
-        W.append(mats)
+        W.append(build_mats(lb, synth, fmt, SEED, 16 * l, MATS))
         if l % 16 == 15:
             torch.cuda.synchronize()
             log(f"  built {l + 1}/{layers} layers ({time.time() - t0:.1f}s)")
@@ -55,19 +73,149 @@ def build_model(lb, synth, torch, fmt, layers):
     return W
 
 
-def packed_step_bytes(lb, fmt, layers):
+def packed_bytes(lb, fmt, shapes):
     tot = 0
-    for _, N, K in MATS:
+    for _, N, K in shapes:
         cb, sb = lb.packed_bytes(fmt, N, K)
         tot += cb + sb
-    return tot * layers
+    return tot
 
 
-def run_step(lb, torch, fmt, W, xs, ys, layers):
+def run_step(lb, fmt, W, xs, ys, layers):
     for l in range(layers):
         for j, (name, N, K) in enumerate(MATS):
             pc, ps = W[l][j]
             lb.gemv(fmt, N, K, pc, ps, xs[j], y=ys[j], y_dtype=lb.F32)
+
+
+def time_region(torch, stream, fn, steps, warmup):
+    """Warm-up, then `steps` calls bracketed by synchronisations; HIP events
+    on `stream` (the stream every launch goes to).  Returns ms per call."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def pmc_traffic(launch_bytes):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    counter summary, scaled by the same counters read on a plain copy of
+    known size; None when the summary is missing or the kernel source changed
+    since the counters were taken."""
+    try:
+        kv = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        with open(GEMV_SOURCE, "rb") as f:
+            src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+        if kv.get("gemv_source_sha256_16") != src_hash:
+            return None, "kernel changed since the counters were taken"
+        copy_bytes = float(kv["copy_bytes_each_way"])
+        f_scale = copy_bytes / (float(kv["copy_FETCH_SIZE_KiB"]) * 1024.0)
+        w_scale = copy_bytes / (float(kv["copy_WRITE_SIZE_KiB"]) * 1024.0)
+        fetch = float(kv["gemv_FETCH_SIZE_KiB_per_dispatch"]) * 1024.0 * f_scale
+        write = float(kv["gemv_WRITE_SIZE_KiB_per_dispatch"]) * 1024.0 * w_scale
+        return fetch + write, (f"rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a "
+                               f"{copy_bytes / 2**20:.0f} MiB copy (x{f_scale:.3f} / x{w_scale:.3f}); "
+                               f"{(fetch + write) / launch_bytes:.3f} x the algorithmic bytes")
+    except (OSError, KeyError, ValueError):
+        return None, "no counter summary"
+
+
+def copy_calibration(torch):
+    """A plain elementwise copy of known size (read 256 MiB, write 256 MiB):
+    the reference the HBM byte counters are scaled by."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_decode(args, lb, synth, torch, np):
+    fmt, layers = args.fmt, args.layers
+    log(f"building {layers} layers, {FMT_NAMES[fmt]}")
+    W = build_model(lb, synth, torch, fmt, layers)
+    xs = [torch.from_numpy(synth.normal_bf16(SEED, 900 + j, 1, K).view(np.int16)).cuda()
+          .view(torch.bfloat16)[0] for j, (_, _, K) in enumerate(MATS)]
+    ys = [torch.empty(N, dtype=torch.float32, device="cuda") for _, N, _ in MATS]
+    step_bytes = packed_bytes(lb, fmt, MATS) * layers
+    launches = len(MATS) * layers
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run_step(lb, fmt, W, xs, ys, layers)  # eager warm-up (allocates the workspace)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run_step(lb, fmt, W, xs, ys, layers)
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(lb, fmt, W, xs, ys, layers)
+
+    t0 = time.perf_counter()
+    ms = time_region(torch, stream, step, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"decode step {ms:.3f} ms, {gbs:.0f} GB/s, {1000 / ms:.1f} tok/s (wall {wall:.2f}s)")
+    launch_bytes = step_bytes / launches
+    launch_us = ms * 1e3 / launches
+    traffic, tnote = pmc_traffic(launch_bytes)
+    roof = {"bound": "hbm", "kernel": "gemv_mfma (ternary 2-bit, bf16 x, fp32 y)" if fmt == 2
+            else "gemv_mfma (binary, bf16 x, fp32 y)",
+            "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(launch_bytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "algorithmic_bytes_per_launch": round(launch_bytes),
+            "avg_launch_us": round(launch_us, 3),
+            "note": f"{launches} launches per step averaged over the timed region (HIP events, "
+                    f"graph replay); traffic: {tnote}"}
+    del W
+    torch.cuda.synchronize()
+    return ms, gbs, step_bytes, roof, graph is not None
+
+
+def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
+    """One pass = every GEMM of `shapes` at M rows (activation staging and,
+    for int8, per-token quantization included).  Returns (ms, TFLOP/s)."""
+    mats = build_mats(lb, synth, fmt, seed, 0, shapes)
+    Xs = [torch.from_numpy(synth.normal_bf16(seed, 700 + j, M, K).view(np.int16)).cuda()
+          .view(torch.bfloat16) for j, (_, _, K) in enumerate(shapes)]
+    Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in shapes]
+    Qs = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _, _, K in shapes]
+    Ss = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in shapes]
+
+    def one():
+        for j, (name, N, K) in enumerate(shapes):
+            pc, ps = mats[j]
+            if xkind == "i8":
+                lb.quantize_act_i8(Xs[j], Q=Qs[j], s_x=Ss[j])
+                lb.gemm(fmt, M, N, K, pc, ps, Qs[j], x_scales=Ss[j], Y=Ys[j])
+            else:
+                lb.gemm(fmt, M, N, K, pc, ps, Xs[j], Y=Ys[j])
+
+    stream = torch.cuda.Stream()
+    ms = time_region(torch, stream, one, reps, 2)
+    flops = sum(2.0 * M * N * K for _, N, K in shapes)
+    del mats, Xs, Ys, Qs, Ss
+    torch.cuda.synchronize()
+    return ms, flops / (ms * 1e-3) / 1e12
 
 
 def cpu_baseline(fmt, budget_s):
@@ -101,19 +249,23 @@ def cpu_baseline(fmt, budget_s):
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--fmt", type=int, default=2, choices=[1, 2])
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(every box has one MI355X)", file=sys.stderr)
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the "
+              "kernels run on one device's share; multi-GPU sharding is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -122,46 +274,8 @@ def main():
     import synth
     from ultra_bit_dit_amd import lowbit as lb
 
-    fmt, layers = args.fmt, args.layers
-    log(f"building {layers} layers, {FMT_NAMES[fmt]}")
-    W = build_model(lb, synth, torch, fmt, layers)
-    xs = [torch.from_numpy(synth.normal_bf16(SEED, 900 + j, 1, K).view(np.int16)).cuda()
-          .view(torch.bfloat16)[0] for j, (_, _, K) in enumerate(MATS)]
-    ys = [torch.empty(N, dtype=torch.float32, device="cuda") for _, N, _ in MATS]
-    step_bytes = packed_step_bytes(lb, fmt, layers)
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        run_step(lb, torch, fmt, W, xs, ys, layers)  # eager warm-up (allocates the workspace)
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            run_step(lb, torch, fmt, W, xs, ys, layers)
-        torch.cuda.synchronize()
-
-    def step():
-        if graph is not None:
-            graph.replay()
-        else:
-            run_step(lb, torch, fmt, W, xs, ys, layers)
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step:.3f} ms, {gbs:.0f} GB/s, {1000 / ms_step:.1f} tok/s (wall {wall:.2f}s)")
+    copy_calibration(torch)
+    ms, gbs, step_bytes, roof, graphed = bench_decode(args, lb, synth, torch, np)
 
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",
@@ -170,22 +284,40 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"27B-class decode step, {FMT_NAMES[fmt]}: {layers} layers x "
+        "config": {"workload": f"27B-class decode step, {FMT_NAMES[args.fmt]}: {args.layers} layers x "
                                "(qkv 15360x5120, o 5120x5120, gate/up 34816x5120, down 5120x17408), "
                                "group-128 fp16 scales, bf16 activations, batch 1",
-                   "tok_s": round(1000.0 / ms_step, 2),
+                   "tok_s": round(1000.0 / ms, 2),
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                    "bytes_per_step": step_bytes,
-                   "graph": graph is not None},
+                   "graph": graphed},
+        "roofline": roof,
     }
+    if not args.no_gemm:
+        pp = {}
+        for xk, peak in (("bf16", MFMA_PEAK_F16_TFLOPS), ("i8", MFMA_PEAK_I8_TOPS)):
+            pms, tf = bench_gemm_pass(lb, synth, torch, np, 2, 512, MATS, PP_SEED, xk, args.gemm_reps)
+            log(f"pp512 {xk}: {pms:.3f} ms per layer, {tf:.1f} TFLOP/s")
+            pp[xk] = {"ms_per_layer": round(pms, 4), "tflops": round(tf, 1),
+                      "pct_mfma_peak": round(100 * tf / peak, 1),
+                      "tok_s_64_layers": round(512 / (pms * LAYERS * 1e-3), 1)}
+        out["config"]["pp512_ternary"] = pp
+        dit = {}
+        for M in (4608, 18432):
+            dms, tf = bench_gemm_pass(lb, synth, torch, np, 1, M, DIT, DIT_SEED, "bf16",
+                                      max(2, args.gemm_reps // (M // 4608)))
+            log(f"DiT block M={M}: {dms:.3f} ms, {tf:.1f} TFLOP/s")
+            dit[str(M)] = {"ms_per_block": round(dms, 4), "tflops": round(tf, 1),
+                           "pct_mfma_peak": round(100 * tf / MFMA_PEAK_F16_TFLOPS, 1)}
+        out["config"]["dit_block_binary_bf16"] = dit
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(fmt, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(args.fmt, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

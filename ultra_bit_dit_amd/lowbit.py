@@ -104,12 +104,15 @@ def unpack(fmt, N, K, pcodes, pscales, bad=None, stream=None):
     return codes, scales
 
 
-def quantize_act_i8(X, stream=None):
-    """bf16 X [M][K] -> (int8 Q [M][K], fp32 s_x [M])."""
+def quantize_act_i8(X, Q=None, s_x=None, stream=None):
+    """bf16 X [M][K] -> (int8 Q [M][K], fp32 s_x [M]); Q and s_x may be given."""
     import torch
     M, K = X.shape
-    Q = torch.empty((M, K), dtype=torch.int8, device=X.device)
-    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    if Q is None:
+        Q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if s_x is None:
+        s_x = torch.empty(M, dtype=torch.float32, device=X.device)
+    sx = s_x
     _check("lowbit_quantize_act_i8", lib().lowbit_quantize_act_i8(M, K, _ptr(X), _ptr(Q), _ptr(sx),
                                                                   _stream(stream)))
     return Q, sx
