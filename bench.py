@@ -6,9 +6,13 @@ layers.  One step = one token through 64 layers; each layer runs the batch-1
 products of its projections in the order a decoder layer uses them: q/k/v
 (one fused 15360 x 5120 matrix), o (5120 x 5120), gate/up (one fused
 34816 x 5120 matrix) and down (5120 x 17408), with group-128 fp16 scales and
-bf16 activations.  All weights (3.35 GB binary, 6.33 GB ternary 2-bit) are
-resident in HBM; the step is captured once as a HIP graph and replayed.
-``value`` is packed-weight GB/s (weights + scales read per step / step time).
+bf16 activations (a fixed synthetic x per shape, outputs not fed back).  All
+weights (3.35 GB binary, 6.33 GB ternary 2-bit) are resident in HBM.  By
+default the step is one persistent launch (lowbit_chain_run) that streams
+the weights of all 256 products; the same step with sequential dependencies
+between products, and as 256 separate launches in a HIP graph, is reported
+beside it.  ``value`` is packed-weight GB/s (weights + scales read per step /
+step time).
 
 Also reported: the pp512 prefill pass (M = 512 tokens through the same four
 ternary layer products, bf16 activations and int8 activations) and the
@@ -104,7 +108,7 @@ def time_region(torch, stream, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def pmc_traffic(launch_bytes):
+def pmc_traffic(launch_bytes, kernel):
     """HBM bytes per launch of the decode kernel from the committed rocprofv3
     counter summary, scaled by the same counters read on a plain copy of
     known size; None when the summary is missing or the kernel source changed
@@ -118,7 +122,7 @@ def pmc_traffic(launch_bytes):
                     kv[k.strip()] = v.strip()
         with open(GEMV_SOURCE, "rb") as f:
             src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-        if kv.get("gemv_source_sha256_16") != src_hash:
+        if kv.get("gemv_source_sha256_16") != src_hash or kv.get("kernel") != kernel:
             return None, "kernel changed since the counters were taken"
         copy_bytes = float(kv["copy_bytes_each_way"])
         f_scale = copy_bytes / (float(kv["copy_FETCH_SIZE_KiB"]) * 1024.0)
@@ -142,53 +146,77 @@ def copy_calibration(torch):
     del src, dst
 
 
+def chain_for(lb, fmt, W, xs, ys, layers, wait):
+    stages = []
+    for l in range(layers):
+        for j, (name, N, K) in enumerate(MATS):
+            stages.append((fmt, N, K, W[l][j][0], W[l][j][1], xs[j], ys[j], wait))
+    return lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+
+
 def bench_decode(args, lb, synth, torch, np):
+    """Times the decode step three ways (see --modes):
+    chain      one persistent launch per step streams all 4 x layers products
+               (the products of this workload are independent: fixed x per shape);
+    chain_dep  the same launch with every product waiting for the previous one
+               to complete before reading its activations (sequential decode);
+    separate   one lowbit_gemv launch per product, the step captured as a HIP graph.
+    The first mode listed is the headline."""
     fmt, layers = args.fmt, args.layers
+    modes = [m for m in args.modes.split(",") if m]
     log(f"building {layers} layers, {FMT_NAMES[fmt]}")
     W = build_model(lb, synth, torch, fmt, layers)
     xs = [torch.from_numpy(synth.normal_bf16(SEED, 900 + j, 1, K).view(np.int16)).cuda()
           .view(torch.bfloat16)[0] for j, (_, _, K) in enumerate(MATS)]
     ys = [torch.empty(N, dtype=torch.float32, device="cuda") for _, N, _ in MATS]
     step_bytes = packed_bytes(lb, fmt, MATS) * layers
-    launches = len(MATS) * layers
-
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        run_step(lb, fmt, W, xs, ys, layers)  # eager warm-up (allocates the workspace)
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            run_step(lb, fmt, W, xs, ys, layers)
-        torch.cuda.synchronize()
-
-    def step():
-        if graph is not None:
-            graph.replay()
+    res = {}
+    for mode in modes:
+        if mode in ("chain", "chain_dep"):
+            ch = chain_for(lb, fmt, W, xs, ys, layers, 1 if mode == "chain_dep" else 0)
+            ms = time_region(torch, stream, lambda: ch.run(stream), args.steps, args.warmup)
+            if ch.failed_waits():
+                raise RuntimeError("chain wait gave up")
+            ch.close()
+            res[mode] = (ms, 1)
+        elif mode == "separate":
+            with torch.cuda.stream(stream):
+                run_step(lb, fmt, W, xs, ys, layers)  # eager warm-up (allocates the workspace)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                run_step(lb, fmt, W, xs, ys, layers)
+            torch.cuda.synchronize()
+            ms = time_region(torch, stream, graph.replay, args.steps, args.warmup)
+            del graph
+            res[mode] = (ms, len(MATS) * layers)
         else:
-            run_step(lb, fmt, W, xs, ys, layers)
-
-    t0 = time.perf_counter()
-    ms = time_region(torch, stream, step, args.steps, args.warmup)
-    wall = time.perf_counter() - t0
+            raise SystemExit(f"unknown mode {mode}")
+        log(f"decode [{mode}] {ms:.3f} ms/step, {step_bytes / ms / 1e6:.0f} GB/s, "
+            f"{1000 / ms:.1f} tok/s")
+    head = modes[0]
+    ms, launches = res[head]
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"decode step {ms:.3f} ms, {gbs:.0f} GB/s, {1000 / ms:.1f} tok/s (wall {wall:.2f}s)")
     launch_bytes = step_bytes / launches
     launch_us = ms * 1e3 / launches
-    traffic, tnote = pmc_traffic(launch_bytes)
-    roof = {"bound": "hbm", "kernel": "gemv_mfma (ternary 2-bit, bf16 x, fp32 y)" if fmt == 2
-            else "gemv_mfma (binary, bf16 x, fp32 y)",
+    traffic, tnote = pmc_traffic(launch_bytes, "gemv_chain" if head.startswith("chain") else "gemv_mfma")
+    kname = ("gemv_chain" if head.startswith("chain") else "gemv_mfma") + \
+        (" (ternary 2-bit" if fmt == 2 else " (binary") + ", bf16 x, fp32 y)"
+    roof = {"bound": "hbm", "kernel": kname,
             "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(launch_bytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
             "algorithmic_bytes_per_launch": round(launch_bytes),
             "avg_launch_us": round(launch_us, 3),
-            "note": f"{launches} launches per step averaged over the timed region (HIP events, "
-                    f"graph replay); traffic: {tnote}"}
+            "note": f"{launches} launch(es) per step, durations from HIP events over the timed "
+                    f"region; traffic: {tnote}"}
+    modes_out = {m: {"ms_per_step": round(v[0], 4), "gb_s": round(step_bytes / v[0] / 1e6, 1),
+                     "tok_s": round(1000.0 / v[0], 2), "launches_per_step": v[1]}
+                 for m, v in res.items()}
     del W
     torch.cuda.synchronize()
-    return ms, gbs, step_bytes, roof, graph is not None
+    return ms, gbs, step_bytes, roof, head, modes_out
 
 
 def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
@@ -259,7 +287,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--modes", default="chain,chain_dep,separate",
+                    help="decode-step modes to time, headline first (chain, chain_dep, separate)")
     ap.add_argument("--no-gemm", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -275,7 +304,7 @@ def main():
     from ultra_bit_dit_amd import lowbit as lb
 
     copy_calibration(torch)
-    ms, gbs, step_bytes, roof, graphed = bench_decode(args, lb, synth, torch, np)
+    ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
 
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",
@@ -296,7 +325,8 @@ def main():
                    "tok_s": round(1000.0 / ms, 2),
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                    "bytes_per_step": step_bytes,
-                   "graph": graphed},
+                   "mode": head,
+                   "decode_modes": modes_out},
         "roofline": roof,
     }
     if not args.no_gemm:

@@ -189,6 +189,48 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* X,
                 const float* x_scales, int y_dtype, void* Y, void* stream);
 
+/* ---- chains of batch-1 products in one persistent launch ------------------
+ * Batch-1 decode streams every weight of every layer once per token and is
+ * bound by memory bandwidth, so the cost that matters is the one paid per
+ * token (speed section of the prismml.com Ternary Bonsai 2 announcement).
+ * A chain runs a fixed list of batch-1 products of one weight format as one
+ * cooperative launch whose workgroups stream the weights of later products
+ * while earlier ones finish.  Stage i with wait_prev != 0 reads its x only
+ * after every output of stage i-1 has been written (so x may be, or be
+ * computed from, an earlier stage's y); its weights may be read earlier.
+ * Outputs are written with device-coherent stores. */
+typedef struct lowbit_gemv_stage {
+  int fmt;              /* LOWBIT_BINARY or LOWBIT_TERNARY_2BIT, equal for all stages */
+  int64_t N, K;         /* W is N x K, K % 128 == 0                                */
+  const void* pcodes;   /* packed codes (16-byte aligned)                          */
+  const void* pscales;  /* packed fp16 scales (16-byte aligned)                    */
+  const void* x;        /* K activations of the chain's x_dtype (16-byte aligned)  */
+  void* y;              /* N outputs of the chain's y_dtype (4-byte aligned)        */
+  int wait_prev;        /* 1: read x only after stage i-1 is complete               */
+} lowbit_gemv_stage;
+
+typedef struct lowbit_chain lowbit_chain; /* opaque */
+
+/* Plan a chain of n_stages products on the current device: copies the stage
+ * list (pointers are used as given at every run), allocates the chain's
+ * device descriptors, counters and split-K partial sums (owned by the chain
+ * until lowbit_chain_destroy).  x_dtype F32 or BF16; y_dtype F32 or BF16.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_HIP, E_NOMEM. */
+int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dtype,
+                        int y_dtype, lowbit_chain** chain);
+
+/* Run every stage once, asynchronously on `stream`.  Runs of one chain must
+ * not overlap (they share its counters); run it on one stream at a time. */
+int lowbit_chain_run(lowbit_chain* chain, void* stream);
+
+/* Synchronous: *failed_waits != 0 if a stage ever gave up waiting for its
+ * predecessor (a bounded wait of about a second; its outputs are then not
+ * meaningful).  Never expected when runs do not overlap. */
+int lowbit_chain_status(lowbit_chain* chain, int* failed_waits);
+
+/* Frees the chain's device memory (synchronizes the device first). */
+int lowbit_chain_destroy(lowbit_chain* chain);
+
 #ifdef __cplusplus
 }
 #endif

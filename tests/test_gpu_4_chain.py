@@ -1,0 +1,105 @@
+"""Chains of batch-1 products in one persistent launch (lowbit_chain_*).
+
+A chain without waits must reproduce separate lowbit_gemv calls bit for bit
+(the same per-item arithmetic); a chain whose stage i reads stage i-1's
+output as its activations must match the oracle applied stage by stage to
+the GPU's own intermediate outputs, and must equal the separate calls on
+those same intermediates."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle as O
+from ultra_bit_dit_amd import lowbit as lb
+
+from helpers import SEED, assert_within, codes_for
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def make(fmt, N, K, tid):
+    codes = codes_for(fmt, SEED, tid, N, K)
+    scales = synth.group_scales(SEED, tid + 1, N, K // 128)
+    pc, ps = lb.pack(fmt, dev(codes), dev(scales.view(np.int16)))
+    return codes, scales, pc, ps
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("wait", [0, 1])
+def test_chain_matches_separate_calls(fmt, wait):
+    shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560)]
+    mats, xs, ys = [], [], []
+    for j, (N, K) in enumerate(shapes):
+        _, _, pc, ps = make(fmt, N, K, tid=200 + 2 * j)
+        mats.append((pc, ps))
+        xs.append(dev(synth.normal_bf16(SEED, 230 + j, 1, K).view(np.int16)).view(torch.bfloat16)[0])
+        ys.append(torch.full((N,), float("nan"), device="cuda"))
+    stages = [(fmt, N, K, mats[j][0], mats[j][1], xs[j], ys[j], wait)
+              for j, (N, K) in enumerate(shapes)]
+    chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+    for rep in range(3):  # counters must be left at zero by every run
+        for y in ys:
+            y.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        for j, (N, K) in enumerate(shapes):
+            ref = lb.gemv(fmt, N, K, mats[j][0], mats[j][1], xs[j])
+            torch.cuda.synchronize()
+            assert torch.equal(ys[j], ref), f"stage {j} run {rep}"
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_chain_dependent_stages(fmt):
+    """x of stage i is y of stage i-1 (fp32): each stage must wait for the
+    whole previous product."""
+    dims = [1024, 640, 5120, 384, 256]
+    mats, codes, scales = [], [], []
+    for j in range(len(dims) - 1):
+        K, N = dims[j], dims[j + 1]
+        c, s, pc, ps = make(fmt, N, K, tid=260 + 2 * j)
+        mats.append((pc, ps))
+        codes.append(c)
+        scales.append(s)
+    x0 = synth.normal_f32(SEED, 290, 1, dims[0])
+    bufs = [dev(x0)[0]] + [torch.full((d,), float("nan"), device="cuda") for d in dims[1:]]
+    stages = [(fmt, dims[j + 1], dims[j], mats[j][0], mats[j][1], bufs[j], bufs[j + 1], 1)
+              for j in range(len(dims) - 1)]
+    chain = lb.Chain(stages, x_dtype=lb.F32, y_dtype=lb.F32)
+    for rep in range(3):
+        for b in bufs[1:]:
+            b.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        outs = [b.cpu().numpy() for b in bufs]
+        for j in range(len(dims) - 1):
+            xin = outs[j][None].astype(np.float32)
+            yref, absY = O.matmul(codes[j], scales[j], O.X_F32, xin)
+            assert_within(outs[j + 1][None], yref, absY, what=f"stage {j} run {rep}")
+            sep = lb.gemv(fmt, dims[j + 1], dims[j], mats[j][0], mats[j][1], bufs[j])
+            torch.cuda.synchronize()
+            assert torch.equal(sep, bufs[j + 1])
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
+def test_chain_rejects_bad_stages():
+    _, _, pc, ps = make(1, 64, 256, tid=300)
+    x = torch.zeros(256, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(64, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:
+        lb.Chain([(1, 64, 200, pc, ps, x, y, 0)])
+    assert e.value.status == lb.E_SHAPE
+    _, _, pc2, ps2 = make(2, 64, 256, tid=302)
+    with pytest.raises(lb.LowbitError) as e:
+        lb.Chain([(1, 64, 256, pc, ps, x, y, 0), (2, 64, 256, pc2, ps2, x, y, 1)])
+    assert e.value.status == lb.E_UNSUPPORTED
+    with pytest.raises(lb.LowbitError) as e:
+        lb.Chain([(1, 64, 256, pc, ps, x, y, 0)], x_dtype=lb.I8)
+    assert e.value.status == lb.E_UNSUPPORTED

@@ -5,6 +5,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/lowbit.h"
 #include "common.hpp"
@@ -250,6 +251,56 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
   return run_gemm(fmt, M, N, K, pcodes, pscales, x_dtype, X, x_scales, y_dtype, Y, s);
+}
+
+struct lowbit_chain {
+  void* plan;
+};
+
+int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dtype, int y_dtype,
+                        lowbit_chain** chain) {
+  if (!stages || !chain) return LOWBIT_E_NULL;
+  *chain = nullptr;
+  if (n_stages < 1) return LOWBIT_E_SHAPE;
+  if (x_dtype != LOWBIT_F32 && x_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
+  if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
+  const int fmt = stages[0].fmt;
+  if (fmt != LOWBIT_BINARY && fmt != LOWBIT_TERNARY_2BIT) return LOWBIT_E_UNSUPPORTED;
+  std::vector<ChainStage> st(n_stages);
+  for (int i = 0; i < n_stages; i++) {
+    const lowbit_gemv_stage& g = stages[i];
+    if (g.fmt != fmt) return LOWBIT_E_UNSUPPORTED;
+    if (!g.pcodes || !g.pscales || !g.x || !g.y) return LOWBIT_E_NULL;
+    if (!shape_ok(g.N, g.K) || cdiv(g.N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
+    if (!aligned(g.pcodes, 16) || !aligned(g.pscales, 16) || !aligned(g.x, 16) || !aligned(g.y, 4))
+      return LOWBIT_E_ALIGN;
+    st[i] = ChainStage{fmt, g.N, g.K, g.pcodes, (const uint16_t*)g.pscales, g.x, g.y,
+                       i > 0 && g.wait_prev ? 1 : 0};
+  }
+  void* plan = nullptr;
+  hipError_t e = chain_create(st.data(), n_stages, x_dtype, y_dtype, &plan);
+  if (e == hipErrorOutOfMemory) return LOWBIT_E_NOMEM;
+  if (e != hipSuccess) return LOWBIT_E_HIP;
+  *chain = new lowbit_chain{plan};
+  return LOWBIT_OK;
+}
+
+int lowbit_chain_run(lowbit_chain* chain, void* stream) {
+  if (!chain) return LOWBIT_E_NULL;
+  return hip_status(chain_run(chain->plan, (hipStream_t)stream));
+}
+
+int lowbit_chain_status(lowbit_chain* chain, int* failed_waits) {
+  if (!chain || !failed_waits) return LOWBIT_E_NULL;
+  return hip_status(chain_status(chain->plan, failed_waits));
+}
+
+int lowbit_chain_destroy(lowbit_chain* chain) {
+  if (!chain) return LOWBIT_OK;
+  const hipError_t e = hipDeviceSynchronize();
+  chain_destroy(chain->plan);
+  delete chain;
+  return hip_status(e);
 }
 
 }  // extern "C"

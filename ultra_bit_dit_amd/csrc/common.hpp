@@ -84,6 +84,22 @@ struct GemvArgs {
 size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind);
 hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t s);
 
+// Persistent chain of batch-1 products (one cooperative launch runs them all;
+// product i may wait for product i-1 to complete before reading its x)
+struct ChainStage {
+  int fmt;
+  int64_t N, K;
+  const void* pcodes;
+  const uint16_t* pscales;
+  const void* x;
+  void* y;
+  int wait_prev;
+};
+hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void** plan);
+hipError_t chain_run(void* plan, hipStream_t s);
+hipError_t chain_status(void* plan, int* failed_waits);
+void chain_destroy(void* plan);
+
 struct SignArgs {
   int64_t N, K, M;
   const void* pcodes;

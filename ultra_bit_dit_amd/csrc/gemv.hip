@@ -22,6 +22,7 @@
 // (the XOR + popcount remark of the "1-bit 嘅數學" section of the
 // richmindsetzone.com 1-bit diffusion page).
 #include <algorithm>
+#include <vector>
 
 #include "common.hpp"
 
@@ -29,6 +30,7 @@ namespace lowbit {
 namespace {
 
 constexpr int kMaxWaves = 16;  // waves per workgroup of the sign kernel
+constexpr uint32_t kChainSpinLimit = 1u << 24;  // sleeps before a chain wait gives up
 constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
 
 template <int T>
@@ -125,8 +127,17 @@ __device__ __attribute__((always_inline)) inline bool stage_unit(const FArgs& a,
 
 // raw activations of one unit: bf16 in ra, f32 in ra:rb, int8 in ra.xy.
 // The load is unconditional (a unit past the end reads element 0) so that
-// no control flow joins wait on it.
-template <int XK>
+// no control flow joins wait on it.  COH: device-coherent loads, for
+// activations another workgroup may just have written.
+__device__ __attribute__((always_inline)) inline uint4 coh_load4(const void* p) {
+  const uint32_t* w = (const uint32_t*)p;
+  return make_uint4(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(w + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(w + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <int XK, bool COH>
 __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a, int64_t q0,
                                                                   int64_t nq, int64_t rd,
                                                                   uint4& ra, uint4& rb) {
@@ -136,11 +147,13 @@ __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a
   const bool valid = stage_unit(a, q0, nq, c, ch, b, t, ql, m, g);
   const int64_t idx = valid ? m * a.K + g * kGroup + kmap(b, 8 * ch) : 0;
   if constexpr (XK == XK_BF16) {
-    ra = *(const uint4*)((const uint16_t*)a.x + idx);
+    const uint16_t* p = (const uint16_t*)a.x + idx;
+    ra = COH ? coh_load4(p) : *(const uint4*)p;
     rb = ra;
   } else if constexpr (XK == XK_F32) {
-    ra = *(const uint4*)((const float*)a.x + idx);
-    rb = *(const uint4*)((const float*)a.x + idx + 4);
+    const float* p = (const float*)a.x + idx;
+    ra = COH ? coh_load4(p) : *(const uint4*)p;
+    rb = COH ? coh_load4(p + 4) : *(const uint4*)(p + 4);
   } else {
     const uint2 w = *(const uint2*)((const int8_t*)a.x + idx);
     ra = make_uint4(w.x, w.y, w.x, w.y);
@@ -253,16 +266,25 @@ __device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs
 // the MFMAs of all W row-blocks.  With several K-slices, each workgroup
 // writes coherent partial sums and the last workgroup of the row group to
 // arrive adds them in slice order.
-template <int FMT, int XK, int MX, int YK, int QM>
-__global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
+//
+// gemv_item does that for work item `blk` (row group blk / KS, K-slice
+// blk % KS).  It is the body of the one-product kernel (item = workgroup)
+// and of the persistent multi-product kernel (CHAIN: items of several
+// products in turn, outputs written with device-coherent stores).  WAIT:
+// the weight loads go out first, then the workgroup waits until `wait_cnt`
+// reaches `wait_target` -- the previous product is complete -- and reads
+// its activations with device-coherent loads.
+template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT>
+__device__ __attribute__((always_inline)) inline void gemv_item(
+    const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
+    uint32_t* err) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   constexpr bool INTC = XK == XK_I8;
   constexpr int NC = FMT == 1 ? 1 : 2;  // 16-byte code vectors per quad
-  extern __shared__ __align__(16) uint8_t smem[];
   __shared__ uint32_t s_last;
   const int W = blockDim.x >> 6;
   const int L = threadIdx.x & 63, w = threadIdx.x >> 6, r = L & 15, lg = L >> 4;
-  const int64_t rg = blockIdx.x / a.KS, ks = blockIdx.x % a.KS;
+  const int64_t rg = blk / a.KS, ks = blk % a.KS;
   const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
   const int nq = (int)(q1 - q0);
   const int64_t rb = (int64_t)W * rg + w;  // this wave's row-block
@@ -275,10 +297,12 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
   uint8_t* zblk = xe + (int64_t)nq * 16 * a.MA;
   if (threadIdx.x < 9) ((uint32_t*)zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
 
-  // activation loads of the first staging rounds go out first
   uint4 ra[kStageRounds], rbv[kStageRounds];
+  if constexpr (!WAIT) {
+    // activation loads of the first staging rounds go out first
 #pragma unroll
-  for (int k = 0; k < kStageRounds; k++) stage_load1<XK>(a, q0, nq, k, ra[k], rbv[k]);
+    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, false>(a, q0, nq, k, ra[k], rbv[k]);
+  }
 
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
   const u4* pcv = (const u4*)a.pcodes;
@@ -303,13 +327,31 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
     }
     sc[q] = sbase[(rbc * a.GQ + gq) * 16 + r];
   }
+  if constexpr (WAIT) {
+    // the previous product must be complete before its outputs are read; the
+    // weight loads above are already in flight
+    if (threadIdx.x == 0) {
+      for (uint32_t spin = 0;
+           __hip_atomic_load(wait_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target;
+           spin++) {
+        if (spin >= kChainSpinLimit) {  // never satisfied: flag it and go on
+          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, true>(a, q0, nq, k, ra[k], rbv[k]);
+  }
 #pragma unroll
   for (int k = 0; k < kStageRounds; k++) stage_convert1<R, XK>(a, q0, nq, k, ra[k], rbv[k], xa, xe);
   // remaining rounds (small-M products with long slices), loaded and converted in turn
   const int64_t rounds = cdiv(nq * 64 * a.M, (int64_t)blockDim.x);
   for (int64_t rd = kStageRounds; rd < rounds; rd++) {
     uint4 r0, r1;
-    stage_load1<XK>(a, q0, nq, rd, r0, r1);
+    stage_load1<XK, WAIT>(a, q0, nq, rd, r0, r1);
     stage_convert1<R, XK>(a, q0, nq, rd, r0, r1, xa, xe);
   }
   __syncthreads();
@@ -380,9 +422,21 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
   // ---- output
   auto store = [&](int64_t m, int64_t n, float f, int iv) {
     const float sxm = a.x_scales ? a.x_scales[m] : a.x_scale;
-    if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = f * sxm;
-    else if (YK == YK_BF16) ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(f * sxm);
-    else ((int32_t*)a.y)[m * a.N + n] = iv;
+    if constexpr (CHAIN) {
+      if (YK == YK_F32)
+        __hip_atomic_store((float*)a.y + m * a.N + n, f * sxm, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else if (YK == YK_BF16)
+        __hip_atomic_store((uint16_t*)a.y + m * a.N + n, (uint16_t)bf16_rne(f * sxm),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_store((int32_t*)a.y + m * a.N + n, iv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = f * sxm;
+      else if (YK == YK_BF16) ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(f * sxm);
+      else ((int32_t*)a.y)[m * a.N + n] = iv;
+    }
   };
   constexpr bool IPART = INTC && YK == YK_I32;
   const int64_t n = 16 * rb + r;
@@ -428,6 +482,62 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.cnt + 16 + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int FMT, int XK, int MX, int YK, int QM>
+__global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  gemv_item<FMT, XK, MX, YK, QM, false, false>(a, blockIdx.x, smem, nullptr, 0, nullptr);
+}
+
+// Persistent kernel over a chain of batch-1 products (items of product s
+// are [first[s], first[s+1]) in a global order that every workgroup walks
+// with stride gridDim.x).  done[s] counts finished items of product s; a
+// product marked `wait` reads its activations only after done[s-1] reaches
+// the previous product's item count.  Workgroups never wait on an item
+// later in the order than their own, and the grid is co-resident
+// (cooperative launch), so every wait ends; a wait is nevertheless bounded
+// by kChainSpinLimit.  The last workgroup to finish resets the counters.
+struct ChainArgs {
+  const FArgs* args;       // [S]
+  const int64_t* first;    // [S + 1]
+  const int32_t* wait;     // [S]
+  uint32_t* done;          // [S], zero between launches
+  uint32_t* finished;      // workgroups done, zero between launches
+  uint32_t* err;           // set when a wait gave up
+  int S;
+};
+
+template <int FMT, int XK, int YK, int QM>
+__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_chain(ChainArgs c) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t total = c.first[c.S];
+  int s = 0;
+  for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
+    while (i >= c.first[s + 1]) s++;
+    const FArgs a = c.args[s];
+    const bool wt = s > 0 && c.wait[s] != 0;
+    __syncthreads();  // the previous item's LDS reads are over
+    if (wt)
+      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - c.first[s], smem, c.done + s - 1,
+                                                (uint32_t)(c.first[s] - c.first[s - 1]), c.err);
+    else
+      gemv_item<FMT, XK, 1, YK, QM, true, false>(a, i - c.first[s], smem, nullptr, 0u, c.err);
+    __builtin_amdgcn_s_waitcnt(0);  // this item's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(c.done + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(c.finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      for (int k = 0; k < c.S; k++)
+        __hip_atomic_store(c.done + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 struct Plan {
@@ -523,6 +633,151 @@ hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
   if (g.fmt == 1) return launch_x<1, kQuadsBinary>(g, k, grid, block, p.lds, s);
   if (g.fmt == 2) return launch_x<2, kQuadsTernary>(g, k, grid, block, p.lds, s);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- chains
+namespace {
+
+struct ChainPlan {
+  void* mem = nullptr;  // descriptors, counters and partial sums (one allocation)
+  ChainArgs args;
+  const void* kernel = nullptr;
+  dim3 grid, block;
+  size_t lds = 0;
+  int device = 0;
+  uint32_t* err = nullptr;
+};
+
+template <int FMT, int XK>
+const void* chain_kernel(int ykind) {
+  constexpr int QM = FMT == 1 ? kQuadsBinary : kQuadsTernary;
+  if (ykind == YK_BF16) return (const void*)gemv_chain<FMT, XK, YK_BF16, QM>;
+  return (const void*)gemv_chain<FMT, XK, YK_F32, QM>;
+}
+
+}  // namespace
+
+hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void** out) {
+  *out = nullptr;
+  if (S < 1) return hipErrorInvalidValue;
+  const int fmt = st[0].fmt;
+  std::vector<FArgs> args(S);
+  std::vector<int64_t> first(S + 1, 0);
+  std::vector<int32_t> wait(S, 0);
+  std::vector<int64_t> cnt_off(S), part_off(S);
+  int64_t cnt_words = 16, part_floats = 0;
+  size_t lds = 0;
+  for (int i = 0; i < S; i++) {
+    if (st[i].fmt != fmt) return hipErrorInvalidValue;
+    const Plan p = make_plan(fmt, st[i].N, st[i].K, 1, xkind);
+    if (p.lds > 64 * 1024) return hipErrorInvalidValue;
+    lds = std::max(lds, p.lds);
+    first[i + 1] = first[i] + p.NRG * p.KS;
+    wait[i] = st[i].wait_prev ? 1 : 0;
+    cnt_off[i] = cnt_words;
+    cnt_words += p.NRG;
+    part_off[i] = part_floats;
+    if (p.KS > 1) part_floats += p.KS * p.Npad;
+    FArgs& k = args[i];
+    k.pcodes = (const uint8_t*)st[i].pcodes;
+    k.pscales = st[i].pscales;
+    k.x = st[i].x;
+    k.x_scales = nullptr;
+    k.y = st[i].y;
+    k.N = st[i].N;
+    k.K = st[i].K;
+    k.G = p.G;
+    k.GQ = p.GQ;
+    k.GP = p.GP;
+    k.M = 1;
+    k.MA = p.MA;
+    k.NB = p.NB;
+    k.KS = p.KS;
+    k.Npad = p.Npad;
+    k.x_scale = 1.0f;
+    k.xkind = xkind;
+  }
+  if (first[S] > 0x7FFFFFFF || cnt_words > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // layout of the one allocation
+  const size_t o_args = 0;
+  const size_t o_first = align256(o_args + sizeof(FArgs) * S);
+  const size_t o_wait = align256(o_first + sizeof(int64_t) * (S + 1));
+  const size_t o_done = align256(o_wait + sizeof(int32_t) * S);
+  const size_t o_fin = align256(o_done + sizeof(uint32_t) * S);
+  const size_t o_cnt = align256(o_fin + 2 * sizeof(uint32_t));
+  const size_t o_part = align256(o_cnt + sizeof(uint32_t) * cnt_words);
+  const size_t bytes = o_part + sizeof(float) * (size_t)part_floats;
+
+  ChainPlan* c = new ChainPlan;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipMalloc(&c->mem, bytes);
+  if (e != hipSuccess) {
+    delete c;
+    return e;
+  }
+  uint8_t* m = (uint8_t*)c->mem;
+  for (int i = 0; i < S; i++) {
+    args[i].cnt = (uint32_t*)(m + o_cnt) + cnt_off[i] - 16;
+    args[i].part = (float*)(m + o_part) + part_off[i];
+  }
+  // counters start at zero; every launch leaves them zero
+  e = hipMemset(m + o_done, 0, o_part - o_done);
+  if (e == hipSuccess) e = hipMemcpy(m + o_args, args.data(), sizeof(FArgs) * S, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_first, first.data(), sizeof(int64_t) * (S + 1), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_wait, wait.data(), sizeof(int32_t) * S, hipMemcpyHostToDevice);
+  if (e == hipSuccess) {
+    if (fmt == 1) c->kernel = xkind == XK_F32 ? chain_kernel<1, XK_F32>(ykind) : chain_kernel<1, XK_BF16>(ykind);
+    else if (fmt == 2) c->kernel = xkind == XK_F32 ? chain_kernel<2, XK_F32>(ykind) : chain_kernel<2, XK_BF16>(ykind);
+    else e = hipErrorInvalidValue;
+  }
+  int per_cu = 0, cus = 0;
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, c->kernel, 64 * kMaxW, lds);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e == hipSuccess && per_cu < 1) e = hipErrorInvalidConfiguration;
+  if (e != hipSuccess) {
+    (void)hipFree(c->mem);
+    delete c;
+    return e;
+  }
+  const int64_t want = (int64_t)per_cu * cus;
+  c->grid = dim3((unsigned)std::min<int64_t>(want, first[S]));
+  c->block = dim3(64 * kMaxW);
+  c->lds = lds;
+  c->args.args = (const FArgs*)(m + o_args);
+  c->args.first = (const int64_t*)(m + o_first);
+  c->args.wait = (const int32_t*)(m + o_wait);
+  c->args.done = (uint32_t*)(m + o_done);
+  c->args.finished = (uint32_t*)(m + o_fin);
+  c->args.err = (uint32_t*)(m + o_fin) + 1;
+  c->args.S = S;
+  c->err = c->args.err;
+  *out = c;
+  return hipSuccess;
+}
+
+hipError_t chain_run(void* plan, hipStream_t s) {
+  ChainPlan* c = (ChainPlan*)plan;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev != c->device) return hipErrorInvalidDevice;
+  void* kargs[] = {&c->args};
+  return hipLaunchCooperativeKernel(c->kernel, c->grid, c->block, kargs, (unsigned)c->lds, s);
+}
+
+hipError_t chain_status(void* plan, int* failed_waits) {
+  ChainPlan* c = (ChainPlan*)plan;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpy(&v, c->err, sizeof(v), hipMemcpyDeviceToHost);
+  *failed_waits = (int)v;
+  return e;
+}
+
+void chain_destroy(void* plan) {
+  ChainPlan* c = (ChainPlan*)plan;
+  if (!c) return;
+  (void)hipFree(c->mem);
+  delete c;
 }
 
 hipError_t launch_gemv_sign(const SignArgs& g, hipStream_t s);

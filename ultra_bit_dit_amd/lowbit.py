@@ -17,7 +17,15 @@ F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
 
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
-           "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm")
+           "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
+           "lowbit_chain_create", "lowbit_chain_run", "lowbit_chain_status", "lowbit_chain_destroy")
+
+
+class GemvStage(ctypes.Structure):
+    """lowbit_gemv_stage"""
+    _fields_ = [("fmt", ctypes.c_int), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("pcodes", ctypes.c_void_p), ("pscales", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("wait_prev", ctypes.c_int)]
 
 
 class LowbitError(RuntimeError):
@@ -47,6 +55,11 @@ def lib():
         L.lowbit_quantize_act_i8.argtypes = [i64, i64, vp, vp, vp, vp]
         L.lowbit_gemv.argtypes = [i32, i64, i64, vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
         L.lowbit_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i32, vp, vp, i32, vp, vp]
+        L.lowbit_chain_create.argtypes = [i32, ctypes.POINTER(GemvStage), i32, i32,
+                                          ctypes.POINTER(vp)]
+        L.lowbit_chain_run.argtypes = [vp, vp]
+        L.lowbit_chain_status.argtypes = [vp, ctypes.POINTER(i32)]
+        L.lowbit_chain_destroy.argtypes = [vp]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -150,3 +163,41 @@ def gemm(fmt, M, N, K, pcodes, pscales, X, x_scales=None, y_dtype=F32, Y=None, x
     _check("lowbit_gemm", lib().lowbit_gemm(fmt, M, N, K, _ptr(pcodes), _ptr(pscales), _xdt(X, x_dtype),
                                             _ptr(X), _ptr(x_scales), y_dtype, _ptr(Y), _stream(stream)))
     return Y
+
+
+class Chain:
+    """A planned chain of batch-1 products run as one persistent launch
+    (lowbit_chain_*).  `stages` is a list of (fmt, N, K, pcodes, pscales, x, y,
+    wait_prev) with device tensors; the tensors are kept referenced for the
+    chain's lifetime."""
+
+    def __init__(self, stages, x_dtype=BF16, y_dtype=F32):
+        self._keep = [t for st in stages for t in st[3:7]]
+        arr = (GemvStage * len(stages))()
+        for i, (fmt, N, K, pc, ps, x, y, wait) in enumerate(stages):
+            arr[i] = GemvStage(fmt, N, K, pc.data_ptr(), ps.data_ptr(), x.data_ptr(), y.data_ptr(),
+                               int(wait))
+        h = ctypes.c_void_p()
+        _check("lowbit_chain_create",
+               lib().lowbit_chain_create(len(stages), arr, x_dtype, y_dtype, ctypes.byref(h)))
+        self._h = h
+
+    def run(self, stream=None):
+        _check("lowbit_chain_run", lib().lowbit_chain_run(self._h, _stream(stream)))
+
+    def failed_waits(self):
+        v = ctypes.c_int(0)
+        _check("lowbit_chain_status", lib().lowbit_chain_status(self._h, ctypes.byref(v)))
+        return v.value
+
+    def close(self):
+        if self._h:
+            _check("lowbit_chain_destroy", lib().lowbit_chain_destroy(self._h))
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
