@@ -29,7 +29,7 @@ def make(fmt, N, K, seed=SEED, tid=1):
 SHAPES = [(16, 128), (1, 128), (37, 384), (5, 1152), (33, 2048), (100, 640), (256, 1024), (48, 1664)]
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("xk", ["bf16", "f32"])
 def test_gemv_float_parity(fmt, N, K, xk):
@@ -63,7 +63,7 @@ def test_c0_binary_256x1024_f32():
     print(f"C0 worst err/tol = {worst:.3e}")
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("N,K", [(5120, 5120), (17408, 5120), (5120, 17408)])
 def test_full_size_shapes(fmt, N, K):
     """27B-class layer shapes, weights generated on the device, full compare."""
@@ -83,7 +83,7 @@ def test_full_size_shapes(fmt, N, K):
     print(f"worst err/tol = {worst:.3e}")
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_dyadic_inputs_are_exact(fmt):
     """Small-integer bf16 activations and power-of-two scales: the product is
     exactly representable and the GPU result equals the oracle exactly."""
@@ -100,7 +100,7 @@ def test_dyadic_inputs_are_exact(fmt):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), yref[0])
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("N,K", [(37, 384), (5120, 5120)])
 def test_int8_activations(fmt, N, K):
     codes, scales, pc, ps = make(fmt, N, K, tid=41)
@@ -143,7 +143,7 @@ def test_repeat_runs_bit_identical(fmt):
     assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_small_m_gemm_bf16(fmt, M):
     """Small-M products (M = k+1 = 5 is a speculative-decoding verify pass)."""
@@ -175,3 +175,25 @@ def test_small_m_gemm_int8(M):
     assert np.array_equal(Yi.cpu().numpy().astype(np.int64), O.group_int_sums(codes, q_ref).sum(axis=2))
     yref, absY = O.matmul(codes, scales, O.X_I8, q_ref, sx_ref)
     assert_within(Yf.cpu().numpy(), yref, absY, what="i8 gemm")
+
+
+@pytest.mark.parametrize("N,K", [(37, 384), (100, 1152), (5120, 5120)])
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+def test_base3_equals_2bit(N, K, xk):
+    """The same ternary codes packed as 2-bit and as base-3 decode to the same
+    fp4 operands, so the two GEMVs agree bit for bit (for K that both formats
+    reduce in one slice; longer rows are split into slices of whole quads
+    for 2-bit and whole octets for base-3, which changes the fp32 summation
+    order -- those shapes are checked against the oracle instead)."""
+    codes = codes_for(2, SEED, 91, N, K)
+    scales = synth.group_scales(SEED, 92, N, K // 128)
+    pc2, ps2 = lb.pack(2, dev(codes), dev(scales.view(np.int16)))
+    pc3, ps3 = lb.pack(3, dev(codes), dev(scales.view(np.int16)))
+    if xk == "bf16":
+        x = dev(synth.normal_bf16(SEED, 93, 1, K).view(np.int16)).view(torch.bfloat16)[0]
+    else:
+        x = dev(synth.normal_f32(SEED, 93, 1, K))[0]
+    y2 = lb.gemv(2, N, K, pc2, ps2, x)
+    y3 = lb.gemv(3, N, K, pc3, ps3, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y3)

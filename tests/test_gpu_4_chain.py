@@ -29,7 +29,7 @@ def make(fmt, N, K, tid):
     return codes, scales, pc, ps
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("wait", [0, 1])
 def test_chain_matches_separate_calls(fmt, wait):
     shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560)]

@@ -200,7 +200,6 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* p
   if (y_dtype == LOWBIT_I32 && !(int_x && pscales == nullptr)) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_I32 && !pscales) return LOWBIT_E_NULL;
   if (x_dtype == LOWBIT_SIGN1 && fmt != LOWBIT_BINARY) return LOWBIT_E_UNSUPPORTED;
-  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;  // packed format only for now
   if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(x, 16) ||
       !aligned(y, 4))
     return LOWBIT_E_ALIGN;
@@ -241,7 +240,6 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
     return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_I32 && !pscales) return LOWBIT_E_NULL;
   if (x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 && !x_scales) return LOWBIT_E_NULL;
-  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;
   if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(X, 16) ||
       !aligned(Y, 16) || (x_scales && !aligned(x_scales, 4)))
     return LOWBIT_E_ALIGN;
@@ -250,6 +248,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
+  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;  // large-M base-3: not provided
   return run_gemm(fmt, M, N, K, pcodes, pscales, x_dtype, X, x_scales, y_dtype, Y, s);
 }
 
@@ -265,7 +264,7 @@ int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dty
   if (x_dtype != LOWBIT_F32 && x_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
   const int fmt = stages[0].fmt;
-  if (fmt != LOWBIT_BINARY && fmt != LOWBIT_TERNARY_2BIT) return LOWBIT_E_UNSUPPORTED;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   std::vector<ChainStage> st(n_stages);
   for (int i = 0; i < n_stages; i++) {
     const lowbit_gemv_stage& g = stages[i];

@@ -280,12 +280,15 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     uint32_t* err) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   constexpr bool INTC = XK == XK_I8;
-  constexpr int NC = FMT == 1 ? 1 : 2;  // 16-byte code vectors per quad
+  constexpr int NC = FMT == 1 ? 1 : 2;  // 16-byte code vectors per quad (2-bit, binary)
   __shared__ uint32_t s_last;
   const int W = blockDim.x >> 6;
   const int L = threadIdx.x & 63, w = threadIdx.x >> 6, r = L & 15, lg = L >> 4;
   const int64_t rg = blk / a.KS, ks = blk % a.KS;
-  const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
+  // K-slices in whole quads; base-3 slices in whole octets (two quads)
+  const int64_t GO = cdiv(a.GQ, 2);
+  const int64_t q0 = FMT == 3 ? 2 * (GO * ks / a.KS) : a.GQ * ks / a.KS;
+  const int64_t q1 = FMT == 3 ? min<int64_t>(2 * (GO * (ks + 1) / a.KS), a.GQ) : a.GQ * (ks + 1) / a.KS;
   const int nq = (int)(q1 - q0);
   const int64_t rb = (int64_t)W * rg + w;  // this wave's row-block
   const bool live = rb < a.NB;
@@ -296,6 +299,21 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   // activation row (their A operand is zero)
   uint8_t* zblk = xe + (int64_t)nq * 16 * a.MA;
   if (threadIdx.x < 9) ((uint32_t*)zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
+  // base-3: byte value -> its 5 trits as fp4 nibbles (trit 0 -> -1 = 0xA,
+  // 1 -> 0, 2 -> +1 = 0x2), nibble e = trit e (least significant first)
+  uint32_t* t3 = (uint32_t*)(zblk + 48);
+  if constexpr (FMT == 3) {
+    if (threadIdx.x < 243) {
+      uint32_t v = threadIdx.x, nib = 0;
+#pragma unroll
+      for (int e = 0; e < 5; e++) {
+        const uint32_t t = v % 3;
+        v /= 3;
+        nib |= (t == 0 ? 0xAu : t == 2 ? 0x2u : 0u) << (4 * e);
+      }
+      t3[threadIdx.x] = nib;
+    }
+  }
 
   uint4 ra[kStageRounds], rbv[kStageRounds];
   if constexpr (!WAIT) {
@@ -307,7 +325,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
   const u4* pcv = (const u4*)a.pcodes;
   const uint2* ps2 = (const uint2*)a.pscales;
-  u4 cw[QM][NC];
+  u4 cw[FMT == 3 ? 1 : QM][NC];
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  u2 c3[FMT == 3 ? QM : 1][3];  // base-3: 24 bytes of 5-trit bytes per quad
+  uint32_t c3t[FMT == 3 ? QM : 1];  // and the lane's word of 4-trit bytes
   uint2 sc[QM];
   // Every code and scale of the wave is requested before anything else.  The
   // loads are unconditional (clamped to the last valid block, results of
@@ -320,6 +341,18 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     const int64_t gq = min<int64_t>(q0 + q, a.GQ - 1);
     if constexpr (FMT == 1) {
       cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GQ + gq) * 64 + L]);
+    } else if constexpr (FMT == 3) {
+      // octet block (rb, gq/2): plane s of lane L at 1024 s + 16 L; the quad's
+      // half h = gq % 2 takes 8-byte chunks 3h .. 3h+2 (chunk c = plane c/2,
+      // half c%2) and bytes 2h, 2h+1 of the 4-byte word at 3072 + 4 L
+      const uint8_t* ob = a.pcodes + (rbc * GO + (gq >> 1)) * 3328;
+      const int h = (int)(gq & 1);
+#pragma unroll
+      for (int cc = 0; cc < 3; cc++) {
+        const int c = 3 * h + cc;
+        c3[q][cc] = __builtin_nontemporal_load((const u2*)(ob + 1024 * (c >> 1) + 16 * L + 8 * (c & 1)));
+      }
+      c3t[q] = __builtin_nontemporal_load((const uint32_t*)(ob + 3072 + 4 * L)) >> (16 * h);
     } else {
       const int64_t p0 = 2 * gq, p1 = min<int64_t>(2 * gq + 1, a.GP - 1);
       cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p0) * 64 + L]);
@@ -386,6 +419,27 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
             d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;
             d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;
             d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;
+          } else if constexpr (FMT == 3) {
+            // group t of the quad: bytes 6t .. 6t+5 hold slots 0..29, the
+            // 4-trit byte t/2 digits 2(t%2), 2(t%2)+1 hold slots 30, 31
+            const uint32_t w6[6] = {c3[q][0].x, c3[q][0].y, c3[q][1].x,
+                                    c3[q][1].y, c3[q][2].x, c3[q][2].y};
+            uint32_t nb[6];
+#pragma unroll
+            for (int i = 0; i < 6; i++) {
+              const int byte = 6 * t + i;
+              nb[i] = t3[(w6[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
+            }
+            const uint32_t tl = (t3[(c3t[q] >> (8 * (t >> 1))) & 0xFFu] >> (8 * (t & 1))) & 0xFFu;
+            // slot s -> nibble s of d0..d3 (5 slots per byte)
+            const uint64_t lo = (uint64_t)nb[0] | ((uint64_t)nb[1] << 20) | ((uint64_t)nb[2] << 40) |
+                                ((uint64_t)nb[3] << 60);
+            const uint64_t hi = (uint64_t)(nb[3] >> 4) | ((uint64_t)nb[4] << 16) |
+                                ((uint64_t)nb[5] << 36) | ((uint64_t)tl << 56);
+            d0 = (uint32_t)lo;
+            d1 = (uint32_t)(lo >> 32);
+            d2 = (uint32_t)hi;
+            d3 = (uint32_t)(hi >> 32);
           } else {
             const u4 c4 = cw[q][(t >> 1) % NC];
             const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
@@ -563,14 +617,20 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
   p.GP = cdiv(p.G, 2);
   p.QM = fmt == 1 ? kQuadsBinary : kQuadsTernary;
   // staged activations of a slice stay within 48 KiB of LDS
-  const int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (48 * 1024) / (16 * p.MA * 33)));
-  p.KS = cdiv(p.GQ, qcap);
+  int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (48 * 1024) / (16 * p.MA * 33)));
+  if (fmt == 3) {
+    // base-3 slices are whole octets (pairs of quads)
+    qcap = std::max<int64_t>(2, qcap & ~int64_t(1));
+    p.KS = cdiv(cdiv(p.GQ, 2), qcap / 2);
+  } else {
+    p.KS = cdiv(p.GQ, qcap);
+  }
   // 4 waves per workgroup: 64 rows share one staged slice, and the slice's
   // activation loads fit in the hoisted staging rounds
   p.W = kMaxW;
   p.NRG = cdiv(p.NB, p.W);
-  const int64_t qmax = cdiv(p.GQ, p.KS);
-  p.lds = (size_t)qmax * 16 * p.MA * 32 + (size_t)qmax * 16 * p.MA + 48;
+  const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
+  p.lds = (size_t)qmax * 16 * p.MA * 32 + (size_t)qmax * 16 * p.MA + 48 + (fmt == 3 ? 1024 : 0);
   p.Npad = p.NRG * p.W * 16;
   p.part_off = kCounterBytes;
   p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
@@ -632,6 +692,7 @@ hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(p.NRG * p.KS)), block((unsigned)(64 * p.W));
   if (g.fmt == 1) return launch_x<1, kQuadsBinary>(g, k, grid, block, p.lds, s);
   if (g.fmt == 2) return launch_x<2, kQuadsTernary>(g, k, grid, block, p.lds, s);
+  if (g.fmt == 3) return launch_x<3, kQuadsTernary>(g, k, grid, block, p.lds, s);
   return hipErrorInvalidValue;
 }
 
@@ -728,6 +789,7 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   if (e == hipSuccess) {
     if (fmt == 1) c->kernel = xkind == XK_F32 ? chain_kernel<1, XK_F32>(ykind) : chain_kernel<1, XK_BF16>(ykind);
     else if (fmt == 2) c->kernel = xkind == XK_F32 ? chain_kernel<2, XK_F32>(ykind) : chain_kernel<2, XK_BF16>(ykind);
+    else if (fmt == 3) c->kernel = xkind == XK_F32 ? chain_kernel<3, XK_F32>(ykind) : chain_kernel<3, XK_BF16>(ykind);
     else e = hipErrorInvalidValue;
   }
   int per_cu = 0, cus = 0;
