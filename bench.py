@@ -46,7 +46,7 @@ DIT = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("out", 3072, 30
 FMT_NAMES = {1: "binary", 2: "ternary-2bit", 3: "ternary-base3"}
 SEED = 1002  # decode-step workload
 PP_SEED, DIT_SEED = 1003, 1004
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_decode_step_pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "{kernel}_decode_step_pmc.txt")
 GEMV_SOURCE = os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", "gemv.hip")
 
 
@@ -115,7 +115,7 @@ def pmc_traffic(launch_bytes, kernel):
     since the counters were taken."""
     try:
         kv = {}
-        with open(PMC_SUMMARY) as f:
+        with open(PMC_SUMMARY.format(kernel=kernel)) as f:
             for line in f:
                 if "=" in line and not line.startswith("#"):
                     k, v = line.split("=", 1)
