@@ -1,7 +1,9 @@
 """Chains of batch-1 products in one persistent launch (lowbit_chain_*).
 
-A chain without waits must reproduce separate lowbit_gemv calls bit for bit
-(the same per-item arithmetic); a chain whose stage i reads stage i-1's
+Every stage of a chain must meet the oracle tolerance, and where its rows
+are reduced in one K-slice it must reproduce a separate lowbit_gemv call
+bit for bit (the same per-group arithmetic in the same order; longer rows
+may be cut into different slices); a chain whose stage i reads stage i-1's
 output as its activations must match the oracle applied stage by stage to
 the GPU's own intermediate outputs, and must equal the separate calls on
 those same intermediates."""
@@ -33,12 +35,14 @@ def make(fmt, N, K, tid):
 @pytest.mark.parametrize("wait", [0, 1])
 def test_chain_matches_separate_calls(fmt, wait):
     shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560)]
-    mats, xs, ys = [], [], []
+    mats, xs, ys, refs = [], [], [], []
     for j, (N, K) in enumerate(shapes):
-        _, _, pc, ps = make(fmt, N, K, tid=200 + 2 * j)
+        codes, scales, pc, ps = make(fmt, N, K, tid=200 + 2 * j)
         mats.append((pc, ps))
-        xs.append(dev(synth.normal_bf16(SEED, 230 + j, 1, K).view(np.int16)).view(torch.bfloat16)[0])
+        xh = synth.normal_bf16(SEED, 230 + j, 1, K)
+        xs.append(dev(xh.view(np.int16)).view(torch.bfloat16)[0])
         ys.append(torch.full((N,), float("nan"), device="cuda"))
+        refs.append(O.matmul(codes, scales, O.X_BF16, xh))
     stages = [(fmt, N, K, mats[j][0], mats[j][1], xs[j], ys[j], wait)
               for j, (N, K) in enumerate(shapes)]
     chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
@@ -48,9 +52,13 @@ def test_chain_matches_separate_calls(fmt, wait):
         chain.run()
         torch.cuda.synchronize()
         for j, (N, K) in enumerate(shapes):
-            ref = lb.gemv(fmt, N, K, mats[j][0], mats[j][1], xs[j])
-            torch.cuda.synchronize()
-            assert torch.equal(ys[j], ref), f"stage {j} run {rep}"
+            yref, absY = refs[j]
+            assert_within(ys[j].cpu().numpy()[None], yref, absY, what=f"stage {j} run {rep}")
+            if K <= 5120:
+                # one K-slice in every kernel: the same arithmetic in the same order
+                ref = lb.gemv(fmt, N, K, mats[j][0], mats[j][1], xs[j])
+                torch.cuda.synchronize()
+                assert torch.equal(ys[j], ref), f"stage {j} run {rep}"
     assert chain.failed_waits() == 0
     chain.close()
 

@@ -274,34 +274,145 @@ __device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs
 // the weight loads go out first, then the workgroup waits until `wait_cnt`
 // reaches `wait_target` -- the previous product is complete -- and reads
 // its activations with device-coherent loads.
-template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT>
-__device__ __attribute__((always_inline)) inline void gemv_item(
-    const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
-    uint32_t* err) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
-  constexpr bool INTC = XK == XK_I8;
-  constexpr int NC = FMT == 1 ? 1 : 2;  // 16-byte code vectors per quad (2-bit, binary)
-  __shared__ uint32_t s_last;
-  const int W = blockDim.x >> 6;
-  const int L = threadIdx.x & 63, w = threadIdx.x >> 6, r = L & 15, lg = L >> 4;
-  const int64_t rg = blk / a.KS, ks = blk % a.KS;
-  // K-slices in whole quads; base-3 slices in whole octets (two quads)
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+// Geometry of one work item: row group rg (W row-blocks, one per wave) and
+// K-slice ks of quads [q0, q1) (base-3 slices are whole octets).
+struct Item {
+  int64_t rg, ks, q0, rb;
+  int nq;
+  bool live;
+};
+
+template <int FMT>
+__device__ __attribute__((always_inline)) inline Item item_of(const FArgs& a, int64_t blk) {
+  Item it;
+  const int W = blockDim.x >> 6, w = threadIdx.x >> 6;
+  it.rg = blk / a.KS;
+  it.ks = blk % a.KS;
   const int64_t GO = cdiv(a.GQ, 2);
-  const int64_t q0 = FMT == 3 ? 2 * (GO * ks / a.KS) : a.GQ * ks / a.KS;
-  const int64_t q1 = FMT == 3 ? min<int64_t>(2 * (GO * (ks + 1) / a.KS), a.GQ) : a.GQ * (ks + 1) / a.KS;
-  const int nq = (int)(q1 - q0);
-  const int64_t rb = (int64_t)W * rg + w;  // this wave's row-block
-  const bool live = rb < a.NB;
-  const bool arow = r < a.MA;
-  uint8_t* xa = smem;
-  uint8_t* xe = smem + (int64_t)nq * 16 * a.MA * 32;
-  // 32 zero bytes + one word of unit exponents, read by lanes that hold no
-  // activation row (their A operand is zero)
-  uint8_t* zblk = xe + (int64_t)nq * 16 * a.MA;
-  if (threadIdx.x < 9) ((uint32_t*)zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
-  // base-3: byte value -> its 5 trits as fp4 nibbles (trit 0 -> -1 = 0xA,
-  // 1 -> 0, 2 -> +1 = 0x2), nibble e = trit e (least significant first)
-  uint32_t* t3 = (uint32_t*)(zblk + 48);
+  it.q0 = FMT == 3 ? 2 * (GO * it.ks / a.KS) : a.GQ * it.ks / a.KS;
+  const int64_t q1 = FMT == 3 ? min<int64_t>(2 * (GO * (it.ks + 1) / a.KS), a.GQ)
+                              : a.GQ * (it.ks + 1) / a.KS;
+  it.nq = (int)(q1 - it.q0);
+  it.rb = (int64_t)W * it.rg + w;
+  it.live = it.rb < a.NB;
+  return it;
+}
+
+// packed codes of one quad (4 groups) of one lane, and its 4 fp16 scales
+template <int FMT>
+struct Quad {
+  u4 w[FMT == 1 ? 1 : 2];  // binary: 4 words; 2-bit: P0/P1 of 2 groups per vector
+  u2 c30, c31, c32;        // base-3: 24 bytes of 5-trit bytes
+  uint32_t t3;             // base-3: the two 4-trit bytes of this quad
+  uint2 sc;
+};
+
+// Unconditional loads (the row-block and quad are clamped into the matrix,
+// results of clamped loads are never used), so no load waits on another.
+template <int FMT>
+__device__ __attribute__((always_inline)) inline void load_quad(const FArgs& a, const Item& it,
+                                                               int q, Quad<FMT>& o) {
+  const int L = threadIdx.x & 63, r = L & 15;
+  const int64_t rbc = it.live ? it.rb : a.NB - 1;
+  const int64_t gq = min<int64_t>(it.q0 + q, a.GQ - 1);
+  const u4* pcv = (const u4*)a.pcodes;
+  if constexpr (FMT == 1) {
+    o.w[0] = __builtin_nontemporal_load(&pcv[(rbc * a.GQ + gq) * 64 + L]);
+  } else if constexpr (FMT == 3) {
+    // octet block (rb, gq/2): plane s of lane L at 1024 s + 16 L; the quad's
+    // half h = gq % 2 takes 8-byte chunks 3h .. 3h+2 (chunk c = plane c/2,
+    // half c%2) and bytes 2h, 2h+1 of the 4-byte word at 3072 + 4 L
+    const int64_t GO = cdiv(a.GQ, 2);
+    const uint8_t* ob = a.pcodes + (rbc * GO + (gq >> 1)) * 3328;
+    const int h = (int)(gq & 1);
+    const uint8_t* lp = ob + 16 * L;
+    // chunk c = 3h + cc: plane c / 2, half c % 2
+    o.c30 = __builtin_nontemporal_load((const u2*)(lp + (h ? 1024 + 8 : 0)));
+    o.c31 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 : 8)));
+    o.c32 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 + 8 : 1024)));
+    o.t3 = __builtin_nontemporal_load((const uint32_t*)(ob + 3072 + 4 * L)) >> (16 * h);
+  } else {
+    const int64_t p0 = 2 * gq, p1 = min<int64_t>(2 * gq + 1, a.GP - 1);
+    o.w[0] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p0) * 64 + L]);
+    o.w[1] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p1) * 64 + L]);
+  }
+  const uint2* sbase = a.pscales ? (const uint2*)a.pscales : (const uint2*)a.pcodes;  // any readable memory
+  o.sc = sbase[(rbc * a.GQ + gq) * 16 + r];
+}
+
+// fp4 operand B of group t of a quad
+template <int FMT>
+__device__ __attribute__((always_inline)) inline v8i decode_group(const Quad<FMT>& qd, int t,
+                                                                  const uint32_t* t3) {
+  uint32_t d0, d1, d2, d3;
+  if constexpr (FMT == 1) {
+    const u4 c4 = qd.w[0];
+    const uint32_t wv = t == 0 ? c4.x : t == 1 ? c4.y : t == 2 ? c4.z : c4.w;
+    d0 = (wv & 0x88888888u) | 0x22222222u;
+    d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;
+    d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;
+    d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;
+  } else if constexpr (FMT == 3) {
+    // group t of the quad: bytes 6t .. 6t+5 hold slots 0..29, the 4-trit
+    // byte t/2 digits 2(t%2), 2(t%2)+1 hold slots 30, 31
+    auto word = [&](int wi) {
+      return wi == 0 ? qd.c30.x : wi == 1 ? qd.c30.y : wi == 2 ? qd.c31.x
+           : wi == 3 ? qd.c31.y : wi == 4 ? qd.c32.x : qd.c32.y;
+    };
+    uint32_t nb[6];
+#pragma unroll
+    for (int i = 0; i < 6; i++) {
+      const int byte = 6 * t + i;
+      nb[i] = t3[(word(byte >> 2) >> (8 * (byte & 3))) & 0xFFu];
+    }
+    const uint32_t tl = (t3[(qd.t3 >> (8 * (t >> 1))) & 0xFFu] >> (8 * (t & 1))) & 0xFFu;
+    // slot s -> nibble s of d0..d3 (5 slots per byte)
+    const uint64_t lo = (uint64_t)nb[0] | ((uint64_t)nb[1] << 20) | ((uint64_t)nb[2] << 40) |
+                        ((uint64_t)nb[3] << 60);
+    const uint64_t hi = (uint64_t)(nb[3] >> 4) | ((uint64_t)nb[4] << 16) |
+                        ((uint64_t)nb[5] << 36) | ((uint64_t)tl << 56);
+    d0 = (uint32_t)lo;
+    d1 = (uint32_t)(lo >> 32);
+    d2 = (uint32_t)hi;
+    d3 = (uint32_t)(hi >> 32);
+  } else {
+    const u4 c4 = qd.w[t >> 1];
+    const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
+    d0 = p0 & 0xAAAAAAAAu;
+    d1 = (p0 << 1) & 0xAAAAAAAAu;
+    d2 = p1 & 0xAAAAAAAAu;
+    d3 = (p1 << 1) & 0xAAAAAAAAu;
+  }
+  return v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
+}
+
+// LDS of an item: staged activations, a zero block, the base-3 table
+struct Lds {
+  uint8_t* xa;
+  uint8_t* xe;
+  uint8_t* zblk;
+  uint32_t* t3;
+};
+
+__device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint8_t* smem, int nq) {
+  Lds l;
+  l.xa = smem;
+  l.xe = smem + (int64_t)nq * 16 * a.MA * 32;
+  l.zblk = l.xe + (int64_t)nq * 16 * a.MA;
+  l.t3 = (uint32_t*)(l.zblk + 48);
+  return l;
+}
+
+// 32 zero bytes + one word of unit exponents (read by lanes that hold no
+// activation row: their A operand is zero); base-3: byte value -> its 5
+// trits as fp4 nibbles (trit 0 -> -1 = 0xA, 1 -> 0, 2 -> +1 = 0x2), nibble e
+// = trit e (least significant first)
+template <int FMT>
+__device__ __attribute__((always_inline)) inline void lds_init(const Lds& l) {
+  if (threadIdx.x < 9) ((uint32_t*)l.zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
   if constexpr (FMT == 3) {
     if (threadIdx.x < 243) {
       uint32_t v = threadIdx.x, nib = 0;
@@ -311,172 +422,75 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
         v /= 3;
         nib |= (t == 0 ? 0xAu : t == 2 ? 0x2u : 0u) << (4 * e);
       }
-      t3[threadIdx.x] = nib;
+      l.t3[threadIdx.x] = nib;
     }
   }
+}
 
-  uint4 ra[kStageRounds], rbv[kStageRounds];
-  if constexpr (!WAIT) {
-    // activation loads of the first staging rounds go out first
-#pragma unroll
-    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, false>(a, q0, nq, k, ra[k], rbv[k]);
-  }
-
-  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  const u4* pcv = (const u4*)a.pcodes;
-  const uint2* ps2 = (const uint2*)a.pscales;
-  u4 cw[FMT == 3 ? 1 : QM][NC];
-  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-  u2 c3[FMT == 3 ? QM : 1][3];  // base-3: 24 bytes of 5-trit bytes per quad
-  uint32_t c3t[FMT == 3 ? QM : 1];  // and the lane's word of 4-trit bytes
-  uint2 sc[QM];
-  // Every code and scale of the wave is requested before anything else.  The
-  // loads are unconditional (clamped to the last valid block, results of
-  // clamped loads are never used) so that none of them waits on another.
+// the 4 groups of quad q: operands first, then 4 independent MFMAs, then the
+// per-group scale epilogues (padding groups have zero activations)
+// (BATCH groups at a time: 4 gives the most independent MFMAs, 2 fewer live
+// registers)
+template <int FMT, int XK, int MX, int BATCH = 4>
+__device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, const Lds& l, int q,
+                                                                const Quad<FMT>& qd,
+                                                                float (&acc)[MX], int (&iacc)[MX]) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr bool INTC = XK == XK_I8;
+  const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
+  const bool arow = r < a.MA;
+  const uint32_t se = *(const uint32_t*)(arow ? l.xe + ((q * 4 + lg) * a.MA + r) * 4 : l.zblk + 32);
   const bool unit_scales = a.pscales == nullptr;
-  const uint2* sbase = unit_scales ? (const uint2*)a.pcodes : ps2;  // any readable memory
-  const int64_t rbc = live ? rb : a.NB - 1;
 #pragma unroll
-  for (int q = 0; q < QM; q++) {
-    const int64_t gq = min<int64_t>(q0 + q, a.GQ - 1);
-    if constexpr (FMT == 1) {
-      cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GQ + gq) * 64 + L]);
-    } else if constexpr (FMT == 3) {
-      // octet block (rb, gq/2): plane s of lane L at 1024 s + 16 L; the quad's
-      // half h = gq % 2 takes 8-byte chunks 3h .. 3h+2 (chunk c = plane c/2,
-      // half c%2) and bytes 2h, 2h+1 of the 4-byte word at 3072 + 4 L
-      const uint8_t* ob = a.pcodes + (rbc * GO + (gq >> 1)) * 3328;
-      const int h = (int)(gq & 1);
+  for (int t0 = 0; t0 < 4; t0 += BATCH) {
+    v8i A[BATCH], B[BATCH];
 #pragma unroll
-      for (int cc = 0; cc < 3; cc++) {
-        const int c = 3 * h + cc;
-        c3[q][cc] = __builtin_nontemporal_load((const u2*)(ob + 1024 * (c >> 1) + 16 * L + 8 * (c & 1)));
-      }
-      c3t[q] = __builtin_nontemporal_load((const uint32_t*)(ob + 3072 + 4 * L)) >> (16 * h);
-    } else {
-      const int64_t p0 = 2 * gq, p1 = min<int64_t>(2 * gq + 1, a.GP - 1);
-      cw[q][0] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p0) * 64 + L]);
-      cw[q][NC - 1] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p1) * 64 + L]);
+    for (int u = 0; u < BATCH; u++) {
+      const int t = t0 + u;
+      const uint4* src = (const uint4*)(arow ? l.xa + ((q * 16 + t * 4 + lg) * a.MA + r) * 32 : l.zblk);
+      const uint4 x0 = src[0], x1 = src[1];
+      A[u] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      B[u] = decode_group<FMT>(qd, t, l.t3);
     }
-    sc[q] = sbase[(rbc * a.GQ + gq) * 16 + r];
-  }
-  if constexpr (WAIT) {
-    // the previous product must be complete before its outputs are read; the
-    // weight loads above are already in flight
-    if (threadIdx.x == 0) {
-      for (uint32_t spin = 0;
-           __hip_atomic_load(wait_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target;
-           spin++) {
-        if (spin >= kChainSpinLimit) {  // never satisfied: flag it and go on
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    v4f c[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; u++) {
+      const int t = t0 + u;
+      c[u] = t == 0 ? mfma_group<0>(A[u], B[u], (int)se)
+           : t == 1 ? mfma_group<1>(A[u], B[u], (int)se)
+           : t == 2 ? mfma_group<2>(A[u], B[u], (int)se)
+                    : mfma_group<3>(A[u], B[u], (int)se);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; u++) {
+      const int t = t0 + u;
+      const float s = unit_scales ? 1.0f : f16_bits_to_f32((t < 2 ? qd.sc.x : qd.sc.y) >> (16 * (t & 1)));
+#pragma unroll
+      for (int j = 0; j < MX; j++) {
+        float tsum = c[u][R * j];
+#pragma unroll
+        for (int i = 1; i < R; i++) tsum += c[u][R * j + i];
+        acc[j] = fmaf(s, tsum, acc[j]);
+        if (INTC) iacc[j] += __float2int_rn(tsum);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, true>(a, q0, nq, k, ra[k], rbv[k]);
   }
-#pragma unroll
-  for (int k = 0; k < kStageRounds; k++) stage_convert1<R, XK>(a, q0, nq, k, ra[k], rbv[k], xa, xe);
-  // remaining rounds (small-M products with long slices), loaded and converted in turn
-  const int64_t rounds = cdiv(nq * 64 * a.M, (int64_t)blockDim.x);
-  for (int64_t rd = kStageRounds; rd < rounds; rd++) {
-    uint4 r0, r1;
-    stage_load1<XK, WAIT>(a, q0, nq, rd, r0, r1);
-    stage_convert1<R, XK>(a, q0, nq, rd, r0, r1, xa, xe);
-  }
-  __syncthreads();
+}
 
-  float acc[MX];
-  int iacc[MX];
-#pragma unroll
-  for (int j = 0; j < MX; j++) {
-    acc[j] = 0.f;
-    iacc[j] = 0;
-  }
-  if (live) {
-#pragma unroll
-    for (int q = 0; q < QM; q++) {
-      if (q < nq) {
-        // the 4 groups of the quad: operands first, then 4 independent MFMAs,
-        // then the epilogues (padding groups have zero activations)
-        const uint32_t se = *(const uint32_t*)(arow ? xe + ((q * 4 + lg) * a.MA + r) * 4 : zblk + 32);
-        v8i A[4], B[4];
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          const uint4* src =
-              (const uint4*)(arow ? xa + ((q * 16 + t * 4 + lg) * a.MA + r) * 32 : zblk);
-          const uint4 x0 = src[0], x1 = src[1];
-          A[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          uint32_t d0, d1, d2, d3;
-          if constexpr (FMT == 1) {
-            const u4 c4 = cw[q][0];
-            const uint32_t wv = t == 0 ? c4.x : t == 1 ? c4.y : t == 2 ? c4.z : c4.w;
-            d0 = (wv & 0x88888888u) | 0x22222222u;
-            d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;
-            d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;
-            d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;
-          } else if constexpr (FMT == 3) {
-            // group t of the quad: bytes 6t .. 6t+5 hold slots 0..29, the
-            // 4-trit byte t/2 digits 2(t%2), 2(t%2)+1 hold slots 30, 31
-            const uint32_t w6[6] = {c3[q][0].x, c3[q][0].y, c3[q][1].x,
-                                    c3[q][1].y, c3[q][2].x, c3[q][2].y};
-            uint32_t nb[6];
-#pragma unroll
-            for (int i = 0; i < 6; i++) {
-              const int byte = 6 * t + i;
-              nb[i] = t3[(w6[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
-            }
-            const uint32_t tl = (t3[(c3t[q] >> (8 * (t >> 1))) & 0xFFu] >> (8 * (t & 1))) & 0xFFu;
-            // slot s -> nibble s of d0..d3 (5 slots per byte)
-            const uint64_t lo = (uint64_t)nb[0] | ((uint64_t)nb[1] << 20) | ((uint64_t)nb[2] << 40) |
-                                ((uint64_t)nb[3] << 60);
-            const uint64_t hi = (uint64_t)(nb[3] >> 4) | ((uint64_t)nb[4] << 16) |
-                                ((uint64_t)nb[5] << 36) | ((uint64_t)tl << 56);
-            d0 = (uint32_t)lo;
-            d1 = (uint32_t)(lo >> 32);
-            d2 = (uint32_t)hi;
-            d3 = (uint32_t)(hi >> 32);
-          } else {
-            const u4 c4 = cw[q][(t >> 1) % NC];
-            const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
-            d0 = p0 & 0xAAAAAAAAu;
-            d1 = (p0 << 1) & 0xAAAAAAAAu;
-            d2 = p1 & 0xAAAAAAAAu;
-            d3 = (p1 << 1) & 0xAAAAAAAAu;
-          }
-          B[t] = v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
-        }
-        v4f c[4];
-        c[0] = mfma_group<0>(A[0], B[0], (int)se);
-        c[1] = mfma_group<1>(A[1], B[1], (int)se);
-        c[2] = mfma_group<2>(A[2], B[2], (int)se);
-        c[3] = mfma_group<3>(A[3], B[3], (int)se);
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          const float s = unit_scales
-                              ? 1.0f
-                              : f16_bits_to_f32((t < 2 ? sc[q].x : sc[q].y) >> (16 * (t & 1)));
-#pragma unroll
-          for (int j = 0; j < MX; j++) {
-            float tsum = c[t][R * j];
-#pragma unroll
-            for (int i = 1; i < R; i++) tsum += c[t][R * j + i];
-            acc[j] = fmaf(s, tsum, acc[j]);
-            if (INTC) iacc[j] += __float2int_rn(tsum);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- output
+// Output of an item: direct stores, or (several K-slices) coherent partial
+// sums and, in the last workgroup of the row group to arrive, their sum in
+// slice order.  COH: the outputs themselves are device-coherent stores.
+template <int XK, int MX, int YK, bool COH>
+__device__ __attribute__((always_inline)) inline void item_output(const FArgs& a, const Item& it,
+                                                                  const float (&acc)[MX],
+                                                                  const int (&iacc)[MX]) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr bool INTC = XK == XK_I8;
+  __shared__ uint32_t s_last;
+  const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
   auto store = [&](int64_t m, int64_t n, float f, int iv) {
     const float sxm = a.x_scales ? a.x_scales[m] : a.x_scale;
-    if constexpr (CHAIN) {
+    if constexpr (COH) {
       if (YK == YK_F32)
         __hip_atomic_store((float*)a.y + m * a.N + n, f * sxm, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -493,12 +507,12 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     }
   };
   constexpr bool IPART = INTC && YK == YK_I32;
-  const int64_t n = 16 * rb + r;
+  const int64_t n = 16 * it.rb + r;
   if (a.KS == 1) {
 #pragma unroll
     for (int j = 0; j < MX; j++) {
       const int64_t m = (int64_t)lg * (4 / R) + j;
-      if (live && m < a.M && n < a.N) store(m, n, acc[j], iacc[j]);
+      if (it.live && m < a.M && n < a.N) store(m, n, acc[j], iacc[j]);
     }
     return;
   }
@@ -507,8 +521,8 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
 #pragma unroll
   for (int j = 0; j < MX; j++) {
     const int64_t m = (int64_t)lg * (4 / R) + j;
-    if (live && m < a.M) {
-      float* dst = a.part + (ks * a.M + m) * a.Npad + n;
+    if (it.live && m < a.M) {
+      float* dst = a.part + (it.ks * a.M + m) * a.Npad + n;
       if (IPART) __hip_atomic_store((int*)dst, iacc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -516,14 +530,14 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.cnt + 16 + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = __hip_atomic_fetch_add(a.cnt + 16 + it.rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_last != (uint32_t)(a.KS - 1)) return;
   // last arrival: add the slices in order (coherent loads) and store
 #pragma unroll
   for (int j = 0; j < MX; j++) {
     const int64_t m = (int64_t)lg * (4 / R) + j;
-    if (live && m < a.M && n < a.N) {
+    if (it.live && m < a.M && n < a.N) {
       float f = 0.f;
       int iv = 0;
       for (int64_t k2 = 0; k2 < a.KS; k2++) {
@@ -535,7 +549,85 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     }
   }
   if (threadIdx.x == 0)
-    __hip_atomic_store(a.cnt + 16 + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.cnt + 16 + it.rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int R, int XK>
+__device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, const Item& it,
+                                                                const Lds& l, uint4 (&ra)[kStageRounds],
+                                                                uint4 (&rbv)[kStageRounds],
+                                                                bool coh) {
+#pragma unroll
+  for (int k = 0; k < kStageRounds; k++)
+    stage_convert1<R, XK>(a, it.q0, it.nq, k, ra[k], rbv[k], l.xa, l.xe);
+  // remaining rounds (small-M products with long slices), loaded and converted in turn
+  const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
+  for (int64_t rd = kStageRounds; rd < rounds; rd++) {
+    uint4 r0, r1;
+    if (coh) stage_load1<XK, true>(a, it.q0, it.nq, rd, r0, r1);
+    else stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
+    stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, l.xa, l.xe);
+  }
+}
+
+// One work item, loads issued all at once: the body of the one-product
+// kernel (CHAIN false) and of the chain kernel with waits (CHAIN: outputs
+// are device-coherent; WAIT: the weight loads go out first, then the
+// workgroup waits until `wait_cnt` reaches `wait_target` -- the previous
+// product is complete -- and reads its activations with coherent loads).
+template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT>
+__device__ __attribute__((always_inline)) inline void gemv_item(
+    const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
+    uint32_t* err) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  const Item it = item_of<FMT>(a, blk);
+  const Lds l = lds_of(a, smem, it.nq);
+  lds_init<FMT>(l);
+
+  uint4 ra[kStageRounds], rbv[kStageRounds];
+  if constexpr (!WAIT) {
+    // activation loads of the first staging rounds go out first
+#pragma unroll
+    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, false>(a, it.q0, it.nq, k, ra[k], rbv[k]);
+  }
+  // every code and scale of the wave is requested before anything else
+  Quad<FMT> qd[QM];
+#pragma unroll
+  for (int q = 0; q < QM; q++) load_quad<FMT>(a, it, q, qd[q]);
+  if constexpr (WAIT) {
+    // the previous product must be complete before its outputs are read; the
+    // weight loads above are already in flight
+    if (threadIdx.x == 0) {
+      for (uint32_t spin = 0;
+           __hip_atomic_load(wait_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target;
+           spin++) {
+        if (spin >= kChainSpinLimit) {  // never satisfied: flag it and go on
+          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, true>(a, it.q0, it.nq, k, ra[k], rbv[k]);
+  }
+  stage_all<R, XK>(a, it, l, ra, rbv, WAIT);
+  __syncthreads();
+
+  float acc[MX];
+  int iacc[MX];
+#pragma unroll
+  for (int j = 0; j < MX; j++) {
+    acc[j] = 0.f;
+    iacc[j] = 0;
+  }
+  if (it.live) {
+#pragma unroll
+    for (int q = 0; q < QM; q++)
+      if (q < it.nq) quad_mfma<FMT, XK, MX>(a, l, q, qd[q], acc, iacc);
+  }
+  item_output<XK, MX, YK, CHAIN>(a, it, acc, iacc);
 }
 
 template <int FMT, int XK, int MX, int YK, int QM>
@@ -554,29 +646,70 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
 // by kChainSpinLimit.  The last workgroup to finish resets the counters.
 struct ChainArgs {
   const FArgs* args;       // [S]
-  const int64_t* first;    // [S + 1]
+  const int64_t* first;    // [S + 1] work items (row group x K-slice) before product s
   const int32_t* wait;     // [S]
   uint32_t* done;          // [S], zero between launches
   uint32_t* finished;      // workgroups done, zero between launches
   uint32_t* err;           // set when a wait gave up
+  // streaming kernel only
+  const int64_t* ufirst;   // [S + 1] row groups before product s
+  const int64_t* sfirst;   // [S + 1] K-slices before product s
+  const int64_t* xoff;     // [S] byte offset of product s's staged activations in xst
+  uint8_t* xst;            // staged activations of every product and K-slice
+  uint32_t* bar;           // grid barrier arrivals, zero between launches
   int S;
 };
+
+// The chain tables are read through the constant address space: scalar
+// loads (counted by lgkmcnt), so reading the next item's descriptor never
+// waits for the vector loads of codes in flight.
+#define LOWBIT_CONST __attribute__((address_space(4)))
+typedef const LOWBIT_CONST FArgs* FArgsTab;
+typedef const LOWBIT_CONST int64_t* I64Tab;
+typedef const LOWBIT_CONST int32_t* I32Tab;
+
+__device__ __attribute__((always_inline)) inline FArgs load_args(FArgsTab t, int s) {
+  FArgs a;
+  a.pcodes = t[s].pcodes;
+  a.pscales = t[s].pscales;
+  a.x = t[s].x;
+  a.x_scales = t[s].x_scales;
+  a.y = t[s].y;
+  a.part = t[s].part;
+  a.cnt = t[s].cnt;
+  a.N = t[s].N;
+  a.K = t[s].K;
+  a.G = t[s].G;
+  a.GQ = t[s].GQ;
+  a.GP = t[s].GP;
+  a.M = t[s].M;
+  a.MA = t[s].MA;
+  a.NB = t[s].NB;
+  a.KS = t[s].KS;
+  a.Npad = t[s].Npad;
+  a.x_scale = t[s].x_scale;
+  a.xkind = t[s].xkind;
+  return a;
+}
 
 template <int FMT, int XK, int YK, int QM>
 __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_chain(ChainArgs c) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int64_t total = c.first[c.S];
+  const FArgsTab args = (FArgsTab)c.args;
+  const I64Tab first = (I64Tab)c.first;
+  const I32Tab waitf = (I32Tab)c.wait;
+  const int64_t total = first[c.S];
   int s = 0;
   for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
-    while (i >= c.first[s + 1]) s++;
-    const FArgs a = c.args[s];
-    const bool wt = s > 0 && c.wait[s] != 0;
+    while (i >= first[s + 1]) s++;
+    const FArgs a = load_args(args, s);
+    const bool wt = s > 0 && waitf[s] != 0;
     __syncthreads();  // the previous item's LDS reads are over
     if (wt)
-      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - c.first[s], smem, c.done + s - 1,
-                                                (uint32_t)(c.first[s] - c.first[s - 1]), c.err);
+      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - first[s], smem, c.done + s - 1,
+                                                (uint32_t)(first[s] - first[s - 1]), c.err);
     else
-      gemv_item<FMT, XK, 1, YK, QM, true, false>(a, i - c.first[s], smem, nullptr, 0u, c.err);
+      gemv_item<FMT, XK, 1, YK, QM, true, false>(a, i - first[s], smem, nullptr, 0u, c.err);
     __builtin_amdgcn_s_waitcnt(0);  // this item's stores have completed
     __syncthreads();
     if (threadIdx.x == 0)
@@ -589,6 +722,267 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     if (prev == gridDim.x - 1) {
       for (int k = 0; k < c.S; k++)
         __hip_atomic_store(c.done + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Persistent chain without waits, software-pipelined.
+//
+// Prologue: the workgroups stage the activations of every product and
+// K-slice (fp8 split terms + block exponents) into a global buffer, then
+// meet at a grid barrier (the launch is cooperative, so all workgroups are
+// resident).
+//
+// Main loop: a workgroup takes whole row groups (all K-slices in turn,
+// accumulating in registers, so there are no split-K partial sums) of the
+// products in order, row group u, u + gridDim.x, ...; each wave owns one
+// row-block of it.  While a wave computes quad q of one slice, the codes
+// and scales of quad q of its next slice (and the staged activations of
+// the slice after) are
+// already in flight, so every wave keeps a full slice of loads outstanding
+// across slice, row-group and product boundaries.
+template <int FMT>
+__device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArgs& a) {
+  const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
+  return qmax * 16 * a.MA * 33;
+}
+
+template <int FMT, int XK, int YK, int QM>
+__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_stream(ChainArgs c) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const FArgsTab args = (FArgsTab)c.args;
+  const I64Tab ufirst = (I64Tab)c.ufirst;
+  const I64Tab sfirst = (I64Tab)c.sfirst;
+  const I64Tab xoff = (I64Tab)c.xoff;
+
+  // ---- prologue: stage every (product, K-slice) once
+  {
+    const int64_t nsl = sfirst[c.S];
+    int s = 0;
+    for (int64_t j = blockIdx.x; j < nsl; j += gridDim.x) {
+      while (j >= sfirst[s + 1]) s++;
+      const FArgs a = load_args(args, s);
+      const int64_t ks = j - sfirst[s];
+      const Item it = item_of<FMT>(a, ks);  // row group 0 of slice ks
+      uint8_t* xa = c.xst + xoff[s] + ks * slice_stride<FMT>(a);
+      uint8_t* xe = xa + (int64_t)it.nq * 16 * a.MA * 32;
+      const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
+      for (int64_t rd = 0; rd < rounds; rd++) {
+        uint4 r0, r1;
+        stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
+        stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(c.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t spin = 0;
+           __hip_atomic_load(c.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x; spin++) {
+        if (spin >= kChainSpinLimit) {
+          __hip_atomic_store(c.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+  }
+
+  // ---- main loop
+  // LDS: two buffers, each the image of one staged slice (slice j uses
+  // buffer j & 1), then the zero block / base-3 table and four counters:
+  // filled[b] counts the waves that wrote their share of an image into
+  // buffer b, consumed[b] the waves that finished computing from it.  A wave
+  // writes its share of slice j+1 part-way through slice j, so waves are
+  // only ever held back by a wave more than about one slice behind (there is
+  // no workgroup barrier in the loop).
+  constexpr int XR = (QM * 16 * R * 33 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
+  constexpr int kWriteAfter = 3;  // quads computed before the next image is written
+  const int64_t bufsz = (int64_t)QM * 16 * R * 33;
+  auto xbuf = [&](uint32_t b) { return smem + b * bufsz; };
+  Lds lfix;
+  lfix.zblk = smem + 2 * bufsz;
+  lfix.t3 = (uint32_t*)(lfix.zblk + 48);
+  uint32_t* filled = (uint32_t*)(lfix.zblk + 48 + 1024);
+  uint32_t* consumed = filled + 2;
+  lds_init<FMT>(lfix);
+  if (threadIdx.x < 4) filled[threadIdx.x] = 0;
+
+  const int64_t total = ufirst[c.S];
+  int64_t u = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (u < total) {
+    int s = 0;
+    while (u >= ufirst[s + 1]) s++;
+    FArgs a = load_args(args, s);
+    int64_t rg = u - ufirst[s], ks = 0;
+    Item it = item_of<FMT>(a, rg * a.KS);
+    // staged activations of a slice, XR 16-byte pieces per thread
+    auto xsrc = [&](const FArgs& f, int sidx, int64_t kslice, int nq, int k) {
+      const int64_t nb = (int64_t)nq * 16 * f.MA * 33 / 16;
+      const int64_t piece = min<int64_t>((int64_t)k * 64 * kMaxW + tid, nb - 1);
+      return (const uint4*)(c.xst + xoff[sidx] + kslice * slice_stride<FMT>(f)) + piece;
+    };
+    // a slice image travels in up to six 16-byte registers per thread (named
+    // registers, not an array, so that they never live in scratch memory)
+    uint4 x0, x1, x2, x3, x4, x5;
+    static_assert(XR <= 6, "slice image larger than six 16-byte pieces per thread");
+#define XLD(F, SI, KS_, NQ)                                                                  \
+  {                                                                                          \
+    x0 = *xsrc(F, SI, KS_, NQ, 0);                                                           \
+    if (XR > 1) x1 = *xsrc(F, SI, KS_, NQ, 1);                                               \
+    if (XR > 2) x2 = *xsrc(F, SI, KS_, NQ, 2);                                               \
+    if (XR > 3) x3 = *xsrc(F, SI, KS_, NQ, 3);                                               \
+    if (XR > 4) x4 = *xsrc(F, SI, KS_, NQ, 4);                                               \
+    if (XR > 5) x5 = *xsrc(F, SI, KS_, NQ, 5);                                               \
+  }
+#define XPUT(DST, NQ)                                                                        \
+  {                                                                                          \
+    const int64_t nb_ = (int64_t)(NQ) * 16 * R * 33 / 16;                                    \
+    uint4* d_ = (uint4*)(DST);                                                               \
+    constexpr int T_ = 64 * kMaxW;                                                           \
+    if (tid < nb_) d_[tid] = x0;                                                             \
+    if (XR > 1 && T_ + tid < nb_) d_[T_ + tid] = x1;                                         \
+    if (XR > 2 && 2 * T_ + tid < nb_) d_[2 * T_ + tid] = x2;                                 \
+    if (XR > 3 && 3 * T_ + tid < nb_) d_[3 * T_ + tid] = x3;                                 \
+    if (XR > 4 && 4 * T_ + tid < nb_) d_[4 * T_ + tid] = x4;                                 \
+    if (XR > 5 && 5 * T_ + tid < nb_) d_[5 * T_ + tid] = x5;                                 \
+  }
+    XLD(a, s, ks, it.nq);
+    XPUT(xbuf(0), it.nq);
+    __syncthreads();
+
+    // next slice of this workgroup after (s, rg, ks): the same row group's
+    // next K-slice, or the next row group; `more` false at the end (then the
+    // current slice is returned again, as harmless dummy loads)
+    auto next = [&](int s0, int64_t u0, int64_t rg0, int64_t ks0, const FArgs& f, int& s1,
+                    int64_t& u1, int64_t& rg1, int64_t& ks1) {
+      s1 = s0;
+      u1 = u0;
+      rg1 = rg0;
+      ks1 = ks0 + 1;
+      if (ks1 < f.KS) return true;
+      ks1 = 0;
+      u1 = u0 + gridDim.x;
+      if (u1 >= total) {
+        u1 = u0;
+        ks1 = ks0;
+        return false;
+      }
+      while (u1 >= ufirst[s1 + 1]) s1++;
+      rg1 = u1 - ufirst[s1];
+      return true;
+    };
+    int sn;
+    int64_t un, rgn, ksn;
+    bool more = next(s, u, rg, ks, a, sn, un, rgn, ksn);
+    FArgs an = load_args(args, sn);
+    Item itn = item_of<FMT>(an, rgn * an.KS + ksn);
+    // the next slice's activations, then the current slice's codes
+    XLD(an, sn, ksn, itn.nq);
+    Quad<FMT> qd[QM];
+#pragma unroll
+    for (int q = 0; q < QM; q++) load_quad<FMT>(a, it, q, qd[q]);
+    float acc[1] = {0.f};
+    int iacc[1] = {0};
+    float tot = 0.f;  // slices added in slice order, as the split-K reduction does
+    uint32_t j = 0;   // slice number of this workgroup
+
+    auto wait_ge = [&](uint32_t* ctr, uint32_t target) {
+      if ((threadIdx.x & 63) == 0) {
+        for (uint32_t spin = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; spin++) {
+          if (spin >= kChainSpinLimit) {
+            __hip_atomic_store(c.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    for (;;) {
+      // the slice after next (its activations are loaded while this one computes)
+      int s2;
+      int64_t u2, rg2, ks2;
+      const bool more2 = more && next(sn, un, rgn, ksn, an, s2, u2, rg2, ks2);
+      if (!more) {
+        s2 = sn;
+        u2 = un;
+        rg2 = rgn;
+        ks2 = ksn;
+      }
+      // slice j's image is complete once every wave wrote its share (slice 0's
+      // was written before the loop; buffer j & 1 is filled for slices j, j-2,
+      // ... down to 1 or 2: (j + 1) / 2 times)
+      const uint32_t b = j & 1;
+      if (j > 0) wait_ge(filled + b, 4u * ((j + 1) >> 1));
+      Lds l = lfix;
+      l.xa = xbuf(b);
+      l.xe = xbuf(b) + (int64_t)it.nq * 16 * a.MA * 32;
+#pragma unroll
+      for (int q = 0; q < QM; q++) {
+        if (q == kWriteAfter) {
+          if (more) {
+            // this wave's share of slice j+1's image, into the other buffer
+            // once every wave is done with slice j-1
+            wait_ge(consumed + (b ^ 1), 4u * ((j + 1) >> 1));
+            XPUT(xbuf(b ^ 1), itn.nq);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the share is written
+            if ((threadIdx.x & 63) == 0)
+              __hip_atomic_fetch_add(filled + (b ^ 1), 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          // then the activations of the slice after next (issued on every
+          // path, so that the wait counts stay exact across iterations)
+          const FArgs a2 = load_args(args, s2);
+          const Item it2 = item_of<FMT>(a2, rg2 * a2.KS + ks2);
+          XLD(a2, s2, ks2, it2.nq);
+        }
+        if (it.live && q < it.nq) quad_mfma<FMT, XK, 1, 2>(a, l, q, qd[q], acc, iacc);
+        load_quad<FMT>(an, itn, q, qd[q]);
+      }
+      // done reading slice j's image
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(consumed + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      tot = a.KS == 1 ? acc[0] : tot + acc[0];
+      acc[0] = 0.f;
+      if (ks == a.KS - 1) {
+        // row group complete: one output per row (lanes of the first row of A)
+        const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
+        const int64_t n = 16 * it.rb + r;
+        if (it.live && lg == 0 && n < a.N) {
+          if (YK == YK_F32) ((float*)a.y)[n] = tot;
+          else ((uint16_t*)a.y)[n] = (uint16_t)bf16_rne(tot);
+        }
+        tot = 0.f;
+      }
+      if (!more) break;
+      s = sn; u = un; rg = rgn; ks = ksn;
+      a = load_args(args, s);
+      it = itn;
+      sn = s2; un = u2; rgn = rg2; ksn = ks2;
+      more = more2;
+      an = load_args(args, sn);
+      itn = item_of<FMT>(an, rgn * an.KS + ksn);
+      j++;
+    }
+  }
+
+#undef XLD
+#undef XPUT
+  // ---- the last workgroup to finish resets the barrier
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(c.finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(c.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -607,7 +1001,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
 constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
 
-Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
+Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0) {
   Plan p;
   p.R = split_terms(xkind);
   p.MA = M * p.R;
@@ -615,7 +1009,7 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
   p.G = K / kGroup;
   p.GQ = cdiv(p.G, 4);
   p.GP = cdiv(p.G, 2);
-  p.QM = fmt == 1 ? kQuadsBinary : kQuadsTernary;
+  p.QM = quads > 0 ? quads : fmt == 1 ? kQuadsBinary : kQuadsTernary;
   // staged activations of a slice stay within 48 KiB of LDS
   int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (48 * 1024) / (16 * p.MA * 33)));
   if (fmt == 3) {
@@ -710,10 +1104,14 @@ struct ChainPlan {
 };
 
 template <int FMT, int XK>
-const void* chain_kernel(int ykind) {
+const void* chain_kernel(int ykind, bool waits) {
   constexpr int QM = FMT == 1 ? kQuadsBinary : kQuadsTernary;
-  if (ykind == YK_BF16) return (const void*)gemv_chain<FMT, XK, YK_BF16, QM>;
-  return (const void*)gemv_chain<FMT, XK, YK_F32, QM>;
+  if (waits) {
+    if (ykind == YK_BF16) return (const void*)gemv_chain<FMT, XK, YK_BF16, QM>;
+    return (const void*)gemv_chain<FMT, XK, YK_F32, QM>;
+  }
+  if (ykind == YK_BF16) return (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary>;
+  return (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary>;
 }
 
 }  // namespace
@@ -726,14 +1124,25 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   std::vector<int64_t> first(S + 1, 0);
   std::vector<int32_t> wait(S, 0);
   std::vector<int64_t> cnt_off(S), part_off(S);
-  int64_t cnt_words = 16, part_floats = 0;
-  size_t lds = 0;
+  std::vector<int64_t> ufirst(S + 1, 0), sfirst(S + 1, 0), xoff(S, 0);
+  int64_t cnt_words = 16, part_floats = 0, xst_bytes = 0;
+  bool waits = false;
+  for (int i = 1; i < S; i++) waits = waits || st[i].wait_prev != 0;
+  // the streaming kernel keeps kQuadsTernary quads of every format in flight
+  const int quads = waits ? 0 : kQuadsTernary;
+  const int R = split_terms(xkind);
+  size_t lds = waits ? 0 : 2 * (size_t)kQuadsTernary * 16 * R * 33 + 48 + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
-    const Plan p = make_plan(fmt, st[i].N, st[i].K, 1, xkind);
+    const Plan p = make_plan(fmt, st[i].N, st[i].K, 1, xkind, quads);
     if (p.lds > 64 * 1024) return hipErrorInvalidValue;
-    lds = std::max(lds, p.lds);
+    if (waits) lds = std::max(lds, p.lds);
     first[i + 1] = first[i] + p.NRG * p.KS;
+    ufirst[i + 1] = ufirst[i] + p.NRG;
+    sfirst[i + 1] = sfirst[i] + p.KS;
+    xoff[i] = xst_bytes;
+    const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
+    xst_bytes += p.KS * qmax * 16 * p.MA * 33;
     wait[i] = st[i].wait_prev ? 1 : 0;
     cnt_off[i] = cnt_words;
     cnt_words += p.NRG;
@@ -765,9 +1174,13 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   const size_t o_wait = align256(o_first + sizeof(int64_t) * (S + 1));
   const size_t o_done = align256(o_wait + sizeof(int32_t) * S);
   const size_t o_fin = align256(o_done + sizeof(uint32_t) * S);
-  const size_t o_cnt = align256(o_fin + 2 * sizeof(uint32_t));
+  const size_t o_cnt = align256(o_fin + 4 * sizeof(uint32_t));
   const size_t o_part = align256(o_cnt + sizeof(uint32_t) * cnt_words);
-  const size_t bytes = o_part + sizeof(float) * (size_t)part_floats;
+  const size_t o_uf = align256(o_part + sizeof(float) * (size_t)part_floats);
+  const size_t o_sf = align256(o_uf + sizeof(int64_t) * (S + 1));
+  const size_t o_xo = align256(o_sf + sizeof(int64_t) * (S + 1));
+  const size_t o_xst = align256(o_xo + sizeof(int64_t) * S);
+  const size_t bytes = o_xst + (size_t)xst_bytes + 256;
 
   ChainPlan* c = new ChainPlan;
   hipError_t e = hipGetDevice(&c->device);
@@ -786,10 +1199,14 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   if (e == hipSuccess) e = hipMemcpy(m + o_args, args.data(), sizeof(FArgs) * S, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(m + o_first, first.data(), sizeof(int64_t) * (S + 1), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(m + o_wait, wait.data(), sizeof(int32_t) * S, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_uf, ufirst.data(), sizeof(int64_t) * (S + 1), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_sf, sfirst.data(), sizeof(int64_t) * (S + 1), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_xo, xoff.data(), sizeof(int64_t) * S, hipMemcpyHostToDevice);
   if (e == hipSuccess) {
-    if (fmt == 1) c->kernel = xkind == XK_F32 ? chain_kernel<1, XK_F32>(ykind) : chain_kernel<1, XK_BF16>(ykind);
-    else if (fmt == 2) c->kernel = xkind == XK_F32 ? chain_kernel<2, XK_F32>(ykind) : chain_kernel<2, XK_BF16>(ykind);
-    else if (fmt == 3) c->kernel = xkind == XK_F32 ? chain_kernel<3, XK_F32>(ykind) : chain_kernel<3, XK_BF16>(ykind);
+    const bool f32 = xkind == XK_F32;
+    if (fmt == 1) c->kernel = f32 ? chain_kernel<1, XK_F32>(ykind, waits) : chain_kernel<1, XK_BF16>(ykind, waits);
+    else if (fmt == 2) c->kernel = f32 ? chain_kernel<2, XK_F32>(ykind, waits) : chain_kernel<2, XK_BF16>(ykind, waits);
+    else if (fmt == 3) c->kernel = f32 ? chain_kernel<3, XK_F32>(ykind, waits) : chain_kernel<3, XK_BF16>(ykind, waits);
     else e = hipErrorInvalidValue;
   }
   int per_cu = 0, cus = 0;
@@ -811,6 +1228,11 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   c->args.done = (uint32_t*)(m + o_done);
   c->args.finished = (uint32_t*)(m + o_fin);
   c->args.err = (uint32_t*)(m + o_fin) + 1;
+  c->args.bar = (uint32_t*)(m + o_fin) + 2;
+  c->args.ufirst = (const int64_t*)(m + o_uf);
+  c->args.sfirst = (const int64_t*)(m + o_sf);
+  c->args.xoff = (const int64_t*)(m + o_xo);
+  c->args.xst = m + o_xst;
   c->args.S = S;
   c->err = c->args.err;
   *out = c;
