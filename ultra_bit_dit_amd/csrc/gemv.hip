@@ -552,14 +552,50 @@ __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a
     __hip_atomic_store(a.cnt + 16 + it.rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The raw activations of the first kStageRounds staging rounds, in named
+// registers (an array of them may be left in scratch memory by the compiler,
+// and every scratch access waits for all loads in flight).
+struct XRegs {
+  uint4 a0, a1, a2, a3, a4, b0, b1, b2, b3, b4;
+};
+static_assert(kStageRounds == 5, "XRegs holds five staging rounds");
+
+template <int K>
+__device__ __attribute__((always_inline)) inline uint4& xa_reg(XRegs& x) {
+  if constexpr (K == 0) return x.a0;
+  else if constexpr (K == 1) return x.a1;
+  else if constexpr (K == 2) return x.a2;
+  else if constexpr (K == 3) return x.a3;
+  else return x.a4;
+}
+template <int K>
+__device__ __attribute__((always_inline)) inline uint4& xb_reg(XRegs& x) {
+  if constexpr (K == 0) return x.b0;
+  else if constexpr (K == 1) return x.b1;
+  else if constexpr (K == 2) return x.b2;
+  else if constexpr (K == 3) return x.b3;
+  else return x.b4;
+}
+
+template <int XK, bool COH, int K = 0>
+__device__ __attribute__((always_inline)) inline void stage_load_rounds(const FArgs& a,
+                                                                        const Item& it, XRegs& x) {
+  stage_load1<XK, COH>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x));
+  if constexpr (K + 1 < kStageRounds) stage_load_rounds<XK, COH, K + 1>(a, it, x);
+}
+
+template <int R, int XK, int K = 0>
+__device__ __attribute__((always_inline)) inline void stage_convert_rounds(const FArgs& a,
+                                                                           const Item& it,
+                                                                           const Lds& l, XRegs& x) {
+  stage_convert1<R, XK>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe);
+  if constexpr (K + 1 < kStageRounds) stage_convert_rounds<R, XK, K + 1>(a, it, l, x);
+}
+
 template <int R, int XK>
 __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, const Item& it,
-                                                                const Lds& l, uint4 (&ra)[kStageRounds],
-                                                                uint4 (&rbv)[kStageRounds],
-                                                                bool coh) {
-#pragma unroll
-  for (int k = 0; k < kStageRounds; k++)
-    stage_convert1<R, XK>(a, it.q0, it.nq, k, ra[k], rbv[k], l.xa, l.xe);
+                                                                const Lds& l, XRegs& x, bool coh) {
+  stage_convert_rounds<R, XK>(a, it, l, x);
   // remaining rounds (small-M products with long slices), loaded and converted in turn
   const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
   for (int64_t rd = kStageRounds; rd < rounds; rd++) {
@@ -584,11 +620,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   const Lds l = lds_of(a, smem, it.nq);
   lds_init<FMT>(l);
 
-  uint4 ra[kStageRounds], rbv[kStageRounds];
+  XRegs xr;
   if constexpr (!WAIT) {
     // activation loads of the first staging rounds go out first
-#pragma unroll
-    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, false>(a, it.q0, it.nq, k, ra[k], rbv[k]);
+    stage_load_rounds<XK, false>(a, it, xr);
   }
   // every code and scale of the wave is requested before anything else
   Quad<FMT> qd[QM];
@@ -609,10 +644,9 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kStageRounds; k++) stage_load1<XK, true>(a, it.q0, it.nq, k, ra[k], rbv[k]);
+    stage_load_rounds<XK, true>(a, it, xr);
   }
-  stage_all<R, XK>(a, it, l, ra, rbv, WAIT);
+  stage_all<R, XK>(a, it, l, xr, WAIT);
   __syncthreads();
 
   float acc[MX];
