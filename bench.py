@@ -129,9 +129,15 @@ def pmc_traffic(launch_bytes, kernel):
         w_scale = copy_bytes / (float(kv["copy_WRITE_SIZE_KiB"]) * 1024.0)
         fetch = float(kv["gemv_FETCH_SIZE_KiB_per_dispatch"]) * 1024.0 * f_scale
         write = float(kv["gemv_WRITE_SIZE_KiB_per_dispatch"]) * 1024.0 * w_scale
-        return fetch + write, (f"rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a "
-                               f"{copy_bytes / 2**20:.0f} MiB copy (x{f_scale:.3f} / x{w_scale:.3f}); "
-                               f"{(fetch + write) / launch_bytes:.3f} x the algorithmic bytes")
+        # the counters were taken on a launch of the same kernel over fewer
+        # layers (the profiler cannot count the full build); traffic per
+        # algorithmic byte carries over to this launch
+        ratio = (fetch + write) / float(kv["profiled_algorithmic_bytes_per_dispatch"])
+        return ratio * launch_bytes, (
+            f"rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a "
+            f"{copy_bytes / 2**20:.0f} MiB copy (x{f_scale:.3f} / x{w_scale:.3f}), measured on a "
+            f"launch of {float(kv['profiled_algorithmic_bytes_per_dispatch']) / 1e6:.0f} MB and "
+            f"carried over per byte: {ratio:.3f} x the algorithmic bytes")
     except (OSError, KeyError, ValueError):
         return None, "no counter summary"
 
@@ -200,9 +206,9 @@ def bench_decode(args, lb, synth, torch, np):
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launch_bytes = step_bytes / launches
     launch_us = ms * 1e3 / launches
-    traffic, tnote = pmc_traffic(launch_bytes, "gemv_chain" if head.startswith("chain") else "gemv_mfma")
-    kname = ("gemv_chain" if head.startswith("chain") else "gemv_mfma") + \
-        (" (ternary 2-bit" if fmt == 2 else " (binary") + ", bf16 x, fp32 y)"
+    kbase = {"chain": "gemv_stream", "chain_dep": "gemv_chain", "separate": "gemv_mfma"}[head]
+    traffic, tnote = pmc_traffic(launch_bytes, kbase)
+    kname = kbase + (" (ternary 2-bit" if fmt == 2 else " (binary") + ", bf16 x, fp32 y)"
     roof = {"bound": "hbm", "kernel": kname,
             "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(launch_bytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
