@@ -124,6 +124,62 @@ __global__ __launch_bounds__(256) void stage_f16(int64_t M, int64_t K, int64_t G
   }
 }
 
+// The same with the row read once, coalesced, into LDS (rows up to
+// kStageLdsMax elements): the maximum is taken during that read and the
+// permuted gather then reads LDS instead of global memory.
+constexpr int64_t kStageLdsMax = 24576;  // bf16 elements (48 KiB of LDS)
+
+template <int FMT>
+__global__ __launch_bounds__(256) void stage_f16_lds(int64_t M, int64_t K, int64_t G,
+                                                     const uint16_t* __restrict__ X,
+                                                     uint8_t* __restrict__ xt,
+                                                     float* __restrict__ xinv) {
+  __shared__ __attribute__((aligned(16))) uint16_t srow[kStageLdsMax];
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const v4u* row = (const v4u*)(X + m * K);
+  float a = 0.0f;
+  for (int64_t k8 = threadIdx.x; k8 < K / 8; k8 += 256) {
+    const v4u w = row[k8];
+    ((v4u*)srow)[k8] = w;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      a = fmaxf(a, fabsf(__uint_as_float(w[j] << 16)));
+      a = fmaxf(a, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (a > 0.0f && a <= 3.0e38f) {
+    int ex;
+    (void)frexpf(a, &ex);
+    e = min(max(15 - ex, -126), 126);
+  }
+  const float up = ldexpf(1.0f, e);
+  if (threadIdx.x == 0) xinv[m] = ldexpf(1.0f, -e);
+  const int64_t mt = m / kTM;
+  const int r = (int)(m % kTM);
+  for (int64_t ci = threadIdx.x; ci < G * 16; ci += 256) {
+    const int64_t g = ci >> 4;
+    const int c = (int)(ci & 15);
+    const uint16_t* src = srow + g * kGroup;
+    uint32_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float v0 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j)] << 16) * up;
+      const float v1 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j + 1)] << 16) * up;
+      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;  // round to nearest even
+      h[j] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
+             ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+    }
+    uint8_t* dst = xt + (mt * G + g) * (int64_t)kTileF16 + swz_f16(r, c);
+    *(v4u*)dst = v4u{h[0], h[1], h[2], h[3]};
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void stage_i8(int64_t M, int64_t K, int64_t G,
                                                 const int8_t* __restrict__ X,
@@ -196,43 +252,58 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, T v) {
 }
 
 // Split-K: every split stores its partial tile (lane-major, so the stores
-// are coalesced) with device-coherent stores, then bumps the tile counter;
-// the last split to arrive adds all partials in split order (deterministic)
-// and resets the counter.  Returns true in the workgroup that must write Y.
-// INT: the values are int32 bit patterns and are added as integers.
+// are coalesced), makes it visible device-wide (agent-scope release) and
+// bumps the tile counter; the last split to arrive (agent-scope acquire)
+// adds all partials in split order (deterministic) and resets the counter.
+// Its loads go out 32 values at a time, so the reduction costs a few memory
+// round trips rather than one per value.  Returns true in the workgroup that
+// must write Y.  INT: the values are int32 bit patterns, added as integers.
 template <int NV, bool INT>
 __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int ks, int wave,
                                              int lane, uint32_t (&v)[NV]) {
+  constexpr int CH = 32;  // values per batch of loads
+  static_assert(NV % CH == 0, "partial tile in whole batches");
   __shared__ uint32_t s_last;
   const int64_t per = (int64_t)(kThreads / 64) * NV * 64;  // words of one partial tile
   uint32_t* part = (uint32_t*)a.part;
   uint32_t* mine = part + (tile * a.KS + ks) * per + (int64_t)wave * NV * 64 + lane;
 #pragma unroll
-  for (int i = 0; i < NV; i++)
-    __hip_atomic_store(mine + i * 64, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < NV; i++) mine[i * 64] = v[i];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev = __hip_atomic_fetch_add(a.cnt + 16 + tile, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (uint32_t)(a.KS - 1);
+    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return false;
 #pragma unroll
-  for (int i = 0; i < NV; i++) {
-    float fs = 0.0f;
-    int32_t is = 0;
-    for (int k = 0; k < a.KS; k++) {
-      const uint32_t* src = part + (tile * a.KS + k) * per + (int64_t)wave * NV * 64 + lane + i * 64;
-      const uint32_t x =
-          k == ks ? v[i] : __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if constexpr (INT)
-        is += (int32_t)x;
-      else
-        fs += __uint_as_float(x);
+  for (int i0 = 0; i0 < NV; i0 += CH) {
+    float fs[CH];
+    int32_t is[CH];
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      fs[i] = 0.0f;
+      is[i] = 0;
     }
-    v[i] = INT ? (uint32_t)is : __float_as_uint(fs);
+    for (int k = 0; k < a.KS; k++) {
+      const uint32_t* src = part + (tile * a.KS + k) * per + (int64_t)wave * NV * 64 + lane;
+      uint32_t x[CH];
+#pragma unroll
+      for (int i = 0; i < CH; i++) x[i] = k == ks ? v[i0 + i] : src[(i0 + i) * 64];
+#pragma unroll
+      for (int i = 0; i < CH; i++) {
+        if constexpr (INT)
+          is[i] += (int32_t)x[i];
+        else
+          fs[i] += __uint_as_float(x[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CH; i++) v[i0 + i] = INT ? (uint32_t)is[i] : __float_as_uint(fs[i]);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.cnt + 16 + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -337,22 +408,34 @@ __global__ __launch_bounds__(kThreads) void gemm_f16(KArgs a) {
     for (int j = 0; j < 8; j++) xr[j] = *(const v4u*)(xt + gn * kTileF16 + (j * kThreads + tid) * 16);
     const WordsF16<FMT> wn = load_words_f16<FMT>(a, rb, r, h, gn);
     const uint8_t* L = lds[buf];
+    // software pipeline over the 8 MFMA steps of the group: the operands of
+    // step t+1 are read from LDS and decoded while the MFMAs of step t run
+    v8h A[2][4], B[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      A[0][i] = __builtin_bit_cast(v8h, *(const v4u*)(L + swz_f16(32 * i + n, h)));
+#pragma unroll
+    for (int b = 0; b < 2; b++) B[0][b] = decode_f16<FMT>(wc, b, 0);
 #pragma unroll
     for (int t = 0; t < 8; t++) {
-      v8h B[2];
+      const int cu = t & 1, nx = cu ^ 1;
+      if (t + 1 < 8) {
 #pragma unroll
-      for (int b = 0; b < 2; b++) B[b] = decode_f16<FMT>(wc, b, t);
+        for (int i = 0; i < 4; i++)
+          A[nx][i] = __builtin_bit_cast(v8h, *(const v4u*)(L + swz_f16(32 * i + n, 2 * (t + 1) + h)));
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const v8h A = __builtin_bit_cast(v8h, *(const v4u*)(L + swz_f16(32 * i + n, 2 * t + h)));
+        for (int b = 0; b < 2; b++) B[nx][b] = decode_f16<FMT>(wc, b, t + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
-          acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[b], acc[i][b], 0, 0, 0);
-      }
-    }
-    if (g + 1 < g1) {
+          acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cu][i], B[cu][b], acc[i][b], 0, 0, 0);
+      if (t == 3 && g + 1 < g1) {
+        // the next group's activation tile into the other buffer
 #pragma unroll
-      for (int j = 0; j < 8; j++) *(v4u*)(&lds[buf ^ 1][(j * kThreads + tid) * 16]) = xr[j];
+        for (int j = 0; j < 8; j++) *(v4u*)(&lds[buf ^ 1][(j * kThreads + tid) * 16]) = xr[j];
+      }
     }
     wc = wn;
     __syncthreads();
@@ -492,18 +575,28 @@ __global__ __launch_bounds__(kThreads) void gemm_i8(KArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; b++) iacc[i][b] = v16i{};
     }
+    // operands of step tt+1 are read and decoded while the MFMAs of step tt run
+    v4i A[2][2], B[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+      A[0][i] = __builtin_bit_cast(v4i, *(const v4u*)(L + swz_i8(64 * wm + 32 * i + n, h)));
+#pragma unroll
+    for (int b = 0; b < 2; b++) B[0][b] = decode_i8<FMT>(wc, b, 0);
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
-      v4i B[2];
+      const int cu = tt & 1, nx = cu ^ 1;
+      if (tt + 1 < 4) {
 #pragma unroll
-      for (int b = 0; b < 2; b++) B[b] = decode_i8<FMT>(wc, b, tt);
+        for (int i = 0; i < 2; i++)
+          A[nx][i] = __builtin_bit_cast(v4i, *(const v4u*)(L + swz_i8(64 * wm + 32 * i + n, 2 * (tt + 1) + h)));
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const v4i A = __builtin_bit_cast(v4i, *(const v4u*)(L + swz_i8(64 * wm + 32 * i + n, 2 * tt + h)));
+        for (int b = 0; b < 2; b++) B[nx][b] = decode_i8<FMT>(wc, b, tt + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int b = 0; b < 2; b++)
-          iacc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[b], iacc[i][b], 0, 0, 0);
-      }
+          iacc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[cu][i], B[cu][b], iacc[i][b], 0, 0, 0);
     }
     if constexpr (SCALED) {
 #pragma unroll
@@ -605,8 +698,12 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   if (p.f16) {
     float* rs = (float*)(ws + p.rs_off);
     k.rowscale = rs;
-    hipLaunchKernelGGL(stage_f16<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
-                       (const uint16_t*)g.x, (uint8_t*)k.xt, rs);
+    if (g.K <= kStageLdsMax && ((uintptr_t)g.x % 16) == 0)
+      hipLaunchKernelGGL(stage_f16_lds<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
+                         (const uint16_t*)g.x, (uint8_t*)k.xt, rs);
+    else
+      hipLaunchKernelGGL(stage_f16<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
+                         (const uint16_t*)g.x, (uint8_t*)k.xt, rs);
     if (g.ykind == YK_BF16)
       hipLaunchKernelGGL((gemm_f16<FMT, YK_BF16>), grid, block, 0, s, k);
     else
