@@ -40,7 +40,7 @@ SHAPES = [(9, 48, 128), (128, 256, 1024), (200, 384, 640), (130, 100, 1152), (30
           (64, 1040, 5120)]
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_bf16_parity(fmt, M, N, K):
     print(f"gemm bf16 fmt={fmt} M={M} N={N} K={K}", flush=True)
@@ -56,7 +56,7 @@ def test_gemm_bf16_parity(fmt, M, N, K):
     print(f"  worst err/tol {w:.3e}")
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_int8_parity(fmt, M, N, K):
     print(f"gemm int8 fmt={fmt} M={M} N={N} K={K}", flush=True)
@@ -76,7 +76,7 @@ def test_gemm_int8_parity(fmt, M, N, K):
     assert_within(Yb.float().cpu().numpy(), yref, absY, bf16_out=True, what="i8 bf16 out")
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_gemm_dyadic_inputs_are_exact(fmt):
     """Small-integer activations and power-of-two scales: every partial sum is
     representable, so the GEMM equals the oracle exactly."""
@@ -92,7 +92,7 @@ def test_gemm_dyadic_inputs_are_exact(fmt):
     assert np.array_equal(Y.cpu().numpy().astype(np.float64), yref)
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_gemm_bf16_wide_exponent_range(fmt):
     """bf16 rows far outside the fp16 range (and a zero row, and one tiny
     element beside large ones) are rescaled per row without loss."""
@@ -184,3 +184,24 @@ def test_pp512_ternary_int8_sampled(N, K):
 def test_dit_binary_bf16_sampled(M, N, K):
     print(f"DiT binary bf16 M={M} N={N} K={K}", flush=True)
     sample_check(1, M, N, K, tid=170 + (M + N + K) % 11, full_rows=1)
+
+
+@pytest.mark.parametrize("N,K", [(5120, 5120), (17408, 5120)])
+def test_pp512_ternary_base3_bf16_sampled(N, K):
+    print(f"pp512 ternary base-3 bf16 N={N} K={K}", flush=True)
+    sample_check(3, 512, N, K, tid=190 + (N + K) % 7)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 384, 640), (512, 5120, 5120)])
+def test_gemm_base3_equals_2bit(M, N, K):
+    """Same ternary codes packed as 2-bit and base-3 decode to the same fp4
+    operands: the two GEMMs agree bit for bit."""
+    codes = codes_for(2, SEED, 195, N, K)
+    scales = synth.group_scales(SEED, 196, N, K // 128)
+    pc2, ps2 = lb.pack(2, dev(codes), dev(scales.view(np.int16)))
+    pc3, ps3 = lb.pack(3, dev(codes), dev(scales.view(np.int16)))
+    X = bf16_dev(synth.normal_bf16(SEED, 197, M, K))
+    Y2 = lb.gemm(2, M, N, K, pc2, ps2, X)
+    Y3 = lb.gemm(3, M, N, K, pc3, ps3, X)
+    torch.cuda.synchronize()
+    assert torch.equal(Y2, Y3)

@@ -248,7 +248,6 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
-  if (fmt == LOWBIT_TERNARY_BASE3) return LOWBIT_E_UNSUPPORTED;  // large-M base-3: not provided
   return run_gemm(fmt, M, N, K, pcodes, pscales, x_dtype, X, x_scales, y_dtype, Y, s);
 }
 

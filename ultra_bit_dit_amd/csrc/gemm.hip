@@ -1,208 +1,29 @@
-// Large-M products Y[M][N] = X[M][K] . W[N][K]^T over packed binary or 2-bit
-// ternary weights with one fp16 scale per 128-weight group (the group-scaled
-// matmul of the "1-bit 嘅數學" section of the ultra_bit_dit page; prefill and
-// diffusion-transformer blocks run it as a dense contraction).
+// Large-M products Y[M][N] = X[M][K] . W[N][K]^T over packed binary or
+// ternary weights (2-bit or base-3) with one fp16 scale per 128-weight group
+// (the group-scaled matmul of the "1-bit 嘅數學" section of the ultra_bit_dit
+// page; prefill and diffusion-transformer blocks run it as a dense
+// contraction).
 //
-// Two kernels, both MFMA 32x32 on gfx950:
+// One MFMA kernel for every format: gfx950's block-scaled
+// v_mfma_scale_f32_16x16x128_f8f6f4 with fp8 e4m3 activations (two exact
+// split terms per element, an E8M0 exponent per 32-element block) against fp4
+// e2m1 weights decoded from the packed words in registers.  The fp16 group
+// scale multiplies each group's fp32 partial; int8 activations with unit
+// scales give the exact int32 product.
 //
-// * bf16 activations -> fp16 MFMA (32x32x16, fp32 accumulate).  The group
-//   scale is folded into the weight operand: a weight is +s, -s or 0, which
-//   fp16 holds exactly because s is an fp16 number.  Activations are
-//   converted to fp16 after an exact per-row power-of-two rescale (bf16 has a
-//   wider exponent range than fp16), so every product is exact and only the
-//   fp32 accumulation rounds; the row's power of two is undone on output.
-//   No per-group epilogue is needed.
-// * int8 activations -> int8 MFMA (32x32x32, int32 accumulate).  Per group
-//   the int32 sum is exact; it is scaled by the group scale in fp32 and,
-//   after the last group, by the row's activation scale.  Without scales the
-//   int32 sum over all of K is returned exactly.
-//
-// Activations are first staged (a separate pass over X) into 128-row tiles,
-// one per (row tile, group), with the k order of each group permuted to the
-// order in which the packed weight bits decode, and the 16-byte chunks of
-// each tile row XOR-swizzled so that the MFMA operand reads from LDS are
-// free of bank conflicts.  The GEMM copies a tile to LDS with plain
-// coalesced 16-byte loads and stores.
-//
-// Weights are read straight from the packed layout into registers and
-// decoded there (each wave decodes only the columns it owns).
+// Activations are first staged (a separate pass over X) into per-(64-row
+// tile, group) images laid out exactly as the MFMA's A operand registers, so
+// the GEMM copies an image to LDS and every lane reads its operand with two
+// 16-byte LDS loads.  Weights are read straight from the packed layout.
 #include <algorithm>
 
 #include "common.hpp"
+#include "fp4.hpp"
 
 namespace lowbit {
 namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef short v2s __attribute__((ext_vector_type(2)));
-
-constexpr int kTM = 128;          // activation rows per tile
-constexpr int kTileF16 = kTM * 256;  // bytes of a staged fp16 tile (128 rows x 128 k)
-constexpr int kTileI8 = kTM * 128;   // bytes of a staged int8 tile
-constexpr int kThreads = 256;
-
-// ---------------------------------------------------------------- k order
-// Position p (0..127) of a staged group row <-> k offset inside the group.
-//
-// fp16 path: MFMA t (0..7) of the group, lane half h, operand element i
-// (0..7) sits at p = 16 t + 8 h + i and multiplies the weight slot that the
-// decode of the lane's words puts there.  The lane (column n, half h) owns
-// quarters 2h and 2h+1 of column n's group; MFMA t takes quarter 2h + t/4.
-__host__ __device__ inline int perm_f16(int fmt, int p) {
-  const int t = p >> 4, h = (p >> 3) & 1, i = p & 7;
-  const int q = 2 * h + (t >> 2);
-  // binary: register j = 4 (t%4) + i/2 takes bit j (low half) and bit j+16 (high half)
-  // ternary: word P_{(t/2)%2}; registers p' = i/2 hold slots (p', p'+4) for
-  //          even t, (8+p', 12+p') for odd t
-  const int slot = fmt == 1 ? bin_slot(4 * (t & 3) + (i >> 1) + 16 * (i & 1))
-                            : 16 * ((t >> 1) & 1) + 8 * (t & 1) + (i >> 1) + 4 * (i & 1);
-  return kmap(q, slot);
-}
-
-// int8 path: MFMA tt (0..3), half h, element i (0..15) at p = 32 tt + 16 h + i
-__host__ __device__ inline int perm_i8(int fmt, int p) {
-  const int tt = p >> 5, h = (p >> 4) & 1, i = p & 15;
-  const int q = 2 * h + (tt >> 1);
-  // binary: register j = 4 (tt%2) + i/4 holds bits j, j+8, j+16, j+24 as bytes
-  // ternary: word P_{tt%2}; register v = i/4 holds slots 8 (v/2) + 2 e + v%2
-  const int slot = fmt == 1 ? bin_slot(4 * (tt & 1) + (i >> 2) + 8 * (i & 3))
-                            : 16 * (tt & 1) + 8 * (i >> 3) + 2 * (i & 3) + ((i >> 2) & 1);
-  return kmap(q, slot);
-}
-
-// staged tile byte offset of 16-byte chunk c of tile row r (rows of 256 B
-// for fp16, 128 B for int8)
-__host__ __device__ inline int swz_f16(int r, int c) { return r * 256 + ((c ^ (r & 7)) << 4); }
-__host__ __device__ inline int swz_i8(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
-
-// ---------------------------------------------------------------- staging
-// One block per activation row: exponent of the row maximum, then the fp16
-// (rescaled) values in staged order.  xinv[m] = 2^-e undoes the rescale.
-template <int FMT>
-__global__ __launch_bounds__(256) void stage_f16(int64_t M, int64_t K, int64_t G,
-                                                 const uint16_t* __restrict__ X,
-                                                 uint8_t* __restrict__ xt,
-                                                 float* __restrict__ xinv) {
-  __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const uint16_t* row = X + m * K;
-  float a = 0.0f;
-  for (int64_t k = threadIdx.x; k < K; k += 256)
-    a = fmaxf(a, fabsf(__uint_as_float((uint32_t)row[k] << 16)));
-  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-  __syncthreads();
-  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // e puts the row maximum in [2^14, 2^15): every finite product with an
-  // fp16 scale stays finite in fp32 and rescaling is exact
-  int e = 0;
-  if (a > 0.0f && a <= 3.0e38f) {
-    int ex;
-    (void)frexpf(a, &ex);
-    e = min(max(15 - ex, -126), 126);
-  }
-  const float up = ldexpf(1.0f, e);
-  if (threadIdx.x == 0) xinv[m] = ldexpf(1.0f, -e);
-  const int64_t mt = m / kTM;
-  const int r = (int)(m % kTM);
-  for (int64_t ci = threadIdx.x; ci < G * 16; ci += 256) {
-    const int64_t g = ci >> 4;
-    const int c = (int)(ci & 15);
-    const uint16_t* src = row + g * kGroup;
-    uint32_t h[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const float v0 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j)] << 16) * up;
-      const float v1 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j + 1)] << 16) * up;
-      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;  // round to nearest even
-      h[j] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
-             ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
-    }
-    uint8_t* dst = xt + (mt * G + g) * (int64_t)kTileF16 + swz_f16(r, c);
-    *(v4u*)dst = v4u{h[0], h[1], h[2], h[3]};
-  }
-}
-
-// The same with the row read once, coalesced, into LDS (rows up to
-// kStageLdsMax elements): the maximum is taken during that read and the
-// permuted gather then reads LDS instead of global memory.
-constexpr int64_t kStageLdsMax = 24576;  // bf16 elements (48 KiB of LDS)
-
-template <int FMT>
-__global__ __launch_bounds__(256) void stage_f16_lds(int64_t M, int64_t K, int64_t G,
-                                                     const uint16_t* __restrict__ X,
-                                                     uint8_t* __restrict__ xt,
-                                                     float* __restrict__ xinv) {
-  __shared__ __attribute__((aligned(16))) uint16_t srow[kStageLdsMax];
-  __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const v4u* row = (const v4u*)(X + m * K);
-  float a = 0.0f;
-  for (int64_t k8 = threadIdx.x; k8 < K / 8; k8 += 256) {
-    const v4u w = row[k8];
-    ((v4u*)srow)[k8] = w;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      a = fmaxf(a, fabsf(__uint_as_float(w[j] << 16)));
-      a = fmaxf(a, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-  __syncthreads();
-  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int e = 0;
-  if (a > 0.0f && a <= 3.0e38f) {
-    int ex;
-    (void)frexpf(a, &ex);
-    e = min(max(15 - ex, -126), 126);
-  }
-  const float up = ldexpf(1.0f, e);
-  if (threadIdx.x == 0) xinv[m] = ldexpf(1.0f, -e);
-  const int64_t mt = m / kTM;
-  const int r = (int)(m % kTM);
-  for (int64_t ci = threadIdx.x; ci < G * 16; ci += 256) {
-    const int64_t g = ci >> 4;
-    const int c = (int)(ci & 15);
-    const uint16_t* src = srow + g * kGroup;
-    uint32_t h[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const float v0 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j)] << 16) * up;
-      const float v1 = __uint_as_float((uint32_t)src[perm_f16(FMT, 8 * c + 2 * j + 1)] << 16) * up;
-      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;  // round to nearest even
-      h[j] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
-             ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
-    }
-    uint8_t* dst = xt + (mt * G + g) * (int64_t)kTileF16 + swz_f16(r, c);
-    *(v4u*)dst = v4u{h[0], h[1], h[2], h[3]};
-  }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256) void stage_i8(int64_t M, int64_t K, int64_t G,
-                                                const int8_t* __restrict__ X,
-                                                uint8_t* __restrict__ xt) {
-  const int64_t m = blockIdx.x;
-  const uint8_t* row = (const uint8_t*)X + m * K;
-  const int64_t mt = m / kTM;
-  const int r = (int)(m % kTM);
-  for (int64_t ci = threadIdx.x; ci < G * 8; ci += 256) {
-    const int64_t g = ci >> 3;
-    const int c = (int)(ci & 7);
-    const uint8_t* src = row + g * kGroup;
-    uint32_t v[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v[j] = 0;
-#pragma unroll
-      for (int b = 0; b < 4; b++) v[j] |= (uint32_t)src[perm_i8(FMT, 16 * c + 4 * j + b)] << (8 * b);
-    }
-    uint8_t* dst = xt + (mt * G + g) * (int64_t)kTileI8 + swz_i8(r, c);
-    *(v4u*)dst = v4u{v[0], v[1], v[2], v[3]};
-  }
-}
 
 // ---------------------------------------------------------------- GEMM args
 struct KArgs {
@@ -258,13 +79,13 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, T v) {
 // Its loads go out 32 values at a time, so the reduction costs a few memory
 // round trips rather than one per value.  Returns true in the workgroup that
 // must write Y.  INT: the values are int32 bit patterns, added as integers.
-template <int NV, bool INT>
+template <int NV, bool INT, int THREADS>
 __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int ks, int wave,
                                              int lane, uint32_t (&v)[NV]) {
   constexpr int CH = 32;  // values per batch of loads
   static_assert(NV % CH == 0, "partial tile in whole batches");
   __shared__ uint32_t s_last;
-  const int64_t per = (int64_t)(kThreads / 64) * NV * 64;  // words of one partial tile
+  const int64_t per = (int64_t)(THREADS / 64) * NV * 64;  // words of one partial tile
   uint32_t* part = (uint32_t*)a.part;
   uint32_t* mine = part + (tile * a.KS + ks) * per + (int64_t)wave * NV * 64 + lane;
 #pragma unroll
@@ -310,337 +131,274 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
   return true;
 }
 
-// ----------------------------------------------------- fp16 (bf16 input) GEMM
-// Workgroup tile 128 rows x 256 columns; wave w owns columns 64w..64w+63
-// (two 32-column MFMA blocks) for all 128 rows (four 32-row blocks).
-constexpr int kF16Cols = 256;
+// ---------------------------------------------- fp8 x fp4 MFMA GEMM (all formats)
+// The batch-1 kernels' operand scheme at full width: activations enter
+// v_mfma_scale_f32_16x16x128_f8f6f4 as two fp8 e4m3 split terms per element
+// with an E8M0 exponent per 32-element hardware block (bf16: term 1 is 16x
+// the residual of term 0; int8 q = 16 (q >> 4) + (q & 15) exactly), weights
+// as fp4 decoded from the packed words with one or two VALU ops per 8
+// weights.  One MFMA multiplies 8 activation rows (x 2 terms) by 16 weight
+// rows over one group; the group's fp32 partial is scaled by the fp16 group
+// scale in fp32 (int8 with unit scales: exact integer per group).
+constexpr int kAT = 8;                   // activation rows per MFMA (x 2 terms = 16 A rows)
+constexpr int kATBytes = 64 * 32 + 64;   // one A-tile of one group: fp8 bytes + exponents
+constexpr int kF8BM = 64;                // activation rows per workgroup tile (8 A-tiles)
+constexpr int kF8BN = 256;               // weight rows per workgroup tile (16 row-blocks)
+constexpr int kF8Threads = 512;          // 8 waves: 2 (rows) x 4 (columns)
+constexpr int kF8Img = (kF8BM / kAT) * kATBytes;  // staged bytes of one workgroup tile and group
 
-// packed words of one group for the lane's two column blocks
-template <int FMT>
-struct WordsF16 {
-  uint32_t w[2][FMT == 1 ? 2 : 4];  // [block][quarter e (binary) | 2e + P-index (ternary)]
-  uint32_t s2[2];                   // fp16 scale in both halves
-};
-
-template <int FMT>
-__device__ __forceinline__ WordsF16<FMT> load_words_f16(const KArgs& a, const int64_t (&rb)[2],
-                                                        int r, int h, int64_t g) {
-  WordsF16<FMT> o;
+// Staging: one thread per (row m, group g, hardware block b).  Block b of a
+// group holds k = 128 g + kmap(b, i), i = 0..31 (two runs of 16); A lane
+// L = r + 16 kb (A row r, lane group kb) holds bytes e of the blocks with
+// b & 1 = kb >> 1, i >> 4 = kb & 1, b >> 1 = e >> 4, i & 15 = e & 15, and
+// lane L also supplies the exponent of (A row L % 16, block L / 16).
+// Layout: per (64-row tile, group) kF8Img bytes; A-tile a of it at a *
+// kATBytes: 64 lanes x 32 fp8 bytes, then 64 exponent bytes (by lane).
+// Rows >= M are staged as zeros.
+template <int XK>
+__global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t K, int64_t G,
+                                                const void* __restrict__ X,
+                                                uint8_t* __restrict__ xs) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= Mpad * G * 4) return;
+  const int b = (int)(tid & 3);
+  const int64_t g = (tid >> 2) % G;
+  const int64_t m = (tid >> 2) / G;
+  float v[32];
 #pragma unroll
-  for (int b = 0; b < 2; b++) {
+  for (int hh = 0; hh < 2; hh++) {
+    const int64_t k0 = g * kGroup + 64 * (b & 1) + 16 * (b >> 1) + 32 * hh;
+    if (m < M) {
+      if constexpr (XK == XK_BF16) {
+        const v4u* src = (const v4u*)((const uint16_t*)X + m * K + k0);
+        const v4u w0 = src[0], w1 = src[1];
 #pragma unroll
-    for (int e = 0; e < 2; e++) {
-      const int L = r + 16 * (2 * h + e);
-      if constexpr (FMT == 1) {
-        const uint32_t* p = (const uint32_t*)a.pcodes + ((rb[b] * a.GQ + (g >> 2)) * 64 + L) * 4 + (g & 3);
-        o.w[b][e] = __builtin_nontemporal_load(p);
+        for (int j = 0; j < 4; j++) {
+          v[16 * hh + 2 * j] = __uint_as_float(w0[j] << 16);
+          v[16 * hh + 2 * j + 1] = __uint_as_float(w0[j] & 0xFFFF0000u);
+          v[16 * hh + 8 + 2 * j] = __uint_as_float(w1[j] << 16);
+          v[16 * hh + 8 + 2 * j + 1] = __uint_as_float(w1[j] & 0xFFFF0000u);
+        }
       } else {
-        const uint32_t* p = (const uint32_t*)a.pcodes + ((rb[b] * a.GP + (g >> 1)) * 64 + L) * 4 + 2 * (g & 1);
-        o.w[b][2 * e] = __builtin_nontemporal_load(p);
-        o.w[b][2 * e + 1] = __builtin_nontemporal_load(p + 1);
+        const v4u w = *(const v4u*)((const int8_t*)X + m * K + k0);
+#pragma unroll
+        for (int j = 0; j < 16; j++) v[16 * hh + j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
       }
-    }
-    const uint32_t s = a.pscales[((rb[b] * a.GQ + (g >> 2)) * 16 + r) * 4 + (g & 3)];
-    o.s2[b] = s | (s << 16);
-  }
-  return o;
-}
-
-// weight operand of MFMA t for one column block: 8 fp16 values +-s / 0
-template <int FMT>
-__device__ __forceinline__ v8h decode_f16(const WordsF16<FMT>& W, int b, int t) {
-  uint32_t v[4];
-  const uint32_t s2 = W.s2[b];
-  if constexpr (FMT == 1) {
-    const uint32_t w = W.w[b][t >> 2];
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int j = 4 * (t & 3) + k;
-      v[k] = s2 ^ ((w << (15 - j)) & 0x80008000u);
+      for (int j = 0; j < 16; j++) v[16 * hh + j] = 0.0f;
     }
+  }
+  float t0[32], t1[32];
+  int e0, e1;
+  if constexpr (XK == XK_BF16) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+    // E puts the block maximum in [128, 256) x 2^E, clamped so that both
+    // terms' exponents stay representable
+    int E = 0;
+    if (amax != 0.0f) {
+      int ex;
+      (void)frexpf(amax, &ex);
+      E = max((ex - 1) - 7, -127 + kSplitShift);
+    }
+    const float sc = ldexpf(1.0f, -E);
+#pragma unroll
+    for (int j = 0; j < 32; j++) t0[j] = v[j] * sc;
+    e0 = 127 + E;
+    e1 = 127 + E - kSplitShift;
   } else {
-    const uint32_t P = W.w[b][2 * (t >> 2) + ((t >> 1) & 1)];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      // even t: slots (k, k+4): z at 4k+1, s at 4k+3; odd t: slots (8+k, 12+k): z 4k, s 4k+2
-      const int ss = (t & 1) ? 13 - 4 * k : 12 - 4 * k;
-      const uint32_t sg = s2 ^ ((P << ss) & 0x80008000u);
-      const v2s z = __builtin_bit_cast(v2s, P << (ss + 2)) >> (short)15;
-      v[k] = sg & __builtin_bit_cast(uint32_t, z);
+    for (int j = 0; j < 32; j++) {
+      const int q = (int)v[j];
+      t0[j] = (float)(q >> 4);
+      t1[j] = (float)(q & 15);
+    }
+    e0 = 127 + kSplitShift;
+    e1 = 127;
+  }
+  uint32_t w0[8], w1[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t0[4 * j], t0[4 * j + 1], 0, false);
+    w0[j] = __builtin_amdgcn_cvt_pk_fp8_f32(t0[4 * j + 2], t0[4 * j + 3], w, true);
+  }
+  if constexpr (XK == XK_BF16) {
+    // term 1 = rne_e4m3(16 x (t - term 0)), the residual exact in fp32
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t w = w0[j];
+      t1[4 * j] = (t0[4 * j] - __builtin_amdgcn_cvt_f32_fp8(w, 0)) * 16.0f;
+      t1[4 * j + 1] = (t0[4 * j + 1] - __builtin_amdgcn_cvt_f32_fp8(w, 1)) * 16.0f;
+      t1[4 * j + 2] = (t0[4 * j + 2] - __builtin_amdgcn_cvt_f32_fp8(w, 2)) * 16.0f;
+      t1[4 * j + 3] = (t0[4 * j + 3] - __builtin_amdgcn_cvt_f32_fp8(w, 3)) * 16.0f;
     }
   }
-  return __builtin_bit_cast(v8h, v4u{v[0], v[1], v[2], v[3]});
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t1[4 * j], t1[4 * j + 1], 0, false);
+    w1[j] = __builtin_amdgcn_cvt_pk_fp8_f32(t1[4 * j + 2], t1[4 * j + 3], w, true);
+  }
+  uint8_t* blk = xs + ((m / kF8BM) * G + g) * (int64_t)kF8Img + ((m % kF8BM) / kAT) * kATBytes;
+  const int r0 = 2 * (int)(m % kAT);  // A row of term 0 (term 1 is the next row)
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+    const int kb = 2 * (b & 1) + hh;
+    const int e = 16 * (b >> 1);
+    *(v4u*)(blk + (r0 + 16 * kb) * 32 + e) = v4u{w0[4 * hh], w0[4 * hh + 1], w0[4 * hh + 2], w0[4 * hh + 3]};
+    *(v4u*)(blk + (r0 + 1 + 16 * kb) * 32 + e) = v4u{w1[4 * hh], w1[4 * hh + 1], w1[4 * hh + 2], w1[4 * hh + 3]};
+  }
+  blk[2048 + r0 + 16 * b] = (uint8_t)e0;
+  blk[2048 + r0 + 1 + 16 * b] = (uint8_t)e1;
 }
 
-template <int FMT, int YK>
-__global__ __launch_bounds__(kThreads) void gemm_f16(KArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTileF16];
+template <int T>
+__device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // A: fp8 e4m3 (0) with the E8M0 block exponent in byte 0 of se; B: fp4 e2m1 (4), unscaled
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, se, 0, 127);
+}
+
+// Workgroup tile 64 rows x 256 columns, 8 waves: wave (wm, wn) owns A-tiles
+// 4 wm .. 4 wm + 3 (32 rows) and row-blocks 4 wn .. 4 wn + 3 (64 columns).
+// Per group: the workgroup's staged activations (kF8Img bytes) sit in one of
+// two LDS buffers; codes and scales are loaded a quad (4 groups) ahead.
+template <int FMT, int XK, int YK, bool SCALED>
+__global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_f8(KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kF8Img];
+  __shared__ uint32_t t3[256];
+  constexpr bool INT = XK == XK_I8 && !SCALED;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, h = lane >> 5, r = n & 15;
+  const int wm = wave >> 2, wn = wave & 3;
   int64_t mt, nt;
   int ks;
   tile_of(a, mt, nt, ks);
-  const int64_t g0 = a.G * ks / a.KS, g1 = a.G * (ks + 1) / a.KS;
-  const int64_t col0 = nt * kF16Cols + wave * 64;
-  int64_t rb[2];
+  const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
+  const int64_t g0 = 4 * q0, g1 = min<int64_t>(4 * q1, a.G);
+  int64_t rbj[4];
+  bool live[4];
 #pragma unroll
-  for (int b = 0; b < 2; b++) rb[b] = min((col0 + 32 * b + n) >> 4, a.NB - 1);
-  const uint8_t* xt = a.xt + mt * a.G * (int64_t)kTileF16;
+  for (int j = 0; j < 4; j++) {
+    const int64_t rb = nt * 16 + wn * 4 + j;
+    live[j] = rb < a.NB;
+    rbj[j] = live[j] ? rb : a.NB - 1;
+  }
+  if constexpr (FMT == 3) fill_trit_table(t3);
+  const uint8_t* xs = a.xt + mt * a.G * (int64_t)kF8Img;
+  constexpr int XR = (kF8Img / 16 + kF8Threads - 1) / kF8Threads;  // 16-byte pieces per thread
+  auto xload = [&](int64_t g, v4u& x0, v4u& x1, v4u& x2) {
+    const v4u* src = (const v4u*)(xs + g * kF8Img);
+    constexpr int NP = kF8Img / 16;
+    x0 = src[tid];
+    x1 = src[min(kF8Threads + tid, NP - 1)];
+    x2 = src[min(2 * kF8Threads + tid, NP - 1)];
+  };
+  auto xput = [&](uint8_t* dst, const v4u& x0, const v4u& x1, const v4u& x2) {
+    constexpr int NP = kF8Img / 16;
+    ((v4u*)dst)[tid] = x0;
+    if (kF8Threads + tid < NP) ((v4u*)dst)[kF8Threads + tid] = x1;
+    if (2 * kF8Threads + tid < NP) ((v4u*)dst)[2 * kF8Threads + tid] = x2;
+  };
+  static_assert(XR == 3, "staged group image in three 16-byte pieces per thread");
 
-  v16f acc[4][2];
+  float acc[4][4][2];
+  int iacc[4][4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int b = 0; b < 2; b++) acc[i][b] = v16f{};
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        acc[i][j][u] = 0.f;
+        iacc[i][j][u] = 0;
+      }
 
-  v4u xr[8];
+  v4u x0, x1, x2;
+  xload(g0, x0, x1, x2);
+  xput(lds[0], x0, x1, x2);
+  Quad<FMT> qd[4], qn[4];
 #pragma unroll
-  for (int j = 0; j < 8; j++) xr[j] = *(const v4u*)(xt + g0 * kTileF16 + (j * kThreads + tid) * 16);
-#pragma unroll
-  for (int j = 0; j < 8; j++) *(v4u*)(&lds[0][(j * kThreads + tid) * 16]) = xr[j];
-  WordsF16<FMT> wc = load_words_f16<FMT>(a, rb, r, h, g0);
+  for (int j = 0; j < 4; j++)
+    load_quad_at<FMT>(a.pcodes, a.pscales, rbj[j], min<int64_t>(q0, a.GQ - 1), a.GQ, a.GP, lane, qd[j]);
   __syncthreads();
 
-  for (int64_t g = g0; g < g1; g++) {
-    const int buf = (int)((g - g0) & 1);
-    const int64_t gn = g + 1 < g1 ? g + 1 : g;
+  for (int64_t q = q0; q < q1; q++) {
+    // next quad's codes and scales
+    const int64_t qnx = min<int64_t>(q + 1 < q1 ? q + 1 : q, a.GQ - 1);
 #pragma unroll
-    for (int j = 0; j < 8; j++) xr[j] = *(const v4u*)(xt + gn * kTileF16 + (j * kThreads + tid) * 16);
-    const WordsF16<FMT> wn = load_words_f16<FMT>(a, rb, r, h, gn);
-    const uint8_t* L = lds[buf];
-    // software pipeline over the 8 MFMA steps of the group: the operands of
-    // step t+1 are read from LDS and decoded while the MFMAs of step t run
-    v8h A[2][4], B[2][2];
+    for (int j = 0; j < 4; j++)
+      load_quad_at<FMT>(a.pcodes, a.pscales, rbj[j], qnx, a.GQ, a.GP, lane, qn[j]);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      A[0][i] = __builtin_bit_cast(v8h, *(const v4u*)(L + swz_f16(32 * i + n, h)));
+    for (int t = 0; t < 4; t++) {
+      const int64_t g = 4 * q + t;
+      if (g < g1) {
+        const int buf = (int)((g - g0) & 1);
+        const int64_t gn = g + 1 < g1 ? g + 1 : g;
+        xload(gn, x0, x1, x2);
+        v8i B[4];
+        float sj[4];
 #pragma unroll
-    for (int b = 0; b < 2; b++) B[0][b] = decode_f16<FMT>(wc, b, 0);
+        for (int j = 0; j < 4; j++) {
+          B[j] = decode_group<FMT>(qd[j], t, t3);
+          sj[j] = a.pscales ? quad_scale<FMT>(qd[j], t) : 1.0f;
+        }
+        const uint8_t* L = lds[buf];
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-      const int cu = t & 1, nx = cu ^ 1;
-      if (t + 1 < 8) {
+        for (int i = 0; i < 4; i++) {
+          const uint8_t* at = L + (4 * wm + i) * kATBytes;
+          const v4u a0 = *(const v4u*)(at + 32 * lane), a1 = *(const v4u*)(at + 32 * lane + 16);
+          const v8i A = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+          const int se = at[2048 + lane];
+          v4f c[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-          A[nx][i] = __builtin_bit_cast(v8h, *(const v4u*)(L + swz_f16(32 * i + n, 2 * (t + 1) + h)));
+          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4<0>(A, B[j], se);
 #pragma unroll
-        for (int b = 0; b < 2; b++) B[nx][b] = decode_f16<FMT>(wc, b, t + 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-          acc[i][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cu][i], B[cu][b], acc[i][b], 0, 0, 0);
-      if (t == 3 && g + 1 < g1) {
-        // the next group's activation tile into the other buffer
-#pragma unroll
-        for (int j = 0; j < 8; j++) *(v4u*)(&lds[buf ^ 1][(j * kThreads + tid) * 16]) = xr[j];
+          for (int j = 0; j < 4; j++) {
+            const float s0 = c[j][0] + c[j][1], s1 = c[j][2] + c[j][3];
+            if constexpr (INT) {
+              iacc[i][j][0] += __float2int_rn(s0);
+              iacc[i][j][1] += __float2int_rn(s1);
+            } else {
+              acc[i][j][0] = fmaf(sj[j], s0, acc[i][j][0]);
+              acc[i][j][1] = fmaf(sj[j], s1, acc[i][j][1]);
+            }
+          }
+        }
+        if (g + 1 < g1) xput(lds[buf ^ 1], x0, x1, x2);
+        __syncthreads();
       }
     }
-    wc = wn;
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; j++) qd[j] = qn[j];
   }
 
-  uint32_t v[128];
+  uint32_t v[32];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int q = 0; q < 16; q++) v[(i * 2 + b) * 16 + q] = __float_as_uint(acc[i][b][q]);
-  if (a.KS > 1 && !split_reduce<128, false>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
+      for (int u = 0; u < 2; u++)
+        v[(i * 4 + j) * 2 + u] = INT ? (uint32_t)iacc[i][j][u] : __float_as_uint(acc[i][j][u]);
+  if (a.KS > 1 && !split_reduce<32, INT, kF8Threads>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
 #pragma unroll
-    for (int q = 0; q < 16; q++) {
-      const int64_t row = mt * kTM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      if (row >= a.M) continue;
-      const float rs = a.rowscale[row];
-#pragma unroll
-      for (int b = 0; b < 2; b++) {
-        const int64_t col = col0 + 32 * b + n;
-        if (col < a.N) store_y<YK>(a.y, row * a.N + col, __uint_as_float(v[(i * 2 + b) * 16 + q]) * rs);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------- int8 GEMM
-// Workgroup tile 128 x 128; waves in a 2 x 2 grid, each 64 rows (two 32-row
-// blocks) x 64 columns (two 32-column blocks).
-constexpr int kI8Cols = 128;
-
-template <int FMT>
-struct WordsI8 {
-  uint32_t w[2][FMT == 1 ? 2 : 4];
-  float s[2];
-};
-
-template <int FMT, bool SCALED>
-__device__ __forceinline__ WordsI8<FMT> load_words_i8(const KArgs& a, const int64_t (&rb)[2],
-                                                      int r, int h, int64_t g) {
-  WordsI8<FMT> o;
-#pragma unroll
-  for (int b = 0; b < 2; b++) {
-#pragma unroll
-    for (int e = 0; e < 2; e++) {
-      const int L = r + 16 * (2 * h + e);
-      if constexpr (FMT == 1) {
-        const uint32_t* p = (const uint32_t*)a.pcodes + ((rb[b] * a.GQ + (g >> 2)) * 64 + L) * 4 + (g & 3);
-        o.w[b][e] = __builtin_nontemporal_load(p);
-      } else {
-        const uint32_t* p = (const uint32_t*)a.pcodes + ((rb[b] * a.GP + (g >> 1)) * 64 + L) * 4 + 2 * (g & 1);
-        o.w[b][2 * e] = __builtin_nontemporal_load(p);
-        o.w[b][2 * e + 1] = __builtin_nontemporal_load(p + 1);
-      }
-    }
-    if constexpr (SCALED)
-      o.s[b] = f16_bits_to_f32(a.pscales[((rb[b] * a.GQ + (g >> 2)) * 16 + r) * 4 + (g & 3)]);
-    else
-      o.s[b] = 0.0f;
-  }
-  return o;
-}
-
-// weight operand of MFMA tt for one column block: 16 int8 values -1/0/+1,
-// each byte chosen by v_perm from a two-entry (binary) or four-entry
-// (ternary) table indexed by the code bits
-template <int FMT>
-__device__ __forceinline__ v4i decode_i8(const WordsI8<FMT>& W, int b, int tt) {
-  uint32_t v[4];
-  if constexpr (FMT == 1) {
-    const uint32_t w = W.w[b][tt >> 1];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const uint32_t sel = (w >> (4 * (tt & 1) + k)) & 0x01010101u;  // 0 -> +1, 1 -> -1
-      v[k] = __builtin_amdgcn_perm(0x0000FF01u, 0x0000FF01u, sel);
-    }
-  } else {
-    const uint32_t P = W.w[b][2 * (tt >> 1) + (tt & 1)];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int sh = k == 0 ? 1 : k == 1 ? 5 : k == 2 ? 0 : 4;
-      // per byte: bit 0 = nonzero, bit 2 = sign -> index 0, 1, 4, 5
-      const uint32_t sel = (P >> sh) & 0x05050505u;
-      v[k] = __builtin_amdgcn_perm(0x0000FF00u, 0x00000100u, sel);
-    }
-  }
-  return v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
-}
-
-template <int FMT, int YK, bool SCALED>
-__global__ __launch_bounds__(kThreads) void gemm_i8(KArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTileI8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n = lane & 31, h = lane >> 5, r = n & 15;
-  int64_t mt, nt;
-  int ks;
-  tile_of(a, mt, nt, ks);
-  const int64_t g0 = a.G * ks / a.KS, g1 = a.G * (ks + 1) / a.KS;
-  const int64_t col0 = nt * kI8Cols + wn * 64;
-  int64_t rb[2];
-#pragma unroll
-  for (int b = 0; b < 2; b++) rb[b] = min((col0 + 32 * b + n) >> 4, a.NB - 1);
-  const uint8_t* xt = a.xt + mt * a.G * (int64_t)kTileI8;
-
-  v16f acc[2][2];
-  v16i iacc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int b = 0; b < 2; b++) {
-      acc[i][b] = v16f{};
-      iacc[i][b] = v16i{};
-    }
-
-  v4u xr[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) xr[j] = *(const v4u*)(xt + g0 * kTileI8 + (j * kThreads + tid) * 16);
-#pragma unroll
-  for (int j = 0; j < 4; j++) *(v4u*)(&lds[0][(j * kThreads + tid) * 16]) = xr[j];
-  WordsI8<FMT> wc = load_words_i8<FMT, SCALED>(a, rb, r, h, g0);
-  __syncthreads();
-
-  for (int64_t g = g0; g < g1; g++) {
-    const int buf = (int)((g - g0) & 1);
-    const int64_t gn = g + 1 < g1 ? g + 1 : g;
-#pragma unroll
-    for (int j = 0; j < 4; j++) xr[j] = *(const v4u*)(xt + gn * kTileI8 + (j * kThreads + tid) * 16);
-    const WordsI8<FMT> wn2 = load_words_i8<FMT, SCALED>(a, rb, r, h, gn);
-    const uint8_t* L = lds[buf];
-    if constexpr (SCALED) {
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int b = 0; b < 2; b++) iacc[i][b] = v16i{};
-    }
-    // operands of step tt+1 are read and decoded while the MFMAs of step tt run
-    v4i A[2][2], B[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-      A[0][i] = __builtin_bit_cast(v4i, *(const v4u*)(L + swz_i8(64 * wm + 32 * i + n, h)));
-#pragma unroll
-    for (int b = 0; b < 2; b++) B[0][b] = decode_i8<FMT>(wc, b, 0);
-#pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-      const int cu = tt & 1, nx = cu ^ 1;
-      if (tt + 1 < 4) {
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-          A[nx][i] = __builtin_bit_cast(v4i, *(const v4u*)(L + swz_i8(64 * wm + 32 * i + n, 2 * (tt + 1) + h)));
-#pragma unroll
-        for (int b = 0; b < 2; b++) B[nx][b] = decode_i8<FMT>(wc, b, tt + 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-          iacc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[cu][i], B[cu][b], iacc[i][b], 0, 0, 0);
-    }
-    if constexpr (SCALED) {
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-          for (int q = 0; q < 16; q++)
-            acc[i][b][q] = fmaf(wc.s[b], (float)iacc[i][b][q], acc[i][b][q]);
-    }
-    if (g + 1 < g1) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) *(v4u*)(&lds[buf ^ 1][(j * kThreads + tid) * 16]) = xr[j];
-    }
-    wc = wn2;
-    __syncthreads();
-  }
-
-  uint32_t v[64];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int q = 0; q < 16; q++)
-        v[(i * 2 + b) * 16 + q] =
-            SCALED ? __float_as_uint(acc[i][b][q]) : (uint32_t)iacc[i][b][q];
-  if (a.KS > 1 && !split_reduce<64, !SCALED>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      const int64_t row = mt * kTM + 64 * wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+    for (int u = 0; u < 2; u++) {
+      const int64_t row = mt * kF8BM + 32 * wm + 8 * i + 2 * (lane >> 4) + u;
       if (row >= a.M) continue;
       const float rs = SCALED ? a.rowscale[row] : 1.0f;
 #pragma unroll
-      for (int b = 0; b < 2; b++) {
-        const int64_t col = col0 + 32 * b + n;
-        if (col >= a.N) continue;
-        const uint32_t x = v[(i * 2 + b) * 16 + q];
-        if constexpr (SCALED)
-          store_y<YK>(a.y, row * a.N + col, __uint_as_float(x) * rs);
-        else
+      for (int j = 0; j < 4; j++) {
+        const int64_t col = (nt * 16 + wn * 4 + j) * 16 + (lane & 15);
+        if (!live[j] || col >= a.N) continue;
+        const uint32_t x = v[(i * 4 + j) * 2 + u];
+        if constexpr (INT)
           store_y<YK>(a.y, row * a.N + col, (int32_t)x);
+        else
+          store_y<YK>(a.y, row * a.N + col, __uint_as_float(x) * rs);
       }
     }
   }
@@ -650,27 +408,40 @@ __global__ __launch_bounds__(kThreads) void gemm_i8(KArgs a) {
 struct GemmPlan {
   int64_t MT, NT, G, KS;
   size_t xt_off, rs_off, part_off, bytes;
-  bool f16;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-GemmPlan make_gemm_plan(int64_t M, int64_t N, int64_t K, int xkind) {
+// K-split count: the smallest that keeps at least ~85% of a whole number of
+// waves of workgroups busy on the 256 compute units (one workgroup each),
+// up to 8 and at most one quad of groups per split
+int64_t pick_splits(int64_t tiles, int64_t GQ) {
+  const int64_t slots = 256;
+  int64_t best = 1;
+  double best_eff = 0.0;
+  for (int64_t ks = 1; ks <= std::min<int64_t>(8, GQ); ks++) {
+    const int64_t wgs = tiles * ks;
+    const double eff = (double)wgs / (double)(slots * cdiv(wgs, slots));
+    if (eff > best_eff + 1e-9) {
+      best = ks;
+      best_eff = eff;
+    }
+    if (eff >= 0.85) return ks;
+  }
+  return best;
+}
+
+GemmPlan make_gemm_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
-  p.f16 = xkind == XK_BF16;
   p.G = K / kGroup;
-  p.MT = cdiv(M, kTM);
-  p.NT = cdiv(N, p.f16 ? kF16Cols : kI8Cols);
+  p.MT = cdiv(M, kF8BM);
+  p.NT = cdiv(N, kF8BN);
   const int64_t tiles = p.MT * p.NT;
-  // split K when the tiles alone leave most compute units idle
-  p.KS = 1;
-  if (tiles < 192) p.KS = std::min<int64_t>(std::min<int64_t>(cdiv(256, tiles), 8), std::max<int64_t>(1, p.G / 4));
-  if (tiles > kMaxRowGroups) p.KS = 1;
-  const size_t tile_bytes = p.f16 ? kTileF16 : kTileI8;
+  p.KS = tiles > kMaxRowGroups ? 1 : pick_splits(tiles, cdiv(p.G, 4));
   p.rs_off = kCounterBytes;
-  p.xt_off = p.rs_off + align256((size_t)M * 4);
-  p.part_off = p.xt_off + align256((size_t)p.MT * p.G * tile_bytes);
-  const size_t part_tile = (size_t)kTM * (p.f16 ? kF16Cols : kI8Cols) * 4;
+  p.xt_off = p.rs_off;
+  p.part_off = p.xt_off + align256((size_t)p.MT * p.G * kF8Img);
+  const size_t part_tile = (size_t)kF8BM * kF8BN * 4;
   p.bytes = p.part_off + (p.KS > 1 ? (size_t)p.KS * tiles * part_tile : 0);
   return p;
 }
@@ -682,6 +453,7 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.xt = ws + p.xt_off;
   k.pcodes = (const uint8_t*)g.pcodes;
   k.pscales = g.pscales;
+  k.rowscale = g.xkind == XK_I8 ? g.x_scales : nullptr;
   k.y = g.y;
   k.part = (float*)(ws + p.part_off);
   k.cnt = (uint32_t*)ws;
@@ -694,38 +466,35 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.MT = p.MT;
   k.NT = p.NT;
   k.KS = (int)p.KS;
-  const dim3 grid((unsigned)(p.MT * p.NT * p.KS)), block(kThreads);
-  if (p.f16) {
-    float* rs = (float*)(ws + p.rs_off);
-    k.rowscale = rs;
-    if (g.K <= kStageLdsMax && ((uintptr_t)g.x % 16) == 0)
-      hipLaunchKernelGGL(stage_f16_lds<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
-                         (const uint16_t*)g.x, (uint8_t*)k.xt, rs);
-    else
-      hipLaunchKernelGGL(stage_f16<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
-                         (const uint16_t*)g.x, (uint8_t*)k.xt, rs);
+  const int64_t Mpad = p.MT * kF8BM;
+  const int64_t units = Mpad * p.G * 4;
+  const dim3 sgrid((unsigned)cdiv(units, 256));
+  const dim3 grid((unsigned)(p.MT * p.NT * p.KS)), block(kF8Threads);
+  if (g.xkind == XK_BF16) {
+    hipLaunchKernelGGL(stage_f8<XK_BF16>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
+                       (uint8_t*)k.xt);
     if (g.ykind == YK_BF16)
-      hipLaunchKernelGGL((gemm_f16<FMT, YK_BF16>), grid, block, 0, s, k);
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_BF16, false>), grid, block, 0, s, k);
     else
-      hipLaunchKernelGGL((gemm_f16<FMT, YK_F32>), grid, block, 0, s, k);
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_F32, false>), grid, block, 0, s, k);
     return hipGetLastError();
   }
-  k.rowscale = g.x_scales;
-  hipLaunchKernelGGL(stage_i8<FMT>, dim3((unsigned)g.M), dim3(256), 0, s, g.M, g.K, p.G,
-                     (const int8_t*)g.x, (uint8_t*)k.xt);
+  hipLaunchKernelGGL(stage_f8<XK_I8>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
+                     (uint8_t*)k.xt);
   if (g.ykind == YK_I32)
-    hipLaunchKernelGGL((gemm_i8<FMT, YK_I32, false>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_I32, false>), grid, block, 0, s, k);
   else if (g.ykind == YK_BF16)
-    hipLaunchKernelGGL((gemm_i8<FMT, YK_BF16, true>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_BF16, true>), grid, block, 0, s, k);
   else
-    hipLaunchKernelGGL((gemm_i8<FMT, YK_F32, true>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_F32, true>), grid, block, 0, s, k);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int xkind) {
-  return make_gemm_plan(M, N, K, xkind).bytes;
+  (void)xkind;
+  return make_gemm_plan(M, N, K).bytes;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
@@ -733,10 +502,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.xkind == XK_BF16 && g.ykind == YK_I32) return hipErrorInvalidValue;
   if (g.xkind == XK_I8 && (g.ykind == YK_I32) != (g.pscales == nullptr)) return hipErrorInvalidValue;
   if (g.xkind == XK_I8 && g.ykind != YK_I32 && g.x_scales == nullptr) return hipErrorInvalidValue;
-  const GemmPlan p = make_gemm_plan(g.M, g.N, g.K, g.xkind);
+  const GemmPlan p = make_gemm_plan(g.M, g.N, g.K);
   if (p.MT * p.NT * p.KS > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (g.fmt == 1) return launch_fmt<1>(g, p, s);
   if (g.fmt == 2) return launch_fmt<2>(g, p, s);
+  if (g.fmt == 3) return launch_fmt<3>(g, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "fp4.hpp"
 
 namespace lowbit {
 namespace {
@@ -274,8 +275,6 @@ __device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs
 // the weight loads go out first, then the workgroup waits until `wait_cnt`
 // reaches `wait_target` -- the previous product is complete -- and reads
 // its activations with device-coherent loads.
-typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 
 // Geometry of one work item: row group rg (W row-blocks, one per wave) and
 // K-slice ks of quads [q0, q1) (base-3 slices are whole octets).
@@ -301,92 +300,14 @@ __device__ __attribute__((always_inline)) inline Item item_of(const FArgs& a, in
   return it;
 }
 
-// packed codes of one quad (4 groups) of one lane, and its 4 fp16 scales
-template <int FMT>
-struct Quad {
-  u4 w[FMT == 1 ? 1 : 2];  // binary: 4 words; 2-bit: P0/P1 of 2 groups per vector
-  u2 c30, c31, c32;        // base-3: 24 bytes of 5-trit bytes
-  uint32_t t3;             // base-3: the two 4-trit bytes of this quad
-  uint2 sc;
-};
-
 // Unconditional loads (the row-block and quad are clamped into the matrix,
 // results of clamped loads are never used), so no load waits on another.
 template <int FMT>
 __device__ __attribute__((always_inline)) inline void load_quad(const FArgs& a, const Item& it,
                                                                int q, Quad<FMT>& o) {
-  const int L = threadIdx.x & 63, r = L & 15;
   const int64_t rbc = it.live ? it.rb : a.NB - 1;
   const int64_t gq = min<int64_t>(it.q0 + q, a.GQ - 1);
-  const u4* pcv = (const u4*)a.pcodes;
-  if constexpr (FMT == 1) {
-    o.w[0] = __builtin_nontemporal_load(&pcv[(rbc * a.GQ + gq) * 64 + L]);
-  } else if constexpr (FMT == 3) {
-    // octet block (rb, gq/2): plane s of lane L at 1024 s + 16 L; the quad's
-    // half h = gq % 2 takes 8-byte chunks 3h .. 3h+2 (chunk c = plane c/2,
-    // half c%2) and bytes 2h, 2h+1 of the 4-byte word at 3072 + 4 L
-    const int64_t GO = cdiv(a.GQ, 2);
-    const uint8_t* ob = a.pcodes + (rbc * GO + (gq >> 1)) * 3328;
-    const int h = (int)(gq & 1);
-    const uint8_t* lp = ob + 16 * L;
-    // chunk c = 3h + cc: plane c / 2, half c % 2
-    o.c30 = __builtin_nontemporal_load((const u2*)(lp + (h ? 1024 + 8 : 0)));
-    o.c31 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 : 8)));
-    o.c32 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 + 8 : 1024)));
-    o.t3 = __builtin_nontemporal_load((const uint32_t*)(ob + 3072 + 4 * L)) >> (16 * h);
-  } else {
-    const int64_t p0 = 2 * gq, p1 = min<int64_t>(2 * gq + 1, a.GP - 1);
-    o.w[0] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p0) * 64 + L]);
-    o.w[1] = __builtin_nontemporal_load(&pcv[(rbc * a.GP + p1) * 64 + L]);
-  }
-  const uint2* sbase = a.pscales ? (const uint2*)a.pscales : (const uint2*)a.pcodes;  // any readable memory
-  o.sc = sbase[(rbc * a.GQ + gq) * 16 + r];
-}
-
-// fp4 operand B of group t of a quad
-template <int FMT>
-__device__ __attribute__((always_inline)) inline v8i decode_group(const Quad<FMT>& qd, int t,
-                                                                  const uint32_t* t3) {
-  uint32_t d0, d1, d2, d3;
-  if constexpr (FMT == 1) {
-    const u4 c4 = qd.w[0];
-    const uint32_t wv = t == 0 ? c4.x : t == 1 ? c4.y : t == 2 ? c4.z : c4.w;
-    d0 = (wv & 0x88888888u) | 0x22222222u;
-    d1 = ((wv << 1) & 0x88888888u) | 0x22222222u;
-    d2 = ((wv << 2) & 0x88888888u) | 0x22222222u;
-    d3 = ((wv << 3) & 0x88888888u) | 0x22222222u;
-  } else if constexpr (FMT == 3) {
-    // group t of the quad: bytes 6t .. 6t+5 hold slots 0..29, the 4-trit
-    // byte t/2 digits 2(t%2), 2(t%2)+1 hold slots 30, 31
-    auto word = [&](int wi) {
-      return wi == 0 ? qd.c30.x : wi == 1 ? qd.c30.y : wi == 2 ? qd.c31.x
-           : wi == 3 ? qd.c31.y : wi == 4 ? qd.c32.x : qd.c32.y;
-    };
-    uint32_t nb[6];
-#pragma unroll
-    for (int i = 0; i < 6; i++) {
-      const int byte = 6 * t + i;
-      nb[i] = t3[(word(byte >> 2) >> (8 * (byte & 3))) & 0xFFu];
-    }
-    const uint32_t tl = (t3[(qd.t3 >> (8 * (t >> 1))) & 0xFFu] >> (8 * (t & 1))) & 0xFFu;
-    // slot s -> nibble s of d0..d3 (5 slots per byte)
-    const uint64_t lo = (uint64_t)nb[0] | ((uint64_t)nb[1] << 20) | ((uint64_t)nb[2] << 40) |
-                        ((uint64_t)nb[3] << 60);
-    const uint64_t hi = (uint64_t)(nb[3] >> 4) | ((uint64_t)nb[4] << 16) |
-                        ((uint64_t)nb[5] << 36) | ((uint64_t)tl << 56);
-    d0 = (uint32_t)lo;
-    d1 = (uint32_t)(lo >> 32);
-    d2 = (uint32_t)hi;
-    d3 = (uint32_t)(hi >> 32);
-  } else {
-    const u4 c4 = qd.w[t >> 1];
-    const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
-    d0 = p0 & 0xAAAAAAAAu;
-    d1 = (p0 << 1) & 0xAAAAAAAAu;
-    d2 = p1 & 0xAAAAAAAAu;
-    d3 = (p1 << 1) & 0xAAAAAAAAu;
-  }
-  return v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
+  load_quad_at<FMT>(a.pcodes, a.pscales, rbc, gq, a.GQ, a.GP, threadIdx.x & 63, o);
 }
 
 // LDS of an item: staged activations, a zero block, the base-3 table
@@ -413,18 +334,7 @@ __device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint
 template <int FMT>
 __device__ __attribute__((always_inline)) inline void lds_init(const Lds& l) {
   if (threadIdx.x < 9) ((uint32_t*)l.zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
-  if constexpr (FMT == 3) {
-    if (threadIdx.x < 243) {
-      uint32_t v = threadIdx.x, nib = 0;
-#pragma unroll
-      for (int e = 0; e < 5; e++) {
-        const uint32_t t = v % 3;
-        v /= 3;
-        nib |= (t == 0 ? 0xAu : t == 2 ? 0x2u : 0u) << (4 * e);
-      }
-      l.t3[threadIdx.x] = nib;
-    }
-  }
+  if constexpr (FMT == 3) fill_trit_table(l.t3);
 }
 
 // the 4 groups of quad q: operands first, then 4 independent MFMAs, then the
