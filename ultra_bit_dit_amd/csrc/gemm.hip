@@ -16,6 +16,7 @@
 // the GEMM copies an image to LDS and every lane reads its operand with two
 // 16-byte LDS loads.  Weights are read straight from the packed layout.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "fp4.hpp"
@@ -24,6 +25,10 @@ namespace lowbit {
 namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// s_waitcnt immediate that waits for vector memory (OR in vmcnt < 16) and
+// for all LDS/scalar-memory accesses (lgkmcnt 0); expcnt at its maximum
+constexpr int kVmLgkmWait = 0x0070;
 
 // ---------------------------------------------------------------- GEMM args
 struct KArgs {
@@ -260,14 +265,109 @@ __device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, se, 0, 127);
 }
 
+// LDS reads of the GEMM main loop, written out so that the compiler does not
+// order them after the global -> LDS copies in flight (it cannot tell the
+// LDS buffers apart and would wait for every copy); each block waits for its
+// own results.
+//
+// A operands of four consecutive A-tiles (kATBytes apart) at LDS byte
+// address pa (this lane's 32 bytes) and their exponents at pe.
+__device__ __forceinline__ void lds_read_a(uint32_t pa, uint32_t pe, v4u (&A0)[4], v4u (&A1)[4],
+                                           uint32_t (&se)[4]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %4, %12 offset:16\n\t"
+      "ds_read_u8 %8, %13\n\t"
+      "ds_read_b128 %1, %12 offset:2112\n\t"
+      "ds_read_b128 %5, %12 offset:2128\n\t"
+      "ds_read_u8 %9, %13 offset:2112\n\t"
+      "ds_read_b128 %2, %12 offset:4224\n\t"
+      "ds_read_b128 %6, %12 offset:4240\n\t"
+      "ds_read_u8 %10, %13 offset:4224\n\t"
+      "ds_read_b128 %3, %12 offset:6336\n\t"
+      "ds_read_b128 %7, %12 offset:6352\n\t"
+      "ds_read_u8 %11, %13 offset:6336\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A0[2]), "=&v"(A0[3]), "=&v"(A1[0]), "=&v"(A1[1]),
+        "=&v"(A1[2]), "=&v"(A1[3]), "=&v"(se[0]), "=&v"(se[1]), "=&v"(se[2]), "=&v"(se[3])
+      : "v"(pa), "v"(pe)
+      : "memory");
+}
+static_assert(kATBytes == 2112, "A-tile offsets in the LDS reads");
+
+// One row-block's codes of a quad from its code-buffer slot (this lane's
+// 16 bytes at pc; base-3 also the tail word at pt) and its scales at ps.
+// Base-3 slots hold planes h and h + 1 of the octet, h = quad % 2: the
+// quad's 8-byte chunks are (plane h: lo, hi; plane h + 1: lo) for h = 0 and
+// (plane 1: hi; plane 2: lo, hi) for h = 1.
+template <int FMT>
+__device__ __forceinline__ void lds_read_codes(uint32_t pc, uint32_t pt, uint32_t ps, int h,
+                                               Quad<FMT>& o) {
+  if constexpr (FMT == 1) {
+    __asm__ volatile("ds_read_b128 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(o.w[0]), "=&v"(o.sc)
+                     : "v"(pc), "v"(ps)
+                     : "memory");
+  } else if constexpr (FMT == 2) {
+    __asm__ volatile(
+        "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:1024\n\tds_read_b64 %2, %4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o.w[0]), "=&v"(o.w[1]), "=&v"(o.sc)
+        : "v"(pc), "v"(ps)
+        : "memory");
+  } else {
+    u4 pa, pb;
+    uint32_t tw;
+    __asm__ volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\tds_read_b32 %2, %5\n\t"
+        "ds_read_b64 %3, %6\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(pa), "=&v"(pb), "=&v"(tw), "=&v"(o.sc)
+        : "v"(pc), "v"(pt), "v"(ps)
+        : "memory");
+    o.c30 = h ? u2{pa.z, pa.w} : u2{pa.x, pa.y};
+    o.c31 = h ? u2{pb.x, pb.y} : u2{pa.z, pa.w};
+    o.c32 = h ? u2{pb.z, pb.w} : u2{pb.x, pb.y};
+    o.t3 = tw >> (16 * h);
+  }
+}
+
 // Workgroup tile 64 rows x 256 columns, 8 waves: wave (wm, wn) owns A-tiles
 // 4 wm .. 4 wm + 3 (32 rows) and row-blocks 4 wn .. 4 wn + 3 (64 columns).
-// Per group: the workgroup's staged activations (kF8Img bytes) sit in one of
-// two LDS buffers; codes and scales are loaded a quad (4 groups) ahead.
+//
+// Every global read of the main loop is a direct global -> LDS copy
+// (global_load_lds), so one counter of this wave's copies orders everything
+// and the waits below are exact:
+// * group images (kF8Img bytes) go into a ring of four LDS buffers, three
+//   groups ahead: group g in buffer (g - g0) % 4, the static t of the
+//   unrolled quad loop; each wave copies three pieces per image;
+// * codes and scales of the next quad go into one LDS code buffer at the
+//   second group of a quad; each wave copies those of two row-blocks, and at
+//   the first group of a quad every wave reads its four row-blocks' codes and
+//   scales from there into registers.
+// Copies past the end of the workgroup's K range re-read its last image or
+// quad into buffers that are no longer read, so that every group issues the
+// same copies.
+template <int FMT>
+struct CodeLds {
+  // bytes per row-block slot: binary one 1 KiB block, 2-bit the P0/P1 pair,
+  // base-3 two 1 KiB planes of the octet + its 256-byte tail
+  static constexpr int kSlot = FMT == 1 ? 1024 : FMT == 2 ? 2048 : 2304;
+  static constexpr int kScales = 16 * kSlot;       // 16 x 128 bytes of scales
+  static constexpr int kBytes = kScales + 16 * 128;
+  // copy instructions per wave per quad: two row-blocks' codes + one scales
+  static constexpr int kCopies = 2 * (FMT == 1 ? 1 : FMT == 2 ? 2 : 3) + 1;
+};
+
 template <int FMT, int XK, int YK, bool SCALED>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_f8(KArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kF8Img];
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space code: device pass only
+  using CL = CodeLds<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[kF8Img], xb1[kF8Img], xb2[kF8Img], xb3[kF8Img];
+  __shared__ __attribute__((aligned(16))) uint8_t cbuf[CL::kBytes];
   __shared__ uint32_t t3[256];
+  auto ring = [&](int t) -> lds_u8* {
+    return (lds_u8*)(t == 0 ? xb0 : t == 1 ? xb1 : t == 2 ? xb2 : xb3);
+  };
   constexpr bool INT = XK == XK_I8 && !SCALED;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -275,32 +375,90 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   int ks;
   tile_of(a, mt, nt, ks);
   const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
-  const int64_t g0 = 4 * q0, g1 = min<int64_t>(4 * q1, a.G);
-  int64_t rbj[4];
+  const int64_t g0 = 4 * q0, g1 = 4 * q1 < a.G ? 4 * q1 : a.G;
   bool live[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t rb = nt * 16 + wn * 4 + j;
-    live[j] = rb < a.NB;
-    rbj[j] = live[j] ? rb : a.NB - 1;
-  }
+  for (int j = 0; j < 4; j++) live[j] = nt * 16 + wn * 4 + j < a.NB;
   if constexpr (FMT == 3) fill_trit_table(t3);
+
+  // ---- copies.  Per-lane offsets stay in the same registers for the whole
+  // loop (a copy's address registers must not change while it is in flight).
   const uint8_t* xs = a.xt + mt * a.G * (int64_t)kF8Img;
-  constexpr int XR = (kF8Img / 16 + kF8Threads - 1) / kF8Threads;  // 16-byte pieces per thread
-  auto xload = [&](int64_t g, v4u& x0, v4u& x1, v4u& x2) {
-    const v4u* src = (const v4u*)(xs + g * kF8Img);
-    constexpr int NP = kF8Img / 16;
-    x0 = src[tid];
-    x1 = src[min(kF8Threads + tid, NP - 1)];
-    x2 = src[min(2 * kF8Threads + tid, NP - 1)];
+  static_assert(kF8Img == 16 * 1024 + 512, "image = 16 KiB + 8 x 64 bytes");
+  const uint32_t vo0 = 1024 * wave + 16 * lane, vo1 = vo0 + 8192;
+  const uint32_t vo2 = 16384 + 64 * wave + 16 * lane;
+  // image of group g into ring buffer t: 1 KiB chunks w and w + 8, and
+  // 64 bytes of the 512-byte tail (lanes 0..3)
+  auto xissue = [&](int64_t g, int t) {
+    const uint8_t* src = xs + g * kF8Img;
+    lds_u8* dst = ring(t);
+    __builtin_amdgcn_global_load_lds(src + vo0, dst + 1024 * wave, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
+    if (lane < 4) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 64 * wave, 16, 0, 0);
   };
-  auto xput = [&](uint8_t* dst, const v4u& x0, const v4u& x1, const v4u& x2) {
-    constexpr int NP = kF8Img / 16;
-    ((v4u*)dst)[tid] = x0;
-    if (kF8Threads + tid < NP) ((v4u*)dst)[kF8Threads + tid] = x1;
-    if (2 * kF8Threads + tid < NP) ((v4u*)dst)[2 * kF8Threads + tid] = x2;
+  // this wave copies row-blocks 4 wn + 2 wm and 4 wn + 2 wm + 1 of the tile
+  const int cr = 4 * wn + 2 * wm;
+  int64_t crb[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int64_t rb = nt * 16 + cr + u;
+    crb[u] = rb < a.NB ? rb : a.NB - 1;
+  }
+  const uint32_t lo16 = 16 * lane;
+  const uint32_t so = 128 * (uint32_t)(lane >> 3) + 16 * (lane & 7);  // scales gather
+  const int64_t GO = (a.GQ + 1) / 2;
+  const uint8_t* sbase = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
+  auto cissue = [&](int64_t gq) {
+    lds_u8* cb = (lds_u8*)cbuf;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      lds_u8* slot = cb + (cr + u) * CL::kSlot;
+      if constexpr (FMT == 1) {
+        const uint8_t* src = a.pcodes + (crb[u] * a.GQ + gq) * 1024;
+        __builtin_amdgcn_global_load_lds(src + lo16, slot, 16, 0, 0);
+      } else if constexpr (FMT == 2) {
+        const int64_t p0 = 2 * gq, p1 = 2 * gq + 1 < a.GP ? 2 * gq + 1 : a.GP - 1;
+        __builtin_amdgcn_global_load_lds(a.pcodes + (crb[u] * a.GP + p0) * 1024 + lo16, slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.pcodes + (crb[u] * a.GP + p1) * 1024 + lo16, slot + 1024,
+                                         16, 0, 0);
+      } else {
+        // planes h, h + 1 of octet gq / 2 (h = gq % 2) and the 256-byte tail
+        const uint8_t* ob = a.pcodes + (crb[u] * GO + (gq >> 1)) * 3328 + 1024 * (gq & 1);
+        __builtin_amdgcn_global_load_lds(ob + lo16, slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ob + 1024 + lo16, slot + 1024, 16, 0, 0);
+        const uint8_t* tail = a.pcodes + (crb[u] * GO + (gq >> 1)) * 3328 + 3072;
+        if (lane < 16) __builtin_amdgcn_global_load_lds(tail + lo16, slot + 2048, 16, 0, 0);
+      }
+    }
+    // scales of both row-blocks: lanes 8u .. 8u + 7 gather row-block u's 128 bytes
+    if (lane < 16) {
+      const int64_t rb = crb[lane >> 3];
+      const uint8_t* src = sbase + (rb * a.GQ + gq) * 128 - 128 * (uint32_t)(lane >> 3);
+      __builtin_amdgcn_global_load_lds(src + so, cb + CL::kScales + 128 * cr, 16, 0, 0);
+    }
   };
-  static_assert(XR == 3, "staged group image in three 16-byte pieces per thread");
+  // Wait until the copies that the coming group reads have landed, with
+  // `later` copies issued after them still in flight, and for this wave's
+  // LDS accesses; then the workgroup barrier.  Copies complete in issue
+  // order.  The barrier carries no memory fence: a workgroup fence would
+  // also wait for every copy still in flight.
+  auto xsync = [&](auto later) {
+    __builtin_amdgcn_s_waitcnt(kVmLgkmWait | decltype(later)::value);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+  // ---- LDS reads (written out, see lds_read_a / lds_read_codes)
+  auto aread = [&](int t, v4u (&A0)[4], v4u (&A1)[4], uint32_t (&se)[4]) {
+    const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
+    lds_read_a(base + 32 * lane, base + 2048 + lane, A0, A1, se);
+  };
+  // codes and scales of row-block 4 wn + j of the quad in the code buffer
+  auto cread = [&](int j, int64_t gq, Quad<FMT>& o) {
+    const uint32_t slot = (uint32_t)(uintptr_t)((lds_u8*)cbuf + (4 * wn + j) * CL::kSlot);
+    const uint32_t sc = (uint32_t)(uintptr_t)((lds_u8*)cbuf + CL::kScales + (4 * wn + j) * 128) +
+                        8 * (lane & 15);
+    lds_read_codes<FMT>(slot + lo16, slot + 2048 + 4 * lane, sc, gq & 1, o);
+  };
 
   float acc[4][4][2];
   int iacc[4][4][2];
@@ -314,28 +472,29 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         iacc[i][j][u] = 0;
       }
 
-  v4u x0, x1, x2;
-  xload(g0, x0, x1, x2);
-  xput(lds[0], x0, x1, x2);
-  Quad<FMT> qd[4], qn[4];
+  // prologue: codes of quad q0, then images g0 .. g0 + 2
+  cissue(q0);
 #pragma unroll
-  for (int j = 0; j < 4; j++)
-    load_quad_at<FMT>(a.pcodes, a.pscales, rbj[j], min<int64_t>(q0, a.GQ - 1), a.GQ, a.GP, lane, qd[j]);
-  __syncthreads();
+  for (int t = 0; t < 3; t++) xissue(g0 + t < g1 ? g0 + t : g1 - 1, t);
 
+  Quad<FMT> qd[4];
   for (int64_t q = q0; q < q1; q++) {
-    // next quad's codes and scales
-    const int64_t qnx = min<int64_t>(q + 1 < q1 ? q + 1 : q, a.GQ - 1);
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-      load_quad_at<FMT>(a.pcodes, a.pscales, rbj[j], qnx, a.GQ, a.GP, lane, qn[j]);
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       const int64_t g = 4 * q + t;
       if (g < g1) {
-        const int buf = (int)((g - g0) & 1);
-        const int64_t gn = g + 1 < g1 ? g + 1 : g;
-        xload(gn, x0, x1, x2);
+        // issued after the copies this group needs: two images, and at t =
+        // 2, 3 also the next quad's codes (issued at t = 1 after its image)
+        if (t < 2)
+          xsync(std::integral_constant<int, 6>());
+        else
+          xsync(std::integral_constant<int, 6 + CL::kCopies>());
+        if (t == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) cread(j, q, qd[j]);
+        }
+        xissue(g + 3 < g1 ? g + 3 : g1 - 1, (t + 3) & 3);
+        if (t == 1) cissue(q + 1 < q1 ? q + 1 : q);
         v8i B[4];
         float sj[4];
 #pragma unroll
@@ -343,17 +502,16 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
           B[j] = decode_group<FMT>(qd[j], t, t3);
           sj[j] = a.pscales ? quad_scale<FMT>(qd[j], t) : 1.0f;
         }
-        const uint8_t* L = lds[buf];
+        v4u A0[4], A1[4];
+        uint32_t se[4];
+        aread(t, A0, A1, se);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint8_t* at = L + (4 * wm + i) * kATBytes;
-          const v4u a0 = *(const v4u*)(at + 32 * lane), a1 = *(const v4u*)(at + 32 * lane + 16);
-          const v8i A = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-          const int se = at[2048 + lane];
+          const v8i A = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
+                            (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
           v4f c[4];
 #pragma unroll
-          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4<0>(A, B[j], se);
+          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4<0>(A, B[j], (int)se[i]);
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const float s0 = c[j][0] + c[j][1], s1 = c[j][2] + c[j][3];
@@ -366,13 +524,11 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
             }
           }
         }
-        if (g + 1 < g1) xput(lds[buf ^ 1], x0, x1, x2);
-        __syncthreads();
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; j++) qd[j] = qn[j];
   }
+  // no copy may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kVmLgkmWait | 0);
 
   uint32_t v[32];
 #pragma unroll
@@ -402,6 +558,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------- planning
