@@ -183,8 +183,8 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
  *     and Y[m][n] = x_scales[m] * sum_g scale[n][g] * A[m][n][g].
  *     y_dtype I32 requires pscales == NULL and returns sum_g A[m][n][g].
  *   y_dtype F32 or BF16 (or I32 as above).
- * Alignment: pcodes, pscales, X, Y 16 bytes.  Uses the per-stream workspace
- * described for lowbit_gemv. */
+ * K <= 2^36 (E_SHAPE beyond).  Alignment: pcodes, pscales, X, Y 16 bytes.
+ * Uses the per-stream workspace described for lowbit_gemv. */
 int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* X,
                 const float* x_scales, int y_dtype, void* Y, void* stream);

@@ -233,6 +233,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
   if (!pcodes || !X || !Y) return LOWBIT_E_NULL;
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   if (!shape_ok(N, K) || M < 1 || M > (int64_t(1) << 31)) return LOWBIT_E_SHAPE;
+  if (K > (int64_t(1) << 36)) return LOWBIT_E_SHAPE;  // 32-bit group indices of the GEMM
   if (x_dtype != LOWBIT_BF16 && x_dtype != LOWBIT_I8) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_I32)
     return LOWBIT_E_UNSUPPORTED;

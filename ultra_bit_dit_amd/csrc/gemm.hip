@@ -142,15 +142,16 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
 // with an E8M0 exponent per 32-element hardware block (bf16: term 1 is 16x
 // the residual of term 0; int8 q = 16 (q >> 4) + (q & 15) exactly), weights
 // as fp4 decoded from the packed words with one or two VALU ops per 8
-// weights.  One MFMA multiplies 8 activation rows (x 2 terms) by 16 weight
-// rows over one group; the group's fp32 partial is scaled by the fp16 group
-// scale in fp32 (int8 with unit scales: exact integer per group).
-constexpr int kAT = 8;                   // activation rows per MFMA (x 2 terms = 16 A rows)
+// weights.  Two MFMAs (term 0, then term 1 accumulated onto it) multiply 16
+// activation rows by 16 weight rows over one group; the group's fp32
+// partial is scaled by the fp16 group scale in fp32 (int8 with unit scales:
+// exact integer per group).
+constexpr int kRT = 16;                  // activation rows per A-tile (one term each)
 constexpr int kATBytes = 64 * 32 + 64;   // one A-tile of one group: fp8 bytes + exponents
-constexpr int kF8BM = 64;                // activation rows per workgroup tile (8 A-tiles)
+constexpr int kF8BM = 64;                // activation rows per workgroup tile (4 x 2 A-tiles)
 constexpr int kF8BN = 256;               // weight rows per workgroup tile (16 row-blocks)
 constexpr int kF8Threads = 512;          // 8 waves: 2 (rows) x 4 (columns)
-constexpr int kF8Img = (kF8BM / kAT) * kATBytes;  // staged bytes of one workgroup tile and group
+constexpr int kF8Img = (kF8BM / kRT) * 2 * kATBytes;  // staged bytes of one workgroup tile and group
 
 // Staging: one thread per (row m, group g, hardware block b).  Block b of a
 // group holds k = 128 g + kmap(b, i), i = 0..31 (two runs of 16); A lane
@@ -159,6 +160,7 @@ constexpr int kF8Img = (kF8BM / kAT) * kATBytes;  // staged bytes of one workgro
 // lane L also supplies the exponent of (A row L % 16, block L / 16).
 // Layout: per (64-row tile, group) kF8Img bytes; A-tile a of it at a *
 // kATBytes: 64 lanes x 32 fp8 bytes, then 64 exponent bytes (by lane).
+// A-tile 2 rt + u holds term u of rows 16 rt .. 16 rt + 15 (A row = row % 16).
 // Rows >= M are staged as zeros.
 template <int XK>
 __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t K, int64_t G,
@@ -245,24 +247,30 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t1[4 * j], t1[4 * j + 1], 0, false);
     w1[j] = __builtin_amdgcn_cvt_pk_fp8_f32(t1[4 * j + 2], t1[4 * j + 3], w, true);
   }
-  uint8_t* blk = xs + ((m / kF8BM) * G + g) * (int64_t)kF8Img + ((m % kF8BM) / kAT) * kATBytes;
-  const int r0 = 2 * (int)(m % kAT);  // A row of term 0 (term 1 is the next row)
+  // term u of row m: A-tile 2 rt + u of the row's 64-row tile, A row r
+  const int rt = (int)((m % kF8BM) / kRT), r = (int)(m % kRT);
+  uint8_t* blk0 = xs + ((m / kF8BM) * G + g) * (int64_t)kF8Img + 2 * rt * kATBytes;
+  uint8_t* blk1 = blk0 + kATBytes;
 #pragma unroll
   for (int hh = 0; hh < 2; hh++) {
     const int kb = 2 * (b & 1) + hh;
     const int e = 16 * (b >> 1);
-    *(v4u*)(blk + (r0 + 16 * kb) * 32 + e) = v4u{w0[4 * hh], w0[4 * hh + 1], w0[4 * hh + 2], w0[4 * hh + 3]};
-    *(v4u*)(blk + (r0 + 1 + 16 * kb) * 32 + e) = v4u{w1[4 * hh], w1[4 * hh + 1], w1[4 * hh + 2], w1[4 * hh + 3]};
+    *(v4u*)(blk0 + (r + 16 * kb) * 32 + e) = v4u{w0[4 * hh], w0[4 * hh + 1], w0[4 * hh + 2], w0[4 * hh + 3]};
+    *(v4u*)(blk1 + (r + 16 * kb) * 32 + e) = v4u{w1[4 * hh], w1[4 * hh + 1], w1[4 * hh + 2], w1[4 * hh + 3]};
   }
-  blk[2048 + r0 + 16 * b] = (uint8_t)e0;
-  blk[2048 + r0 + 1 + 16 * b] = (uint8_t)e1;
+  blk0[2048 + r + 16 * b] = (uint8_t)e0;
+  blk1[2048 + r + 16 * b] = (uint8_t)e1;
 }
 
-template <int T>
-__device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se, const v4f& C) {
   // A: fp8 e4m3 (0) with the E8M0 block exponent in byte 0 of se; B: fp4 e2m1 (4), unscaled
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, se, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 0, 4, 0, se, 0, 127);
 }
 
 // LDS reads of the GEMM main loop, written out so that the compiler does not
@@ -332,7 +340,8 @@ __device__ __forceinline__ void lds_read_codes(uint32_t pc, uint32_t pt, uint32_
 }
 
 // Workgroup tile 64 rows x 256 columns, 8 waves: wave (wm, wn) owns A-tiles
-// 4 wm .. 4 wm + 3 (32 rows) and row-blocks 4 wn .. 4 wn + 3 (64 columns).
+// 4 wm .. 4 wm + 3 (rows 32 wm .. 32 wm + 31, both terms) and row-blocks
+// 4 wn .. 4 wn + 3 (64 columns).
 //
 // Every global read of the main loop is a direct global -> LDS copy
 // (global_load_lds), so one counter of this wave's copies orders everything
@@ -369,13 +378,20 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     return (lds_u8*)(t == 0 ? xb0 : t == 1 ? xb1 : t == 2 ? xb2 : xb3);
   };
   constexpr bool INT = XK == XK_I8 && !SCALED;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave-uniform values are kept in scalar registers (the copy addresses
+  // below are then a scalar base plus a fixed per-lane offset)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   int64_t mt, nt;
   int ks;
   tile_of(a, mt, nt, ks);
-  const int64_t q0 = a.GQ * ks / a.KS, q1 = a.GQ * (ks + 1) / a.KS;
-  const int64_t g0 = 4 * q0, g1 = 4 * q1 < a.G ? 4 * q1 : a.G;
+  mt = uniform64(mt);
+  nt = uniform64(nt);
+  ks = __builtin_amdgcn_readfirstlane(ks);
+  // group and quad indices fit 32 bits (K < 2^38)
+  const int q0 = __builtin_amdgcn_readfirstlane((int)(a.GQ * ks / a.KS));
+  const int q1 = __builtin_amdgcn_readfirstlane((int)(a.GQ * (ks + 1) / a.KS));
+  const int g0 = 4 * q0, g1 = 4 * q1 < (int)a.G ? 4 * q1 : (int)a.G;
   bool live[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) live[j] = nt * 16 + wn * 4 + j < a.NB;
@@ -389,8 +405,8 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   const uint32_t vo2 = 16384 + 64 * wave + 16 * lane;
   // image of group g into ring buffer t: 1 KiB chunks w and w + 8, and
   // 64 bytes of the 512-byte tail (lanes 0..3)
-  auto xissue = [&](int64_t g, int t) {
-    const uint8_t* src = xs + g * kF8Img;
+  auto xissue = [&](int g, int t) {
+    const uint8_t* src = xs + (int64_t)g * kF8Img;
     lds_u8* dst = ring(t);
     __builtin_amdgcn_global_load_lds(src + vo0, dst + 1024 * wave, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
@@ -408,7 +424,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   const uint32_t so = 128 * (uint32_t)(lane >> 3) + 16 * (lane & 7);  // scales gather
   const int64_t GO = (a.GQ + 1) / 2;
   const uint8_t* sbase = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
-  auto cissue = [&](int64_t gq) {
+  auto cissue = [&](int gq) {
     lds_u8* cb = (lds_u8*)cbuf;
 #pragma unroll
     for (int u = 0; u < 2; u++) {
@@ -453,23 +469,24 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     lds_read_a(base + 32 * lane, base + 2048 + lane, A0, A1, se);
   };
   // codes and scales of row-block 4 wn + j of the quad in the code buffer
-  auto cread = [&](int j, int64_t gq, Quad<FMT>& o) {
+  auto cread = [&](int j, int gq, Quad<FMT>& o) {
     const uint32_t slot = (uint32_t)(uintptr_t)((lds_u8*)cbuf + (4 * wn + j) * CL::kSlot);
     const uint32_t sc = (uint32_t)(uintptr_t)((lds_u8*)cbuf + CL::kScales + (4 * wn + j) * 128) +
                         8 * (lane & 15);
     lds_read_codes<FMT>(slot + lo16, slot + 2048 + 4 * lane, sc, gq & 1, o);
   };
 
-  float acc[4][4][2];
-  int iacc[4][4][2];
+  // acc[rt][j][e]: row 32 wm + 16 rt + 4 (lane / 16) + e, column 16 (4 wn + j) + lane % 16
+  float acc[2][4][4];
+  int iacc[2][4][4];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        acc[i][j][u] = 0.f;
-        iacc[i][j][u] = 0;
+      for (int e = 0; e < 4; e++) {
+        acc[i][j][e] = 0.f;
+        iacc[i][j][e] = 0;
       }
 
   // prologue: codes of quad q0, then images g0 .. g0 + 2
@@ -478,10 +495,10 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   for (int t = 0; t < 3; t++) xissue(g0 + t < g1 ? g0 + t : g1 - 1, t);
 
   Quad<FMT> qd[4];
-  for (int64_t q = q0; q < q1; q++) {
+  for (int q = q0; q < q1; q++) {
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      const int64_t g = 4 * q + t;
+      const int g = 4 * q + t;
       if (g < g1) {
         // issued after the copies this group needs: two images, and at t =
         // 2, 3 also the next quad's codes (issued at t = 1 after its image)
@@ -505,22 +522,29 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         v4u A0[4], A1[4];
         uint32_t se[4];
         aread(t, A0, A1, se);
+        // row-tile rt (16 rows): term 0 (A-tile 2 rt) and term 1 (2 rt + 1)
+        // accumulate into one MFMA result, scaled once per group
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const v8i A = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
-                            (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+        for (int rt = 0; rt < 2; rt++) {
+          const v8i At0 = v8i{(int)A0[2 * rt].x, (int)A0[2 * rt].y, (int)A0[2 * rt].z,
+                              (int)A0[2 * rt].w, (int)A1[2 * rt].x, (int)A1[2 * rt].y,
+                              (int)A1[2 * rt].z, (int)A1[2 * rt].w};
+          const v8i At1 = v8i{(int)A0[2 * rt + 1].x, (int)A0[2 * rt + 1].y, (int)A0[2 * rt + 1].z,
+                              (int)A0[2 * rt + 1].w, (int)A1[2 * rt + 1].x, (int)A1[2 * rt + 1].y,
+                              (int)A1[2 * rt + 1].z, (int)A1[2 * rt + 1].w};
           v4f c[4];
 #pragma unroll
-          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4<0>(A, B[j], (int)se[i]);
+          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At0, B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At1, B[j], (int)se[2 * rt + 1], c[j]);
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            const float s0 = c[j][0] + c[j][1], s1 = c[j][2] + c[j][3];
-            if constexpr (INT) {
-              iacc[i][j][0] += __float2int_rn(s0);
-              iacc[i][j][1] += __float2int_rn(s1);
-            } else {
-              acc[i][j][0] = fmaf(sj[j], s0, acc[i][j][0]);
-              acc[i][j][1] = fmaf(sj[j], s1, acc[i][j][1]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              if constexpr (INT)
+                iacc[rt][j][e] += __float2int_rn(c[j][e]);
+              else
+                acc[rt][j][e] = fmaf(sj[j], c[j][e], acc[rt][j][e]);
             }
           }
         }
@@ -532,25 +556,25 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 
   uint32_t v[32];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int u = 0; u < 2; u++)
-        v[(i * 4 + j) * 2 + u] = INT ? (uint32_t)iacc[i][j][u] : __float_as_uint(acc[i][j][u]);
+      for (int e = 0; e < 4; e++)
+        v[(i * 4 + j) * 4 + e] = INT ? (uint32_t)iacc[i][j][e] : __float_as_uint(acc[i][j][e]);
   if (a.KS > 1 && !split_reduce<32, INT, kF8Threads>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 2; i++) {
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int64_t row = mt * kF8BM + 32 * wm + 8 * i + 2 * (lane >> 4) + u;
+    for (int e = 0; e < 4; e++) {
+      const int64_t row = mt * kF8BM + 32 * wm + 16 * i + 4 * (lane >> 4) + e;
       if (row >= a.M) continue;
       const float rs = SCALED ? a.rowscale[row] : 1.0f;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int64_t col = (nt * 16 + wn * 4 + j) * 16 + (lane & 15);
         if (!live[j] || col >= a.N) continue;
-        const uint32_t x = v[(i * 4 + j) * 2 + u];
+        const uint32_t x = v[(i * 4 + j) * 4 + e];
         if constexpr (INT)
           store_y<YK>(a.y, row * a.N + col, (int32_t)x);
         else
