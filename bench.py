@@ -47,7 +47,17 @@ FMT_NAMES = {1: "binary", 2: "ternary-2bit", 3: "ternary-base3"}
 SEED = 1002  # decode-step workload
 PP_SEED, DIT_SEED = 1003, 1004
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "{kernel}_decode_step_pmc.txt")
-GEMV_SOURCE = os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", "gemv.hip")
+# sources the decode kernels are built from (their hash ties a counter summary to them)
+GEMV_SOURCES = [os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", f)
+                for f in ("gemv.hip", "fp4.hpp", "common.hpp")]
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for path in GEMV_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -120,9 +130,7 @@ def pmc_traffic(launch_bytes, kernel):
                 if "=" in line and not line.startswith("#"):
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
-        with open(GEMV_SOURCE, "rb") as f:
-            src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-        if kv.get("gemv_source_sha256_16") != src_hash or kv.get("kernel") != kernel:
+        if kv.get("gemv_source_sha256_16") != gemv_source_hash() or kv.get("kernel") != kernel:
             return None, "kernel changed since the counters were taken"
         copy_bytes = float(kv["copy_bytes_each_way"])
         f_scale = copy_bytes / (float(kv["copy_FETCH_SIZE_KiB"]) * 1024.0)

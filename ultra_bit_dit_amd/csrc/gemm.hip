@@ -168,9 +168,12 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
                                                 uint8_t* __restrict__ xs) {
   const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (tid >= Mpad * G * 4) return;
+  // thread order: b fastest, then 16 consecutive rows, then g, so that a
+  // wavefront's stores fill whole 512-byte runs of one A-tile (and its 64
+  // exponent bytes) and its loads read 256-byte row segments
   const int b = (int)(tid & 3);
-  const int64_t g = (tid >> 2) % G;
-  const int64_t m = (tid >> 2) / G;
+  const int64_t g = (tid >> 6) % G;
+  const int64_t m = (tid >> 6) / G * 16 + ((tid >> 2) & 15);
   float v[32];
 #pragma unroll
   for (int hh = 0; hh < 2; hh++) {
