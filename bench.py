@@ -160,6 +160,18 @@ def copy_calibration(torch):
     del src, dst
 
 
+def hbm_read_rate(lb, torch, steps=10, warmup=2, nbytes=4 << 30):
+    """Sustained HBM read rate of this device: a plain streaming read of a
+    4 GiB buffer (lowbit_hbm_read_probe), timed like the decode step."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    ms = time_region(torch, stream, lambda: lb.hbm_read_probe(buf, out, stream), steps, warmup)
+    del buf, out
+    torch.cuda.synchronize()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def chain_for(lb, fmt, W, xs, ys, layers, wait):
     stages = []
     for l in range(layers):
@@ -318,7 +330,11 @@ def main():
     from ultra_bit_dit_amd import lowbit as lb
 
     copy_calibration(torch)
+    read_gbs = hbm_read_rate(lb, torch)
+    log(f"streaming read of 4 GiB: {read_gbs:.0f} GB/s")
     ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
+    roof["measured_read_gb_s"] = round(read_gbs, 1)
+    roof["frac_of_measured_read"] = round(roof["achieved"] / read_gbs, 4)
 
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",

@@ -231,6 +231,14 @@ int lowbit_chain_status(lowbit_chain* chain, int* failed_waits);
 /* Frees the chain's device memory (synchronizes the device first). */
 int lowbit_chain_destroy(lowbit_chain* chain);
 
+/* Measurement helper, not part of the matrix-product path: reads the
+ * `bytes` (a positive multiple of 16) at src once with 16-byte streaming
+ * loads spread over the whole device and XORs the data into *out (device
+ * uint32, caller-initialised), so the sustained HBM read rate can be timed
+ * beside the decode kernels.  src 16-byte aligned, out 4-byte aligned.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_HIP. */
+int lowbit_hbm_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

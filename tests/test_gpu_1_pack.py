@@ -90,3 +90,19 @@ def test_unpack_counts_reserved_patterns():
     c2, _ = lb.unpack(3, N, K, dev(pc), dev(ps.view(np.int16)), bad=bad)
     torch.cuda.synchronize()
     assert int(bad.item()) == 9 and not c2.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 << 20])
+def test_hbm_read_probe_reads_every_byte(nbytes):
+    """The streaming-read helper folds every 16-byte piece it reads into one
+    XOR: equal to numpy's XOR of the same data (ragged tail included)."""
+    print(f"read probe {nbytes} B", flush=True)
+    rng = np.random.default_rng(nbytes)
+    data = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lb.hbm_read_probe(dev(data.view(np.int32)), out)
+    torch.cuda.synchronize()
+    assert int(out.item()) & 0xFFFFFFFF == int(np.bitwise_xor.reduce(data))
+    with pytest.raises(lb.LowbitError) as e:
+        lb.hbm_read_probe(dev(data.view(np.int32))[:3], out)
+    assert e.value.status == lb.E_SHAPE

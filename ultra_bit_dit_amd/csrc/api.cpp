@@ -303,3 +303,10 @@ int lowbit_chain_destroy(lowbit_chain* chain) {
 }
 
 }  // extern "C"
+
+int lowbit_hbm_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream) {
+  if (!src || !out) return LOWBIT_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return LOWBIT_E_SHAPE;
+  if (!aligned(src, 16) || !aligned(out, 4)) return LOWBIT_E_ALIGN;
+  return hip_status(launch_hbm_read(src, bytes, out, (hipStream_t)stream));
+}

@@ -128,4 +128,7 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int xkind);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// streaming read of `bytes` (a multiple of 16) at src; XOR of the data into *out
+hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
+
 }  // namespace lowbit

@@ -18,7 +18,8 @@ F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
            "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
-           "lowbit_chain_create", "lowbit_chain_run", "lowbit_chain_status", "lowbit_chain_destroy")
+           "lowbit_chain_create", "lowbit_chain_run", "lowbit_chain_status", "lowbit_chain_destroy",
+           "lowbit_hbm_read_probe")
 
 
 class GemvStage(ctypes.Structure):
@@ -60,6 +61,7 @@ def lib():
         L.lowbit_chain_run.argtypes = [vp, vp]
         L.lowbit_chain_status.argtypes = [vp, ctypes.POINTER(i32)]
         L.lowbit_chain_destroy.argtypes = [vp]
+        L.lowbit_hbm_read_probe.argtypes = [vp, i64, vp, vp]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -163,6 +165,14 @@ def gemm(fmt, M, N, K, pcodes, pscales, X, x_scales=None, y_dtype=F32, Y=None, x
     _check("lowbit_gemm", lib().lowbit_gemm(fmt, M, N, K, _ptr(pcodes), _ptr(pscales), _xdt(X, x_dtype),
                                             _ptr(X), _ptr(x_scales), y_dtype, _ptr(Y), _stream(stream)))
     return Y
+
+
+def hbm_read_probe(src, out, stream=None):
+    """Stream-read every byte of device tensor `src` once, XOR-folding the
+    data into the int32 device tensor `out` (see lowbit_hbm_read_probe)."""
+    nbytes = src.numel() * src.element_size()
+    _check("lowbit_hbm_read_probe",
+           lib().lowbit_hbm_read_probe(_ptr(src), nbytes, _ptr(out), _stream(stream)))
 
 
 class Chain:
