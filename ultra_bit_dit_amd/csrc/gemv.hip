@@ -310,6 +310,88 @@ __device__ __attribute__((always_inline)) inline void load_quad(const FArgs& a, 
   load_quad_at<FMT>(a.pcodes, a.pscales, rbc, gq, a.GQ, a.GP, threadIdx.x & 63, o);
 }
 
+// Item of row group rg, K-slice ks, for callers that know both: the same
+// slicing as item_of with 32-bit divisions only (a product's quads and
+// slices fit 32 bits: GQ < 2^28 in every chain).
+template <int FMT>
+__device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, int64_t rg,
+                                                              int64_t ks) {
+  Item it;
+  const int W = blockDim.x >> 6, w = threadIdx.x >> 6;
+  it.rg = rg;
+  it.ks = ks;
+  const uint32_t KS = (uint32_t)a.KS, k = (uint32_t)ks;
+  // floor(T * k / KS) without a 64-bit product: T = (T / KS) KS + T % KS
+  auto split = [&](uint32_t T, uint32_t kk) { return (T / KS) * kk + (T % KS) * kk / KS; };
+  uint32_t q0, q1;
+  if (FMT == 3) {
+    const uint32_t GO = (uint32_t)((a.GQ + 1) / 2);
+    q0 = 2 * split(GO, k);
+    q1 = min(2 * split(GO, k + 1), (uint32_t)a.GQ);
+  } else {
+    q0 = split((uint32_t)a.GQ, k);
+    q1 = split((uint32_t)a.GQ, k + 1);
+  }
+  it.q0 = q0;
+  it.nq = (int)(q1 - q0);
+  it.rb = (int64_t)W * rg + w;
+  it.live = it.rb < a.NB;
+  return it;
+}
+
+// Code and scale addresses of an item's first quad for this lane, so that
+// quad q of the item is a fixed offset from them (quads past the item's end
+// re-read its last quad).
+struct QuadPtr {
+  const uint8_t* c;
+  const uint8_t* s;
+  int nq;
+  bool p1_last;  // 2-bit: the last quad's second word block is clamped onto its first
+};
+
+template <int FMT>
+__device__ __attribute__((always_inline)) inline QuadPtr quad_ptr(const FArgs& a, const Item& it) {
+  QuadPtr p;
+  const int L = threadIdx.x & 63;
+  const int64_t rbc = it.live ? it.rb : a.NB - 1;
+  if constexpr (FMT == 1) {
+    p.c = a.pcodes + (rbc * a.GQ + it.q0) * 1024 + 16 * L;
+  } else if constexpr (FMT == 2) {
+    p.c = a.pcodes + (rbc * a.GP + 2 * it.q0) * 1024 + 16 * L;
+  } else {
+    p.c = a.pcodes + (rbc * ((a.GQ + 1) / 2) + (it.q0 >> 1)) * 3328 + 16 * L;
+  }
+  const uint8_t* sb = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
+  p.s = sb + ((rbc * a.GQ + it.q0) * 16 + (L & 15)) * 8;
+  p.nq = it.nq;
+  p.p1_last = 2 * (it.q0 + it.nq - 1) + 1 >= a.GP;
+  return p;
+}
+
+// quad q of an item through its QuadPtr (the same words as load_quad)
+template <int FMT>
+__device__ __attribute__((always_inline)) inline void load_quad_p(const QuadPtr& p, int q,
+                                                                 Quad<FMT>& o) {
+  const int qq = q < p.nq ? q : p.nq - 1;
+  if constexpr (FMT == 1) {
+    o.w[0] = __builtin_nontemporal_load((const u4*)(p.c + qq * 1024));
+  } else if constexpr (FMT == 2) {
+    const uint8_t* c = p.c + qq * 2048;
+    o.w[0] = __builtin_nontemporal_load((const u4*)c);
+    o.w[1] = __builtin_nontemporal_load((const u4*)(c + (p.p1_last && qq == p.nq - 1 ? 0 : 1024)));
+  } else {
+    // octet block qq / 2 (item slices start on whole octets), half h = qq % 2
+    const uint8_t* lp = p.c + (qq >> 1) * 3328;
+    const int h = qq & 1;
+    o.c30 = __builtin_nontemporal_load((const u2*)(lp + (h ? 1024 + 8 : 0)));
+    o.c31 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 : 8)));
+    o.c32 = __builtin_nontemporal_load((const u2*)(lp + (h ? 2048 + 8 : 1024)));
+    const int L = threadIdx.x & 63;
+    o.t3 = __builtin_nontemporal_load((const uint32_t*)(lp - 16 * L + 3072 + 4 * L)) >> (16 * h);
+  }
+  o.sc = *(const uint2*)(p.s + qq * 128);
+}
+
 // LDS of an item: staged activations, a zero block, the base-3 table
 struct Lds {
   uint8_t* xa;
@@ -709,7 +791,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
       while (j >= sfirst[s + 1]) s++;
       const FArgs a = load_args(args, s);
       const int64_t ks = j - sfirst[s];
-      const Item it = item_of<FMT>(a, ks);  // row group 0 of slice ks
+      const Item it = item_at<FMT>(a, 0, ks);  // row group 0 of slice ks
       uint8_t* xa = c.xst + xoff[s] + ks * slice_stride<FMT>(a);
       uint8_t* xe = xa + (int64_t)it.nq * 16 * a.MA * 32;
       const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
@@ -764,7 +846,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     while (u >= ufirst[s + 1]) s++;
     FArgs a = load_args(args, s);
     int64_t rg = u - ufirst[s], ks = 0;
-    Item it = item_of<FMT>(a, rg * a.KS);
+    Item it = item_at<FMT>(a, rg, 0);
     // staged activations of a slice, XR 16-byte pieces per thread
     auto xsrc = [&](const FArgs& f, int sidx, int64_t kslice, int nq, int k) {
       const int64_t nb = (int64_t)nq * 16 * f.MA * 33 / 16;
@@ -825,12 +907,16 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     int64_t un, rgn, ksn;
     bool more = next(s, u, rg, ks, a, sn, un, rgn, ksn);
     FArgs an = load_args(args, sn);
-    Item itn = item_of<FMT>(an, rgn * an.KS + ksn);
+    Item itn = item_at<FMT>(an, rgn, ksn);
+    QuadPtr pn = quad_ptr<FMT>(an, itn);
     // the next slice's activations, then the current slice's codes
     XLD(an, sn, ksn, itn.nq);
     Quad<FMT> qd[QM];
+    {
+      const QuadPtr p0 = quad_ptr<FMT>(a, it);
 #pragma unroll
-    for (int q = 0; q < QM; q++) load_quad<FMT>(a, it, q, qd[q]);
+      for (int q = 0; q < QM; q++) load_quad_p<FMT>(p0, q, qd[q]);
+    }
     float acc[1] = {0.f};
     int iacc[1] = {0};
     float tot = 0.f;  // slices added in slice order, as the split-K reduction does
@@ -884,11 +970,11 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
           // then the activations of the slice after next (issued on every
           // path, so that the wait counts stay exact across iterations)
           const FArgs a2 = load_args(args, s2);
-          const Item it2 = item_of<FMT>(a2, rg2 * a2.KS + ks2);
+          const Item it2 = item_at<FMT>(a2, rg2, ks2);
           XLD(a2, s2, ks2, it2.nq);
         }
         if (it.live && q < it.nq) quad_mfma<FMT, XK, 1, 2>(a, l, q, qd[q], acc, iacc);
-        load_quad<FMT>(an, itn, q, qd[q]);
+        load_quad_p<FMT>(pn, q, qd[q]);
       }
       // done reading slice j's image
       __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -913,7 +999,8 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
       sn = s2; un = u2; rgn = rg2; ksn = ks2;
       more = more2;
       an = load_args(args, sn);
-      itn = item_of<FMT>(an, rgn * an.KS + ksn);
+      itn = item_at<FMT>(an, rgn, ksn);
+      pn = quad_ptr<FMT>(an, itn);
       j++;
     }
   }
