@@ -317,7 +317,9 @@ template <int FMT>
 __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, int64_t rg,
                                                               int64_t ks) {
   Item it;
-  const int W = blockDim.x >> 6, w = threadIdx.x >> 6;
+  // the wave index is uniform in the wave: scalar, so that the item's tests
+  // are scalar branches
+  const int W = blockDim.x >> 6, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   it.rg = rg;
   it.ks = ks;
   const uint32_t KS = (uint32_t)a.KS, k = (uint32_t)ks;
