@@ -103,7 +103,7 @@ int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const
              hipStream_t s) {
   if (cdiv(N, 16) > (int64_t(1) << 40) / 16) return LOWBIT_E_SHAPE;
   void* ws = nullptr;
-  int rc = workspace(s, gemm_workspace_bytes(M, N, K, x_dtype), &ws);
+  int rc = workspace(s, gemm_workspace_bytes(fmt, M, N, K), &ws);
   if (rc) return rc;
   GemmArgs g;
   g.fmt = fmt;

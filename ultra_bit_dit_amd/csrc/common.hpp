@@ -125,7 +125,7 @@ struct GemmArgs {
   void* y;                  // [M][N]
   void* ws;                 // workspace (counters first)
 };
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int xkind);
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 // streaming read of `bytes` (a multiple of 16) at src; XOR of the data into *out

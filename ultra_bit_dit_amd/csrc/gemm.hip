@@ -26,9 +26,6 @@ namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-// s_waitcnt immediate that waits for vector memory (OR in vmcnt < 16) and
-// for all LDS/scalar-memory accesses (lgkmcnt 0); expcnt at its maximum
-constexpr int kVmLgkmWait = 0x0070;
 
 // ---------------------------------------------------------------- GEMM args
 struct KArgs {
@@ -149,7 +146,6 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
 constexpr int kRT = 16;                  // activation rows per A-tile (one term each)
 constexpr int kATBytes = 64 * 32 + 64;   // one A-tile of one group: fp8 bytes + exponents
 constexpr int kF8BM = 64;                // activation rows per workgroup tile (4 x 2 A-tiles)
-constexpr int kF8BN = 256;               // weight rows per workgroup tile (16 row-blocks)
 constexpr int kF8Threads = 512;          // 8 waves: 2 (rows) x 4 (columns)
 constexpr int kF8Img = (kF8BM / kRT) * 2 * kATBytes;  // staged bytes of one workgroup tile and group
 
@@ -342,9 +338,11 @@ __device__ __forceinline__ void lds_read_codes(uint32_t pc, uint32_t pt, uint32_
   }
 }
 
-// Workgroup tile 64 rows x 256 columns, 8 waves: wave (wm, wn) owns A-tiles
-// 4 wm .. 4 wm + 3 (rows 32 wm .. 32 wm + 31, both terms) and row-blocks
-// 4 wn .. 4 wn + 3 (64 columns).
+// Workgroup tile 64 rows x 64 RBW columns, 8 waves: wave (wm, wn) owns
+// A-tiles 4 wm .. 4 wm + 3 (rows 32 wm .. 32 wm + 31, both terms) and
+// row-blocks RBW wn .. RBW wn + RBW - 1 (16 RBW columns).  RBW = 8 halves
+// the LDS operand bytes per MFMA of RBW = 4 (each A-tile read feeds 8 row-
+// blocks) for wide products.
 //
 // Every global read of the main loop is a direct global -> LDS copy
 // (global_load_lds), so one counter of this wave's copies orders everything
@@ -353,27 +351,33 @@ __device__ __forceinline__ void lds_read_codes(uint32_t pc, uint32_t pt, uint32_
 //   groups ahead: group g in buffer (g - g0) % 4, the static t of the
 //   unrolled quad loop; each wave copies three pieces per image;
 // * codes and scales of the next quad go into one LDS code buffer at the
-//   second group of a quad; each wave copies those of two row-blocks, and at
-//   the first group of a quad every wave reads its four row-blocks' codes and
-//   scales from there into registers.
+//   second group of a quad; each wave copies those of RBW / 2 row-blocks, and
+//   at the first group of a quad every wave reads its RBW row-blocks' codes
+//   and scales from there into registers.
 // Copies past the end of the workgroup's K range re-read its last image or
 // quad into buffers that are no longer read, so that every group issues the
 // same copies.
-template <int FMT>
+template <int FMT, int RBW>
 struct CodeLds {
+  static constexpr int kRows = 4 * RBW;  // row-blocks of the workgroup tile
   // bytes per row-block slot: binary one 1 KiB block, 2-bit the P0/P1 pair,
   // base-3 two 1 KiB planes of the octet + its 256-byte tail
   static constexpr int kSlot = FMT == 1 ? 1024 : FMT == 2 ? 2048 : 2304;
-  static constexpr int kScales = 16 * kSlot;       // 16 x 128 bytes of scales
-  static constexpr int kBytes = kScales + 16 * 128;
-  // copy instructions per wave per quad: two row-blocks' codes + one scales
-  static constexpr int kCopies = 2 * (FMT == 1 ? 1 : FMT == 2 ? 2 : 3) + 1;
+  static constexpr int kScales = kRows * kSlot;  // then 128 bytes of scales per row-block
+  static constexpr int kBytes = kScales + kRows * 128;
+  // copy instructions per wave per quad: RBW / 2 row-blocks' codes + one for scales
+  static constexpr int kCopies = (RBW / 2) * (FMT == 1 ? 1 : FMT == 2 ? 2 : 3) + 1;
 };
 
-template <int FMT, int XK, int YK, bool SCALED>
+// s_waitcnt immediate: vmcnt n (6 bits, split over two fields), lgkmcnt 0,
+// expcnt at its maximum
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+
+template <int FMT, int XK, int YK, bool SCALED, int RBW>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_f8(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space code: device pass only
-  using CL = CodeLds<FMT>;
+  using CL = CodeLds<FMT, RBW>;
+  constexpr int HR = RBW / 2;  // row-blocks this wave copies
   __shared__ __attribute__((aligned(16))) uint8_t xb0[kF8Img], xb1[kF8Img], xb2[kF8Img], xb3[kF8Img];
   __shared__ __attribute__((aligned(16))) uint8_t cbuf[CL::kBytes];
   __shared__ uint32_t t3[256];
@@ -395,9 +399,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   const int q0 = __builtin_amdgcn_readfirstlane((int)(a.GQ * ks / a.KS));
   const int q1 = __builtin_amdgcn_readfirstlane((int)(a.GQ * (ks + 1) / a.KS));
   const int g0 = 4 * q0, g1 = 4 * q1 < (int)a.G ? 4 * q1 : (int)a.G;
-  bool live[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) live[j] = nt * 16 + wn * 4 + j < a.NB;
+  const int64_t rb0 = nt * CL::kRows + RBW * wn;  // this wave's first row-block
   if constexpr (FMT == 3) fill_trit_table(t3);
 
   // ---- copies.  Per-lane offsets stay in the same registers for the whole
@@ -415,22 +417,21 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
     if (lane < 4) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 64 * wave, 16, 0, 0);
   };
-  // this wave copies row-blocks 4 wn + 2 wm and 4 wn + 2 wm + 1 of the tile
-  const int cr = 4 * wn + 2 * wm;
-  int64_t crb[2];
+  // this wave copies row-blocks RBW wn + HR wm .. + HR - 1 of the tile
+  const int cr = RBW * wn + HR * wm;
+  int64_t crb[HR];
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int64_t rb = nt * 16 + cr + u;
+  for (int u = 0; u < HR; u++) {
+    const int64_t rb = nt * CL::kRows + cr + u;
     crb[u] = rb < a.NB ? rb : a.NB - 1;
   }
   const uint32_t lo16 = 16 * lane;
-  const uint32_t so = 128 * (uint32_t)(lane >> 3) + 16 * (lane & 7);  // scales gather
   const int64_t GO = (a.GQ + 1) / 2;
   const uint8_t* sbase = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
   auto cissue = [&](int gq) {
     lds_u8* cb = (lds_u8*)cbuf;
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
+    for (int u = 0; u < HR; u++) {
       lds_u8* slot = cb + (cr + u) * CL::kSlot;
       if constexpr (FMT == 1) {
         const uint8_t* src = a.pcodes + (crb[u] * a.GQ + gq) * 1024;
@@ -449,11 +450,11 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         if (lane < 16) __builtin_amdgcn_global_load_lds(tail + lo16, slot + 2048, 16, 0, 0);
       }
     }
-    // scales of both row-blocks: lanes 8u .. 8u + 7 gather row-block u's 128 bytes
-    if (lane < 16) {
-      const int64_t rb = crb[lane >> 3];
-      const uint8_t* src = sbase + (rb * a.GQ + gq) * 128 - 128 * (uint32_t)(lane >> 3);
-      __builtin_amdgcn_global_load_lds(src + so, cb + CL::kScales + 128 * cr, 16, 0, 0);
+    // scales of the HR row-blocks: lanes 8u .. 8u + 7 gather row-block u's 128 bytes
+    if (lane < 8 * HR) {
+      const int u = lane >> 3;
+      const uint8_t* src = sbase + (crb[u] * a.GQ + gq) * 128 + 16 * (lane & 7);
+      __builtin_amdgcn_global_load_lds(src, cb + CL::kScales + 128 * cr, 16, 0, 0);
     }
   };
   // Wait until the copies that the coming group reads have landed, with
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   // order.  The barrier carries no memory fence: a workgroup fence would
   // also wait for every copy still in flight.
   auto xsync = [&](auto later) {
-    __builtin_amdgcn_s_waitcnt(kVmLgkmWait | decltype(later)::value);
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(decltype(later)::value));
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
   };
@@ -471,21 +472,21 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
     lds_read_a(base + 32 * lane, base + 2048 + lane, A0, A1, se);
   };
-  // codes and scales of row-block 4 wn + j of the quad in the code buffer
+  // codes and scales of row-block RBW wn + j of the quad in the code buffer
   auto cread = [&](int j, int gq, Quad<FMT>& o) {
-    const uint32_t slot = (uint32_t)(uintptr_t)((lds_u8*)cbuf + (4 * wn + j) * CL::kSlot);
-    const uint32_t sc = (uint32_t)(uintptr_t)((lds_u8*)cbuf + CL::kScales + (4 * wn + j) * 128) +
+    const uint32_t slot = (uint32_t)(uintptr_t)((lds_u8*)cbuf + (RBW * wn + j) * CL::kSlot);
+    const uint32_t sc = (uint32_t)(uintptr_t)((lds_u8*)cbuf + CL::kScales + (RBW * wn + j) * 128) +
                         8 * (lane & 15);
     lds_read_codes<FMT>(slot + lo16, slot + 2048 + 4 * lane, sc, gq & 1, o);
   };
 
-  // acc[rt][j][e]: row 32 wm + 16 rt + 4 (lane / 16) + e, column 16 (4 wn + j) + lane % 16
-  float acc[2][4][4];
-  int iacc[2][4][4];
+  // acc[rt][j][e]: row 32 wm + 16 rt + 4 (lane / 16) + e, column 16 (RBW wn + j) + lane % 16
+  float acc[2][RBW][4];
+  int iacc[2][RBW][4];
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < RBW; j++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         acc[i][j][e] = 0.f;
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
   for (int t = 0; t < 3; t++) xissue(g0 + t < g1 ? g0 + t : g1 - 1, t);
 
-  Quad<FMT> qd[4];
+  Quad<FMT> qd[RBW];
   for (int q = q0; q < q1; q++) {
 #pragma unroll
     for (int t = 0; t < 4; t++) {
@@ -511,43 +512,47 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
           xsync(std::integral_constant<int, 6 + CL::kCopies>());
         if (t == 0) {
 #pragma unroll
-          for (int j = 0; j < 4; j++) cread(j, q, qd[j]);
+          for (int j = 0; j < RBW; j++) cread(j, q, qd[j]);
         }
         xissue(g + 3 < g1 ? g + 3 : g1 - 1, (t + 3) & 3);
         if (t == 1) cissue(q + 1 < q1 ? q + 1 : q);
-        v8i B[4];
-        float sj[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          B[j] = decode_group<FMT>(qd[j], t, t3);
-          sj[j] = a.pscales ? quad_scale<FMT>(qd[j], t) : 1.0f;
-        }
         v4u A0[4], A1[4];
         uint32_t se[4];
         aread(t, A0, A1, se);
-        // row-tile rt (16 rows): term 0 (A-tile 2 rt) and term 1 (2 rt + 1)
-        // accumulate into one MFMA result, scaled once per group
+        v8i At[4];
 #pragma unroll
-        for (int rt = 0; rt < 2; rt++) {
-          const v8i At0 = v8i{(int)A0[2 * rt].x, (int)A0[2 * rt].y, (int)A0[2 * rt].z,
-                              (int)A0[2 * rt].w, (int)A1[2 * rt].x, (int)A1[2 * rt].y,
-                              (int)A1[2 * rt].z, (int)A1[2 * rt].w};
-          const v8i At1 = v8i{(int)A0[2 * rt + 1].x, (int)A0[2 * rt + 1].y, (int)A0[2 * rt + 1].z,
-                              (int)A0[2 * rt + 1].w, (int)A1[2 * rt + 1].x, (int)A1[2 * rt + 1].y,
-                              (int)A1[2 * rt + 1].z, (int)A1[2 * rt + 1].w};
-          v4f c[4];
+        for (int i = 0; i < 4; i++)
+          At[i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
+                      (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+        // row-blocks four at a time: decode, then per row-tile rt (16 rows)
+        // term 0 (A-tile 2 rt) and term 1 (2 rt + 1) accumulate into one MFMA
+        // result, scaled once per group
 #pragma unroll
-          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At0, B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At1, B[j], (int)se[2 * rt + 1], c[j]);
+        for (int h = 0; h < RBW; h += 4) {
+          v8i B[4];
+          float sj[4];
 #pragma unroll
           for (int j = 0; j < 4; j++) {
+            B[j] = decode_group<FMT>(qd[h + j], t, t3);
+            sj[j] = a.pscales ? quad_scale<FMT>(qd[h + j], t) : 1.0f;
+          }
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-              if constexpr (INT)
-                iacc[rt][j][e] += __float2int_rn(c[j][e]);
-              else
-                acc[rt][j][e] = fmaf(sj[j], c[j][e], acc[rt][j][e]);
+          for (int rt = 0; rt < 2; rt++) {
+            v4f c[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              c[j] = mfma_f8f4(At[2 * rt], B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At[2 * rt + 1], B[j], (int)se[2 * rt + 1], c[j]);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+              for (int e = 0; e < 4; e++) {
+                if constexpr (INT)
+                  iacc[rt][h + j][e] += __float2int_rn(c[j][e]);
+                else
+                  acc[rt][h + j][e] = fmaf(sj[j], c[j][e], acc[rt][h + j][e]);
+              }
             }
           }
         }
@@ -555,17 +560,18 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   }
   // no copy may still be writing LDS when the workgroup ends
-  __builtin_amdgcn_s_waitcnt(kVmLgkmWait | 0);
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
 
-  uint32_t v[32];
+  constexpr int NV = 2 * RBW * 4;
+  uint32_t v[NV];
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < RBW; j++)
 #pragma unroll
       for (int e = 0; e < 4; e++)
-        v[(i * 4 + j) * 4 + e] = INT ? (uint32_t)iacc[i][j][e] : __float_as_uint(acc[i][j][e]);
-  if (a.KS > 1 && !split_reduce<32, INT, kF8Threads>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
+        v[(i * RBW + j) * 4 + e] = INT ? (uint32_t)iacc[i][j][e] : __float_as_uint(acc[i][j][e]);
+  if (a.KS > 1 && !split_reduce<NV, INT, kF8Threads>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -574,10 +580,10 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
       if (row >= a.M) continue;
       const float rs = SCALED ? a.rowscale[row] : 1.0f;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int64_t col = (nt * 16 + wn * 4 + j) * 16 + (lane & 15);
-        if (!live[j] || col >= a.N) continue;
-        const uint32_t x = v[(i * 4 + j) * 4 + e];
+      for (int j = 0; j < RBW; j++) {
+        const int64_t col = (rb0 + j) * 16 + (lane & 15);
+        if (rb0 + j >= a.NB || col >= a.N) continue;
+        const uint32_t x = v[(i * RBW + j) * 4 + e];
         if constexpr (INT)
           store_y<YK>(a.y, row * a.N + col, (int32_t)x);
         else
@@ -591,16 +597,20 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 // ---------------------------------------------------------------- planning
 struct GemmPlan {
   int64_t MT, NT, G, KS;
+  int RBW;
   size_t xt_off, rs_off, part_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// K-split count: the smallest that keeps at least ~85% of a whole number of
-// waves of workgroups busy on the 256 compute units (one workgroup each),
-// up to 8 and at most one quad of groups per split
+// K-split count when the tile grid does not fill the 256 compute units once
+// (one workgroup each): the smallest that keeps at least ~85% of a whole
+// number of waves of workgroups busy, up to 8 and at most one quad of groups
+// per split.  Grids of a full round or more are not split (the partial sums
+// would cost more HBM traffic than the idle tail).
 int64_t pick_splits(int64_t tiles, int64_t GQ) {
   const int64_t slots = 256;
+  if (tiles >= slots) return 1;
   int64_t best = 1;
   double best_eff = 0.0;
   for (int64_t ks = 1; ks <= std::min<int64_t>(8, GQ); ks++) {
@@ -615,22 +625,25 @@ int64_t pick_splits(int64_t tiles, int64_t GQ) {
   return best;
 }
 
-GemmPlan make_gemm_plan(int64_t M, int64_t N, int64_t K) {
+GemmPlan make_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
   p.G = K / kGroup;
   p.MT = cdiv(M, kF8BM);
-  p.NT = cdiv(N, kF8BN);
+  // 512-column tiles for wide products, 256 otherwise (base-3 codes need
+  // more registers per row-block than a 512-column wave tile leaves)
+  p.RBW = N >= 2048 && fmt != 3 ? 8 : 4;
+  p.NT = cdiv(N, 64 * p.RBW);
   const int64_t tiles = p.MT * p.NT;
   p.KS = tiles > kMaxRowGroups ? 1 : pick_splits(tiles, cdiv(p.G, 4));
   p.rs_off = kCounterBytes;
   p.xt_off = p.rs_off;
   p.part_off = p.xt_off + align256((size_t)p.MT * p.G * kF8Img);
-  const size_t part_tile = (size_t)kF8BM * kF8BN * 4;
+  const size_t part_tile = (size_t)kF8BM * 64 * p.RBW * 4;
   p.bytes = p.part_off + (p.KS > 1 ? (size_t)p.KS * tiles * part_tile : 0);
   return p;
 }
 
-template <int FMT>
+template <int FMT, int RBW>
 hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   uint8_t* ws = (uint8_t*)g.ws;
   KArgs k;
@@ -658,27 +671,34 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
     hipLaunchKernelGGL(stage_f8<XK_BF16>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                        (uint8_t*)k.xt);
     if (g.ykind == YK_BF16)
-      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_BF16, false>), grid, block, 0, s, k);
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_BF16, false, RBW>), grid, block, 0, s, k);
     else
-      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_F32, false>), grid, block, 0, s, k);
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_F32, false, RBW>), grid, block, 0, s, k);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(stage_f8<XK_I8>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                      (uint8_t*)k.xt);
   if (g.ykind == YK_I32)
-    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_I32, false>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_I32, false, RBW>), grid, block, 0, s, k);
   else if (g.ykind == YK_BF16)
-    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_BF16, true>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_BF16, true, RBW>), grid, block, 0, s, k);
   else
-    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_F32, true>), grid, block, 0, s, k);
+    hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_F32, true, RBW>), grid, block, 0, s, k);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_rbw(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
+  if constexpr (FMT == 3)
+    return launch_fmt<FMT, 4>(g, p, s);
+  else
+    return p.RBW == 8 ? launch_fmt<FMT, 8>(g, p, s) : launch_fmt<FMT, 4>(g, p, s);
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int xkind) {
-  (void)xkind;
-  return make_gemm_plan(M, N, K).bytes;
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  return make_gemm_plan(fmt, M, N, K).bytes;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
@@ -686,11 +706,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.xkind == XK_BF16 && g.ykind == YK_I32) return hipErrorInvalidValue;
   if (g.xkind == XK_I8 && (g.ykind == YK_I32) != (g.pscales == nullptr)) return hipErrorInvalidValue;
   if (g.xkind == XK_I8 && g.ykind != YK_I32 && g.x_scales == nullptr) return hipErrorInvalidValue;
-  const GemmPlan p = make_gemm_plan(g.M, g.N, g.K);
+  const GemmPlan p = make_gemm_plan(g.fmt, g.M, g.N, g.K);
   if (p.MT * p.NT * p.KS > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (g.fmt == 1) return launch_fmt<1>(g, p, s);
-  if (g.fmt == 2) return launch_fmt<2>(g, p, s);
-  if (g.fmt == 3) return launch_fmt<3>(g, p, s);
+  if (g.fmt == 1) return launch_rbw<1>(g, p, s);
+  if (g.fmt == 2) return launch_rbw<2>(g, p, s);
+  if (g.fmt == 3) return launch_rbw<3>(g, p, s);
   return hipErrorInvalidValue;
 }
 
