@@ -155,7 +155,9 @@ constexpr int kF8Img = (kF8BM / kRT) * 2 * kATBytes;  // staged bytes of one wor
 // b & 1 = kb >> 1, i >> 4 = kb & 1, b >> 1 = e >> 4, i & 15 = e & 15, and
 // lane L also supplies the exponent of (A row L % 16, block L / 16).
 // Layout: per (64-row tile, group) kF8Img bytes; A-tile a of it at a *
-// kATBytes: 64 lanes x 32 fp8 bytes, then 64 exponent bytes (by lane).
+// kATBytes: bytes 0..15 of the 64 lanes (16 L), bytes 16..31 (1024 + 16 L),
+// then 64 exponent bytes (by lane): each 16-byte LDS read of the 64 lanes is
+// one contiguous KiB (no bank conflicts).
 // A-tile 2 rt + u holds term u of rows 16 rt .. 16 rt + 15 (A row = row % 16).
 // Rows >= M are staged as zeros.
 template <int XK>
@@ -254,8 +256,8 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
   for (int hh = 0; hh < 2; hh++) {
     const int kb = 2 * (b & 1) + hh;
     const int e = 16 * (b >> 1);
-    *(v4u*)(blk0 + (r + 16 * kb) * 32 + e) = v4u{w0[4 * hh], w0[4 * hh + 1], w0[4 * hh + 2], w0[4 * hh + 3]};
-    *(v4u*)(blk1 + (r + 16 * kb) * 32 + e) = v4u{w1[4 * hh], w1[4 * hh + 1], w1[4 * hh + 2], w1[4 * hh + 3]};
+    *(v4u*)(blk0 + 64 * e + (r + 16 * kb) * 16) = v4u{w0[4 * hh], w0[4 * hh + 1], w0[4 * hh + 2], w0[4 * hh + 3]};
+    *(v4u*)(blk1 + 64 * e + (r + 16 * kb) * 16) = v4u{w1[4 * hh], w1[4 * hh + 1], w1[4 * hh + 2], w1[4 * hh + 3]};
   }
   blk0[2048 + r + 16 * b] = (uint8_t)e0;
   blk1[2048 + r + 16 * b] = (uint8_t)e1;
@@ -277,22 +279,23 @@ __device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se, con
 // LDS buffers apart and would wait for every copy); each block waits for its
 // own results.
 //
-// A operands of four consecutive A-tiles (kATBytes apart) at LDS byte
-// address pa (this lane's 32 bytes) and their exponents at pe.
+// A operands of four consecutive A-tiles (kATBytes apart): this lane's two
+// 16-byte halves at LDS byte addresses pa and pa + 1024, and their exponents
+// at pe.
 __device__ __forceinline__ void lds_read_a(uint32_t pa, uint32_t pe, v4u (&A0)[4], v4u (&A1)[4],
                                            uint32_t (&se)[4]) {
   __asm__ volatile(
       "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %4, %12 offset:16\n\t"
+      "ds_read_b128 %4, %12 offset:1024\n\t"
       "ds_read_u8 %8, %13\n\t"
       "ds_read_b128 %1, %12 offset:2112\n\t"
-      "ds_read_b128 %5, %12 offset:2128\n\t"
+      "ds_read_b128 %5, %12 offset:3136\n\t"
       "ds_read_u8 %9, %13 offset:2112\n\t"
       "ds_read_b128 %2, %12 offset:4224\n\t"
-      "ds_read_b128 %6, %12 offset:4240\n\t"
+      "ds_read_b128 %6, %12 offset:5248\n\t"
       "ds_read_u8 %10, %13 offset:4224\n\t"
       "ds_read_b128 %3, %12 offset:6336\n\t"
-      "ds_read_b128 %7, %12 offset:6352\n\t"
+      "ds_read_b128 %7, %12 offset:7360\n\t"
       "ds_read_u8 %11, %13 offset:6336\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A0[2]), "=&v"(A0[3]), "=&v"(A1[0]), "=&v"(A1[1]),
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   // ---- LDS reads (written out, see lds_read_a / lds_read_codes)
   auto aread = [&](int t, v4u (&A0)[4], v4u (&A1)[4], uint32_t (&se)[4]) {
     const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
-    lds_read_a(base + 32 * lane, base + 2048 + lane, A0, A1, se);
+    lds_read_a(base + 16 * lane, base + 2048 + lane, A0, A1, se);
   };
   // codes and scales of row-block RBW wn + j of the quad in the code buffer
   auto cread = [&](int j, int gq, Quad<FMT>& o) {
