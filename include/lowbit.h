@@ -182,6 +182,15 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
  *     x_scales[M] (device fp32); per 128-group integer sums are exact in int32
  *     and Y[m][n] = x_scales[m] * sum_g scale[n][g] * A[m][n][g].
  *     y_dtype I32 requires pscales == NULL and returns sum_g A[m][n][g].
+ *   x_dtype SIGN1 (batched sign activations, any weight format): X holds
+ *     K/8 bytes of sign bits per row (bit k%8 of byte k/8, 1 = negative) and
+ *     x_scales[M] the per-row magnitude alpha_m (device fp32), so that
+ *     x[m][k] = alpha_m (-1)^bit.  Per group D[m][n][g] = sum_k code * sign
+ *     is an exact integer (for binary weights 128 - 2 popcount(w XOR x) per
+ *     group, the XOR + popcount product of the "1-bit 嘅數學" section of the
+ *     richmindsetzone.com page) and Y = alpha_m sum_g scale[n][g] D[m][n][g];
+ *     y_dtype I32 requires pscales == NULL and returns sum_g D (x_scales
+ *     ignored).
  *   y_dtype F32 or BF16 (or I32 as above).
  * K <= 2^36 (E_SHAPE beyond).  Alignment: pcodes, pscales, X, Y 16 bytes.
  * Uses the per-stream workspace described for lowbit_gemv. */

@@ -205,3 +205,69 @@ def test_gemm_base3_equals_2bit(M, N, K):
     Y3 = lb.gemm(3, M, N, K, pc3, ps3, X)
     torch.cuda.synchronize()
     assert torch.equal(Y2, Y3)
+
+
+# ------------------------------------------------ sign activations (batched)
+def sign_scales(M, tid):
+    rng = np.random.default_rng(tid)
+    return rng.uniform(0.25, 2.0, size=M).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_sign_parity(fmt, M, N, K):
+    """Sign-bit activations x = alpha_m (-1)^bit: the unit-scale product is the
+    exact integer sum of code x sign (for binary weights the XOR + popcount
+    count, checked against the oracle's popcount routine too); scaled outputs
+    meet the float bound."""
+    print(f"gemm sign fmt={fmt} M={M} N={N} K={K}", flush=True)
+    codes, scales, pc, ps = make(fmt, N, K, tid=211)
+    xb = synth.sign_bits(SEED, 213, M, K)
+    alpha = sign_scales(M, 215)
+    Xd = dev(xb)
+    Yi = lb.gemm(fmt, M, N, K, pc, None, Xd, y_dtype=lb.I32, x_dtype=lb.SIGN1)
+    Yf = lb.gemm(fmt, M, N, K, pc, ps, Xd, x_scales=dev(alpha), y_dtype=lb.F32, x_dtype=lb.SIGN1)
+    Yb = lb.gemm(fmt, M, N, K, pc, ps, Xd, x_scales=dev(alpha), y_dtype=lb.BF16, x_dtype=lb.SIGN1)
+    torch.cuda.synchronize()
+    D = O.matmul(codes, None, O.X_SIGN1, xb, np.ones(M, np.float32), with_abs=False)
+    assert np.array_equal(Yi.cpu().numpy().astype(np.float64), D)
+    if fmt == 1:
+        _, Dpop = O.xor_popcount(codes, None, xb)
+        assert np.array_equal(Yi.cpu().numpy().astype(np.int64), Dpop)
+    yref, absY = O.matmul(codes, scales, O.X_SIGN1, xb, alpha)
+    assert_within(Yf.cpu().numpy(), yref, absY, what="sign f32 out")
+    assert_within(Yb.float().cpu().numpy(), yref, absY, bf16_out=True, what="sign bf16 out")
+
+
+def test_gemm_sign_dit_block_sampled():
+    """A DiT projection with sign activations at full size: exact integer
+    outputs on whole rows and a sampled block."""
+    M, N, K = 4608, 3072, 3072
+    print(f"DiT sign binary M={M} N={N} K={K}", flush=True)
+    codes_t = synth.device_codes(False, SEED, 221, N, K, "cuda", chunk_rows=2048)
+    scales_t = synth.device_scales(SEED, 222, N, K // 128, "cuda")
+    pc, ps = lb.pack(1, codes_t, scales_t)
+    del codes_t, scales_t
+    xb = synth.sign_bits(SEED, 223, M, K)
+    Yi = lb.gemm(1, M, N, K, pc, None, dev(xb), y_dtype=lb.I32, x_dtype=lb.SIGN1)
+    torch.cuda.synchronize()
+    codes_all = codes_for(1, SEED, 221, N, K)
+    rng = np.random.default_rng(224)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, size=32)]))
+    cols = np.sort(rng.choice(N, size=32, replace=False))
+    Yh = Yi.cpu().numpy().astype(np.int64)
+    _, Dw = O.xor_popcount(codes_all, None, xb[[0, M - 1]])
+    assert np.array_equal(Yh[[0, M - 1]], Dw)
+    _, Db = O.xor_popcount(codes_all[cols], None, xb[rows])
+    assert np.array_equal(Yh[np.ix_(rows, cols)], Db)
+
+
+def test_gemm_sign_rejects():
+    _, _, pc, ps = make(1, 64, 256, tid=230)
+    xb = dev(synth.sign_bits(SEED, 231, 40, 256))
+    with pytest.raises(lb.LowbitError) as e:  # scaled output needs alpha per row
+        lb.gemm(1, 40, 64, 256, pc, ps, xb, y_dtype=lb.F32, x_dtype=lb.SIGN1)
+    assert e.value.status == lb.E_NULL
+    with pytest.raises(lb.LowbitError) as e:  # the exact integer output takes unit scales
+        lb.gemm(1, 40, 64, 256, pc, ps, xb, y_dtype=lb.I32, x_dtype=lb.SIGN1)
+    assert e.value.status == lb.E_UNSUPPORTED

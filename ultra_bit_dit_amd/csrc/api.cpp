@@ -103,7 +103,7 @@ int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const
              hipStream_t s) {
   if (cdiv(N, 16) > (int64_t(1) << 40) / 16) return LOWBIT_E_SHAPE;
   void* ws = nullptr;
-  int rc = workspace(s, gemm_workspace_bytes(fmt, M, N, K), &ws);
+  int rc = workspace(s, gemm_workspace_bytes(fmt, x_dtype, M, N, K), &ws);
   if (rc) return rc;
   GemmArgs g;
   g.fmt = fmt;
@@ -114,7 +114,7 @@ int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const
   g.pscales = (const uint16_t*)pscales;
   g.xkind = x_dtype;
   g.x = X;
-  g.x_scales = x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr;
+  g.x_scales = x_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_I32 ? x_scales : nullptr;
   g.ykind = y_dtype;
   g.y = Y;
   g.ws = ws;
@@ -234,18 +234,19 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   if (!shape_ok(N, K) || M < 1 || M > (int64_t(1) << 31)) return LOWBIT_E_SHAPE;
   if (K > (int64_t(1) << 36)) return LOWBIT_E_SHAPE;  // 32-bit group indices of the GEMM
-  if (x_dtype != LOWBIT_BF16 && x_dtype != LOWBIT_I8) return LOWBIT_E_UNSUPPORTED;
+  const bool sign = x_dtype == LOWBIT_SIGN1;
+  if (x_dtype != LOWBIT_BF16 && x_dtype != LOWBIT_I8 && !sign) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_I32)
     return LOWBIT_E_UNSUPPORTED;
-  if (y_dtype == LOWBIT_I32 && !(x_dtype == LOWBIT_I8 && pscales == nullptr))
+  if (y_dtype == LOWBIT_I32 && !((x_dtype == LOWBIT_I8 || sign) && pscales == nullptr))
     return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_I32 && !pscales) return LOWBIT_E_NULL;
-  if (x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 && !x_scales) return LOWBIT_E_NULL;
+  if ((x_dtype == LOWBIT_I8 || sign) && y_dtype != LOWBIT_I32 && !x_scales) return LOWBIT_E_NULL;
   if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(X, 16) ||
       !aligned(Y, 16) || (x_scales && !aligned(x_scales, 4)))
     return LOWBIT_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (M <= max_small_m(x_dtype))
+  if (!sign && M <= max_small_m(x_dtype))
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);

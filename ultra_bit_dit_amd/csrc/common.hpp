@@ -118,14 +118,14 @@ struct GemmArgs {
   int64_t M, N, K;
   const void* pcodes;
   const uint16_t* pscales;  // NULL only for the exact int32 product
-  int xkind;                // XK_BF16 or XK_I8
-  const void* x;            // [M][K]
-  const float* x_scales;    // per-row scales of int8 activations (scaled outputs)
+  int xkind;                // XK_BF16, XK_I8 or XK_SIGN1
+  const void* x;            // [M][K] (sign bits: [M][K/8])
+  const float* x_scales;    // per-row scales of int8 / sign activations (scaled outputs)
   int ykind;
   void* y;                  // [M][N]
   void* ws;                 // workspace (counters first)
 };
-size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_bytes(int fmt, int xkind, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 // streaming read of `bytes` (a multiple of 16) at src; XOR of the data into *out

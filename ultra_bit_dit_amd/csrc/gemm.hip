@@ -263,10 +263,60 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
   blk1[2048 + r + 16 * b] = (uint8_t)e1;
 }
 
+// ------------------------------------------------- sign activations (fp4 A)
+// Sign-bit activations (x = alpha_m (-1)^bit) enter the MFMA as fp4 +-1, the
+// same encoding as binary weights, with unit block scales: every product is
+// +-1 x code and each group's MFMA result is the exact integer sum that
+// XOR + popcount would give.  Image per (64-row tile, group): 4 A-tiles (16
+// rows each) x 64 lanes x 16 bytes, lane L = r + 16 q holding slots 8 j + n
+// (register j, nibble n) at k = 128 g + KMAP(q, 8 j + n), as the packed
+// weights do.
+constexpr int kS1Img = 4 * 1024;
+
+// 8 sign bits -> 8 fp4 nibbles (bit 1 -> -1 = 0xA, 0 -> +1 = 0x2)
+__device__ __forceinline__ uint32_t sign_nibbles(uint32_t b8) {
+  uint32_t w = 0x22222222u;
+#pragma unroll
+  for (int n = 0; n < 8; n++) w |= ((b8 >> n) & 1u) << (4 * n + 3);
+  return w;
+}
+
+// One thread per (row m, group g, quarter q); thread order q, then 16 rows,
+// then g, so that a wavefront writes one contiguous KiB.  Rows >= M get
+// zero nibbles (no contribution).
+__global__ __launch_bounds__(256) void stage_s1(int64_t M, int64_t Mpad, int64_t K, int64_t G,
+                                                const uint8_t* __restrict__ X,
+                                                uint8_t* __restrict__ xs) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= Mpad * G * 4) return;
+  const int q = (int)(tid & 3), r = (int)((tid >> 2) & 15);
+  const int64_t g = (tid >> 6) % G;
+  const int64_t m = (tid >> 6) / G * 16 + r;
+  v4u out = {0u, 0u, 0u, 0u};
+  if (m < M) {
+    const v4u bits = *(const v4u*)(X + m * (K / 8) + g * 16);  // the group's 128 bits
+    // slots 0..15: k = run0 + i, slots 16..31: k = run0 + 32 + (i - 16)
+    const int run0 = 64 * (q & 1) + 16 * (q >> 1);
+    auto bits16 = [&](int k0) { return (bits[k0 >> 5] >> (k0 & 31)) & 0xFFFFu; };
+    const uint32_t lo = bits16(run0), hi = bits16(run0 + 32);
+    out = v4u{sign_nibbles(lo & 0xFF), sign_nibbles(lo >> 8), sign_nibbles(hi & 0xFF),
+              sign_nibbles(hi >> 8)};
+  }
+  *(v4u*)(xs + ((m / kF8BM) * G + g) * (int64_t)kS1Img + ((m % kF8BM) / kRT) * 1024 +
+          (r + 16 * q) * 16) = out;
+}
+
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ v4f mfma_f4f4(const v4u& A, const v8i& B) {
+  const v8i A8 = v8i{(int)A.x, (int)A.y, (int)A.z, (int)A.w, 0, 0, 0, 0};
+  // A and B fp4 e2m1 (4), unit block scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A8, B, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                          127, 0, 127);
 }
 
 __device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se, const v4f& C) {
@@ -304,6 +354,14 @@ __device__ __forceinline__ void lds_read_a(uint32_t pa, uint32_t pe, v4u (&A0)[4
       : "memory");
 }
 static_assert(kATBytes == 2112, "A-tile offsets in the LDS reads");
+
+// fp4 A operands of two consecutive sign A-tiles (1 KiB apart) at pa
+__device__ __forceinline__ void lds_read_s1(uint32_t pa, v4u (&A)[2]) {
+  __asm__ volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(A[0]), "=&v"(A[1])
+                   : "v"(pa)
+                   : "memory");
+}
 
 // One row-block's codes of a quad from its code-buffer slot (this lane's
 // 16 bytes at pc; base-3 also the tail word at pt) and its scales at ps.
@@ -381,13 +439,16 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space code: device pass only
   using CL = CodeLds<FMT, RBW>;
   constexpr int HR = RBW / 2;  // row-blocks this wave copies
-  __shared__ __attribute__((aligned(16))) uint8_t xb0[kF8Img], xb1[kF8Img], xb2[kF8Img], xb3[kF8Img];
+  constexpr bool S1 = XK == XK_SIGN1;  // sign activations: fp4 A, one term
+  constexpr int IMG = S1 ? kS1Img : kF8Img;
+  constexpr int XC = S1 ? 1 : 3;       // copies per image and wave
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[IMG], xb1[IMG], xb2[IMG], xb3[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t cbuf[CL::kBytes];
   __shared__ uint32_t t3[256];
   auto ring = [&](int t) -> lds_u8* {
     return (lds_u8*)(t == 0 ? xb0 : t == 1 ? xb1 : t == 2 ? xb2 : xb3);
   };
-  constexpr bool INT = XK == XK_I8 && !SCALED;
+  constexpr bool INT = (XK == XK_I8 || S1) && !SCALED;
   // wave-uniform values are kept in scalar registers (the copy addresses
   // below are then a scalar base plus a fixed per-lane offset)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -407,18 +468,24 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 
   // ---- copies.  Per-lane offsets stay in the same registers for the whole
   // loop (a copy's address registers must not change while it is in flight).
-  const uint8_t* xs = a.xt + mt * a.G * (int64_t)kF8Img;
+  const uint8_t* xs = a.xt + mt * a.G * (int64_t)IMG;
   static_assert(kF8Img == 16 * 1024 + 512, "image = 16 KiB + 8 x 64 bytes");
   const uint32_t vo0 = 1024 * wave + 16 * lane, vo1 = vo0 + 8192;
   const uint32_t vo2 = 16384 + 64 * wave + 16 * lane;
   // image of group g into ring buffer t: 1 KiB chunks w and w + 8, and
   // 64 bytes of the 512-byte tail (lanes 0..3)
+  // (sign images: 512 bytes per wave, lanes 0..31)
+  const uint32_t vs = 512 * wave + 16 * lane;
   auto xissue = [&](int g, int t) {
-    const uint8_t* src = xs + (int64_t)g * kF8Img;
+    const uint8_t* src = xs + (int64_t)g * IMG;
     lds_u8* dst = ring(t);
-    __builtin_amdgcn_global_load_lds(src + vo0, dst + 1024 * wave, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
-    if (lane < 4) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 64 * wave, 16, 0, 0);
+    if constexpr (S1) {
+      if (lane < 32) __builtin_amdgcn_global_load_lds(src + vs, dst + 512 * wave, 16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(src + vo0, dst + 1024 * wave, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
+      if (lane < 4) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 64 * wave, 16, 0, 0);
+    }
   };
   // this wave copies row-blocks RBW wn + HR wm .. + HR - 1 of the tile
   const int cr = RBW * wn + HR * wm;
@@ -510,26 +577,32 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         // issued after the copies this group needs: two images, and at t =
         // 2, 3 also the next quad's codes (issued at t = 1 after its image)
         if (t < 2)
-          xsync(std::integral_constant<int, 6>());
+          xsync(std::integral_constant<int, 2 * XC>());
         else
-          xsync(std::integral_constant<int, 6 + CL::kCopies>());
+          xsync(std::integral_constant<int, 2 * XC + CL::kCopies>());
         if (t == 0) {
 #pragma unroll
           for (int j = 0; j < RBW; j++) cread(j, q, qd[j]);
         }
         xissue(g + 3 < g1 ? g + 3 : g1 - 1, (t + 3) & 3);
         if (t == 1) cissue(q + 1 < q1 ? q + 1 : q);
-        v4u A0[4], A1[4];
-        uint32_t se[4];
-        aread(t, A0, A1, se);
         v8i At[4];
+        uint32_t se[4];
+        v4u As[2];
+        if constexpr (S1) {
+          lds_read_s1((uint32_t)(uintptr_t)(ring(t) + 2 * wm * 1024) + 16 * lane, As);
+        } else {
+          v4u A0[4], A1[4];
+          aread(t, A0, A1, se);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-          At[i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
-                      (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+          for (int i = 0; i < 4; i++)
+            At[i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
+                        (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+        }
         // row-blocks four at a time: decode, then per row-tile rt (16 rows)
         // term 0 (A-tile 2 rt) and term 1 (2 rt + 1) accumulate into one MFMA
-        // result, scaled once per group
+        // result (sign activations: one fp4 A-tile per row-tile), scaled once
+        // per group
 #pragma unroll
         for (int h = 0; h < RBW; h += 4) {
           v8i B[4];
@@ -542,11 +615,16 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
           for (int rt = 0; rt < 2; rt++) {
             v4f c[4];
+            if constexpr (S1) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-              c[j] = mfma_f8f4(At[2 * rt], B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
+              for (int j = 0; j < 4; j++) c[j] = mfma_f4f4(As[rt], B[j]);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At[2 * rt + 1], B[j], (int)se[2 * rt + 1], c[j]);
+              for (int j = 0; j < 4; j++)
+                c[j] = mfma_f8f4(At[2 * rt], B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At[2 * rt + 1], B[j], (int)se[2 * rt + 1], c[j]);
+            }
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll
@@ -628,7 +706,7 @@ int64_t pick_splits(int64_t tiles, int64_t GQ) {
   return best;
 }
 
-GemmPlan make_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K) {
+GemmPlan make_gemm_plan(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
   p.G = K / kGroup;
   p.MT = cdiv(M, kF8BM);
@@ -640,7 +718,7 @@ GemmPlan make_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   p.KS = tiles > kMaxRowGroups ? 1 : pick_splits(tiles, cdiv(p.G, 4));
   p.rs_off = kCounterBytes;
   p.xt_off = p.rs_off;
-  p.part_off = p.xt_off + align256((size_t)p.MT * p.G * kF8Img);
+  p.part_off = p.xt_off + align256((size_t)p.MT * p.G * (xkind == XK_SIGN1 ? kS1Img : kF8Img));
   const size_t part_tile = (size_t)kF8BM * 64 * p.RBW * 4;
   p.bytes = p.part_off + (p.KS > 1 ? (size_t)p.KS * tiles * part_tile : 0);
   return p;
@@ -653,7 +731,7 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.xt = ws + p.xt_off;
   k.pcodes = (const uint8_t*)g.pcodes;
   k.pscales = g.pscales;
-  k.rowscale = g.xkind == XK_I8 ? g.x_scales : nullptr;
+  k.rowscale = g.xkind != XK_BF16 ? g.x_scales : nullptr;
   k.y = g.y;
   k.part = (float*)(ws + p.part_off);
   k.cnt = (uint32_t*)ws;
@@ -679,6 +757,17 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
       hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_F32, false, RBW>), grid, block, 0, s, k);
     return hipGetLastError();
   }
+  if (g.xkind == XK_SIGN1) {
+    hipLaunchKernelGGL(stage_s1, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, (const uint8_t*)g.x,
+                       (uint8_t*)k.xt);
+    if (g.ykind == YK_I32)
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_SIGN1, YK_I32, false, RBW>), grid, block, 0, s, k);
+    else if (g.ykind == YK_BF16)
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_SIGN1, YK_BF16, true, RBW>), grid, block, 0, s, k);
+    else
+      hipLaunchKernelGGL((gemm_f8<FMT, XK_SIGN1, YK_F32, true, RBW>), grid, block, 0, s, k);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(stage_f8<XK_I8>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                      (uint8_t*)k.xt);
   if (g.ykind == YK_I32)
@@ -700,16 +789,16 @@ hipError_t launch_rbw(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  return make_gemm_plan(fmt, M, N, K).bytes;
+size_t gemm_workspace_bytes(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
+  return make_gemm_plan(fmt, xkind, M, N, K).bytes;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.xkind != XK_BF16 && g.xkind != XK_I8) return hipErrorInvalidValue;
+  if (g.xkind != XK_BF16 && g.xkind != XK_I8 && g.xkind != XK_SIGN1) return hipErrorInvalidValue;
   if (g.xkind == XK_BF16 && g.ykind == YK_I32) return hipErrorInvalidValue;
-  if (g.xkind == XK_I8 && (g.ykind == YK_I32) != (g.pscales == nullptr)) return hipErrorInvalidValue;
-  if (g.xkind == XK_I8 && g.ykind != YK_I32 && g.x_scales == nullptr) return hipErrorInvalidValue;
-  const GemmPlan p = make_gemm_plan(g.fmt, g.M, g.N, g.K);
+  if (g.xkind != XK_BF16 && (g.ykind == YK_I32) != (g.pscales == nullptr)) return hipErrorInvalidValue;
+  if (g.xkind != XK_BF16 && g.ykind != YK_I32 && g.x_scales == nullptr) return hipErrorInvalidValue;
+  const GemmPlan p = make_gemm_plan(g.fmt, g.xkind, g.M, g.N, g.K);
   if (p.MT * p.NT * p.KS > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (g.fmt == 1) return launch_rbw<1>(g, p, s);
   if (g.fmt == 2) return launch_rbw<2>(g, p, s);
