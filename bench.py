@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_PEAK_F16_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA
 MFMA_PEAK_I8_TOPS = 5033.2     # dense int8 MFMA
+MFMA_PEAK_F4_TOPS = 10100.0    # dense fp4 MFMA
 LAYERS = 64
 HIDDEN, FFN = 5120, 17408
 # (name, N, K) of the per-layer products, fused where the inputs are shared
@@ -254,6 +255,10 @@ def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
     Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in shapes]
     Qs = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _, _, K in shapes]
     Ss = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in shapes]
+    if xkind == "sign":
+        Bs = [torch.from_numpy(synth.sign_bits(seed, 800 + j, M, K)).cuda()
+              for j, (_, _, K) in enumerate(shapes)]
+        alpha = torch.ones(M, dtype=torch.float32, device="cuda")
 
     def one():
         for j, (name, N, K) in enumerate(shapes):
@@ -261,6 +266,8 @@ def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
             if xkind == "i8":
                 lb.quantize_act_i8(Xs[j], Q=Qs[j], s_x=Ss[j])
                 lb.gemm(fmt, M, N, K, pc, ps, Qs[j], x_scales=Ss[j], Y=Ys[j])
+            elif xkind == "sign":
+                lb.gemm(fmt, M, N, K, pc, ps, Bs[j], x_scales=alpha, Y=Ys[j], x_dtype=lb.SIGN1)
             else:
                 lb.gemm(fmt, M, N, K, pc, ps, Xs[j], Y=Ys[j])
 
@@ -376,6 +383,15 @@ def main():
             dit[str(M)] = {"ms_per_block": round(dms, 4), "tflops": round(tf, 1),
                            "pct_mfma_peak": round(100 * tf / MFMA_PEAK_F16_TFLOPS, 1)}
         out["config"]["dit_block_binary_bf16"] = dit
+        # the same blocks with sign activations (binary x binary on the fp4 MFMA)
+        sg = {}
+        for M in (4608, 18432):
+            dms, tf = bench_gemm_pass(lb, synth, torch, np, 1, M, DIT, DIT_SEED, "sign",
+                                      max(2, args.gemm_reps // (M // 4608)))
+            log(f"DiT block sign M={M}: {dms:.3f} ms, {tf:.1f} TOP/s")
+            sg[str(M)] = {"ms_per_block": round(dms, 4), "tops": round(tf, 1),
+                          "pct_mfma_peak_fp4": round(100 * tf / MFMA_PEAK_F4_TOPS, 1)}
+        out["config"]["dit_block_binary_sign"] = sg
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.fmt, args.cpu_budget)
     print(json.dumps(out), flush=True)
