@@ -13,8 +13,9 @@
  *  [R3] kongchang.com, "三值权重压缩：27B模型缩至6GB…", section
  *       "精度保留了多少": ternary values need about log2(3) bits and a
  *       product with -1/0/+1 reduces to additions and sign flips.
- *  [R4] ainewscove.com OpenBonsai post, method list: one FP16 scale per 128
- *       weights.
+ *  [R4] ainewscove.com OpenBonsai post, method list ("工作原理"): one FP16
+ *       scale per 128 weights; a signed Hadamard rotation to reduce weight
+ *       outliers before the weights are quantized.
  *  The byte layout is the one written in the layout specification of the
  *  library header (it is not on the pages); this file re-implements it from
  *  that text.
@@ -417,3 +418,114 @@ int orc_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
   }
   return 0;
 }
+
+/* ------------------------------------------------------- weight quantizer */
+
+/* fp64 -> IEEE binary16 bits, round to nearest even (subnormals kept,
+ * overflow to infinity). */
+uint16_t orc_f64_to_f16(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (isnan(x)) return 0x7E00;
+  if (a >= 65520.0) return sign | 0x7C00; /* rounds past the largest finite */
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal (or zero): a multiple of 2^-24 */
+    double q = a * ldexp(1.0, 24); /* exact: a < 2^-14 */
+    double r = nearbyint(q);       /* ties to even */
+    return sign | (uint16_t)r;     /* r = 1024 becomes the smallest normal */
+  }
+  int e;
+  double f = frexp(a, &e); /* a = f 2^e, f in [0.5, 1) */
+  /* significand with 10 fraction bits: a = m 2^(e - 11), m in [1024, 2048) */
+  double m = nearbyint(ldexp(f, 11));
+  if (m == 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  int biased = e - 1 + 15;
+  if (biased >= 31) return sign | 0x7C00;
+  return sign | (uint16_t)(biased << 10) | (uint16_t)((int)m - 1024);
+}
+
+/* Data-free quantizer front end [R4] (the rotation and the per-128 FP16
+ * scale of its method list; the calibrated GPTQ step needs data and is not
+ * part of it).  Per row n and group g of 128 weights:
+ *   v_i = W[n][128 g + i] * d[128 g + i]           (signs d in {-1, +1})
+ *   u_i = sum_j H[i][j] v_j,  H[i][j] = (-1)^popcount(i & j)   (index order)
+ *   t_i = u_i / sqrt(128)                          (orthonormal rotation)
+ *   s   = (sum_i |u_i| / 128) / sqrt(128)          (mean |t|)
+ *   s16 = fp16(s) (round to nearest even); scales[n][g] = s16
+ *   ternary: c_i = +1 if t_i / s16 > 1/2, -1 if < -1/2, else 0
+ *            (round to nearest even of t / s16, clamped to [-1, 1])
+ *   binary:  c_i = -1 if t_i < 0, else +1
+ *   s16 == 0: every c_i = 0 (ternary) or +1 (binary).
+ * signs == NULL: no rotation (u = t = v, s = sum |v| / 128), the plain
+ * absmean rounding.  All in fp64. */
+int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
+                         const int8_t* signs, int8_t* codes, uint16_t* scales) {
+  if ((fmt != 1 && fmt != 2 && fmt != 3) || N < 1 || K < 1 || K % GROUP) return -2;
+  const int64_t G = K / GROUP;
+  const double r128 = sqrt(128.0);
+  double v[GROUP], t[GROUP];
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t g = 0; g < G; g++) {
+      for (int i = 0; i < GROUP; i++) {
+        double w = orc_bf16_to_f64(W_bf16[n * K + g * GROUP + i]);
+        v[i] = signs ? w * (double)signs[g * GROUP + i] : w;
+      }
+      double S = 0.0;
+      for (int i = 0; i < GROUP; i++) {
+        double u = v[i];
+        if (signs) {
+          u = 0.0;
+          for (int j = 0; j < GROUP; j++) {
+            int par = __builtin_popcount((unsigned)(i & j)) & 1;
+            u += par ? -v[j] : v[j];
+          }
+        }
+        S += fabs(u);
+        t[i] = signs ? u / r128 : u;
+      }
+      double sc = signs ? (S / 128.0) / r128 : S / 128.0;
+      uint16_t s16 = orc_f64_to_f16(sc);
+      double sd = orc_f16_to_f64(s16);
+      scales[n * G + g] = s16;
+      for (int i = 0; i < GROUP; i++) {
+        int c;
+        if (fmt == 1) {
+          c = (sd == 0.0 || !(t[i] < 0.0)) ? 1 : -1;
+        } else if (sd == 0.0) {
+          c = 0;
+        } else {
+          double q = t[i] / sd;
+          c = q > 0.5 ? 1 : (q < -0.5 ? -1 : 0);
+        }
+        codes[n * K + g * GROUP + i] = (int8_t)c;
+      }
+    }
+  return 0;
+}
+
+/* The rotation step alone: T[n][k] = t of the quantizer above (fp64). */
+int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* signs,
+                    double* T) {
+  if (N < 1 || K < 1 || K % GROUP || !signs) return -2;
+  const int64_t G = K / GROUP;
+  const double r128 = sqrt(128.0);
+  double v[GROUP];
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t g = 0; g < G; g++) {
+      for (int i = 0; i < GROUP; i++)
+        v[i] = orc_bf16_to_f64(W_bf16[n * K + g * GROUP + i]) * (double)signs[g * GROUP + i];
+      for (int i = 0; i < GROUP; i++) {
+        double u = 0.0;
+        for (int j = 0; j < GROUP; j++) {
+          int par = __builtin_popcount((unsigned)(i & j)) & 1;
+          u += par ? -v[j] : v[j];
+        }
+        T[n * K + g * GROUP + i] = u / r128;
+      }
+    }
+  return 0;
+}
+

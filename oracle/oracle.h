@@ -73,6 +73,20 @@ int orc_xor_popcount(int64_t M, int64_t N, int64_t K, const int8_t* codes,
 int orc_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
                         int8_t* Q, float* s_x);
 
+/* fp64 -> binary16 bits, round to nearest even. */
+uint16_t orc_f64_to_f16(double x);
+
+/* Data-free weight quantizer: signed Hadamard rotation per 128-group (signs
+ * may be NULL: no rotation), absmean fp16 scale, rounding to the format's
+ * codes.  codes int8 [N][K], scales fp16 bits [N][K/128]. */
+int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
+                         const int8_t* signs, int8_t* codes, uint16_t* scales);
+
+/* The quantizer's rotation step: T [N][K] = per-group signed Hadamard
+ * rotation (orthonormal) of W, fp64. */
+int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* signs,
+                    double* T);
+
 #ifdef __cplusplus
 }
 #endif

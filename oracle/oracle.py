@@ -38,6 +38,10 @@ def lib():
         L.orc_group_int_sums.argtypes = [i64, i64, i64, vp, vp, vp]
         L.orc_xor_popcount.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.orc_quantize_act_i8.argtypes = [i64, i64, vp, vp, vp]
+        L.orc_f64_to_f16.argtypes = [ctypes.c_double]
+        L.orc_f64_to_f16.restype = ctypes.c_uint16
+        L.orc_quantize_weights.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp]
+        L.orc_rotate_rows.argtypes = [i64, i64, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -158,3 +162,31 @@ def quantize_act_i8(X_bf16):
     if rc:
         raise ValueError(f"orc_quantize_act_i8 failed: {rc}")
     return Q, sx
+
+
+def f64_to_f16(x):
+    return lib().orc_f64_to_f16(float(x))
+
+
+def quantize_weights(fmt, W_bf16, signs=None):
+    """Data-free quantizer: (codes int8 [N][K], scales fp16 bits [N][K/128])
+    from bf16 bits W [N][K]; signs int8 [K] in {-1, +1} or None (no rotation)."""
+    W = _c(W_bf16, np.uint16)
+    N, K = W.shape
+    codes = np.empty((N, K), dtype=np.int8)
+    scales = np.empty((N, K // 128), dtype=np.uint16)
+    rc = lib().orc_quantize_weights(fmt, N, K, _p(W), _p(_c(signs, np.int8)), _p(codes), _p(scales))
+    if rc:
+        raise ValueError(f"orc_quantize_weights failed: {rc}")
+    return codes, scales
+
+
+def rotate_rows(W_bf16, signs):
+    """fp64 T [N][K]: the quantizer's per-group signed Hadamard rotation."""
+    W = _c(W_bf16, np.uint16)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.float64)
+    rc = lib().orc_rotate_rows(N, K, _p(W), _p(_c(signs, np.int8)), _p(T))
+    if rc:
+        raise ValueError(f"orc_rotate_rows failed: {rc}")
+    return T
