@@ -240,6 +240,31 @@ int lowbit_chain_status(lowbit_chain* chain, int* failed_waits);
 /* Frees the chain's device memory (synchronizes the device first). */
 int lowbit_chain_destroy(lowbit_chain* chain);
 
+/* Data-free quantizer front end (the signed Hadamard rotation and the
+ * FP16 scale per 128 weights of the method list, section 工作原理, of the
+ * ainewscove.com OpenBonsai post; its calibrated GPTQ step needs data and is
+ * not part of it).  From bf16 weights W [N][K] writes dense codes [N][K]
+ * (int8, the input of lowbit_pack) and fp16 scales [N][K/128].  Per row and
+ * group of 128: v = W * d (signs d[K], int8 +-1; signs == NULL: no
+ * rotation), u = H v with H[i][j] = (-1)^popcount(i & j), t = u / sqrt(128),
+ * s16 = fp16(mean |t|) (round to nearest even); ternary formats: c = +1 if
+ * t / s16 > 1/2, -1 if < -1/2, else 0; binary: c = -1 if t < 0 else +1;
+ * s16 = 0 gives codes 0 / +1.  Computed in fp64 (exact up to the final
+ * divisions while a group's magnitudes span less than 2^38).  Rotated
+ * weights expect rotated activations (lowbit_rotate_act with the same
+ * signs).  Errors: E_NULL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_HIP. */
+int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
+                            const int8_t* signs, int8_t* codes, uint16_t* scales,
+                            void* stream);
+
+/* Activations for rotated weights: per row of bf16 X [M][K] and block of 128,
+ * X_rot = H (d * x) / sqrt(128) in fp32 (signs as given to
+ * lowbit_quantize_weights), so that products with the rotated weights
+ * equal those with the original ones.  Output fp32 [M][K].
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_HIP. */
+int lowbit_rotate_act(int64_t M, int64_t K, const uint16_t* X_bf16, const int8_t* signs,
+                      float* X_rot, void* stream);
+
 /* Measurement helper, not part of the matrix-product path: reads the
  * `bytes` (a positive multiple of 16) at src once with 16-byte streaming
  * loads spread over the whole device and XORs the data into *out (device

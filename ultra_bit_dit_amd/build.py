@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(OUT_DIR, "obj")
 LIB = os.path.join(OUT_DIR, "liblowbit.so")
-SOURCES = ["api.cpp", "pack.hip", "stage.hip", "gemv.hip", "gemm.hip", "probe.hip"]
+SOURCES = ["api.cpp", "pack.hip", "stage.hip", "gemv.hip", "gemm.hip", "probe.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

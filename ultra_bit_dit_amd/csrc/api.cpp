@@ -311,3 +311,22 @@ int lowbit_hbm_read_probe(const void* src, int64_t bytes, uint32_t* out, void* s
   if (!aligned(src, 16) || !aligned(out, 4)) return LOWBIT_E_ALIGN;
   return hip_status(launch_hbm_read(src, bytes, out, (hipStream_t)stream));
 }
+
+int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
+                            const int8_t* signs, int8_t* codes, uint16_t* scales, void* stream) {
+  if (!W_bf16 || !codes || !scales) return LOWBIT_E_NULL;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
+  if (!aligned(W_bf16, 2) || !aligned(scales, 2)) return LOWBIT_E_ALIGN;
+  return hip_status(launch_quantize_weights(fmt, N, K, W_bf16, signs, codes, scales,
+                                            (hipStream_t)stream));
+}
+
+int lowbit_rotate_act(int64_t M, int64_t K, const uint16_t* X_bf16, const int8_t* signs,
+                      float* X_rot, void* stream) {
+  if (!X_bf16 || !signs || !X_rot) return LOWBIT_E_NULL;
+  if (!shape_ok(M, K)) return LOWBIT_E_SHAPE;
+  if (!aligned(X_bf16, 2) || !aligned(X_rot, 4)) return LOWBIT_E_ALIGN;
+  return hip_status(launch_rotate_act(M, K, X_bf16, signs, X_rot, (hipStream_t)stream));
+}
+

@@ -131,4 +131,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // streaming read of `bytes` (a multiple of 16) at src; XOR of the data into *out
 hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
 
+// data-free weight quantizer and the matching activation rotation
+hipError_t launch_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W,
+                                   const int8_t* signs, int8_t* codes, uint16_t* scales,
+                                   hipStream_t s);
+hipError_t launch_rotate_act(int64_t M, int64_t K, const uint16_t* X, const int8_t* signs,
+                             float* Xr, hipStream_t s);
+
 }  // namespace lowbit

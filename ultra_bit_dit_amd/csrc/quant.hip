@@ -1,0 +1,157 @@
+// Data-free quantizer front end: bf16 weights -> binary / ternary codes and
+// one fp16 scale per 128-weight group, with an optional signed Hadamard
+// rotation of each group (the rotation and the per-128 FP16 scale of the
+// method list, section 工作原理, of the ainewscove.com OpenBonsai post; its
+// calibrated GPTQ step needs data and is not part of this front end), and
+// the matching rotation of activations.
+//
+// Per row n and group g (one wavefront, lane l holding elements l and l+64):
+//   v = W[n][128 g ..] * d[128 g ..]            (signs d = +-1)
+//   u = H v, H[i][j] = (-1)^popcount(i & j)      (fast Walsh-Hadamard, fp64)
+//   t = u / sqrt(128); s = mean |t|; s16 = fp16(s), round to nearest even
+//   ternary: c = +1 if t / s16 > 1/2, -1 if < -1/2, else 0; binary: sign(t)
+//   (s16 = 0: codes 0 / +1).  Without signs: u = t = v, s = mean |v|.
+// The weights are bf16 (8 significant bits), so every partial sum of the
+// transform and of sum |u| is exact in fp64 whenever a group's magnitudes
+// span less than 2^38: the result does not depend on the summation order,
+// and the rounding decisions are taken in fp64.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace lowbit {
+namespace {
+
+__device__ __forceinline__ double bf16_f64(uint16_t b) {
+  return (double)__uint_as_float((uint32_t)b << 16);
+}
+
+// fp64 -> binary16 bits, round to nearest even, from the bit pattern
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+  if (a > 0x7FF0000000000000ull) return 0x7E00;      // NaN
+  if (a >= 0x40EFFE0000000000ull) return sign | 0x7C00;  // >= 65520: rounds to infinity
+  int e = (int)(a >> 52) - 1023;
+  if (e < -14) {
+    // subnormal half (or zero): an integer multiple of 2^-24, exact scaling
+    const double q = __longlong_as_double((long long)a) * 16777216.0;
+    return sign | (uint16_t)__builtin_rint(q);  // 1024 becomes the smallest normal
+  }
+  const uint64_t mant = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
+  uint64_t q = mant >> 42;
+  const uint64_t rem = mant & 0x3FFFFFFFFFFull, half = 0x20000000000ull;
+  if (rem > half || (rem == half && (q & 1))) q++;
+  if (q == 2048) {
+    q = 1024;
+    e++;
+  }
+  return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q & 0x3FF);
+}
+
+__device__ __forceinline__ double f16_bits_f64(uint16_t h) {
+  return (double)f16_bits_to_f32(h);
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int d) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(b & 0xFFFFFFFF), d, 64);
+  const int hi = __shfl_xor((int)(b >> 32), d, 64);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// one wavefront per (row, group)
+__global__ __launch_bounds__(256) void quantize_weights(int fmt, int64_t N, int64_t K, int64_t G,
+                                                        const uint16_t* __restrict__ W,
+                                                        const int8_t* __restrict__ signs,
+                                                        int8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= N * G) return;
+  const int64_t n = unit / G, g = unit % G;
+  const int64_t base = n * K + g * 128;
+  double v0 = bf16_f64(W[base + lane]), v1 = bf16_f64(W[base + lane + 64]);
+  const bool rot = signs != nullptr;
+  const double r128 = __builtin_sqrt(128.0);
+  if (rot) {
+    v0 *= (double)signs[g * 128 + lane];
+    v1 *= (double)signs[g * 128 + lane + 64];
+    // bit 6 of the element index is the register; bits 0..5 are the lane
+    const double a = v0 + v1, b = v0 - v1;
+    v0 = a;
+    v1 = b;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const double p0 = shfl_xor_f64(v0, d), p1 = shfl_xor_f64(v1, d);
+      v0 = (lane & d) ? p0 - v0 : v0 + p0;
+      v1 = (lane & d) ? p1 - v1 : v1 + p1;
+    }
+  }
+  double S = __builtin_fabs(v0) + __builtin_fabs(v1);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) S += shfl_xor_f64(S, d);
+  const double t0 = rot ? v0 / r128 : v0, t1 = rot ? v1 / r128 : v1;
+  const double sc = rot ? (S / 128.0) / r128 : S / 128.0;
+  const uint16_t s16 = f64_to_f16_bits(sc);
+  const double sd = f16_bits_f64(s16);
+  auto code = [&](double t) -> int8_t {
+    if (fmt == 1) return (sd == 0.0 || !(t < 0.0)) ? 1 : -1;
+    if (sd == 0.0) return 0;
+    const double q = t / sd;
+    return q > 0.5 ? 1 : (q < -0.5 ? -1 : 0);
+  };
+  codes[base + lane] = code(t0);
+  codes[base + lane + 64] = code(t1);
+  if (lane == 0) scales[n * G + g] = s16;
+}
+
+// Activations rotated to match rotated weights: per 128-block,
+// Xr = H (d * x) / sqrt(128) in fp32, so that sum_k Wr[n][k] Xr[m][k] equals
+// sum_k W[n][k] X[m][k] (H d / sqrt(128) is orthogonal and symmetric up to d).
+__global__ __launch_bounds__(256) void rotate_act(int64_t M, int64_t K, int64_t G,
+                                                  const uint16_t* __restrict__ X,
+                                                  const int8_t* __restrict__ signs,
+                                                  float* __restrict__ Xr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= M * G) return;
+  const int64_t m = unit / G, g = unit % G;
+  const int64_t base = m * K + g * 128;
+  float v0 = __uint_as_float((uint32_t)X[base + lane] << 16) * (float)signs[g * 128 + lane];
+  float v1 = __uint_as_float((uint32_t)X[base + lane + 64] << 16) * (float)signs[g * 128 + lane + 64];
+  const float a = v0 + v1, b = v0 - v1;
+  v0 = a;
+  v1 = b;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float p0 = __shfl_xor(v0, d, 64), p1 = __shfl_xor(v1, d, 64);
+    v0 = (lane & d) ? p0 - v0 : v0 + p0;
+    v1 = (lane & d) ? p1 - v1 : v1 + p1;
+  }
+  const float inv = 0.08838834764831845f;  // 1 / sqrt(128) rounded to fp32
+  Xr[base + lane] = v0 * inv;
+  Xr[base + lane + 64] = v1 * inv;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W,
+                                   const int8_t* signs, int8_t* codes, uint16_t* scales,
+                                   hipStream_t s) {
+  const int64_t G = K / kGroup, units = N * G;
+  hipLaunchKernelGGL(quantize_weights, dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, fmt, N, K,
+                     G, W, signs, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_act(int64_t M, int64_t K, const uint16_t* X, const int8_t* signs,
+                             float* Xr, hipStream_t s) {
+  const int64_t G = K / kGroup, units = M * G;
+  hipLaunchKernelGGL(rotate_act, dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, M, K, G, X,
+                     signs, Xr);
+  return hipGetLastError();
+}
+
+}  // namespace lowbit

@@ -19,7 +19,7 @@ F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
            "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
            "lowbit_chain_create", "lowbit_chain_run", "lowbit_chain_status", "lowbit_chain_destroy",
-           "lowbit_hbm_read_probe")
+           "lowbit_hbm_read_probe", "lowbit_quantize_weights", "lowbit_rotate_act")
 
 
 class GemvStage(ctypes.Structure):
@@ -62,6 +62,8 @@ def lib():
         L.lowbit_chain_status.argtypes = [vp, ctypes.POINTER(i32)]
         L.lowbit_chain_destroy.argtypes = [vp]
         L.lowbit_hbm_read_probe.argtypes = [vp, i64, vp, vp]
+        L.lowbit_quantize_weights.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
+        L.lowbit_rotate_act.argtypes = [i64, i64, vp, vp, vp, vp]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -165,6 +167,29 @@ def gemm(fmt, M, N, K, pcodes, pscales, X, x_scales=None, y_dtype=F32, Y=None, x
     _check("lowbit_gemm", lib().lowbit_gemm(fmt, M, N, K, _ptr(pcodes), _ptr(pscales), _xdt(X, x_dtype),
                                             _ptr(X), _ptr(x_scales), y_dtype, _ptr(Y), _stream(stream)))
     return Y
+
+
+def quantize_weights(fmt, W, signs=None, stream=None):
+    """Dense (codes int8 [N][K], scales int16 fp16 bits [N][K/128]) from bf16
+    weights W [N][K] (see lowbit_quantize_weights); signs int8 [K] or None."""
+    import torch
+    N, K = W.shape
+    codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    scales = torch.empty((N, K // 128), dtype=torch.int16, device=W.device)
+    _check("lowbit_quantize_weights",
+           lib().lowbit_quantize_weights(fmt, N, K, _ptr(W), _ptr(signs), _ptr(codes),
+                                         _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def rotate_act(X, signs, stream=None):
+    """fp32 X_rot [M][K] from bf16 X [M][K] (see lowbit_rotate_act)."""
+    import torch
+    M, K = X.shape
+    Xr = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    _check("lowbit_rotate_act",
+           lib().lowbit_rotate_act(M, K, _ptr(X), _ptr(signs), _ptr(Xr), _stream(stream)))
+    return Xr
 
 
 def hbm_read_probe(src, out, stream=None):
