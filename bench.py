@@ -279,6 +279,28 @@ def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
+def bench_quantizer(lb, synth, torch, np, N, K, reps):
+    """lowbit_quantize_weights with rotation on an N x K bf16 matrix; returns
+    (ms, GB/s of bf16 read + codes and scales written)."""
+    W = torch.randn(N, K, device="cuda").mul_(0.02).to(torch.bfloat16).view(torch.int16)
+    d = torch.from_numpy(np.where(np.random.default_rng(5).random(K) < 0.5, -1, 1)
+                         .astype(np.int8)).cuda()
+    codes = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    scales = torch.empty((N, K // 128), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def one():
+        lb._check("lowbit_quantize_weights",
+                  lb.lib().lowbit_quantize_weights(2, N, K, lb._ptr(W), lb._ptr(d), lb._ptr(codes),
+                                                   lb._ptr(scales), lb._stream(stream)))
+
+    ms = time_region(torch, stream, one, reps, 2)
+    nbytes = N * K * 2 + N * K + N * (K // 128) * 2
+    del W, codes, scales
+    torch.cuda.synchronize()
+    return ms, nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(fmt, budget_s):
     """The oracle, as it stands, on a bounded sample: 64-row slices of the four
     layer matrices (regenerated bit-exactly on the host), timed over as many
@@ -392,6 +414,12 @@ def main():
             sg[str(M)] = {"ms_per_block": round(dms, 4), "tops": round(tf, 1),
                           "pct_mfma_peak_fp4": round(100 * tf / MFMA_PEAK_F4_TOPS, 1)}
         out["config"]["dit_block_binary_sign"] = sg
+        # data-free quantizer front end on the gate/up matrix (rotated, ternary)
+        qms, qgbs = bench_quantizer(lb, synth, torch, np, 34816, 5120, args.gemm_reps)
+        log(f"quantizer 34816x5120: {qms:.3f} ms, {qgbs:.0f} GB/s")
+        out["config"]["quantizer_gate_up"] = {"ms": round(qms, 4), "gb_s": round(qgbs, 1),
+                                              "pct_hbm_peak": round(100 * qgbs / HBM_PEAK_GBS, 1),
+                                              "bytes": "bf16 in + int8 codes + fp16 scales out"}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.fmt, args.cpu_budget)
     print(json.dumps(out), flush=True)

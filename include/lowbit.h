@@ -246,11 +246,12 @@ int lowbit_chain_destroy(lowbit_chain* chain);
  * not part of it).  From bf16 weights W [N][K] writes dense codes [N][K]
  * (int8, the input of lowbit_pack) and fp16 scales [N][K/128].  Per row and
  * group of 128: v = W * d (signs d[K], int8 +-1; signs == NULL: no
- * rotation), u = H v with H[i][j] = (-1)^popcount(i & j), t = u / sqrt(128),
- * s16 = fp16(mean |t|) (round to nearest even); ternary formats: c = +1 if
- * t / s16 > 1/2, -1 if < -1/2, else 0; binary: c = -1 if t < 0 else +1;
- * s16 = 0 gives codes 0 / +1.  Computed in fp64 (exact up to the final
- * divisions while a group's magnitudes span less than 2^38).  Rotated
+ * rotation), u = H v with H[i][j] = (-1)^popcount(i & j), t = u r with
+ * r = 1/sqrt(128) as an fp64 number, s16 = fp16((sum |u| / 128) r) (round to
+ * nearest even); ternary formats: c = +1 if t > s16/2, -1 if t < -s16/2,
+ * else 0; binary: c = -1 if t < 0 else +1; s16 = 0 gives codes 0 / +1.
+ * Computed in fp64 (sums exact while a group's magnitudes span less than
+ * 2^38, so the result does not depend on the summation order).  Rotated
  * weights expect rotated activations (lowbit_rotate_act with the same
  * signs).  Errors: E_NULL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_HIP. */
 int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,

@@ -452,11 +452,12 @@ uint16_t orc_f64_to_f16(double x) {
  * part of it).  Per row n and group g of 128 weights:
  *   v_i = W[n][128 g + i] * d[128 g + i]           (signs d in {-1, +1})
  *   u_i = sum_j H[i][j] v_j,  H[i][j] = (-1)^popcount(i & j)   (index order)
- *   t_i = u_i / sqrt(128)                          (orthonormal rotation)
- *   s   = (sum_i |u_i| / 128) / sqrt(128)          (mean |t|)
+ *   t_i = u_i * r, r = 1/sqrt(128) as an fp64 number (orthonormal rotation)
+ *   s   = (sum_i |u_i| / 128) * r                  (mean |t|)
  *   s16 = fp16(s) (round to nearest even); scales[n][g] = s16
- *   ternary: c_i = +1 if t_i / s16 > 1/2, -1 if < -1/2, else 0
- *            (round to nearest even of t / s16, clamped to [-1, 1])
+ *   ternary: c_i = +1 if t_i > s16 / 2, -1 if t_i < -s16 / 2, else 0
+ *            (t / s16 rounded to the nearest integer, ties to even, clamped
+ *            to [-1, 1], decided by exact comparison)
  *   binary:  c_i = -1 if t_i < 0, else +1
  *   s16 == 0: every c_i = 0 (ternary) or +1 (binary).
  * signs == NULL: no rotation (u = t = v, s = sum |v| / 128), the plain
@@ -465,7 +466,7 @@ int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
                          const int8_t* signs, int8_t* codes, uint16_t* scales) {
   if ((fmt != 1 && fmt != 2 && fmt != 3) || N < 1 || K < 1 || K % GROUP) return -2;
   const int64_t G = K / GROUP;
-  const double r128 = sqrt(128.0);
+  const double r = 1.0 / sqrt(128.0);
   double v[GROUP], t[GROUP];
   for (int64_t n = 0; n < N; n++)
     for (int64_t g = 0; g < G; g++) {
@@ -484,9 +485,9 @@ int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
           }
         }
         S += fabs(u);
-        t[i] = signs ? u / r128 : u;
+        t[i] = signs ? u * r : u;
       }
-      double sc = signs ? (S / 128.0) / r128 : S / 128.0;
+      double sc = signs ? (S / 128.0) * r : S / 128.0;
       uint16_t s16 = orc_f64_to_f16(sc);
       double sd = orc_f16_to_f64(s16);
       scales[n * G + g] = s16;
@@ -497,8 +498,8 @@ int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
         } else if (sd == 0.0) {
           c = 0;
         } else {
-          double q = t[i] / sd;
-          c = q > 0.5 ? 1 : (q < -0.5 ? -1 : 0);
+          double h = sd * 0.5; /* exact */
+          c = t[i] > h ? 1 : (t[i] < -h ? -1 : 0);
         }
         codes[n * K + g * GROUP + i] = (int8_t)c;
       }
@@ -511,7 +512,7 @@ int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* 
                     double* T) {
   if (N < 1 || K < 1 || K % GROUP || !signs) return -2;
   const int64_t G = K / GROUP;
-  const double r128 = sqrt(128.0);
+  const double r = 1.0 / sqrt(128.0);
   double v[GROUP];
   for (int64_t n = 0; n < N; n++)
     for (int64_t g = 0; g < G; g++) {
@@ -523,7 +524,7 @@ int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* 
           int par = __builtin_popcount((unsigned)(i & j)) & 1;
           u += par ? -v[j] : v[j];
         }
-        T[n * K + g * GROUP + i] = u / r128;
+        T[n * K + g * GROUP + i] = u * r;
       }
     }
   return 0;

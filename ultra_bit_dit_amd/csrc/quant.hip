@@ -8,8 +8,10 @@
 // Per row n and group g (one wavefront, lane l holding elements l and l+64):
 //   v = W[n][128 g ..] * d[128 g ..]            (signs d = +-1)
 //   u = H v, H[i][j] = (-1)^popcount(i & j)      (fast Walsh-Hadamard, fp64)
-//   t = u / sqrt(128); s = mean |t|; s16 = fp16(s), round to nearest even
-//   ternary: c = +1 if t / s16 > 1/2, -1 if < -1/2, else 0; binary: sign(t)
+//   t = u r with r = 1/sqrt(128) in fp64; s = (sum |u| / 128) r (mean |t|);
+//   s16 = fp16(s), round to nearest even
+//   ternary: c = +1 if t > s16/2, -1 if t < -s16/2, else 0 (t / s16 rounded,
+//   ties to even, clamped to [-1, 1], by exact comparison); binary: sign(t)
 //   (s16 = 0: codes 0 / +1).  Without signs: u = t = v, s = mean |v|.
 // The weights are bf16 (8 significant bits), so every partial sum of the
 // transform and of sum |u| is exact in fp64 whenever a group's magnitudes
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void quantize_weights(int fmt, int64_t N, int6
   const int64_t base = n * K + g * 128;
   double v0 = bf16_f64(W[base + lane]), v1 = bf16_f64(W[base + lane + 64]);
   const bool rot = signs != nullptr;
-  const double r128 = __builtin_sqrt(128.0);
+  const double r = 1.0 / __builtin_sqrt(128.0);  // folded to the fp64 constant
   if (rot) {
     v0 *= (double)signs[g * 128 + lane];
     v1 *= (double)signs[g * 128 + lane + 64];
@@ -92,15 +94,14 @@ __global__ __launch_bounds__(256) void quantize_weights(int fmt, int64_t N, int6
   double S = __builtin_fabs(v0) + __builtin_fabs(v1);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) S += shfl_xor_f64(S, d);
-  const double t0 = rot ? v0 / r128 : v0, t1 = rot ? v1 / r128 : v1;
-  const double sc = rot ? (S / 128.0) / r128 : S / 128.0;
+  const double t0 = rot ? v0 * r : v0, t1 = rot ? v1 * r : v1;
+  const double sc = rot ? (S / 128.0) * r : S / 128.0;
   const uint16_t s16 = f64_to_f16_bits(sc);
-  const double sd = f16_bits_f64(s16);
+  const double sd = f16_bits_f64(s16), h = sd * 0.5;
   auto code = [&](double t) -> int8_t {
     if (fmt == 1) return (sd == 0.0 || !(t < 0.0)) ? 1 : -1;
     if (sd == 0.0) return 0;
-    const double q = t / sd;
-    return q > 0.5 ? 1 : (q < -0.5 ? -1 : 0);
+    return t > h ? 1 : (t < -h ? -1 : 0);
   };
   codes[base + lane] = code(t0);
   codes[base + lane + 64] = code(t1);
