@@ -215,7 +215,8 @@ typedef struct lowbit_gemv_stage {
   const void* pscales;  /* packed fp16 scales (16-byte aligned)                    */
   const void* x;        /* K activations of the chain's x_dtype (16-byte aligned)  */
   void* y;              /* N outputs of the chain's y_dtype (4-byte aligned)        */
-  int wait_prev;        /* 1: read x only after stage i-1 is complete               */
+  int wait_prev;        /* 1: read x only after stage i-1 is complete (then K times
+                           the x element size must stay below 2^31 bytes)          */
 } lowbit_gemv_stage;
 
 typedef struct lowbit_chain lowbit_chain; /* opaque */

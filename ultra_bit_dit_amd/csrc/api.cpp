@@ -272,6 +272,9 @@ int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dty
     if (g.fmt != fmt) return LOWBIT_E_UNSUPPORTED;
     if (!g.pcodes || !g.pscales || !g.x || !g.y) return LOWBIT_E_NULL;
     if (!shape_ok(g.N, g.K) || cdiv(g.N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
+    // a waiting stage reads x through a buffer descriptor (32-bit byte offsets)
+    if (i > 0 && g.wait_prev && g.K * (x_dtype == LOWBIT_F32 ? 4 : 2) > INT32_MAX)
+      return LOWBIT_E_SHAPE;
     if (!aligned(g.pcodes, 16) || !aligned(g.pscales, 16) || !aligned(g.x, 16) || !aligned(g.y, 4))
       return LOWBIT_E_ALIGN;
     st[i] = ChainStage{fmt, g.N, g.K, g.pcodes, (const uint16_t*)g.pscales, g.x, g.y,

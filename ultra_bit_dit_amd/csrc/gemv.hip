@@ -126,18 +126,22 @@ __device__ __attribute__((always_inline)) inline bool stage_unit(const FArgs& a,
   return c < nq * 64 * a.M && g < a.G;
 }
 
-// raw activations of one unit: bf16 in ra, f32 in ra:rb, int8 in ra.xy.
-// The load is unconditional (a unit past the end reads element 0) so that
-// no control flow joins wait on it.  COH: device-coherent loads, for
-// activations another workgroup may just have written.
-__device__ __attribute__((always_inline)) inline uint4 coh_load4(const void* p) {
-  const uint32_t* w = (const uint32_t*)p;
-  return make_uint4(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(w + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(w + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+// 16 bytes at byte offset `off` of x (nbytes long) read with a device-coherent
+// (sc1) buffer load, for activations another workgroup may just have
+// written; offsets past nbytes read zeros.
+__device__ __attribute__((always_inline)) inline uint4 coh_load16(const void* x, uint32_t nbytes,
+                                                                 uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(x), (short)0, (int)nbytes, 0x00020000);
+  typedef unsigned v4u_ __attribute__((ext_vector_type(4)));
+  const v4u_ v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16 /* sc1 */);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// raw activations of one unit: bf16 in ra, f32 in ra:rb, int8 in ra.xy.
+// The load is unconditional (a unit past the end reads element 0) so that
+// no control flow joins wait on it.  COH: device-coherent loads (x of M = 1
+// rows shorter than 2^31 bytes).
 template <int XK, bool COH>
 __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a, int64_t q0,
                                                                   int64_t nq, int64_t rd,
@@ -149,12 +153,12 @@ __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a
   const int64_t idx = valid ? m * a.K + g * kGroup + kmap(b, 8 * ch) : 0;
   if constexpr (XK == XK_BF16) {
     const uint16_t* p = (const uint16_t*)a.x + idx;
-    ra = COH ? coh_load4(p) : *(const uint4*)p;
+    ra = COH ? coh_load16(a.x, (uint32_t)(a.M * a.K * 2), (uint32_t)(idx * 2)) : *(const uint4*)p;
     rb = ra;
   } else if constexpr (XK == XK_F32) {
     const float* p = (const float*)a.x + idx;
-    ra = COH ? coh_load4(p) : *(const uint4*)p;
-    rb = COH ? coh_load4(p + 4) : *(const uint4*)(p + 4);
+    ra = COH ? coh_load16(a.x, (uint32_t)(a.M * a.K * 4), (uint32_t)(idx * 4)) : *(const uint4*)p;
+    rb = COH ? coh_load16(a.x, (uint32_t)(a.M * a.K * 4), (uint32_t)(idx * 4 + 16)) : *(const uint4*)(p + 4);
   } else {
     const uint2 w = *(const uint2*)((const int8_t*)a.x + idx);
     ra = make_uint4(w.x, w.y, w.x, w.y);
@@ -626,15 +630,20 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   if constexpr (WAIT) {
     // the previous product must be complete before its outputs are read; the
     // weight loads above are already in flight
-    if (threadIdx.x == 0) {
-      for (uint32_t spin = 0;
-           __hip_atomic_load(wait_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target;
-           spin++) {
+    if (threadIdx.x < 64) {
+      const int L = threadIdx.x;
+      for (uint32_t spin = 0;; spin++) {
+        uint32_t v = L < 16 ? __hip_atomic_load(wait_cnt + 16 * L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        if (__builtin_amdgcn_readfirstlane(v) >= wait_target) break;
         if (spin >= kChainSpinLimit) {  // never satisfied: flag it and go on
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (L == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(10);
       }
     }
     __syncthreads();
@@ -666,9 +675,12 @@ __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
 
 // Persistent kernel over a chain of batch-1 products (items of product s
 // are [first[s], first[s+1]) in a global order that every workgroup walks
-// with stride gridDim.x).  done[s] counts finished items of product s; a
-// product marked `wait` reads its activations only after done[s-1] reaches
-// the previous product's item count.  Workgroups never wait on an item
+// with stride gridDim.x).  Finished items of product s are counted in 16
+// counters done[256 s + 16 j], one 64-byte line each (item i adds to
+// counter i mod 16, so no one address takes every workgroup's atomic), and a
+// product marked `wait` reads its activations only after the 16 counters of
+// product s-1, read together by 16 lanes, sum to its item count.
+// Workgroups never wait on an item
 // later in the order than their own, and the grid is co-resident
 // (cooperative launch), so every wait ends; a wait is nevertheless bounded
 // by kChainSpinLimit.  The last workgroup to finish resets the counters.
@@ -676,7 +688,7 @@ struct ChainArgs {
   const FArgs* args;       // [S]
   const int64_t* first;    // [S + 1] work items (row group x K-slice) before product s
   const int32_t* wait;     // [S]
-  uint32_t* done;          // [S], zero between launches
+  uint32_t* done;          // [256 S] (16 used per product), zero between launches
   uint32_t* finished;      // workgroups done, zero between launches
   uint32_t* err;           // set when a wait gave up
   // streaming kernel only
@@ -734,24 +746,26 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     const bool wt = s > 0 && waitf[s] != 0;
     __syncthreads();  // the previous item's LDS reads are over
     if (wt)
-      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - first[s], smem, c.done + s - 1,
+      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - first[s], smem, c.done + 256 * (s - 1),
                                                 (uint32_t)(first[s] - first[s - 1]), c.err);
     else
       gemv_item<FMT, XK, 1, YK, QM, true, false>(a, i - first[s], smem, nullptr, 0u, c.err);
     __builtin_amdgcn_s_waitcnt(0);  // this item's stores have completed
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(c.done + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(c.finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      for (int k = 0; k < c.S; k++)
-        __hip_atomic_store(c.done + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      const uint32_t idx = (uint32_t)(i - first[s]);
+      __hip_atomic_fetch_add(c.done + 256 * s + 16 * (idx & 15), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  __shared__ uint32_t s_prev;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_prev = __hip_atomic_fetch_add(c.finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_prev == gridDim.x - 1) {
+    for (int k = threadIdx.x; k < 16 * c.S; k += blockDim.x)
+      __hip_atomic_store(c.done + 256 * (k >> 4) + 16 * (k & 15), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1206,7 +1220,7 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   const size_t o_first = align256(o_args + sizeof(FArgs) * S);
   const size_t o_wait = align256(o_first + sizeof(int64_t) * (S + 1));
   const size_t o_done = align256(o_wait + sizeof(int32_t) * S);
-  const size_t o_fin = align256(o_done + sizeof(uint32_t) * S);
+  const size_t o_fin = align256(o_done + sizeof(uint32_t) * S * 256);
   const size_t o_cnt = align256(o_fin + 4 * sizeof(uint32_t));
   const size_t o_part = align256(o_cnt + sizeof(uint32_t) * cnt_words);
   const size_t o_uf = align256(o_part + sizeof(float) * (size_t)part_floats);
