@@ -475,6 +475,67 @@ __device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, 
   }
 }
 
+// fp4 operand B of binary group t with the two masks held in registers
+// (a VOP3 instruction takes no literal here): one v_and_or_b32 for slot
+// register 0 and a shift plus v_and_or_b32 for each of the other three.
+__device__ __attribute__((always_inline)) inline v8i decode_binary_reg(uint32_t wv, uint32_t sign_mask,
+                                                                       uint32_t one_bits) {
+  const uint32_t d0 = (wv & sign_mask) | one_bits;
+  const uint32_t d1 = ((wv << 1) & sign_mask) | one_bits;
+  const uint32_t d2 = ((wv << 2) & sign_mask) | one_bits;
+  const uint32_t d3 = ((wv << 3) & sign_mask) | one_bits;
+  return v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
+}
+
+// quad_mfma for one activation row (M = 1, MA = R rows of A) with scales:
+// `arow` points at this lane's A row of group 0 of the slice image (lanes
+// with r >= R read row r mod R: their output rows are never used, and
+// rows of the MFMA are independent), `erow` at its exponent word, so every
+// group's operand sits at a compile-time offset.  The scale epilogue of
+// group t runs after the MFMA of group t+1 is issued; the accumulation order
+// (group 0..3, terms 0..R-1) is the one quad_mfma uses.
+template <int FMT, int XK>
+__device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t* arow,
+                                                                   const uint8_t* erow, int q,
+                                                                   const Quad<FMT>& qd,
+                                                                   const uint32_t* t3,
+                                                                   uint32_t sign_mask,
+                                                                   uint32_t one_bits, float& acc) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
+  v4f cp;
+  float sp = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
+    const uint4 x0 = src[0], x1 = src[1];
+    const v8i A = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    v8i B;
+    if constexpr (FMT == 1) {
+      const uint32_t wv = t == 0 ? qd.w[0].x : t == 1 ? qd.w[0].y : t == 2 ? qd.w[0].z : qd.w[0].w;
+      B = decode_binary_reg(wv, sign_mask, one_bits);
+    } else {
+      B = decode_group<FMT>(qd, t, t3);
+    }
+    const v4f c = t == 0 ? mfma_group<0>(A, B, (int)se)
+                : t == 1 ? mfma_group<1>(A, B, (int)se)
+                : t == 2 ? mfma_group<2>(A, B, (int)se)
+                         : mfma_group<3>(A, B, (int)se);
+    if (t > 0) {
+      float tsum = cp[0];
+#pragma unroll
+      for (int i = 1; i < R; i++) tsum += cp[i];
+      acc = fmaf(sp, tsum, acc);
+    }
+    cp = c;
+    sp = quad_scale<FMT>(qd, t);
+  }
+  float tsum = cp[0];
+#pragma unroll
+  for (int i = 1; i < R; i++) tsum += cp[i];
+  acc = fmaf(sp, tsum, acc);
+}
+
 // Output of an item: direct stores, or (several K-slices) coherent partial
 // sums and, in the last workgroup of the row group to arrive, their sum in
 // slice order.  COH: the outputs themselves are device-coherent stores.
@@ -790,8 +851,12 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
   return qmax * 16 * a.MA * 33;
 }
 
+// Binary weights carry half the bytes of 2-bit ternary per quad, so the
+// binary kernel with bf16 activations is held to 128 registers (one MFMA
+// group in flight per step) to run four workgroups per CU and keep as many
+// bytes in flight.
 template <int FMT, int XK, int YK, int QM>
-__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_stream(ChainArgs c) {
+__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 ? 4 : 2))) void gemv_stream(ChainArgs c) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
@@ -853,6 +918,12 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
   uint32_t* consumed = filled + 2;
   lds_init<FMT>(lfix);
   if (threadIdx.x < 4) filled[threadIdx.x] = 0;
+  // binary decode masks, in registers (opaque to constant folding)
+  uint32_t sign_mask = 0x88888888u, one_bits = 0x22222222u;
+  if constexpr (FMT == 1) {
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(sign_mask));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(one_bits));
+  }
 
   const int64_t total = ufirst[c.S];
   int64_t u = blockIdx.x;
@@ -925,16 +996,22 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     FArgs an = load_args(args, sn);
     Item itn = item_at<FMT>(an, rgn, ksn);
     QuadPtr pn = quad_ptr<FMT>(an, itn);
-    // the next slice's activations, then the current slice's codes
-    XLD(an, sn, ksn, itn.nq);
+    // the current slice's codes quad by quad with the next slice's
+    // activations after quad kWriteAfter - 1: the order the loop issues them
+    // in, kept by scheduling barriers, so that the wait counts in the loop
+    // (the stricter of loop entry and back edge) leave a whole slice of loads
+    // in flight
     Quad<FMT> qd[QM];
     {
       const QuadPtr p0 = quad_ptr<FMT>(a, it);
 #pragma unroll
-      for (int q = 0; q < QM; q++) load_quad_p<FMT>(p0, q, qd[q]);
+      for (int q = 0; q < QM; q++) {
+        if (q == kWriteAfter) XLD(an, sn, ksn, itn.nq);
+        load_quad_p<FMT>(p0, q, qd[q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     float acc[1] = {0.f};
-    int iacc[1] = {0};
     float tot = 0.f;  // slices added in slice order, as the split-K reduction does
     uint32_t j = 0;   // slice number of this workgroup
 
@@ -967,9 +1044,10 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
       // ... down to 1 or 2: (j + 1) / 2 times)
       const uint32_t b = j & 1;
       if (j > 0) wait_ge(filled + b, 4u * ((j + 1) >> 1));
-      Lds l = lfix;
-      l.xa = xbuf(b);
-      l.xe = xbuf(b) + (int64_t)it.nq * 16 * a.MA * 32;
+      // this lane's A row and exponent word in the slice image
+      const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
+      const uint8_t* arow = xbuf(b) + (lg * R + rr) * 32;
+      const uint8_t* erow = xbuf(b) + it.nq * 16 * R * 32 + (lg * R + rr) * 4;
 #pragma unroll
       for (int q = 0; q < QM; q++) {
         if (q == kWriteAfter) {
@@ -989,7 +1067,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
           const Item it2 = item_at<FMT>(a2, rg2, ks2);
           XLD(a2, s2, ks2, it2.nq);
         }
-        if (it.live && q < it.nq) quad_mfma<FMT, XK, 1, 2>(a, l, q, qd[q], acc, iacc);
+        if (it.live && q < it.nq) quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
         load_quad_p<FMT>(pn, q, qd[q]);
       }
       // done reading slice j's image
