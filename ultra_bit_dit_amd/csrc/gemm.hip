@@ -38,12 +38,16 @@ struct KArgs {
   uint32_t* cnt;            // zero-initialised arrival counters
   int64_t M, N, G, GQ, GP, NB, MT, NT;
   int KS;
+  int row_fast;             // tile order: row tile fastest (else column tile fastest)
 };
 
 // Workgroup -> (split, row tile, column tile).  Workgroups are dealt to the
-// 8 XCDs round-robin; each XCD gets a contiguous run of the tile order
-// (column tile fastest), so the workgroups resident on one XCD share their
-// activation tiles in that XCD's L2.
+// 8 XCDs round-robin; each XCD gets a contiguous run of the tile order.  With
+// the column tile fastest the workgroups resident on one XCD share their
+// activation tiles in that XCD's L2 and every XCD streams all the weights;
+// with the row tile fastest (products whose packed weights outweigh their
+// staged activations, e.g. 512-token prefill) each XCD keeps its share of
+// the weights in L2 and streams the activation tiles instead.
 __device__ inline void tile_of(const KArgs& a, int64_t& mt, int64_t& nt, int& ks) {
   const int64_t T = a.MT * a.NT * a.KS;
   const int64_t bid = blockIdx.x;
@@ -52,8 +56,13 @@ __device__ inline void tile_of(const KArgs& a, int64_t& mt, int64_t& nt, int& ks
     const int64_t base = T / 8, rem = T % 8, x = bid % 8, loc = bid / 8;
     id = x * base + min(x, rem) + loc;
   }
-  nt = id % a.NT;
-  mt = (id / a.NT) % a.MT;
+  if (a.row_fast) {
+    mt = id % a.MT;
+    nt = (id / a.MT) % a.NT;
+  } else {
+    nt = id % a.NT;
+    mt = (id / a.NT) % a.MT;
+  }
   ks = (int)(id / (a.NT * a.MT));
 }
 
@@ -363,40 +372,102 @@ __device__ __forceinline__ void lds_read_s1(uint32_t pa, v4u (&A)[2]) {
                    : "memory");
 }
 
-// One row-block's codes of a quad from its code-buffer slot (this lane's
-// 16 bytes at pc; base-3 also the tail word at pt) and its scales at ps.
-// Base-3 slots hold planes h and h + 1 of the octet, h = quad % 2: the
-// quad's 8-byte chunks are (plane h: lo, hi; plane h + 1: lo) for h = 0 and
-// (plane 1: hi; plane 2: lo, hi) for h = 1.
+// Codes and scales of four row-blocks of a quad from their code-buffer slots
+// (this lane's 16 bytes of each slot; base-3 also the slot's tail word) and
+// their scales, with one wait.  Base-3 slots hold planes h and h + 1 of the
+// octet, h = quad % 2: the quad's 8-byte chunks are (plane h: lo, hi; plane
+// h + 1: lo) for h = 0 and (plane 1: hi; plane 2: lo, hi) for h = 1.
+// Slots are CodeLds::kSlot apart and scales 128 bytes apart; pc, pt and ps
+// are the first row-block's addresses.
 template <int FMT>
-__device__ __forceinline__ void lds_read_codes(uint32_t pc, uint32_t pt, uint32_t ps, int h,
-                                               Quad<FMT>& o) {
+__device__ __forceinline__ void lds_read_codes4(uint32_t pc, uint32_t pt, uint32_t ps, int h,
+                                                Quad<FMT>* o) {
   if constexpr (FMT == 1) {
-    __asm__ volatile("ds_read_b128 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(o.w[0]), "=&v"(o.sc)
-                     : "v"(pc), "v"(ps)
-                     : "memory");
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b64 %4, %9\n\t"
+        "ds_read_b64 %5, %9 offset:128\n\t"
+        "ds_read_b64 %6, %9 offset:256\n\t"
+        "ds_read_b64 %7, %9 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0].w[0]), "=&v"(o[1].w[0]), "=&v"(o[2].w[0]), "=&v"(o[3].w[0]),
+          "=&v"(o[0].sc), "=&v"(o[1].sc), "=&v"(o[2].sc), "=&v"(o[3].sc)
+        : "v"(pc), "v"(ps)
+        : "memory");
   } else if constexpr (FMT == 2) {
     __asm__ volatile(
-        "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:1024\n\tds_read_b64 %2, %4\n\t"
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %12 offset:1024\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\t"
+        "ds_read_b128 %3, %12 offset:3072\n\t"
+        "ds_read_b128 %4, %12 offset:4096\n\t"
+        "ds_read_b128 %5, %12 offset:5120\n\t"
+        "ds_read_b128 %6, %12 offset:6144\n\t"
+        "ds_read_b128 %7, %12 offset:7168\n\t"
+        "ds_read_b64 %8, %13\n\t"
+        "ds_read_b64 %9, %13 offset:128\n\t"
+        "ds_read_b64 %10, %13 offset:256\n\t"
+        "ds_read_b64 %11, %13 offset:384\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(o.w[0]), "=&v"(o.w[1]), "=&v"(o.sc)
+        : "=&v"(o[0].w[0]), "=&v"(o[0].w[1]), "=&v"(o[1].w[0]), "=&v"(o[1].w[1]),
+          "=&v"(o[2].w[0]), "=&v"(o[2].w[1]), "=&v"(o[3].w[0]), "=&v"(o[3].w[1]),
+          "=&v"(o[0].sc), "=&v"(o[1].sc), "=&v"(o[2].sc), "=&v"(o[3].sc)
         : "v"(pc), "v"(ps)
         : "memory");
   } else {
-    u4 pa, pb;
-    uint32_t tw;
+    u4 pa[4], pb[4];
+    uint32_t tw[4];
     __asm__ volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\tds_read_b32 %2, %5\n\t"
-        "ds_read_b64 %3, %6\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(pa), "=&v"(pb), "=&v"(tw), "=&v"(o.sc)
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %4, %16 offset:1024\n\t"
+        "ds_read_b128 %1, %16 offset:2304\n\t"
+        "ds_read_b128 %5, %16 offset:3328\n\t"
+        "ds_read_b128 %2, %16 offset:4608\n\t"
+        "ds_read_b128 %6, %16 offset:5632\n\t"
+        "ds_read_b128 %3, %16 offset:6912\n\t"
+        "ds_read_b128 %7, %16 offset:7936\n\t"
+        "ds_read_b32 %8, %17\n\t"
+        "ds_read_b32 %9, %17 offset:2304\n\t"
+        "ds_read_b32 %10, %17 offset:4608\n\t"
+        "ds_read_b32 %11, %17 offset:6912\n\t"
+        "ds_read_b64 %12, %18\n\t"
+        "ds_read_b64 %13, %18 offset:128\n\t"
+        "ds_read_b64 %14, %18 offset:256\n\t"
+        "ds_read_b64 %15, %18 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(pa[0]), "=&v"(pa[1]), "=&v"(pa[2]), "=&v"(pa[3]), "=&v"(pb[0]), "=&v"(pb[1]),
+          "=&v"(pb[2]), "=&v"(pb[3]), "=&v"(tw[0]), "=&v"(tw[1]), "=&v"(tw[2]), "=&v"(tw[3]),
+          "=&v"(o[0].sc), "=&v"(o[1].sc), "=&v"(o[2].sc), "=&v"(o[3].sc)
         : "v"(pc), "v"(pt), "v"(ps)
         : "memory");
-    o.c30 = h ? u2{pa.z, pa.w} : u2{pa.x, pa.y};
-    o.c31 = h ? u2{pb.x, pb.y} : u2{pa.z, pa.w};
-    o.c32 = h ? u2{pb.z, pb.w} : u2{pb.x, pb.y};
-    o.t3 = tw >> (16 * h);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      o[j].c30 = h ? u2{pa[j].z, pa[j].w} : u2{pa[j].x, pa[j].y};
+      o[j].c31 = h ? u2{pb[j].x, pb[j].y} : u2{pa[j].z, pa[j].w};
+      o[j].c32 = h ? u2{pb[j].z, pb[j].w} : u2{pb[j].x, pb[j].y};
+      o[j].t3 = tw[j] >> (16 * h);
+    }
   }
+}
+
+// Two row-blocks of 2-bit codes (the 4-wide read leaves the widest 2-bit
+// kernel without registers to spare).
+__device__ __forceinline__ void lds_read_codes2_t2(uint32_t pc, uint32_t ps, Quad<2>* o) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b128 %2, %6 offset:2048\n\t"
+      "ds_read_b128 %3, %6 offset:3072\n\t"
+      "ds_read_b64 %4, %7\n\t"
+      "ds_read_b64 %5, %7 offset:128\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0].w[0]), "=&v"(o[0].w[1]), "=&v"(o[1].w[0]), "=&v"(o[1].w[1]), "=&v"(o[0].sc),
+        "=&v"(o[1].sc)
+      : "v"(pc), "v"(ps)
+      : "memory");
 }
 
 // Workgroup tile 64 rows x 64 RBW columns, 8 waves: wave (wm, wn) owns
@@ -542,12 +613,19 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
     lds_read_a(base + 16 * lane, base + 2048 + lane, A0, A1, se);
   };
-  // codes and scales of row-block RBW wn + j of the quad in the code buffer
-  auto cread = [&](int j, int gq, Quad<FMT>& o) {
+  // codes and scales of row-blocks RBW wn + j .. + 3 of the quad in the code buffer
+  static_assert(RBW % 4 == 0, "code reads go four row-blocks at a time");
+  static_assert(CL::kSlot == (FMT == 1 ? 1024 : FMT == 2 ? 2048 : 2304), "slot offsets of the code reads");
+  auto cread4 = [&](int j, int gq, Quad<FMT>* o) {
     const uint32_t slot = (uint32_t)(uintptr_t)((lds_u8*)cbuf + (RBW * wn + j) * CL::kSlot);
     const uint32_t sc = (uint32_t)(uintptr_t)((lds_u8*)cbuf + CL::kScales + (RBW * wn + j) * 128) +
                         8 * (lane & 15);
-    lds_read_codes<FMT>(slot + lo16, slot + 2048 + 4 * lane, sc, gq & 1, o);
+    if constexpr (FMT == 2 && RBW == 8) {
+      lds_read_codes2_t2(slot + lo16, sc, o);
+      lds_read_codes2_t2(slot + 2 * CL::kSlot + lo16, sc + 256, o + 2);
+    } else {
+      lds_read_codes4<FMT>(slot + lo16, slot + 2048 + 4 * lane, sc, gq & 1, o);
+    }
   };
 
   // acc[rt][j][e]: row 32 wm + 16 rt + 4 (lane / 16) + e, column 16 (RBW wn + j) + lane % 16
@@ -582,7 +660,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
           xsync(std::integral_constant<int, 2 * XC + CL::kCopies>());
         if (t == 0) {
 #pragma unroll
-          for (int j = 0; j < RBW; j++) cread(j, q, qd[j]);
+          for (int j = 0; j < RBW; j += 4) cread4(j, q, qd + j);
         }
         xissue(g + 3 < g1 ? g + 3 : g1 - 1, (t + 3) & 3);
         if (t == 1) cissue(q + 1 < q1 ? q + 1 : q);
@@ -679,6 +757,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 struct GemmPlan {
   int64_t MT, NT, G, KS;
   int RBW;
+  int row_fast;  // tile order of the launch (see tile_of)
   size_t xt_off, rs_off, part_off, bytes;
 };
 
@@ -716,6 +795,10 @@ GemmPlan make_gemm_plan(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
   p.NT = cdiv(N, 64 * p.RBW);
   const int64_t tiles = p.MT * p.NT;
   p.KS = tiles > kMaxRowGroups ? 1 : pick_splits(tiles, cdiv(p.G, 4));
+  // packed weight bytes (codes and scales) against staged activation bytes
+  const double wbytes = (double)N * K * (fmt == 1 ? 1.0 : fmt == 2 ? 2.0 : 1.625) / 8 + (double)N * p.G * 2;
+  const double xbytes = (double)p.MT * p.G * (xkind == XK_SIGN1 ? kS1Img : kF8Img);
+  p.row_fast = wbytes > xbytes ? 1 : 0;
   p.rs_off = kCounterBytes;
   p.xt_off = p.rs_off;
   p.part_off = p.xt_off + align256((size_t)p.MT * p.G * (xkind == XK_SIGN1 ? kS1Img : kF8Img));
@@ -744,6 +827,7 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.MT = p.MT;
   k.NT = p.NT;
   k.KS = (int)p.KS;
+  k.row_fast = p.row_fast;
   const int64_t Mpad = p.MT * kF8BM;
   const int64_t units = Mpad * p.G * 4;
   const dim3 sgrid((unsigned)cdiv(units, 256));
