@@ -530,3 +530,14 @@ int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* 
   return 0;
 }
 
+/* Gated FFN activation feeding the down projection: z[k] = silu(g[k]) u[k],
+ * silu(v) = v / (1 + e^-v), in fp64.  The pages state that the compressed
+ * models keep their base model's architecture and change only how weights
+ * are stored (kongchang.com Ternary Bonsai 2 article, model-card paragraph;
+ * the Japanese Bonsai 27B article, section on the base network); the gated
+ * SiLU FFN is that base family's, which the pages do not print. */
+int orc_silu_mul(int64_t K, const double* g, const double* u, double* z) {
+  if (K < 0 || (K && (!g || !u || !z))) return -2;
+  for (int64_t k = 0; k < K; k++) z[k] = g[k] / (1.0 + exp(-g[k])) * u[k];
+  return 0;
+}

@@ -87,6 +87,9 @@ int orc_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
 int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* signs,
                     double* T);
 
+/* z[k] = silu(g[k]) * u[k], silu(v) = v / (1 + exp(-v)), fp64. */
+int orc_silu_mul(int64_t K, const double* g, const double* u, double* z);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,7 @@ def lib():
         L.orc_f64_to_f16.restype = ctypes.c_uint16
         L.orc_quantize_weights.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp]
         L.orc_rotate_rows.argtypes = [i64, i64, vp, vp, vp]
+        L.orc_silu_mul.argtypes = [i64, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -190,3 +191,40 @@ def rotate_rows(W_bf16, signs):
     if rc:
         raise ValueError(f"orc_rotate_rows failed: {rc}")
     return T
+
+
+def silu_mul(g, u):
+    """fp64 z = silu(g) * u elementwise (orc_silu_mul)."""
+    g = _c(g, np.float64).ravel()
+    u = _c(u, np.float64).ravel()
+    if g.shape != u.shape:
+        raise ValueError("silu_mul: shapes differ")
+    z = np.empty_like(g)
+    rc = lib().orc_silu_mul(g.size, _p(g), _p(u), _p(z))
+    if rc:
+        raise ValueError(f"orc_silu_mul failed: {rc}")
+    return z
+
+
+def fuse_gate_up(gate_rows, up_rows):
+    """Row order of a fused gate/up matrix for the SiLU-mul epilogue: within
+    every 16-row block b, rows 0..7 are gate rows 8b..8b+7 and rows 8..15 the
+    up rows 8b..8b+7.  Takes two [F][...] arrays (F % 8 == 0), returns the
+    [2F][...] fused array."""
+    g = np.asarray(gate_rows)
+    u = np.asarray(up_rows)
+    F = g.shape[0]
+    if u.shape != g.shape or F % 8:
+        raise ValueError("fuse_gate_up: gate and up must have the same shape, rows % 8 == 0")
+    out = np.empty((2 * F,) + g.shape[1:], dtype=g.dtype)
+    for b in range(F // 8):
+        out[16 * b:16 * b + 8] = g[8 * b:8 * b + 8]
+        out[16 * b + 8:16 * b + 16] = u[8 * b:8 * b + 8]
+    return out
+
+
+def split_fused(y):
+    """Inverse of fuse_gate_up on a fused output vector: (gate [F], up [F])."""
+    y = np.asarray(y)
+    blocks = y.reshape(-1, 2, 8)
+    return blocks[:, 0, :].reshape(-1), blocks[:, 1, :].reshape(-1)
