@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 1
+#define LOWBIT_ABI_VERSION 2
 
 enum lowbit_status {
   LOWBIT_OK = 0,
@@ -217,7 +217,21 @@ typedef struct lowbit_gemv_stage {
   void* y;              /* N outputs of the chain's y_dtype (4-byte aligned)        */
   int wait_prev;        /* 1: read x only after stage i-1 is complete (then K times
                            the x element size must stay below 2^31 bytes)          */
+  int epilogue;         /* LOWBIT_EPI_NONE or LOWBIT_EPI_SILU_MUL (see below)      */
 } lowbit_gemv_stage;
+
+/* Stage epilogues.  LOWBIT_EPI_SILU_MUL: the stage is a fused gate/up
+ * product of a gated FFN (the compressed models keep their base model's
+ * architecture: kongchang.com Ternary Bonsai 2 article, model-card
+ * paragraph) whose N rows (N % 16 == 0) are ordered so that in every 16-row
+ * block rows 0..7 are gate rows 8b..8b+7 and rows 8..15 the up rows
+ * 8b..8b+7; y then receives N/2 values z[i] = silu(g[i]) u[i],
+ * silu(v) = v / (1 + e^-v), computed in fp32 from the fp32 products and
+ * stored in the chain's y_dtype -- the input of the down projection, which a
+ * later stage (wait_prev = 1, K = N/2, x = this y when y_dtype equals
+ * x_dtype) reads. */
+#define LOWBIT_EPI_NONE 0
+#define LOWBIT_EPI_SILU_MUL 1
 
 typedef struct lowbit_chain lowbit_chain; /* opaque */
 

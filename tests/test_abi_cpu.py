@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lb.lib().lowbit_abi_version() == 1
+    assert lb.lib().lowbit_abi_version() == 2
     for st in range(-8, 1):
         assert isinstance(lb.status_str(st), str) and lb.status_str(st)
 

@@ -111,3 +111,100 @@ def test_chain_rejects_bad_stages():
     with pytest.raises(lb.LowbitError) as e:
         lb.Chain([(1, 64, 256, pc, ps, x, y, 0)], x_dtype=lb.I8)
     assert e.value.status == lb.E_UNSUPPORTED
+
+
+def silu_mul_tolerance(gref, uref, absG, absU, zref, bf16_out):
+    """Bound on |z_gpu - z_ref| for z = silu(g) u when g and u each carry the
+    product tolerance t = 1e-3 sum|w x|: |silu'| <= 1.1 and |silu''| <= 0.5,
+    so |dz| <= 1.1 |u| tg + |silu(g)| tu + tg tu + 0.5 tg^2 (|u| + tu), plus
+    fp32 evaluation (1e-6 |z|) and, for bf16 outputs, one rounding (2^-8 |z|)."""
+    tg, tu = 1e-3 * absG, 1e-3 * absU
+    sg = np.abs(O.silu_mul(gref, np.ones_like(gref)))
+    tol = 1.1 * np.abs(uref) * tg + sg * tu + tg * tu + 0.5 * tg * tg * (np.abs(uref) + tu)
+    tol += 1e-6 * np.abs(zref) + 1e-30
+    if bf16_out:
+        tol += 2.0 ** -8 * np.abs(zref)
+    return tol
+
+
+def to_np(t):
+    """fp64 values of a float32 or bfloat16 device vector."""
+    if t.dtype == torch.bfloat16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("F,K", [(640, 1024), (256, 17408)])
+@pytest.mark.parametrize("with_down", [False, True])
+def test_chain_silu_mul_epilogue(fmt, dt, F, K, with_down):
+    """A fused gate/up stage with the SiLU-mul epilogue writes F values
+    z = silu(g) u; alone it runs in the streaming kernel, followed by a
+    waiting down projection (x = z) in the dependent kernel.  z must meet the
+    tolerance propagated from the product tolerance of g and u; the down
+    stage must match the oracle applied to the GPU's own z."""
+    xdt = lb.F32 if dt == "f32" else lb.BF16
+    cg = codes_for(fmt, SEED, 400 + F % 7, F, K)
+    cu = codes_for(fmt, SEED, 410 + F % 7, F, K)
+    sg = synth.group_scales(SEED, 420, F, K // 128)
+    su = synth.group_scales(SEED, 421, F, K // 128)
+    fused_c, fused_s = O.fuse_gate_up(cg, cu), O.fuse_gate_up(sg, su)
+    pc, ps = lb.pack(fmt, dev(fused_c), dev(fused_s.view(np.int16)))
+    if dt == "f32":
+        xh = synth.normal_f32(SEED, 430, 1, K)
+        x = dev(xh)[0]
+        xkind = O.X_F32
+    else:
+        xh = synth.normal_bf16(SEED, 430, 1, K)
+        x = dev(xh.view(np.int16)).view(torch.bfloat16)[0]
+        xkind = O.X_BF16
+    gref, absG = O.matmul(cg, sg, xkind, xh)
+    uref, absU = O.matmul(cu, su, xkind, xh)
+    gref, absG, uref, absU = gref[0], absG[0], uref[0], absU[0]
+    zref = O.silu_mul(gref, uref)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    z = torch.full((F,), float("nan"), device="cuda", dtype=tdt)
+    stages = [(fmt, 2 * F, K, pc, ps, x, z, 0, lb.EPI_SILU_MUL)]
+    if with_down:
+        Nd = 384
+        cd = codes_for(fmt, SEED, 440, Nd, F)
+        sd = synth.group_scales(SEED, 441, Nd, F // 128)
+        pcd, psd = lb.pack(fmt, dev(cd), dev(sd.view(np.int16)))
+        yd = torch.full((Nd,), float("nan"), device="cuda", dtype=tdt)
+        stages.append((fmt, Nd, F, pcd, psd, z, yd, 1))
+    chain = lb.Chain(stages, x_dtype=xdt, y_dtype=xdt)
+    for rep in range(3):
+        z.fill_(float("nan"))
+        if with_down:
+            yd.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        zg = to_np(z)
+        tol = silu_mul_tolerance(gref, uref, absG, absU, zref, dt == "bf16")
+        err = np.abs(zg - zref)
+        assert np.all(np.isfinite(zg)), f"run {rep}: non-finite z"
+        assert np.all(err <= tol), f"run {rep}: z error {np.max(err / tol):.3g} x tolerance"
+        if with_down:
+            if dt == "f32":
+                zin, kind = zg.astype(np.float32)[None], O.X_F32
+            else:
+                zin, kind = z.view(torch.int16).cpu().numpy().view(np.uint16)[None], O.X_BF16
+            ydr, absYd = O.matmul(cd, sd, kind, zin)
+            assert_within(to_np(yd)[None], ydr, absYd, bf16_out=dt == "bf16", what=f"down run {rep}")
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
+def test_chain_epilogue_rejects():
+    _, _, pc, ps = make(1, 72, 256, tid=450)
+    x = torch.zeros(256, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(72, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:  # 72 rows: not whole 16-row blocks
+        lb.Chain([(1, 72, 256, pc, ps, x, y, 0, lb.EPI_SILU_MUL)])
+    assert e.value.status == lb.E_SHAPE
+    _, _, pc, ps = make(1, 64, 256, tid=452)
+    with pytest.raises(lb.LowbitError) as e:
+        lb.Chain([(1, 64, 256, pc, ps, x, y, 0, 7)])
+    assert e.value.status == lb.E_UNSUPPORTED

@@ -277,8 +277,10 @@ int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dty
       return LOWBIT_E_SHAPE;
     if (!aligned(g.pcodes, 16) || !aligned(g.pscales, 16) || !aligned(g.x, 16) || !aligned(g.y, 4))
       return LOWBIT_E_ALIGN;
+    if (g.epilogue != LOWBIT_EPI_NONE && g.epilogue != LOWBIT_EPI_SILU_MUL) return LOWBIT_E_UNSUPPORTED;
+    if (g.epilogue == LOWBIT_EPI_SILU_MUL && g.N % 16 != 0) return LOWBIT_E_SHAPE;
     st[i] = ChainStage{fmt, g.N, g.K, g.pcodes, (const uint16_t*)g.pscales, g.x, g.y,
-                       i > 0 && g.wait_prev ? 1 : 0};
+                       i > 0 && g.wait_prev ? 1 : 0, g.epilogue};
   }
   void* plan = nullptr;
   hipError_t e = chain_create(st.data(), n_stages, x_dtype, y_dtype, &plan);

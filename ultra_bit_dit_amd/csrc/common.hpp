@@ -94,6 +94,7 @@ struct ChainStage {
   const void* x;
   void* y;
   int wait_prev;
+  int epi;  // 1: SiLU-mul epilogue (N fused gate/up rows -> N/2 outputs)
 };
 hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void** plan);
 hipError_t chain_run(void* plan, hipStream_t s);

@@ -102,6 +102,7 @@ struct FArgs {
   int64_t N, K, G, GQ, GP, M, MA, NB, KS, Npad;
   float x_scale;
   int xkind;
+  int epi;        // 1: SiLU-mul epilogue (chains, M = 1)
 };
 
 // Staging of quads [q0, q1) of the M activation rows into LDS by all threads
@@ -536,6 +537,16 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
   acc = fmaf(sp, tsum, acc);
 }
 
+// SiLU-mul epilogue of a fused gate/up product: in every 16-row block the
+// rows 0..7 are gate rows and 8..15 the matching up rows, so lane r < 8 of
+// a 16-lane row group holds g and lane r + 8 holds u; output 8 b + r of
+// row-block b is silu(g) u = g / (1 + e^-g) u in fp32.  Every lane of the
+// wave must call it (it shuffles); the result is meaningful in lanes r < 8.
+__device__ __attribute__((always_inline)) inline float silu_mul_lanes(float f) {
+  const float u = __shfl_down(f, 8);
+  return f / (1.0f + expf(-f)) * u;
+}
+
 // Output of an item: direct stores, or (several K-slices) coherent partial
 // sums and, in the last workgroup of the row group to arrive, their sum in
 // slice order.  COH: the outputs themselves are device-coherent stores.
@@ -567,6 +578,11 @@ __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a
   };
   constexpr bool IPART = INTC && YK == YK_I32;
   const int64_t n = 16 * it.rb + r;
+  if (a.KS == 1 && a.epi) {
+    const float z = silu_mul_lanes(acc[0]);
+    if (it.live && lg == 0 && r < 8) store(0, 8 * it.rb + r, z, 0);
+    return;
+  }
   if (a.KS == 1) {
 #pragma unroll
     for (int j = 0; j < MX; j++) {
@@ -593,6 +609,17 @@ __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a
   __syncthreads();
   if (s_last != (uint32_t)(a.KS - 1)) return;
   // last arrival: add the slices in order (coherent loads) and store
+  if (a.epi) {
+    float f = 0.f;
+    if (it.live && lg == 0)
+      for (int64_t k2 = 0; k2 < a.KS; k2++)
+        f += __hip_atomic_load(a.part + k2 * a.Npad + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float z = silu_mul_lanes(f);
+    if (it.live && lg == 0 && r < 8) store(0, 8 * it.rb + r, z, 0);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.cnt + 16 + it.rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < MX; j++) {
     const int64_t m = (int64_t)lg * (4 / R) + j;
@@ -790,6 +817,7 @@ __device__ __attribute__((always_inline)) inline FArgs load_args(FArgsTab t, int
   a.Npad = t[s].Npad;
   a.x_scale = t[s].x_scale;
   a.xkind = t[s].xkind;
+  a.epi = t[s].epi;
   return a;
 }
 
@@ -1080,7 +1108,14 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         // row group complete: one output per row (lanes of the first row of A)
         const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
         const int64_t n = 16 * it.rb + r;
-        if (it.live && lg == 0 && n < a.N) {
+        if (a.epi) {
+          const float z = silu_mul_lanes(tot);
+          const int64_t nz = 8 * it.rb + r;
+          if (it.live && lg == 0 && r < 8) {
+            if (YK == YK_F32) ((float*)a.y)[nz] = z;
+            else ((uint16_t*)a.y)[nz] = (uint16_t)bf16_rne(z);
+          }
+        } else if (it.live && lg == 0 && n < a.N) {
           if (YK == YK_F32) ((float*)a.y)[n] = tot;
           else ((uint16_t*)a.y)[n] = (uint16_t)bf16_rne(tot);
         }
@@ -1208,6 +1243,7 @@ hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
   k.Npad = p.Npad;
   k.x_scale = g.x_scale;
   k.xkind = g.xkind;
+  k.epi = 0;
   const dim3 grid((unsigned)(p.NRG * p.KS)), block((unsigned)(64 * p.W));
   if (g.fmt == 1) return launch_x<1, kQuadsBinary>(g, k, grid, block, p.lds, s);
   if (g.fmt == 2) return launch_x<2, kQuadsTernary>(g, k, grid, block, p.lds, s);
@@ -1291,6 +1327,7 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
     k.Npad = p.Npad;
     k.x_scale = 1.0f;
     k.xkind = xkind;
+    k.epi = st[i].epi;
   }
   if (first[S] > 0x7FFFFFFF || cnt_words > 0x7FFFFFFF) return hipErrorInvalidValue;
   // layout of the one allocation

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "liblowbit.so")
 OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_BADCODE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 BINARY, TERNARY_2BIT, TERNARY_BASE3 = 1, 2, 3
 F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
+EPI_NONE, EPI_SILU_MUL = 0, 1
 
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
@@ -26,7 +27,8 @@ class GemvStage(ctypes.Structure):
     """lowbit_gemv_stage"""
     _fields_ = [("fmt", ctypes.c_int), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("pcodes", ctypes.c_void_p), ("pscales", ctypes.c_void_p),
-                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("wait_prev", ctypes.c_int)]
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("wait_prev", ctypes.c_int),
+                ("epilogue", ctypes.c_int)]
 
 
 class LowbitError(RuntimeError):
@@ -203,15 +205,17 @@ def hbm_read_probe(src, out, stream=None):
 class Chain:
     """A planned chain of batch-1 products run as one persistent launch
     (lowbit_chain_*).  `stages` is a list of (fmt, N, K, pcodes, pscales, x, y,
-    wait_prev) with device tensors; the tensors are kept referenced for the
-    chain's lifetime."""
+    wait_prev[, epilogue]) with device tensors (epilogue EPI_NONE or
+    EPI_SILU_MUL); the tensors are kept referenced for the chain's lifetime."""
 
     def __init__(self, stages, x_dtype=BF16, y_dtype=F32):
         self._keep = [t for st in stages for t in st[3:7]]
         arr = (GemvStage * len(stages))()
-        for i, (fmt, N, K, pc, ps, x, y, wait) in enumerate(stages):
+        for i, st in enumerate(stages):
+            fmt, N, K, pc, ps, x, y, wait = st[:8]
+            epi = st[8] if len(st) > 8 else EPI_NONE
             arr[i] = GemvStage(fmt, N, K, pc.data_ptr(), ps.data_ptr(), x.data_ptr(), y.data_ptr(),
-                               int(wait))
+                               int(wait), int(epi))
         h = ctypes.c_void_p()
         _check("lowbit_chain_create",
                lib().lowbit_chain_create(len(stages), arr, x_dtype, y_dtype, ctypes.byref(h)))
