@@ -173,12 +173,31 @@ def hbm_read_rate(lb, torch, steps=10, warmup=2, nbytes=4 << 30):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def chain_for(lb, fmt, W, xs, ys, layers, wait):
+def chain_for(lb, fmt, W, xs, ys, layers, wait, torch=None):
+    """One persistent chain over every product of the step.  With waits the
+    chain is a sequential decode layer: the gate/up product runs the SiLU-mul
+    epilogue and the down projection reads its output z (bf16 activations
+    throughout); q/k/v and o read fixed activations (attention is not part of
+    the path)."""
+    if not wait:
+        stages = []
+        for l in range(layers):
+            for j, (name, N, K) in enumerate(MATS):
+                stages.append((fmt, N, K, W[l][j][0], W[l][j][1], xs[j], ys[j], 0))
+        return lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+    names = [m[0] for m in MATS]
+    gu, dn = names.index("gateup"), names.index("down")
+    outs = [torch.empty(N // 2 if j == gu else N, dtype=torch.bfloat16, device="cuda")
+            for j, (_, N, _) in enumerate(MATS)]
     stages = []
     for l in range(layers):
         for j, (name, N, K) in enumerate(MATS):
-            stages.append((fmt, N, K, W[l][j][0], W[l][j][1], xs[j], ys[j], wait))
-    return lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+            x = outs[gu] if j == dn else xs[j]
+            epi = lb.EPI_SILU_MUL if j == gu else lb.EPI_NONE
+            stages.append((fmt, N, K, W[l][j][0], W[l][j][1], x, outs[j], 1, epi))
+    ch = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.BF16)
+    ch._outs = outs
+    return ch
 
 
 def bench_decode(args, lb, synth, torch, np):
@@ -186,7 +205,8 @@ def bench_decode(args, lb, synth, torch, np):
     chain      one persistent launch per step streams all 4 x layers products
                (the products of this workload are independent: fixed x per shape);
     chain_dep  the same launch with every product waiting for the previous one
-               to complete before reading its activations (sequential decode);
+               to complete before reading its activations (sequential decode),
+               gate/up with the SiLU-mul epilogue feeding the down projection;
     separate   one lowbit_gemv launch per product, the step captured as a HIP graph.
     The first mode listed is the headline."""
     fmt, layers = args.fmt, args.layers
@@ -201,7 +221,7 @@ def bench_decode(args, lb, synth, torch, np):
     res = {}
     for mode in modes:
         if mode in ("chain", "chain_dep"):
-            ch = chain_for(lb, fmt, W, xs, ys, layers, 1 if mode == "chain_dep" else 0)
+            ch = chain_for(lb, fmt, W, xs, ys, layers, 1 if mode == "chain_dep" else 0, torch)
             ms = time_region(torch, stream, lambda: ch.run(stream), args.steps, args.warmup)
             if ch.failed_waits():
                 raise RuntimeError("chain wait gave up")

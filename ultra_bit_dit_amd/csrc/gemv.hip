@@ -748,9 +748,24 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     iacc[j] = 0;
   }
   if (it.live) {
+    if constexpr (CHAIN) {
+      // chains: one activation row with scales (the single-row routine)
+      const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
+      const uint8_t* arow = l.xa + (lg * R + rr) * 32;
+      const uint8_t* erow = l.xe + (lg * R + rr) * 4;
+      uint32_t sign_mask = 0x88888888u, one_bits = 0x22222222u;
+      if constexpr (FMT == 1) {
+        asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(sign_mask));
+        asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(one_bits));
+      }
 #pragma unroll
-    for (int q = 0; q < QM; q++)
-      if (q < it.nq) quad_mfma<FMT, XK, MX>(a, l, q, qd[q], acc, iacc);
+      for (int q = 0; q < QM; q++)
+        if (q < it.nq) quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc[0]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < QM; q++)
+        if (q < it.nq) quad_mfma<FMT, XK, MX>(a, l, q, qd[q], acc, iacc);
+    }
   }
   item_output<XK, MX, YK, CHAIN>(a, it, acc, iacc);
 }
