@@ -494,8 +494,11 @@ __device__ __attribute__((always_inline)) inline v8i decode_binary_reg(uint32_t 
 // rows of the MFMA are independent), `erow` at its exponent word, so every
 // group's operand sits at a compile-time offset.  The scale epilogue of
 // group t runs after the MFMA of group t+1 is issued; the accumulation order
-// (group 0..3, terms 0..R-1) is the one quad_mfma uses.
-template <int FMT, int XK>
+// (group 0..3, terms 0..R-1) is the one quad_mfma uses.  AHEAD: the A
+// operands of all four groups are read from LDS first (eight more live
+// registers per group), for callers with few waves per SIMD to hide the
+// LDS latency behind.
+template <int FMT, int XK, bool AHEAD = false>
 __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t* arow,
                                                                    const uint8_t* erow, int q,
                                                                    const Quad<FMT>& qd,
@@ -504,12 +507,25 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
                                                                    uint32_t one_bits, float& acc) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
+  uint4 xa[4][2];
+  if constexpr (AHEAD) {
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
+      xa[t][0] = src[0];
+      xa[t][1] = src[1];
+    }
+  }
   v4f cp;
   float sp = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
-    const uint4 x0 = src[0], x1 = src[1];
+    if constexpr (!AHEAD) {
+      const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
+      xa[t][0] = src[0];
+      xa[t][1] = src[1];
+    }
+    const uint4 x0 = xa[t][0], x1 = xa[t][1];
     const v8i A = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     v8i B;
     if constexpr (FMT == 1) {
@@ -760,7 +776,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc[0]);
+        if (q < it.nq) quad_mfma_m1<FMT, XK, true>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc[0]);
     } else {
 #pragma unroll
       for (int q = 0; q < QM; q++)
