@@ -299,6 +299,44 @@ def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
+def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
+    """One product per launch over `copies` distinct weight matrices (more
+    packed bytes than the 256 MB last-level cache, so every launch streams
+    from HBM), the launches replayed as one HIP graph.  mode "sign": batch-1
+    binary weights x sign activations (XOR + popcount, lowbit_gemv SIGN1);
+    "m5": five bf16 activation rows (small-M verification pass, lowbit_gemm).
+    Returns (us per product, GB/s of packed weight bytes)."""
+    mats = build_mats(lb, synth, fmt, SEED + 10, 0, [("w", N, K)] * copies)
+    if mode == "sign":
+        xb = torch.from_numpy(synth.sign_bits(SEED + 10, 850, 1, K)).cuda()[0]
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+
+        def one():
+            for pc, ps in mats:
+                lb.gemv(1, N, K, pc, ps, xb, x_scale=1.0, y=y, x_dtype=lb.SIGN1)
+    else:
+        X = torch.from_numpy(synth.normal_bf16(SEED + 10, 851, 5, K).view(np.int16)).cuda() \
+            .view(torch.bfloat16)
+        Y = torch.empty((5, N), dtype=torch.float32, device="cuda")
+
+        def one():
+            for pc, ps in mats:
+                lb.gemm(fmt, 5, N, K, pc, ps, X, Y=Y)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        one()  # eager warm-up (allocates the workspace)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        one()
+    torch.cuda.synchronize()
+    ms = time_region(torch, stream, graph.replay, reps, 2)
+    nbytes = packed_bytes(lb, fmt, [("w", N, K)]) * copies
+    del graph, mats
+    torch.cuda.synchronize()
+    return ms * 1e3 / copies, nbytes / (ms * 1e-3) / 1e9
+
+
 def bench_quantizer(lb, synth, torch, np, N, K, reps):
     """lowbit_quantize_weights with rotation on an N x K bf16 matrix; returns
     (ms, GB/s of bf16 read + codes and scales written)."""
@@ -434,6 +472,17 @@ def main():
             sg[str(M)] = {"ms_per_block": round(dms, 4), "tops": round(tf, 1),
                           "pct_mfma_peak_fp4": round(100 * tf / MFMA_PEAK_F4_TOPS, 1)}
         out["config"]["dit_block_binary_sign"] = sg
+        # batch-1 XOR + popcount and the five-row verification pass, gate/up shape
+        gv = {}
+        us, gb = bench_gemv_product(lb, synth, torch, np, 1, 34816, 5120, 16, "sign", args.gemm_reps)
+        log(f"XOR+popcount GEMV 34816x5120 binary: {us:.1f} us per product, {gb:.0f} GB/s")
+        gv["xor_popcount_binary_34816x5120"] = {"us_per_product": round(us, 2), "gb_s": round(gb, 1),
+                                                "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
+        us, gb = bench_gemv_product(lb, synth, torch, np, 2, 34816, 5120, 8, "m5", args.gemm_reps)
+        log(f"M=5 ternary 34816x5120: {us:.1f} us per product, {gb:.0f} GB/s")
+        gv["m5_ternary_34816x5120"] = {"us_per_product": round(us, 2), "gb_s": round(gb, 1),
+                                       "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
+        out["config"]["gemv_products"] = gv
         # data-free quantizer front end on the gate/up matrix (rotated, ternary)
         qms, qgbs = bench_quantizer(lb, synth, torch, np, 34816, 5120, args.gemm_reps)
         log(f"quantizer 34816x5120: {qms:.3f} ms, {qgbs:.0f} GB/s")

@@ -163,8 +163,9 @@ int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
 /* Batch-1 product y[n] = sum_k W[n][k] * x[k] for n < N.
  *   x_dtype F32 / BF16: x holds K values.
  *   x_dtype I8: x holds K int8 q; the result is multiplied by x_scale.
- *   x_dtype SIGN1 (binary weights only): x holds K/8 bytes of sign bits;
- *     the result is multiplied by x_scale (alpha).
+ *   x_dtype SIGN1 (binary weights only, K <= 393216): x holds K/8 bytes of
+ *     sign bits; the result is multiplied by x_scale (alpha).  Runs as one
+ *     launch without the workspace.
  *   y_dtype F32 or BF16 (round to nearest even).  y_dtype I32 is allowed
  *   only for x_dtype I8 / SIGN1 with pscales == NULL: y = exact integer
  *   sum_k code * q (or the signed bit agreement count), x_scale ignored.

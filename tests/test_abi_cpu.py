@@ -71,6 +71,8 @@ def test_gemv_validation_without_gpu():
     assert f(1, 16, 128, A16, None, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_NULL
     # sign activations only with binary weights
     assert f(2, 16, 128, A16, A16, lb.SIGN1, A16, 1.0, lb.F32, A16, None) == lb.E_UNSUPPORTED
+    # the sign words of a row must fit the kernel's 48 KiB of LDS
+    assert f(1, 16, 393216 + 128, A16, A16, lb.SIGN1, A16, 1.0, lb.F32, A16, None) == lb.E_SHAPE
     assert f(1, 16, 128, A4, A16, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_ALIGN
     assert f(1, 16, 128, A16, A16, lb.BF16, A4, 1.0, lb.F32, A16, None) == lb.E_ALIGN
     assert f(1, 16, 128, A16, A16, lb.BF16, A16, 1.0, lb.F32, A1, None) == lb.E_ALIGN

@@ -118,7 +118,8 @@ def test_int8_activations(fmt, N, K):
     assert_within(yf.cpu().numpy()[None], yref, absY, what="i8 float")
 
 
-@pytest.mark.parametrize("N,K", [(37, 384), (256, 1024), (5120, 5120)])
+@pytest.mark.parametrize("N,K", [(37, 384), (256, 1024), (5120, 5120), (300, 17408), (16, 128),
+                                 (48, 640), (16, 393216)])
 def test_sign_activations_xor_popcount(N, K):
     codes, scales, pc, ps = make(1, N, K, tid=51)
     xb = synth.sign_bits(SEED, 53, 1, K)

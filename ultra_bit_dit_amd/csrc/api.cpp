@@ -205,19 +205,14 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* p
     return LOWBIT_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   if (x_dtype == LOWBIT_SIGN1) {
-    const int64_t G = K / kGroup, GQ = cdiv(G, 4);
-    void* ws = nullptr;
-    int rc = workspace(s, kCounterBytes + (size_t)GQ * 16 * 4, &ws);
-    if (rc) return rc;
-    uint32_t* xw = (uint32_t*)((uint8_t*)ws + kCounterBytes);
-    if (launch_stage_sign(1, K, (const uint8_t*)x, xw, s) != hipSuccess) return LOWBIT_E_HIP;
+    if (K > kSignMaxK) return LOWBIT_E_SHAPE;  // the row's sign words live in LDS
     SignArgs a;
     a.N = N;
     a.K = K;
     a.M = 1;
     a.pcodes = pcodes;
     a.pscales = (const uint16_t*)pscales;
-    a.xw = xw;
+    a.xbits = (const uint8_t*)x;
     a.alpha = x_scale;
     a.ykind = y_dtype;
     a.y = y;

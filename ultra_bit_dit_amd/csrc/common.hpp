@@ -56,9 +56,6 @@ hipError_t launch_unpack(int fmt, int64_t N, int64_t K, const void* pcodes,
 hipError_t launch_quantize_i8(int64_t M, int64_t K, const uint16_t* X, int8_t* Q,
                               float* sx, hipStream_t s);
 
-// sign bits permuted into the binary word order: M * G * 4 words
-hipError_t launch_stage_sign(int64_t M, int64_t K, const uint8_t* xbits, uint32_t* xw,
-                             hipStream_t s);
 
 // Workspace of the fused GEMV: a fixed block of zero-initialised counters
 // (self-resetting: every launch leaves them zero) followed by the staged
@@ -66,6 +63,9 @@ hipError_t launch_stage_sign(int64_t M, int64_t K, const uint8_t* xbits, uint32_
 constexpr int64_t kCounterWords = 65536;
 constexpr int64_t kCounterBytes = kCounterWords * 4;
 constexpr int64_t kMaxRowGroups = kCounterWords - 16;  // row groups of 64 rows
+// batch-1 sign activations: the reordered sign words of a row (K / 8 bytes)
+// are built in 48 KiB of LDS per workgroup
+constexpr int64_t kSignMaxK = 48 * 1024 * 8;
 
 struct GemvArgs {
   int fmt;
@@ -105,7 +105,7 @@ struct SignArgs {
   int64_t N, K, M;
   const void* pcodes;
   const uint16_t* pscales;
-  const uint32_t* xw;
+  const uint8_t* xbits;  // K sign bits (the kernel reorders them into the binary word order)
   float alpha;
   int ykind;
   void* y;

@@ -1467,39 +1467,87 @@ namespace {
 struct SArgs {
   const void* pcodes;
   const uint16_t* pscales;
-  const uint32_t* xw;
+  const uint8_t* xbits;  // K sign bits, bit k % 8 of byte k / 8
   void* y;
-  int64_t N, G, GQ;
+  int64_t N, K, G, GQ;
   float alpha;
 };
+
+// Sign-bit word of (group g, quarter q) in the binary weight word order:
+// slot i of the quarter is k = 128 g + KMAP(q, i), i.e. the two 16-bit runs
+// at bit offsets base and base + 32 of the group (base = 64 (q & 1) +
+// 16 (q >> 1)); bit b of the word holds slot 8 (3 - (b & 3)) + (b >> 2),
+// a 4 x 8 bit transpose of the slot-ordered word.
+__device__ inline uint32_t sign_word(const uint8_t* xbits, int64_t g, int q) {
+  const int base = 64 * (q & 1) + 16 * (q >> 1);
+  const uint8_t* gp = xbits + g * (kGroup / 8);
+  const uint32_t v = (uint32_t)*(const uint16_t*)(gp + base / 8) |
+                     ((uint32_t)*(const uint16_t*)(gp + base / 8 + 4) << 16);
+  uint32_t w = 0;
+#pragma unroll
+  for (int a = 0; a < 8; a++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) w |= ((v >> (8 * (3 - c) + a)) & 1u) << (4 * a + c);
+  return w;
+}
+
+constexpr int kSignQB = 8;  // quads of codes a wave holds in registers per round
 
 template <int YK>
 __global__ __launch_bounds__(1024) void gemv_sign(SArgs a) {
   __shared__ float red_f[kMaxWaves][64];
   __shared__ int red_i[kMaxWaves][64];
+  extern __shared__ __align__(16) uint32_t xw_lds[];  // [GQ][4 quarters][4 groups]
   const int L = threadIdx.x & 63, w = threadIdx.x >> 6, S = blockDim.x >> 6;
   const int r = L & 15, q = L >> 4;
   const int64_t rb = blockIdx.x;
   const int64_t q0 = (a.GQ * w) / S, q1 = (a.GQ * (w + 1)) / S;
-  const uint4* pc4 = (const uint4*)a.pcodes;
+  const u4* pc4 = (const u4*)a.pcodes;
   const uint2* ps2 = (const uint2*)a.pscales;
-  const uint4* xw4 = (const uint4*)a.xw;
+  // the first round's codes and scales go out before the row's sign words
+  // are built (they do not depend on x)
+  u4 cw[kSignQB];
+  uint2 sc[kSignQB];
+  auto load_round = [&](int64_t base) {
+#pragma unroll
+    for (int i = 0; i < kSignQB; i++) {
+      const int64_t gq = min<int64_t>(base + i, q1 - 1);  // clamped into the wave's range
+      cw[i] = __builtin_nontemporal_load(&pc4[(rb * a.GQ + gq) * 64 + L]);
+      sc[i] = a.pscales ? ps2[(rb * a.GQ + gq) * 16 + r] : make_uint2(0x3C003C00u, 0x3C003C00u);
+    }
+  };
+  if (q0 < q1) load_round(q0);
+  // this row's sign words, built once per workgroup
+  for (int64_t i = threadIdx.x; i < a.GQ * 16; i += blockDim.x) {
+    const int t = (int)(i & 3), qq = (int)((i >> 2) & 3);
+    const int64_t g = 4 * (i >> 4) + t;
+    xw_lds[i] = g < a.G ? sign_word(a.xbits, g, qq) : 0u;
+  }
+  __syncthreads();
+  const uint4* xw4 = (const uint4*)xw_lds;
   float acc = 0.f;
   int iacc = 0;
-  for (int64_t gq = q0; gq < q1; gq++) {
-    uint4 cw = pc4[(rb * a.GQ + gq) * 64 + L];
-    uint4 xv = xw4[gq * 4 + q];
-    uint2 sc = a.pscales ? ps2[(rb * a.GQ + gq) * 16 + r] : make_uint2(0x3C003C00u, 0x3C003C00u);
-    const int ng = (int)min<int64_t>(4, a.G - 4 * gq);
-    uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
-    uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w};
-    uint32_t ss[4] = {sc.x & 0xFFFF, sc.x >> 16, sc.y & 0xFFFF, sc.y >> 16};
+  // up to kSignQB quads per round: every load of a round is issued before
+  // any of it is used
+  for (int64_t base = q0; base < q1; base += kSignQB) {
+    if (base != q0) load_round(base);
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      if (t < ng) {
-        int d = 32 - 2 * __popc(wv[t] ^ xx[t]);
-        iacc += d;
-        acc = fmaf(f16_bits_to_f32(ss[t]), (float)d, acc);
+    for (int i = 0; i < kSignQB; i++) {
+      const int64_t gq = base + i;
+      if (gq < q1) {
+        const uint4 xv = xw4[gq * 4 + q];
+        const int ng = (int)min<int64_t>(4, a.G - 4 * gq);
+        const uint32_t wv[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+        const uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t ss[4] = {sc[i].x & 0xFFFF, sc[i].x >> 16, sc[i].y & 0xFFFF, sc[i].y >> 16};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          if (t < ng) {
+            const int d = 32 - 2 * __popc(wv[t] ^ xx[t]);
+            iacc += d;
+            acc = fmaf(f16_bits_to_f32(ss[t]), (float)d, acc);
+          }
+        }
       }
     }
   }
@@ -1538,17 +1586,20 @@ hipError_t launch_gemv_sign(const SignArgs& g, hipStream_t s) {
   int64_t NB = cdiv(g.N, 16), G = g.K / kGroup;
   k.pcodes = g.pcodes;
   k.pscales = g.pscales;
-  k.xw = g.xw;
+  k.xbits = g.xbits;
   k.y = g.y;
   k.N = g.N;
+  k.K = g.K;
   k.G = G;
   k.GQ = cdiv(G, 4);
   k.alpha = g.alpha;
+  const size_t lds = (size_t)k.GQ * 16 * 4;  // the sign words of the whole row
+  if (g.K > kSignMaxK || lds > 48 * 1024) return hipErrorInvalidValue;
   int S = pick_waves(NB, k.GQ);
   dim3 grid((unsigned)NB), block(64 * S);
-  if (g.ykind == YK_F32) hipLaunchKernelGGL(gemv_sign<YK_F32>, grid, block, 0, s, k);
-  else if (g.ykind == YK_BF16) hipLaunchKernelGGL(gemv_sign<YK_BF16>, grid, block, 0, s, k);
-  else hipLaunchKernelGGL(gemv_sign<YK_I32>, grid, block, 0, s, k);
+  if (g.ykind == YK_F32) hipLaunchKernelGGL(gemv_sign<YK_F32>, grid, block, lds, s, k);
+  else if (g.ykind == YK_BF16) hipLaunchKernelGGL(gemv_sign<YK_BF16>, grid, block, lds, s, k);
+  else hipLaunchKernelGGL(gemv_sign<YK_I32>, grid, block, lds, s, k);
   return hipGetLastError();
 }
 

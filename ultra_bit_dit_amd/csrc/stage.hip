@@ -1,30 +1,11 @@
-// Activation preparation kernels that run as their own launches: sign-bit
-// reordering for the XOR + popcount path, and per-row absmax int8
-// quantization.  (fp8 split staging for the MFMA path runs inside the GEMV
-// launch, see gemv.hip.)
+// Activation preparation that runs as its own launch: per-row absmax int8
+// quantization.  (fp8 split staging for the MFMA path and the sign-bit
+// reordering of the XOR + popcount path run inside the GEMV launch, see
+// gemv.hip.)
 #include "common.hpp"
 
 namespace lowbit {
 namespace {
-
-// sign bits -> binary word order; xw[((m * GQ + gq) * 4 + q) * 4 + g % 4]
-__global__ void stage_sign(int64_t M, int64_t K, int64_t G, int64_t GQ,
-                           const uint8_t* __restrict__ xbits, uint32_t* __restrict__ xw) {
-  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= M * GQ * 16) return;
-  int t = tid & 3, q = (tid >> 2) & 3;
-  int64_t gq = (tid >> 4) % GQ, m = (tid >> 4) / GQ;
-  int64_t g = 4 * gq + t;
-  uint32_t w = 0;
-  if (g < G) {
-    const uint8_t* row = xbits + m * (K / 8);
-    for (int b = 0; b < 32; b++) {
-      int64_t k = g * kGroup + kmap(q, bin_slot(b));
-      w |= (uint32_t)((row[k >> 3] >> (k & 7)) & 1) << b;
-    }
-  }
-  xw[tid] = w;
-}
 
 // per-row absmax int8 quantization, one block per row
 __global__ void quantize_i8(int64_t K, const uint16_t* __restrict__ X, int8_t* __restrict__ Q,
@@ -56,14 +37,6 @@ __global__ void quantize_i8(int64_t K, const uint16_t* __restrict__ X, int8_t* _
 }
 
 }  // namespace
-
-hipError_t launch_stage_sign(int64_t M, int64_t K, const uint8_t* xbits, uint32_t* xw,
-                             hipStream_t s) {
-  int64_t G = K / kGroup, GQ = cdiv(G, 4), n = M * GQ * 16;
-  hipLaunchKernelGGL(stage_sign, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, M, K, G, GQ,
-                     xbits, xw);
-  return hipGetLastError();
-}
 
 hipError_t launch_quantize_i8(int64_t M, int64_t K, const uint16_t* X, int8_t* Q, float* sx,
                               hipStream_t s) {
