@@ -261,6 +261,23 @@ def bench_decode(args, lb, synth, torch, np):
     modes_out = {m: {"ms_per_step": round(v[0], 4), "gb_s": round(step_bytes / v[0] / 1e6, 1),
                      "tok_s": round(1000.0 / v[0], 2), "launches_per_step": v[1]}
                  for m, v in res.items()}
+    if args.verify_rows > 1:
+        # one pass of `verify_rows` activation rows through every product of
+        # the step (checking verify_rows - 1 drafted tokens and the next one)
+        M = args.verify_rows
+        xv = [torch.from_numpy(synth.normal_bf16(SEED, 950 + j, M, K).view(np.int16)).cuda()
+              .view(torch.bfloat16) for j, (_, _, K) in enumerate(MATS)]
+        yv = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in MATS]
+        stages = [(fmt, N, K, W[l][j][0], W[l][j][1], xv[j], yv[j], 0)
+                  for l in range(layers) for j, (name, N, K) in enumerate(MATS)]
+        ch = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32, rows=M)
+        vms = time_region(torch, stream, lambda: ch.run(stream), args.steps, args.warmup)
+        ch.close()
+        log(f"verify pass, {M} rows: {vms:.3f} ms, {step_bytes / vms / 1e6:.0f} GB/s, "
+            f"{M * 1000 / vms:.1f} tokens checked/s")
+        modes_out["verify_pass"] = {"rows": M, "ms_per_pass": round(vms, 4),
+                                    "gb_s": round(step_bytes / vms / 1e6, 1),
+                                    "tokens_per_s": round(M * 1000.0 / vms, 1)}
     del W
     torch.cuda.synchronize()
     return ms, gbs, step_bytes, roof, head, modes_out
@@ -304,7 +321,7 @@ def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
     packed bytes than the 256 MB last-level cache, so every launch streams
     from HBM), the launches replayed as one HIP graph.  mode "sign": batch-1
     binary weights x sign activations (XOR + popcount, lowbit_gemv SIGN1);
-    "m5": five bf16 activation rows (small-M verification pass, lowbit_gemm).
+    "m<M>": M bf16 activation rows (M = 5: the small-M verification pass).
     Returns (us per product, GB/s of packed weight bytes)."""
     mats = build_mats(lb, synth, fmt, SEED + 10, 0, [("w", N, K)] * copies)
     if mode == "sign":
@@ -315,13 +332,17 @@ def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
             for pc, ps in mats:
                 lb.gemv(1, N, K, pc, ps, xb, x_scale=1.0, y=y, x_dtype=lb.SIGN1)
     else:
-        X = torch.from_numpy(synth.normal_bf16(SEED + 10, 851, 5, K).view(np.int16)).cuda() \
+        M = int(mode[1:])  # "m<rows>"
+        X = torch.from_numpy(synth.normal_bf16(SEED + 10, 851, M, K).view(np.int16)).cuda() \
             .view(torch.bfloat16)
-        Y = torch.empty((5, N), dtype=torch.float32, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
         def one():
             for pc, ps in mats:
-                lb.gemm(fmt, 5, N, K, pc, ps, X, Y=Y)
+                if M == 1:
+                    lb.gemv(fmt, N, K, pc, ps, X[0], y=Y[0])
+                else:
+                    lb.gemm(fmt, M, N, K, pc, ps, X, Y=Y)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         one()  # eager warm-up (allocates the workspace)
@@ -403,6 +424,8 @@ def main():
     ap.add_argument("--modes", default="chain,chain_dep,separate",
                     help="decode-step modes to time, headline first (chain, chain_dep, separate)")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--verify-rows", type=int, default=5,
+                    help="rows of the small-M verification pass through the whole step (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the "

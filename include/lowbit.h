@@ -214,10 +214,12 @@ typedef struct lowbit_gemv_stage {
   int64_t N, K;         /* W is N x K, K % 128 == 0                                */
   const void* pcodes;   /* packed codes (16-byte aligned)                          */
   const void* pscales;  /* packed fp16 scales (16-byte aligned)                    */
-  const void* x;        /* K activations of the chain's x_dtype (16-byte aligned)  */
-  void* y;              /* N outputs of the chain's y_dtype (4-byte aligned)        */
-  int wait_prev;        /* 1: read x only after stage i-1 is complete (then K times
-                           the x element size must stay below 2^31 bytes)          */
+  const void* x;        /* rows x K activations of the chain's x_dtype (row-major,
+                           16-byte aligned; rows = 1 unless created with rows)      */
+  void* y;              /* rows x N outputs of the chain's y_dtype (4-byte aligned) */
+  int wait_prev;        /* 1: read x only after stage i-1 is complete (then rows
+                           times K times the x element size must stay below 2^31
+                           bytes)                                                  */
   int epilogue;         /* LOWBIT_EPI_NONE or LOWBIT_EPI_SILU_MUL (see below)      */
 } lowbit_gemv_stage;
 
@@ -243,6 +245,16 @@ typedef struct lowbit_chain lowbit_chain; /* opaque */
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_HIP, E_NOMEM. */
 int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dtype,
                         int y_dtype, lowbit_chain** chain);
+
+/* The same with `rows` activation rows per product (1 <= rows <= 8 for BF16 x,
+ * <= 4 for F32 x; every stage takes rows x K activations and writes rows x N
+ * outputs): a small-M chain such as one pass that verifies rows - 1 drafted
+ * tokens and the next one through every product of a model (speed section
+ * of the Japanese Bonsai 27B article: drafts are checked by the target model
+ * in one pass).  The SiLU-mul epilogue needs rows == 1.  Errors as
+ * lowbit_chain_create (E_SHAPE for rows out of range). */
+int lowbit_chain_create_rows(int n_stages, const lowbit_gemv_stage* stages, int64_t rows,
+                             int x_dtype, int y_dtype, lowbit_chain** chain);
 
 /* Run every stage once, asynchronously on `stream`.  Runs of one chain must
  * not overlap (they share its counters); run it on one stream at a time. */

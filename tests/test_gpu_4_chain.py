@@ -208,3 +208,73 @@ def test_chain_epilogue_rejects():
     with pytest.raises(lb.LowbitError) as e:
         lb.Chain([(1, 64, 256, pc, ps, x, y, 0, 7)])
     assert e.value.status == lb.E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("wait", [0, 1])
+@pytest.mark.parametrize("rows", [2, 5, 8])
+def test_chain_rows(fmt, wait, rows):
+    """Chains of small-M products (every stage takes rows x K activations):
+    each row of each stage within the oracle tolerance, on ragged N, K from
+    one group to 136 groups, and on repeated runs."""
+    shapes = [(640, 1024), (100, 5120), (256, 17408), (48, 128), (3000, 2560)]
+    mats, xs, ys, refs = [], [], [], []
+    for j, (N, K) in enumerate(shapes):
+        codes, scales, pc, ps = make(fmt, N, K, tid=500 + 2 * j)
+        mats.append((pc, ps))
+        xh = synth.normal_bf16(SEED, 530 + j, rows, K)
+        xs.append(dev(xh.view(np.int16)).view(torch.bfloat16))
+        ys.append(torch.full((rows, N), float("nan"), device="cuda"))
+        refs.append(O.matmul(codes, scales, O.X_BF16, xh))
+    stages = [(fmt, N, K, mats[j][0], mats[j][1], xs[j], ys[j], wait)
+              for j, (N, K) in enumerate(shapes)]
+    chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32, rows=rows)
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        for j, (N, K) in enumerate(shapes):
+            yref, absY = refs[j]
+            assert_within(ys[j].cpu().numpy(), yref, absY, what=f"stage {j} run {rep}")
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
+def test_chain_rows_dependent_f32():
+    """rows = 3, f32 activations: stage i reads stage i-1's [3][N] output."""
+    fmt, rows = 2, 3
+    dims = [1024, 640, 5120, 384]
+    mats, codes, scales = [], [], []
+    for j in range(len(dims) - 1):
+        K, N = dims[j], dims[j + 1]
+        c, s, pc, ps = make(fmt, N, K, tid=560 + 2 * j)
+        mats.append((pc, ps))
+        codes.append(c)
+        scales.append(s)
+    x0 = synth.normal_f32(SEED, 590, rows, dims[0])
+    bufs = [dev(x0)] + [torch.full((rows, d), float("nan"), device="cuda") for d in dims[1:]]
+    stages = [(fmt, dims[j + 1], dims[j], mats[j][0], mats[j][1], bufs[j], bufs[j + 1], 1)
+              for j in range(len(dims) - 1)]
+    chain = lb.Chain(stages, x_dtype=lb.F32, y_dtype=lb.F32, rows=rows)
+    chain.run()
+    torch.cuda.synchronize()
+    outs = [b.cpu().numpy() for b in bufs]
+    for j in range(len(dims) - 1):
+        yref, absY = O.matmul(codes[j], scales[j], O.X_F32, outs[j].astype(np.float32))
+        assert_within(outs[j + 1], yref, absY, what=f"stage {j}")
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
+def test_chain_rows_rejects():
+    _, _, pc, ps = make(2, 64, 256, tid=600)
+    x = torch.zeros((9, 256), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((9, 64), device="cuda")
+    for rows, xdt in ((9, lb.BF16), (5, lb.F32), (0, lb.BF16)):
+        with pytest.raises(lb.LowbitError) as e:
+            lb.Chain([(2, 64, 256, pc, ps, x, y, 0)], x_dtype=xdt, rows=rows)
+        assert e.value.status == lb.E_SHAPE
+    with pytest.raises(lb.LowbitError) as e:  # the SiLU-mul epilogue is single-row
+        lb.Chain([(2, 64, 256, pc, ps, x, y, 0, lb.EPI_SILU_MUL)], rows=2)
+    assert e.value.status == lb.E_SHAPE

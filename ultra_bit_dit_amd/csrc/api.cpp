@@ -252,13 +252,14 @@ struct lowbit_chain {
   void* plan;
 };
 
-int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dtype, int y_dtype,
-                        lowbit_chain** chain) {
+int lowbit_chain_create_rows(int n_stages, const lowbit_gemv_stage* stages, int64_t rows,
+                             int x_dtype, int y_dtype, lowbit_chain** chain) {
   if (!stages || !chain) return LOWBIT_E_NULL;
   *chain = nullptr;
   if (n_stages < 1) return LOWBIT_E_SHAPE;
   if (x_dtype != LOWBIT_F32 && x_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
+  if (rows < 1 || rows > max_small_m(x_dtype)) return LOWBIT_E_SHAPE;
   const int fmt = stages[0].fmt;
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   std::vector<ChainStage> st(n_stages);
@@ -268,21 +269,26 @@ int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dty
     if (!g.pcodes || !g.pscales || !g.x || !g.y) return LOWBIT_E_NULL;
     if (!shape_ok(g.N, g.K) || cdiv(g.N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
     // a waiting stage reads x through a buffer descriptor (32-bit byte offsets)
-    if (i > 0 && g.wait_prev && g.K * (x_dtype == LOWBIT_F32 ? 4 : 2) > INT32_MAX)
+    if (i > 0 && g.wait_prev && rows * g.K * (x_dtype == LOWBIT_F32 ? 4 : 2) > INT32_MAX)
       return LOWBIT_E_SHAPE;
     if (!aligned(g.pcodes, 16) || !aligned(g.pscales, 16) || !aligned(g.x, 16) || !aligned(g.y, 4))
       return LOWBIT_E_ALIGN;
     if (g.epilogue != LOWBIT_EPI_NONE && g.epilogue != LOWBIT_EPI_SILU_MUL) return LOWBIT_E_UNSUPPORTED;
-    if (g.epilogue == LOWBIT_EPI_SILU_MUL && g.N % 16 != 0) return LOWBIT_E_SHAPE;
+    if (g.epilogue == LOWBIT_EPI_SILU_MUL && (g.N % 16 != 0 || rows != 1)) return LOWBIT_E_SHAPE;
     st[i] = ChainStage{fmt, g.N, g.K, g.pcodes, (const uint16_t*)g.pscales, g.x, g.y,
                        i > 0 && g.wait_prev ? 1 : 0, g.epilogue};
   }
   void* plan = nullptr;
-  hipError_t e = chain_create(st.data(), n_stages, x_dtype, y_dtype, &plan);
+  hipError_t e = chain_create(st.data(), n_stages, rows, x_dtype, y_dtype, &plan);
   if (e == hipErrorOutOfMemory) return LOWBIT_E_NOMEM;
   if (e != hipSuccess) return LOWBIT_E_HIP;
   *chain = new lowbit_chain{plan};
   return LOWBIT_OK;
+}
+
+int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dtype, int y_dtype,
+                        lowbit_chain** chain) {
+  return lowbit_chain_create_rows(n_stages, stages, 1, x_dtype, y_dtype, chain);
 }
 
 int lowbit_chain_run(lowbit_chain* chain, void* stream) {

@@ -96,7 +96,7 @@ struct ChainStage {
   int wait_prev;
   int epi;  // 1: SiLU-mul epilogue (N fused gate/up rows -> N/2 outputs)
 };
-hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void** plan);
+hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int ykind, void** plan);
 hipError_t chain_run(void* plan, hipStream_t s);
 hipError_t chain_status(void* plan, int* failed_waits);
 void chain_destroy(void* plan);

@@ -694,17 +694,25 @@ __device__ __attribute__((always_inline)) inline void stage_convert_rounds(const
   if constexpr (K + 1 < kStageRounds) stage_convert_rounds<R, XK, K + 1>(a, it, l, x);
 }
 
-template <int R, int XK>
+template <int R, int XK, int SB>
 __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, const Item& it,
                                                                 const Lds& l, XRegs& x, bool coh) {
   stage_convert_rounds<R, XK>(a, it, l, x);
-  // remaining rounds (small-M products with long slices), loaded and converted in turn
+  // remaining rounds (small-M products with long slices): SB rounds' loads
+  // go out together, then their conversions
   const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
-  for (int64_t rd = kStageRounds; rd < rounds; rd++) {
-    uint4 r0, r1;
-    if (coh) stage_load1<XK, true>(a, it.q0, it.nq, rd, r0, r1);
-    else stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
-    stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, l.xa, l.xe);
+  for (int64_t rd = kStageRounds; rd < rounds; rd += SB) {
+    uint4 r0[SB], r1[SB];
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      if (rd + u < rounds) {
+        if (coh) stage_load1<XK, true>(a, it.q0, it.nq, rd + u, r0[u], r1[u]);
+        else stage_load1<XK, false>(a, it.q0, it.nq, rd + u, r0[u], r1[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SB; u++)
+      if (rd + u < rounds) stage_convert1<R, XK>(a, it.q0, it.nq, rd + u, r0[u], r1[u], l.xa, l.xe);
   }
 }
 
@@ -713,7 +721,7 @@ __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, 
 // are device-coherent; WAIT: the weight loads go out first, then the
 // workgroup waits until `wait_cnt` reaches `wait_target` -- the previous
 // product is complete -- and reads its activations with coherent loads).
-template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT>
+template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
 __device__ __attribute__((always_inline)) inline void gemv_item(
     const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
     uint32_t* err) {
@@ -753,7 +761,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     __syncthreads();
     stage_load_rounds<XK, true>(a, it, xr);
   }
-  stage_all<R, XK>(a, it, l, xr, WAIT);
+  stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
   __syncthreads();
 
   float acc[MX];
@@ -764,8 +772,8 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     iacc[j] = 0;
   }
   if (it.live) {
-    if constexpr (CHAIN) {
-      // chains: one activation row with scales (the single-row routine)
+    if constexpr (CHAIN && ONE) {
+      // chains of one activation row, with scales: the single-row routine
       const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
       const uint8_t* arow = l.xa + (lg * R + rr) * 32;
       const uint8_t* erow = l.xe + (lg * R + rr) * 4;
@@ -852,8 +860,10 @@ __device__ __attribute__((always_inline)) inline FArgs load_args(FArgsTab t, int
   return a;
 }
 
-template <int FMT, int XK, int YK, int QM>
+// MR: several activation rows per product (lane group lg keeps 4 / R rows)
+template <int FMT, int XK, int YK, int QM, bool MR>
 __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_chain(ChainArgs c) {
+  constexpr int MX = MR ? 4 / (XK == XK_F32 ? kSplitF32 : kSplitBF16) : 1;
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab first = (I64Tab)c.first;
@@ -866,10 +876,10 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     const bool wt = s > 0 && waitf[s] != 0;
     __syncthreads();  // the previous item's LDS reads are over
     if (wt)
-      gemv_item<FMT, XK, 1, YK, QM, true, true>(a, i - first[s], smem, c.done + 256 * (s - 1),
-                                                (uint32_t)(first[s] - first[s - 1]), c.err);
+      gemv_item<FMT, XK, MX, YK, QM, true, true, !MR>(a, i - first[s], smem, c.done + 256 * (s - 1),
+                                                      (uint32_t)(first[s] - first[s - 1]), c.err);
     else
-      gemv_item<FMT, XK, 1, YK, QM, true, false>(a, i - first[s], smem, nullptr, 0u, c.err);
+      gemv_item<FMT, XK, MX, YK, QM, true, false, !MR>(a, i - first[s], smem, nullptr, 0u, c.err);
     __builtin_amdgcn_s_waitcnt(0);  // this item's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -914,9 +924,16 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 // binary kernel with bf16 activations is held to 128 registers (one MFMA
 // group in flight per step) to run four workgroups per CU and keep as many
 // bytes in flight.
-template <int FMT, int XK, int YK, int QM>
-__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 ? 4 : 2))) void gemv_stream(ChainArgs c) {
+//
+// MR: chains of small-M products (M activation rows, M R <= 16, all stages
+// alike, e.g. a verification pass over drafted tokens): the slice images
+// hold M R rows of A, the quads go through the generic quad routine, and
+// lane group lg keeps rows (4 / R) lg .. (4 / R) lg + 4 / R - 1 of its
+// output row.
+template <int FMT, int XK, int YK, int QM, bool MR>
+__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 && !MR ? 4 : 2))) void gemv_stream(ChainArgs c) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr int MX = MR ? 4 / R : 1;  // accumulator rows per lane
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab ufirst = (I64Tab)c.ufirst;
@@ -966,9 +983,13 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // writes its share of slice j+1 part-way through slice j, so waves are
   // only ever held back by a wave more than about one slice behind (there is
   // no workgroup barrier in the loop).
-  constexpr int XR = (QM * 16 * R * 33 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
+  constexpr int MAX_MA = MR ? 16 : R;  // rows of A an image may hold
+  constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
   constexpr int kWriteAfter = 3;  // quads computed before the next image is written
-  const int64_t bufsz = (int64_t)QM * 16 * R * 33;
+  static_assert(QM > kWriteAfter, "the next image is written part-way through a slice");
+  const int64_t bufsz = (int64_t)QM * 16 * MAX_MA * 33;
+  // rows of A of every stage (one M per chain)
+  const int64_t MAc = MR ? args[0].MA : R;
   auto xbuf = [&](uint32_t b) { return smem + b * bufsz; };
   Lds lfix;
   lfix.zblk = smem + 2 * bufsz;
@@ -999,10 +1020,10 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       const int64_t piece = min<int64_t>((int64_t)k * 64 * kMaxW + tid, nb - 1);
       return (const uint4*)(c.xst + xoff[sidx] + kslice * slice_stride<FMT>(f)) + piece;
     };
-    // a slice image travels in up to six 16-byte registers per thread (named
+    // a slice image travels in up to nine 16-byte registers per thread (named
     // registers, not an array, so that they never live in scratch memory)
-    uint4 x0, x1, x2, x3, x4, x5;
-    static_assert(XR <= 6, "slice image larger than six 16-byte pieces per thread");
+    uint4 x0, x1, x2, x3, x4, x5, x6, x7, x8;
+    static_assert(XR <= 9, "slice image larger than nine 16-byte pieces per thread");
 #define XLD(F, SI, KS_, NQ)                                                                  \
   {                                                                                          \
     x0 = *xsrc(F, SI, KS_, NQ, 0);                                                           \
@@ -1011,10 +1032,13 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     if (XR > 3) x3 = *xsrc(F, SI, KS_, NQ, 3);                                               \
     if (XR > 4) x4 = *xsrc(F, SI, KS_, NQ, 4);                                               \
     if (XR > 5) x5 = *xsrc(F, SI, KS_, NQ, 5);                                               \
+    if (XR > 6) x6 = *xsrc(F, SI, KS_, NQ, 6);                                               \
+    if (XR > 7) x7 = *xsrc(F, SI, KS_, NQ, 7);                                               \
+    if (XR > 8) x8 = *xsrc(F, SI, KS_, NQ, 8);                                               \
   }
 #define XPUT(DST, NQ)                                                                        \
   {                                                                                          \
-    const int64_t nb_ = (int64_t)(NQ) * 16 * R * 33 / 16;                                    \
+    const int64_t nb_ = (int64_t)(NQ) * 16 * MAc * 33 / 16;                                  \
     uint4* d_ = (uint4*)(DST);                                                               \
     constexpr int T_ = 64 * kMaxW;                                                           \
     if (tid < nb_) d_[tid] = x0;                                                             \
@@ -1023,6 +1047,9 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     if (XR > 3 && 3 * T_ + tid < nb_) d_[3 * T_ + tid] = x3;                                 \
     if (XR > 4 && 4 * T_ + tid < nb_) d_[4 * T_ + tid] = x4;                                 \
     if (XR > 5 && 5 * T_ + tid < nb_) d_[5 * T_ + tid] = x5;                                 \
+    if (XR > 6 && 6 * T_ + tid < nb_) d_[6 * T_ + tid] = x6;                                 \
+    if (XR > 7 && 7 * T_ + tid < nb_) d_[7 * T_ + tid] = x7;                                 \
+    if (XR > 8 && 8 * T_ + tid < nb_) d_[8 * T_ + tid] = x8;                                 \
   }
     XLD(a, s, ks, it.nq);
     XPUT(xbuf(0), it.nq);
@@ -1070,8 +1097,14 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float acc[1] = {0.f};
-    float tot = 0.f;  // slices added in slice order, as the split-K reduction does
+    float acc[MX], tot[MX];  // tot: slices added in slice order, as the split-K reduction does
+    int iacc[MX];
+#pragma unroll
+    for (int m = 0; m < MX; m++) {
+      acc[m] = 0.f;
+      tot[m] = 0.f;
+      iacc[m] = 0;
+    }
     uint32_t j = 0;   // slice number of this workgroup
 
     auto wait_ge = [&](uint32_t* ctr, uint32_t target) {
@@ -1103,10 +1136,14 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       // ... down to 1 or 2: (j + 1) / 2 times)
       const uint32_t b = j & 1;
       if (j > 0) wait_ge(filled + b, 4u * ((j + 1) >> 1));
-      // this lane's A row and exponent word in the slice image
+      // this lane's A row and exponent word in the slice image (one row), or
+      // the image as the generic quad routine reads it (several rows)
       const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
       const uint8_t* arow = xbuf(b) + (lg * R + rr) * 32;
       const uint8_t* erow = xbuf(b) + it.nq * 16 * R * 32 + (lg * R + rr) * 4;
+      Lds lq = lfix;
+      lq.xa = xbuf(b);
+      lq.xe = xbuf(b) + (int64_t)it.nq * 16 * MAc * 32;
 #pragma unroll
       for (int q = 0; q < QM; q++) {
         if (q == kWriteAfter) {
@@ -1126,31 +1163,49 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
           const Item it2 = item_at<FMT>(a2, rg2, ks2);
           XLD(a2, s2, ks2, it2.nq);
         }
-        if (it.live && q < it.nq) quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
+        if (it.live && q < it.nq) {
+          if constexpr (!MR)
+            quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
+          else
+            quad_mfma<FMT, XK, MX, 2>(a, lq, q, qd[q], acc, iacc);
+        }
         load_quad_p<FMT>(pn, q, qd[q]);
       }
       // done reading slice j's image
       __builtin_amdgcn_s_waitcnt(0xC07F);
       if ((threadIdx.x & 63) == 0)
         __hip_atomic_fetch_add(consumed + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      tot = a.KS == 1 ? acc[0] : tot + acc[0];
-      acc[0] = 0.f;
+#pragma unroll
+      for (int m = 0; m < MX; m++) {
+        tot[m] = a.KS == 1 ? acc[m] : tot[m] + acc[m];
+        acc[m] = 0.f;
+      }
       if (ks == a.KS - 1) {
         // row group complete: one output per row (lanes of the first row of A)
         const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
         const int64_t n = 16 * it.rb + r;
-        if (a.epi) {
-          const float z = silu_mul_lanes(tot);
+        if constexpr (MR) {
+#pragma unroll
+          for (int jj = 0; jj < MX; jj++) {
+            const int64_t m = (int64_t)lg * (4 / R) + jj;
+            if (it.live && m < a.M && n < a.N) {
+              if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = tot[jj];
+              else ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(tot[jj]);
+            }
+            tot[jj] = 0.f;
+          }
+        } else if (a.epi) {
+          const float z = silu_mul_lanes(tot[0]);
           const int64_t nz = 8 * it.rb + r;
           if (it.live && lg == 0 && r < 8) {
             if (YK == YK_F32) ((float*)a.y)[nz] = z;
             else ((uint16_t*)a.y)[nz] = (uint16_t)bf16_rne(z);
           }
         } else if (it.live && lg == 0 && n < a.N) {
-          if (YK == YK_F32) ((float*)a.y)[n] = tot;
-          else ((uint16_t*)a.y)[n] = (uint16_t)bf16_rne(tot);
+          if (YK == YK_F32) ((float*)a.y)[n] = tot[0];
+          else ((uint16_t*)a.y)[n] = (uint16_t)bf16_rne(tot[0]);
         }
-        tot = 0.f;
+        tot[0] = 0.f;
       }
       if (!more) break;
       s = sn; u = un; rg = rgn; ks = ksn;
@@ -1191,6 +1246,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
 constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
+constexpr int kQuadsMulti = 4;     // quads per slice of the several-row streaming kernel
 
 Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0) {
   Plan p;
@@ -1296,21 +1352,28 @@ struct ChainPlan {
 };
 
 template <int FMT, int XK>
-const void* chain_kernel(int ykind, bool waits) {
+const void* chain_kernel(int ykind, bool waits, int64_t M) {
   constexpr int QM = FMT == 1 ? kQuadsBinary : kQuadsTernary;
+  const bool b16 = ykind == YK_BF16;
   if (waits) {
-    if (ykind == YK_BF16) return (const void*)gemv_chain<FMT, XK, YK_BF16, QM>;
-    return (const void*)gemv_chain<FMT, XK, YK_F32, QM>;
+    if (M == 1)
+      return b16 ? (const void*)gemv_chain<FMT, XK, YK_BF16, QM, false>
+                 : (const void*)gemv_chain<FMT, XK, YK_F32, QM, false>;
+    return b16 ? (const void*)gemv_chain<FMT, XK, YK_BF16, QM, true>
+               : (const void*)gemv_chain<FMT, XK, YK_F32, QM, true>;
   }
-  if (ykind == YK_BF16) return (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary>;
-  return (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary>;
+  if (M == 1)
+    return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false>
+               : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false>;
+  return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true>
+             : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMulti, true>;
 }
 
 }  // namespace
 
-hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void** out) {
+hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int ykind, void** out) {
   *out = nullptr;
-  if (S < 1) return hipErrorInvalidValue;
+  if (S < 1 || M < 1 || M * split_terms(xkind) > 16) return hipErrorInvalidValue;
   const int fmt = st[0].fmt;
   std::vector<FArgs> args(S);
   std::vector<int64_t> first(S + 1, 0);
@@ -1321,12 +1384,15 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   bool waits = false;
   for (int i = 1; i < S; i++) waits = waits || st[i].wait_prev != 0;
   // the streaming kernel keeps kQuadsTernary quads of every format in flight
-  const int quads = waits ? 0 : kQuadsTernary;
+  // (kQuadsMulti with several activation rows); its two image buffers are
+  // sized for the most rows of A it handles (R, or 16)
+  const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : kQuadsMulti);
   const int R = split_terms(xkind);
-  size_t lds = waits ? 0 : 2 * (size_t)kQuadsTernary * 16 * R * 33 + 48 + 1024 + 16;
+  size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : 16) * 33 + 48 + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
-    const Plan p = make_plan(fmt, st[i].N, st[i].K, 1, xkind, quads);
+    if (st[i].epi && M != 1) return hipErrorInvalidValue;
+    const Plan p = make_plan(fmt, st[i].N, st[i].K, M, xkind, quads);
     if (p.lds > 64 * 1024) return hipErrorInvalidValue;
     if (waits) lds = std::max(lds, p.lds);
     first[i + 1] = first[i] + p.NRG * p.KS;
@@ -1351,7 +1417,7 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
     k.G = p.G;
     k.GQ = p.GQ;
     k.GP = p.GP;
-    k.M = 1;
+    k.M = M;
     k.MA = p.MA;
     k.NB = p.NB;
     k.KS = p.KS;
@@ -1397,9 +1463,9 @@ hipError_t chain_create(const ChainStage* st, int S, int xkind, int ykind, void*
   if (e == hipSuccess) e = hipMemcpy(m + o_xo, xoff.data(), sizeof(int64_t) * S, hipMemcpyHostToDevice);
   if (e == hipSuccess) {
     const bool f32 = xkind == XK_F32;
-    if (fmt == 1) c->kernel = f32 ? chain_kernel<1, XK_F32>(ykind, waits) : chain_kernel<1, XK_BF16>(ykind, waits);
-    else if (fmt == 2) c->kernel = f32 ? chain_kernel<2, XK_F32>(ykind, waits) : chain_kernel<2, XK_BF16>(ykind, waits);
-    else if (fmt == 3) c->kernel = f32 ? chain_kernel<3, XK_F32>(ykind, waits) : chain_kernel<3, XK_BF16>(ykind, waits);
+    if (fmt == 1) c->kernel = f32 ? chain_kernel<1, XK_F32>(ykind, waits, M) : chain_kernel<1, XK_BF16>(ykind, waits, M);
+    else if (fmt == 2) c->kernel = f32 ? chain_kernel<2, XK_F32>(ykind, waits, M) : chain_kernel<2, XK_BF16>(ykind, waits, M);
+    else if (fmt == 3) c->kernel = f32 ? chain_kernel<3, XK_F32>(ykind, waits, M) : chain_kernel<3, XK_BF16>(ykind, waits, M);
     else e = hipErrorInvalidValue;
   }
   int per_cu = 0, cus = 0;

@@ -19,7 +19,8 @@ EPI_NONE, EPI_SILU_MUL = 0, 1
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
            "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
-           "lowbit_chain_create", "lowbit_chain_run", "lowbit_chain_status", "lowbit_chain_destroy",
+           "lowbit_chain_create", "lowbit_chain_create_rows", "lowbit_chain_run", "lowbit_chain_status",
+           "lowbit_chain_destroy",
            "lowbit_hbm_read_probe", "lowbit_quantize_weights", "lowbit_rotate_act")
 
 
@@ -60,6 +61,8 @@ def lib():
         L.lowbit_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i32, vp, vp, i32, vp, vp]
         L.lowbit_chain_create.argtypes = [i32, ctypes.POINTER(GemvStage), i32, i32,
                                           ctypes.POINTER(vp)]
+        L.lowbit_chain_create_rows.argtypes = [i32, ctypes.POINTER(GemvStage), i64, i32, i32,
+                                               ctypes.POINTER(vp)]
         L.lowbit_chain_run.argtypes = [vp, vp]
         L.lowbit_chain_status.argtypes = [vp, ctypes.POINTER(i32)]
         L.lowbit_chain_destroy.argtypes = [vp]
@@ -206,9 +209,11 @@ class Chain:
     """A planned chain of batch-1 products run as one persistent launch
     (lowbit_chain_*).  `stages` is a list of (fmt, N, K, pcodes, pscales, x, y,
     wait_prev[, epilogue]) with device tensors (epilogue EPI_NONE or
-    EPI_SILU_MUL); the tensors are kept referenced for the chain's lifetime."""
+    EPI_SILU_MUL); rows > 1: every x is [rows][K] and every y [rows][N]
+    (lowbit_chain_create_rows).  The tensors are kept referenced for the
+    chain's lifetime."""
 
-    def __init__(self, stages, x_dtype=BF16, y_dtype=F32):
+    def __init__(self, stages, x_dtype=BF16, y_dtype=F32, rows=1):
         self._keep = [t for st in stages for t in st[3:7]]
         arr = (GemvStage * len(stages))()
         for i, st in enumerate(stages):
@@ -217,8 +222,9 @@ class Chain:
             arr[i] = GemvStage(fmt, N, K, pc.data_ptr(), ps.data_ptr(), x.data_ptr(), y.data_ptr(),
                                int(wait), int(epi))
         h = ctypes.c_void_p()
-        _check("lowbit_chain_create",
-               lib().lowbit_chain_create(len(stages), arr, x_dtype, y_dtype, ctypes.byref(h)))
+        _check("lowbit_chain_create_rows",
+               lib().lowbit_chain_create_rows(len(stages), arr, ctypes.c_int64(rows), x_dtype, y_dtype,
+                                              ctypes.byref(h)))
         self._h = h
 
     def run(self, stream=None):
