@@ -34,7 +34,10 @@ def make(fmt, N, K, tid):
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("wait", [0, 1])
 def test_chain_matches_separate_calls(fmt, wait):
-    shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560)]
+    # (48, 20480): four K-slices per row group and an odd number of row-blocks
+    # (the binary streaming kernel gives each wave two row-blocks)
+    shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560),
+              (48, 20480)]
     mats, xs, ys, refs = [], [], [], []
     for j, (N, K) in enumerate(shapes):
         codes, scales, pc, ps = make(fmt, N, K, tid=200 + 2 * j)

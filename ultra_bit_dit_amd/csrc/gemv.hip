@@ -318,7 +318,7 @@ __device__ __attribute__((always_inline)) inline void load_quad(const FArgs& a, 
 // Item of row group rg, K-slice ks, for callers that know both: the same
 // slicing as item_of with 32-bit divisions only (a product's quads and
 // slices fit 32 bits: GQ < 2^28 in every chain).
-template <int FMT>
+template <int FMT, int RB = 1>
 __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, int64_t rg,
                                                               int64_t ks) {
   Item it;
@@ -341,7 +341,7 @@ __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, in
   }
   it.q0 = q0;
   it.nq = (int)(q1 - q0);
-  it.rb = (int64_t)W * rg + w;
+  it.rb = ((int64_t)W * rg + w) * RB;  // the wave's first row-block
   it.live = it.rb < a.NB;
   return it;
 }
@@ -352,11 +352,13 @@ __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, in
 struct QuadPtr {
   const uint8_t* c;
   const uint8_t* s;
+  const uint8_t* c2;  // binary waves of two row-blocks: the second one's codes and scales
+  const uint8_t* s2;
   int nq;
   bool p1_last;  // 2-bit: the last quad's second word block is clamped onto its first
 };
 
-template <int FMT>
+template <int FMT, int RB = 1>
 __device__ __attribute__((always_inline)) inline QuadPtr quad_ptr(const FArgs& a, const Item& it) {
   QuadPtr p;
   const int L = threadIdx.x & 63;
@@ -370,6 +372,15 @@ __device__ __attribute__((always_inline)) inline QuadPtr quad_ptr(const FArgs& a
   }
   const uint8_t* sb = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
   p.s = sb + ((rbc * a.GQ + it.q0) * 16 + (L & 15)) * 8;
+  if constexpr (RB == 2) {
+    static_assert(FMT == 1, "two row-blocks per wave: binary only");
+    const int64_t rbc2 = it.rb + 1 < a.NB ? it.rb + 1 : rbc;  // past the end: a dummy re-read
+    p.c2 = a.pcodes + (rbc2 * a.GQ + it.q0) * 1024 + 16 * L;
+    p.s2 = sb + ((rbc2 * a.GQ + it.q0) * 16 + (L & 15)) * 8;
+  } else {
+    p.c2 = p.c;
+    p.s2 = p.s;
+  }
   p.nq = it.nq;
   p.p1_last = 2 * (it.q0 + it.nq - 1) + 1 >= a.GP;
   return p;
@@ -397,6 +408,16 @@ __device__ __attribute__((always_inline)) inline void load_quad_p(const QuadPtr&
     o.t3 = __builtin_nontemporal_load((const uint32_t*)(lp - 16 * L + 3072 + 4 * L)) >> (16 * h);
   }
   o.sc = *(const uint2*)(p.s + qq * 128);
+}
+
+// quad q of both row-blocks of a binary wave that holds two
+__device__ __attribute__((always_inline)) inline void load_quad_p2(const QuadPtr& p, int q,
+                                                                  Quad<1>& o, Quad<1>& o2) {
+  const int qq = q < p.nq ? q : p.nq - 1;
+  o.w[0] = __builtin_nontemporal_load((const u4*)(p.c + qq * 1024));
+  o2.w[0] = __builtin_nontemporal_load((const u4*)(p.c2 + qq * 1024));
+  o.sc = *(const uint2*)(p.s + qq * 128);
+  o2.sc = *(const uint2*)(p.s2 + qq * 128);
 }
 
 // LDS of an item: staged activations, a zero block, the base-3 table
@@ -561,6 +582,59 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
 __device__ __attribute__((always_inline)) inline float silu_mul_lanes(float f) {
   const float u = __shfl_down(f, 8);
   return f / (1.0f + expf(-f)) * u;
+}
+
+// quad_mfma_m1 for a binary wave of two row-blocks: each group's A operand
+// is read once and feeds both row-blocks' MFMAs (two independent chains);
+// each row-block's accumulation order is that of quad_mfma_m1.
+template <int XK>
+__device__ __attribute__((always_inline)) inline void quad_mfma_m1x2(const uint8_t* arow,
+                                                                     const uint8_t* erow, int q,
+                                                                     const Quad<1>& qd,
+                                                                     const Quad<1>& qd2,
+                                                                     uint32_t sign_mask,
+                                                                     uint32_t one_bits, float& acc0,
+                                                                     float& acc1) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
+  v4f cp0, cp1;
+  float sp0 = 0.f, sp1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
+    const uint4 x0 = src[0], x1 = src[1];
+    const v8i A = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    const uint32_t w0 = t == 0 ? qd.w[0].x : t == 1 ? qd.w[0].y : t == 2 ? qd.w[0].z : qd.w[0].w;
+    const uint32_t w1 = t == 0 ? qd2.w[0].x : t == 1 ? qd2.w[0].y : t == 2 ? qd2.w[0].z : qd2.w[0].w;
+    const v8i B0 = decode_binary_reg(w0, sign_mask, one_bits);
+    const v8i B1 = decode_binary_reg(w1, sign_mask, one_bits);
+    const v4f c0 = t == 0 ? mfma_group<0>(A, B0, (int)se) : t == 1 ? mfma_group<1>(A, B0, (int)se)
+                 : t == 2 ? mfma_group<2>(A, B0, (int)se) : mfma_group<3>(A, B0, (int)se);
+    const v4f c1 = t == 0 ? mfma_group<0>(A, B1, (int)se) : t == 1 ? mfma_group<1>(A, B1, (int)se)
+                 : t == 2 ? mfma_group<2>(A, B1, (int)se) : mfma_group<3>(A, B1, (int)se);
+    if (t > 0) {
+      float s0 = cp0[0], s1 = cp1[0];
+#pragma unroll
+      for (int i = 1; i < R; i++) {
+        s0 += cp0[i];
+        s1 += cp1[i];
+      }
+      acc0 = fmaf(sp0, s0, acc0);
+      acc1 = fmaf(sp1, s1, acc1);
+    }
+    cp0 = c0;
+    cp1 = c1;
+    sp0 = quad_scale<1>(qd, t);
+    sp1 = quad_scale<1>(qd2, t);
+  }
+  float s0 = cp0[0], s1 = cp1[0];
+#pragma unroll
+  for (int i = 1; i < R; i++) {
+    s0 += cp0[i];
+    s1 += cp1[i];
+  }
+  acc0 = fmaf(sp0, s0, acc0);
+  acc1 = fmaf(sp1, s1, acc1);
 }
 
 // Output of an item: direct stores, or (several K-slices) coherent partial
@@ -930,10 +1004,16 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 // hold M R rows of A, the quads go through the generic quad routine, and
 // lane group lg keeps rows (4 / R) lg .. (4 / R) lg + 4 / R - 1 of its
 // output row.
-template <int FMT, int XK, int YK, int QM, bool MR>
-__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 && !MR ? 4 : 2))) void gemv_stream(ChainArgs c) {
+//
+// RB = 2 (binary, one row): every wave holds two row-blocks, whose MFMAs
+// share each A operand read (row groups of 128 rows, two workgroups per CU
+// keep as many bytes in flight as four of one row-block each).
+template <int FMT, int XK, int YK, int QM, bool MR, int RB>
+__global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 && !MR && RB == 1 ? 4 : 2))) void gemv_stream(ChainArgs c) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   constexpr int MX = MR ? 4 / R : 1;  // accumulator rows per lane
+  constexpr int NACC = MR ? MX : RB;  // accumulators per lane
+  static_assert(RB == 1 || (FMT == 1 && !MR), "two row-blocks per wave: binary, one row");
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab ufirst = (I64Tab)c.ufirst;
@@ -1013,7 +1093,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     while (u >= ufirst[s + 1]) s++;
     FArgs a = load_args(args, s);
     int64_t rg = u - ufirst[s], ks = 0;
-    Item it = item_at<FMT>(a, rg, 0);
+    Item it = item_at<FMT, RB>(a, rg, 0);
     // staged activations of a slice, XR 16-byte pieces per thread
     auto xsrc = [&](const FArgs& f, int sidx, int64_t kslice, int nq, int k) {
       const int64_t nb = (int64_t)nq * 16 * f.MA * 33 / 16;
@@ -1080,27 +1160,29 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     int64_t un, rgn, ksn;
     bool more = next(s, u, rg, ks, a, sn, un, rgn, ksn);
     FArgs an = load_args(args, sn);
-    Item itn = item_at<FMT>(an, rgn, ksn);
-    QuadPtr pn = quad_ptr<FMT>(an, itn);
+    Item itn = item_at<FMT, RB>(an, rgn, ksn);
+    QuadPtr pn = quad_ptr<FMT, RB>(an, itn);
     // the current slice's codes quad by quad with the next slice's
     // activations after quad kWriteAfter - 1: the order the loop issues them
     // in, kept by scheduling barriers, so that the wait counts in the loop
     // (the stricter of loop entry and back edge) leave a whole slice of loads
     // in flight
     Quad<FMT> qd[QM];
+    Quad<FMT> qd2[RB == 2 ? QM : 1];
     {
-      const QuadPtr p0 = quad_ptr<FMT>(a, it);
+      const QuadPtr p0 = quad_ptr<FMT, RB>(a, it);
 #pragma unroll
       for (int q = 0; q < QM; q++) {
         if (q == kWriteAfter) XLD(an, sn, ksn, itn.nq);
-        load_quad_p<FMT>(p0, q, qd[q]);
+        if constexpr (RB == 2) load_quad_p2(p0, q, qd[q], qd2[q]);
+        else load_quad_p<FMT>(p0, q, qd[q]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float acc[MX], tot[MX];  // tot: slices added in slice order, as the split-K reduction does
-    int iacc[MX];
+    float acc[NACC], tot[NACC];  // tot: slices added in slice order, as the split-K reduction does
+    int iacc[NACC];
 #pragma unroll
-    for (int m = 0; m < MX; m++) {
+    for (int m = 0; m < NACC; m++) {
       acc[m] = 0.f;
       tot[m] = 0.f;
       iacc[m] = 0;
@@ -1160,23 +1242,26 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
           // then the activations of the slice after next (issued on every
           // path, so that the wait counts stay exact across iterations)
           const FArgs a2 = load_args(args, s2);
-          const Item it2 = item_at<FMT>(a2, rg2, ks2);
+          const Item it2 = item_at<FMT, RB>(a2, rg2, ks2);
           XLD(a2, s2, ks2, it2.nq);
         }
         if (it.live && q < it.nq) {
-          if constexpr (!MR)
-            quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
-          else
+          if constexpr (MR)
             quad_mfma<FMT, XK, MX, 2>(a, lq, q, qd[q], acc, iacc);
+          else if constexpr (RB == 2)
+            quad_mfma_m1x2<XK>(arow, erow, q, qd[q], qd2[q], sign_mask, one_bits, acc[0], acc[1]);
+          else
+            quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
         }
-        load_quad_p<FMT>(pn, q, qd[q]);
+        if constexpr (RB == 2) load_quad_p2(pn, q, qd[q], qd2[q]);
+        else load_quad_p<FMT>(pn, q, qd[q]);
       }
       // done reading slice j's image
       __builtin_amdgcn_s_waitcnt(0xC07F);
       if ((threadIdx.x & 63) == 0)
         __hip_atomic_fetch_add(consumed + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-      for (int m = 0; m < MX; m++) {
+      for (int m = 0; m < NACC; m++) {
         tot[m] = a.KS == 1 ? acc[m] : tot[m] + acc[m];
         acc[m] = 0.f;
       }
@@ -1194,18 +1279,25 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
             }
             tot[jj] = 0.f;
           }
-        } else if (a.epi) {
-          const float z = silu_mul_lanes(tot[0]);
-          const int64_t nz = 8 * it.rb + r;
-          if (it.live && lg == 0 && r < 8) {
-            if (YK == YK_F32) ((float*)a.y)[nz] = z;
-            else ((uint16_t*)a.y)[nz] = (uint16_t)bf16_rne(z);
+        } else {
+#pragma unroll
+          for (int i = 0; i < RB; i++) {
+            const int64_t rbi = it.rb + i, ni = 16 * rbi + r;
+            const bool live = rbi < a.NB;
+            if (a.epi) {
+              const float z = silu_mul_lanes(tot[i]);
+              const int64_t nz = 8 * rbi + r;
+              if (live && lg == 0 && r < 8) {
+                if (YK == YK_F32) ((float*)a.y)[nz] = z;
+                else ((uint16_t*)a.y)[nz] = (uint16_t)bf16_rne(z);
+              }
+            } else if (live && lg == 0 && ni < a.N) {
+              if (YK == YK_F32) ((float*)a.y)[ni] = tot[i];
+              else ((uint16_t*)a.y)[ni] = (uint16_t)bf16_rne(tot[i]);
+            }
+            tot[i] = 0.f;
           }
-        } else if (it.live && lg == 0 && n < a.N) {
-          if (YK == YK_F32) ((float*)a.y)[n] = tot[0];
-          else ((uint16_t*)a.y)[n] = (uint16_t)bf16_rne(tot[0]);
         }
-        tot[0] = 0.f;
       }
       if (!more) break;
       s = sn; u = un; rg = rgn; ks = ksn;
@@ -1214,8 +1306,8 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       sn = s2; un = u2; rgn = rg2; ksn = ks2;
       more = more2;
       an = load_args(args, sn);
-      itn = item_at<FMT>(an, rgn, ksn);
-      pn = quad_ptr<FMT>(an, itn);
+      itn = item_at<FMT, RB>(an, rgn, ksn);
+      pn = quad_ptr<FMT, RB>(an, itn);
       j++;
     }
   }
@@ -1248,7 +1340,7 @@ constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
 constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
 constexpr int kQuadsMulti = 4;     // quads per slice of the several-row streaming kernel
 
-Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0) {
+Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0, int rb = 1) {
   Plan p;
   p.R = split_terms(xkind);
   p.MA = M * p.R;
@@ -1269,10 +1361,10 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   // 4 waves per workgroup: 64 rows share one staged slice, and the slice's
   // activation loads fit in the hoisted staging rounds
   p.W = kMaxW;
-  p.NRG = cdiv(p.NB, p.W);
+  p.NRG = cdiv(p.NB, p.W * rb);  // rb row-blocks per wave (the binary streaming kernel: 2)
   const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
   p.lds = (size_t)qmax * 16 * p.MA * 32 + (size_t)qmax * 16 * p.MA + 48 + (fmt == 3 ? 1024 : 0);
-  p.Npad = p.NRG * p.W * 16;
+  p.Npad = p.NRG * p.W * rb * 16;
   p.part_off = kCounterBytes;
   p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
   return p;
@@ -1352,7 +1444,7 @@ struct ChainPlan {
 };
 
 template <int FMT, int XK>
-const void* chain_kernel(int ykind, bool waits, int64_t M) {
+const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
   constexpr int QM = FMT == 1 ? kQuadsBinary : kQuadsTernary;
   const bool b16 = ykind == YK_BF16;
   if (waits) {
@@ -1362,11 +1454,16 @@ const void* chain_kernel(int ykind, bool waits, int64_t M) {
     return b16 ? (const void*)gemv_chain<FMT, XK, YK_BF16, QM, true>
                : (const void*)gemv_chain<FMT, XK, YK_F32, QM, true>;
   }
+  if constexpr (FMT == 1 && XK == XK_BF16) {
+    if (M == 1 && rb == 2)
+      return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 2>
+                 : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 2>;
+  }
   if (M == 1)
-    return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false>
-               : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false>;
-  return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true>
-             : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMulti, true>;
+    return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 1>
+               : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 1>;
+  return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true, 1>
+             : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMulti, true, 1>;
 }
 
 }  // namespace
@@ -1387,12 +1484,14 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   // (kQuadsMulti with several activation rows); its two image buffers are
   // sized for the most rows of A it handles (R, or 16)
   const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : kQuadsMulti);
+  // binary, one bf16 row, no waits: two row-blocks per wave
+  const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? 2 : 1;
   const int R = split_terms(xkind);
   size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : 16) * 33 + 48 + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
     if (st[i].epi && M != 1) return hipErrorInvalidValue;
-    const Plan p = make_plan(fmt, st[i].N, st[i].K, M, xkind, quads);
+    const Plan p = make_plan(fmt, st[i].N, st[i].K, M, xkind, quads, rb);
     if (p.lds > 64 * 1024) return hipErrorInvalidValue;
     if (waits) lds = std::max(lds, p.lds);
     first[i + 1] = first[i] + p.NRG * p.KS;
@@ -1463,9 +1562,9 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   if (e == hipSuccess) e = hipMemcpy(m + o_xo, xoff.data(), sizeof(int64_t) * S, hipMemcpyHostToDevice);
   if (e == hipSuccess) {
     const bool f32 = xkind == XK_F32;
-    if (fmt == 1) c->kernel = f32 ? chain_kernel<1, XK_F32>(ykind, waits, M) : chain_kernel<1, XK_BF16>(ykind, waits, M);
-    else if (fmt == 2) c->kernel = f32 ? chain_kernel<2, XK_F32>(ykind, waits, M) : chain_kernel<2, XK_BF16>(ykind, waits, M);
-    else if (fmt == 3) c->kernel = f32 ? chain_kernel<3, XK_F32>(ykind, waits, M) : chain_kernel<3, XK_BF16>(ykind, waits, M);
+    if (fmt == 1) c->kernel = f32 ? chain_kernel<1, XK_F32>(ykind, waits, M, rb) : chain_kernel<1, XK_BF16>(ykind, waits, M, rb);
+    else if (fmt == 2) c->kernel = f32 ? chain_kernel<2, XK_F32>(ykind, waits, M, rb) : chain_kernel<2, XK_BF16>(ykind, waits, M, rb);
+    else if (fmt == 3) c->kernel = f32 ? chain_kernel<3, XK_F32>(ykind, waits, M, rb) : chain_kernel<3, XK_BF16>(ykind, waits, M, rb);
     else e = hipErrorInvalidValue;
   }
   int per_cu = 0, cus = 0;
