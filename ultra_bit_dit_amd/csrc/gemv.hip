@@ -33,6 +33,8 @@ namespace {
 constexpr int kMaxWaves = 16;  // waves per workgroup of the sign kernel
 constexpr uint32_t kChainSpinLimit = 1u << 24;  // sleeps before a chain wait gives up
 constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
+constexpr int kQuadsMulti = 4;      // quads per slice of the several-row streaming kernel
+constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
 
 template <int T>
 __device__ inline v4f mfma_group(const v8i& A, const v8i& B, int sa) {
@@ -1063,7 +1065,9 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // writes its share of slice j+1 part-way through slice j, so waves are
   // only ever held back by a wave more than about one slice behind (there is
   // no workgroup barrier in the loop).
-  constexpr int MAX_MA = MR ? 16 : R;  // rows of A an image may hold
+  // rows of A an image may hold: several-row chains use 6-quad slices up to
+  // 10 rows of A and 4-quad slices up to 16
+  constexpr int MAX_MA = MR ? (QM == kQuadsMultiWide ? 10 : 16) : R;
   constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
   constexpr int kWriteAfter = 3;  // quads computed before the next image is written
   static_assert(QM > kWriteAfter, "the next image is written part-way through a slice");
@@ -1338,7 +1342,6 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
 constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
-constexpr int kQuadsMulti = 4;     // quads per slice of the several-row streaming kernel
 
 Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0, int rb = 1) {
   Plan p;
@@ -1462,6 +1465,10 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
   if (M == 1)
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 1>;
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  if (M * R <= 10)
+    return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMultiWide, true, 1>
+               : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMultiWide, true, 1>;
   return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true, 1>
              : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMulti, true, 1>;
 }
@@ -1483,11 +1490,12 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   // the streaming kernel keeps kQuadsTernary quads of every format in flight
   // (kQuadsMulti with several activation rows); its two image buffers are
   // sized for the most rows of A it handles (R, or 16)
-  const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : kQuadsMulti);
+  const int R = split_terms(xkind);
+  const bool wide = M * R <= 10;
+  const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : wide ? kQuadsMultiWide : kQuadsMulti);
   // binary, one bf16 row, no waits: two row-blocks per wave
   const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? 2 : 1;
-  const int R = split_terms(xkind);
-  size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : 16) * 33 + 48 + 1024 + 16;
+  size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : wide ? 10 : 16) * 33 + 48 + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
     if (st[i].epi && M != 1) return hipErrorInvalidValue;
