@@ -281,7 +281,8 @@ int lowbit_chain_destroy(lowbit_chain* chain);
  * Computed in fp64 (sums exact while a group's magnitudes span less than
  * 2^38, so the result does not depend on the summation order).  Rotated
  * weights expect rotated activations (lowbit_rotate_act with the same
- * signs).  Errors: E_NULL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_HIP. */
+ * signs).  Alignment: W, signs and codes 16 bytes, scales 2 bytes.
+ * Errors: E_NULL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_HIP. */
 int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf16,
                             const int8_t* signs, int8_t* codes, uint16_t* scales,
                             void* stream);

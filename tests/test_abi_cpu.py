@@ -96,3 +96,15 @@ def test_gemm_pack_quant_validation_without_gpu():
     assert q(0, 128, A16, A16, A16, None) == lb.E_SHAPE
     assert q(1, 128, None, A16, A16, None) == lb.E_NULL
     assert q(1, 128, A16, A16, A1, None) == lb.E_ALIGN
+
+
+def test_quantizer_validation_without_gpu():
+    f = lb.lib().lowbit_quantize_weights
+    assert f(2, 4, 128, None, None, A16, A16, None) == lb.E_NULL
+    assert f(7, 4, 128, A16, None, A16, A16, None) == lb.E_UNSUPPORTED
+    assert f(2, 4, 200, A16, None, A16, A16, None) == lb.E_SHAPE
+    # 16-byte loads of weights and signs, 16-byte stores of codes
+    assert f(2, 4, 128, A4, None, A16, A16, None) == lb.E_ALIGN
+    assert f(2, 4, 128, A16, A4, A16, A16, None) == lb.E_ALIGN
+    assert f(2, 4, 128, A16, None, A4, A16, None) == lb.E_ALIGN
+    assert f(2, 4, 128, A16, None, A16, A1, None) == lb.E_ALIGN

@@ -323,7 +323,9 @@ int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf1
   if (!W_bf16 || !codes || !scales) return LOWBIT_E_NULL;
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
-  if (!aligned(W_bf16, 2) || !aligned(scales, 2)) return LOWBIT_E_ALIGN;
+  if (!aligned(W_bf16, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)) ||
+      !aligned(scales, 2))
+    return LOWBIT_E_ALIGN;
   return hip_status(launch_quantize_weights(fmt, N, K, W_bf16, signs, codes, scales,
                                             (hipStream_t)stream));
 }

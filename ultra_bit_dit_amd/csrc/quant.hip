@@ -5,7 +5,7 @@
 // calibrated GPTQ step needs data and is not part of this front end), and
 // the matching rotation of activations.
 //
-// Per row n and group g (one wavefront, lane l holding elements l and l+64):
+// Per row n and group g (eight lanes, see the kernel):
 //   v = W[n][128 g ..] * d[128 g ..]            (signs d = +-1)
 //   u = H v, H[i][j] = (-1)^popcount(i & j)      (fast Walsh-Hadamard, fp64)
 //   t = u r with r = 1/sqrt(128) in fp64; s = (sum |u| / 128) r (mean |t|);
@@ -63,49 +63,82 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int d) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-// one wavefront per (row, group)
+// Eight lanes per (row, group): lane l8 = lane % 8 of the eight holds the
+// 16 consecutive elements 16 l8 .. 16 l8 + 15, so the transform's strides
+// 1..8 are butterflies inside the lane and strides 16, 32, 64 exchange
+// with lanes l8 ^ 1, 2, 4; a wavefront covers eight groups.  Loads are 32
+// bytes and code stores 16 bytes per lane.
+constexpr int kQuantGroupsPerWave = 8;
+
 __global__ __launch_bounds__(256) void quantize_weights(int fmt, int64_t N, int64_t K, int64_t G,
                                                         const uint16_t* __restrict__ W,
                                                         const int8_t* __restrict__ signs,
                                                         int8_t* __restrict__ codes,
                                                         uint16_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= N * G) return;
-  const int64_t n = unit / G, g = unit % G;
-  const int64_t base = n * K + g * 128;
-  double v0 = bf16_f64(W[base + lane]), v1 = bf16_f64(W[base + lane + 64]);
+  const int lane = threadIdx.x & 63, l8 = lane & 7;
+  const int64_t unit = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kQuantGroupsPerWave + (lane >> 3);
+  const bool valid = unit < N * G;
+  const int64_t uc = valid ? unit : N * G - 1;  // lanes past the end recompute the last group
+  const int64_t n = uc / G, g = uc % G;
+  const int64_t base = n * K + g * 128 + 16 * l8;
+  const uint4 w0 = *(const uint4*)(W + base), w1 = *(const uint4*)(W + base + 8);
+  const uint32_t wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  double v[16];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    v[2 * i] = (double)__uint_as_float(wb[i] << 16);
+    v[2 * i + 1] = (double)__uint_as_float(wb[i] & 0xFFFF0000u);
+  }
   const bool rot = signs != nullptr;
   const double r = 1.0 / __builtin_sqrt(128.0);  // folded to the fp64 constant
   if (rot) {
-    v0 *= (double)signs[g * 128 + lane];
-    v1 *= (double)signs[g * 128 + lane + 64];
-    // bit 6 of the element index is the register; bits 0..5 are the lane
-    const double a = v0 + v1, b = v0 - v1;
-    v0 = a;
-    v1 = b;
+    const uint4 sg = *(const uint4*)(signs + g * 128 + 16 * l8);
+    const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const double p0 = shfl_xor_f64(v0, d), p1 = shfl_xor_f64(v1, d);
-      v0 = (lane & d) ? p0 - v0 : v0 + p0;
-      v1 = (lane & d) ? p1 - v1 : v1 + p1;
+    for (int i = 0; i < 16; i++) v[i] *= (double)(int8_t)((sw[i >> 2] >> (8 * (i & 3))) & 0xFF);
+    // strides 1, 2, 4, 8: inside the lane (bits 0..3 of the element index)
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        if (i & d) continue;
+        const double a = v[i], b = v[i + d];
+        v[i] = a + b;
+        v[i + d] = a - b;
+      }
+    }
+    // strides 16, 32, 64: lanes l8 ^ 1, 2, 4 (bits 4..6)
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const double p = shfl_xor_f64(v[i], d);
+        v[i] = (l8 & d) ? p - v[i] : v[i] + p;
+      }
     }
   }
-  double S = __builtin_fabs(v0) + __builtin_fabs(v1);
+  double S = 0.0;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) S += shfl_xor_f64(S, d);
-  const double t0 = rot ? v0 * r : v0, t1 = rot ? v1 * r : v1;
+  for (int i = 0; i < 16; i++) S += __builtin_fabs(v[i]);
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) S += shfl_xor_f64(S, d);
   const double sc = rot ? (S / 128.0) * r : S / 128.0;
   const uint16_t s16 = f64_to_f16_bits(sc);
   const double sd = f16_bits_f64(s16), h = sd * 0.5;
-  auto code = [&](double t) -> int8_t {
-    if (fmt == 1) return (sd == 0.0 || !(t < 0.0)) ? 1 : -1;
-    if (sd == 0.0) return 0;
-    return t > h ? 1 : (t < -h ? -1 : 0);
-  };
-  codes[base + lane] = code(t0);
-  codes[base + lane + 64] = code(t1);
-  if (lane == 0) scales[n * G + g] = s16;
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const double t = rot ? v[i] * r : v[i];
+    int8_t c;
+    if (fmt == 1) c = (sd == 0.0 || !(t < 0.0)) ? 1 : -1;
+    else if (sd == 0.0) c = 0;
+    else c = t > h ? 1 : (t < -h ? -1 : 0);
+    cw[i >> 2] |= (uint32_t)(uint8_t)c << (8 * (i & 3));
+  }
+  if (valid) {
+    *(uint4*)(codes + base) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    if (l8 == 0) scales[n * G + g] = s16;
+  }
 }
 
 // Activations rotated to match rotated weights: per 128-block,
@@ -142,8 +175,8 @@ hipError_t launch_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t
                                    const int8_t* signs, int8_t* codes, uint16_t* scales,
                                    hipStream_t s) {
   const int64_t G = K / kGroup, units = N * G;
-  hipLaunchKernelGGL(quantize_weights, dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, fmt, N, K,
-                     G, W, signs, codes, scales);
+  hipLaunchKernelGGL(quantize_weights, dim3((unsigned)cdiv(units, 4 * kQuantGroupsPerWave)), dim3(256),
+                     0, s, fmt, N, K, G, W, signs, codes, scales);
   return hipGetLastError();
 }
 
