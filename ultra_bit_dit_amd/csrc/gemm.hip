@@ -84,12 +84,15 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, T v) {
 }
 
 // Split-K: every split stores its partial tile (lane-major, so the stores
-// are coalesced), makes it visible device-wide (agent-scope release) and
-// bumps the tile counter; the last split to arrive (agent-scope acquire)
-// adds all partials in split order (deterministic) and resets the counter.
-// Its loads go out 32 values at a time, so the reduction costs a few memory
-// round trips rather than one per value.  Returns true in the workgroup that
-// must write Y.  INT: the values are int32 bit patterns, added as integers.
+// are coalesced) with device-coherent (write-through) stores, waits until
+// they have completed and bumps the tile counter; the last split to arrive
+// reads the other partials with device-coherent loads and adds all of them in
+// split order (deterministic), then resets the counter.  No fences: an
+// agent-scope fence writes back or invalidates the whole L2 of the XCD, for
+// every split.  The loads go out 32 values at a time, so the reduction
+// costs a few memory round trips rather than one per value.  Returns true in
+// the workgroup that must write Y.  INT: the values are int32 bit patterns,
+// added as integers.
 template <int NV, bool INT, int THREADS>
 __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int ks, int wave,
                                              int lane, uint32_t (&v)[NV]) {
@@ -100,15 +103,14 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
   uint32_t* part = (uint32_t*)a.part;
   uint32_t* mine = part + (tile * a.KS + ks) * per + (int64_t)wave * NV * 64 + lane;
 #pragma unroll
-  for (int i = 0; i < NV; i++) mine[i * 64] = v[i];
-  __builtin_amdgcn_s_waitcnt(0);
+  for (int i = 0; i < NV; i++)
+    __hip_atomic_store(mine + i * 64, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev = __hip_atomic_fetch_add(a.cnt + 16 + tile, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (uint32_t)(a.KS - 1);
-    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return false;
@@ -125,7 +127,9 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
       const uint32_t* src = part + (tile * a.KS + k) * per + (int64_t)wave * NV * 64 + lane;
       uint32_t x[CH];
 #pragma unroll
-      for (int i = 0; i < CH; i++) x[i] = k == ks ? v[i0 + i] : src[(i0 + i) * 64];
+      for (int i = 0; i < CH; i++)
+        x[i] = k == ks ? v[i0 + i]
+                       : __hip_atomic_load(src + (i0 + i) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int i = 0; i < CH; i++) {
         if constexpr (INT)
