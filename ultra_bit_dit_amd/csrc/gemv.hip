@@ -1353,8 +1353,9 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   p.GQ = cdiv(p.G, 4);
   p.GP = cdiv(p.G, 2);
   p.QM = quads > 0 ? quads : fmt == 1 ? kQuadsBinary : kQuadsTernary;
-  // staged activations of a slice stay within 48 KiB of LDS
-  int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (48 * 1024) / (16 * p.MA * 33)));
+  // staged activations of a slice stay within 56 KiB of LDS (small-M
+  // products of 10 rows of A keep a 5120-long row in one slice)
+  int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (56 * 1024) / (16 * p.MA * 33)));
   if (fmt == 3) {
     // base-3 slices are whole octets (pairs of quads)
     qcap = std::max<int64_t>(2, qcap & ~int64_t(1));
