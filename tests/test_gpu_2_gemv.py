@@ -198,3 +198,27 @@ def test_base3_equals_2bit(N, K, xk):
     y3 = lb.gemv(3, N, K, pc3, ps3, x)
     torch.cuda.synchronize()
     assert torch.equal(y2, y3)
+
+
+@pytest.mark.parametrize("K,offset", [(1024, 0), (17408, 0), (1000, 0), (1024, 1)])
+def test_quantize_act_i8_paths(K, offset):
+    """Per-row int8 quantization, bit-exact: the 16-byte path (K % 8 == 0,
+    aligned) and the element path (K % 8 != 0, or X at a 2-byte offset), with
+    a zero row and a row of exact ties (max 127: x * inv = x, so 2.5 -> 2,
+    -3.5 -> -4, 0.5 -> 0)."""
+    M = 5
+    Xb = synth.normal_bf16(SEED, 91, M, K)
+    Xb[2] = 0
+    ties = np.array([127.0, 2.5, -3.5, 0.5, 1.5, -0.5, -126.5, 63.5], np.float32)
+    row3 = np.resize(ties, K).astype(np.float32)
+    Xb[3] = (row3.view(np.uint32) >> 16).astype(np.uint16)
+    flat = torch.empty(M * K + offset, dtype=torch.int16, device="cuda")
+    flat[offset:] = dev(Xb.view(np.int16).reshape(-1))
+    X = flat[offset:].view(M, K).view(torch.bfloat16)
+    Q, sx = lb.quantize_act_i8(X)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = O.quantize_act_i8(Xb)
+    assert np.array_equal(Q.cpu().numpy(), q_ref)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert sx_ref[2] == 0 and not q_ref[2].any()
+    assert q_ref[3][:8].tolist() == [127, 2, -4, 0, 2, 0, -126, 64]
