@@ -354,8 +354,10 @@ __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, in
 struct QuadPtr {
   const uint8_t* c;
   const uint8_t* s;
-  const uint8_t* c2;  // binary waves of two row-blocks: the second one's codes and scales
+  const uint8_t* c2;  // binary waves of two or three row-blocks: the second one's codes and scales
   const uint8_t* s2;
+  const uint8_t* c3;  // (three: the third one's)
+  const uint8_t* s3;
   int nq;
   bool p1_last;  // 2-bit: the last quad's second word block is clamped onto its first
 };
@@ -374,14 +376,22 @@ __device__ __attribute__((always_inline)) inline QuadPtr quad_ptr(const FArgs& a
   }
   const uint8_t* sb = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
   p.s = sb + ((rbc * a.GQ + it.q0) * 16 + (L & 15)) * 8;
-  if constexpr (RB == 2) {
-    static_assert(FMT == 1, "two row-blocks per wave: binary only");
+  if constexpr (RB >= 2) {
+    static_assert(FMT == 1, "several row-blocks per wave: binary only");
     const int64_t rbc2 = it.rb + 1 < a.NB ? it.rb + 1 : rbc;  // past the end: a dummy re-read
     p.c2 = a.pcodes + (rbc2 * a.GQ + it.q0) * 1024 + 16 * L;
     p.s2 = sb + ((rbc2 * a.GQ + it.q0) * 16 + (L & 15)) * 8;
   } else {
     p.c2 = p.c;
     p.s2 = p.s;
+  }
+  if constexpr (RB == 3) {
+    const int64_t rbc3 = it.rb + 2 < a.NB ? it.rb + 2 : rbc;
+    p.c3 = a.pcodes + (rbc3 * a.GQ + it.q0) * 1024 + 16 * L;
+    p.s3 = sb + ((rbc3 * a.GQ + it.q0) * 16 + (L & 15)) * 8;
+  } else {
+    p.c3 = p.c2;
+    p.s3 = p.s2;
   }
   p.nq = it.nq;
   p.p1_last = 2 * (it.q0 + it.nq - 1) + 1 >= a.GP;
@@ -420,6 +430,56 @@ __device__ __attribute__((always_inline)) inline void load_quad_p2(const QuadPtr
   o2.w[0] = __builtin_nontemporal_load((const u4*)(p.c2 + qq * 1024));
   o.sc = *(const uint2*)(p.s + qq * 128);
   o2.sc = *(const uint2*)(p.s2 + qq * 128);
+}
+
+// Binary waves of three row-blocks address codes and scales through buffer
+// resources with wave-uniform offsets (scalar registers): only the lane's
+// fixed offset stays in a vector register, which leaves the registers a
+// wave needs for three row-blocks of ten quads in flight.  Every stage's
+// codes and scales are shorter than 2^31 bytes.
+struct QuadBuf {
+  __amdgpu_buffer_rsrc_t rc, rs;
+  int32_t oc, oc2, oc3, os, os2, os3;  // byte offsets of the item's first quad
+  int nq;
+};
+
+__device__ __attribute__((always_inline)) inline QuadBuf quad_buf3(const FArgs& a, const Item& it) {
+  QuadBuf p;
+  const int64_t rbc = it.live ? it.rb : a.NB - 1;
+  const int64_t rbc2 = it.rb + 1 < a.NB ? it.rb + 1 : rbc;  // past the end: a dummy re-read
+  const int64_t rbc3 = it.rb + 2 < a.NB ? it.rb + 2 : rbc;
+  const uint8_t* sb = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
+  p.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.pcodes), (short)0,
+                                           (int)(a.NB * a.GQ * 1024), 0x00020000);
+  p.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sb), (short)0,
+                                           (int)(a.NB * a.GQ * 128), 0x00020000);
+  p.oc = (int32_t)((rbc * a.GQ + it.q0) * 1024);
+  p.oc2 = (int32_t)((rbc2 * a.GQ + it.q0) * 1024);
+  p.oc3 = (int32_t)((rbc3 * a.GQ + it.q0) * 1024);
+  p.os = (int32_t)((rbc * a.GQ + it.q0) * 128);
+  p.os2 = (int32_t)((rbc2 * a.GQ + it.q0) * 128);
+  p.os3 = (int32_t)((rbc3 * a.GQ + it.q0) * 128);
+  p.nq = it.nq;
+  return p;
+}
+
+// quad q of the three row-blocks (the words load_quad_p2 reads for two);
+// vc = 16 * lane, vs = 8 * (lane % 16).  Codes stream past the caches
+// (non-temporal), as in load_quad_p2.
+__device__ __attribute__((always_inline)) inline void load_quad_b3(const QuadBuf& p, int q,
+                                                                  int vc, int vs, Quad<1>& o,
+                                                                  Quad<1>& o2, Quad<1>& o3) {
+  constexpr int kNT = 2;  // cache policy: non-temporal
+  const int qq = q < p.nq ? q : p.nq - 1;
+  o.w[0] = __builtin_amdgcn_raw_buffer_load_b128(p.rc, vc, p.oc + qq * 1024, kNT);
+  o2.w[0] = __builtin_amdgcn_raw_buffer_load_b128(p.rc, vc, p.oc2 + qq * 1024, kNT);
+  o3.w[0] = __builtin_amdgcn_raw_buffer_load_b128(p.rc, vc, p.oc3 + qq * 1024, kNT);
+  const u2 s1 = __builtin_amdgcn_raw_buffer_load_b64(p.rs, vs, p.os + qq * 128, 0);
+  const u2 s2 = __builtin_amdgcn_raw_buffer_load_b64(p.rs, vs, p.os2 + qq * 128, 0);
+  const u2 s3 = __builtin_amdgcn_raw_buffer_load_b64(p.rs, vs, p.os3 + qq * 128, 0);
+  o.sc = make_uint2(s1.x, s1.y);
+  o2.sc = make_uint2(s2.x, s2.y);
+  o3.sc = make_uint2(s3.x, s3.y);
 }
 
 // LDS of an item: staged activations, a zero block, the base-3 table
@@ -637,6 +697,64 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1x2(const uint8
   }
   acc0 = fmaf(sp0, s0, acc0);
   acc1 = fmaf(sp1, s1, acc1);
+}
+
+// The same for a binary wave of three row-blocks.
+template <int XK>
+__device__ __attribute__((always_inline)) inline void quad_mfma_m1x3(
+    const uint8_t* arow, const uint8_t* erow, int q, const Quad<1>& qd, const Quad<1>& qd2,
+    const Quad<1>& qd3, uint32_t sign_mask, uint32_t one_bits, float& acc0, float& acc1,
+    float& acc2) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
+  v4f cp0, cp1, cp2;
+  float sp0 = 0.f, sp1 = 0.f, sp2 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint4* src = (const uint4*)(arow + (q * 16 + t * 4) * R * 32);
+    const uint4 x0 = src[0], x1 = src[1];
+    const v8i A = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    const uint32_t w0 = t == 0 ? qd.w[0].x : t == 1 ? qd.w[0].y : t == 2 ? qd.w[0].z : qd.w[0].w;
+    const uint32_t w1 = t == 0 ? qd2.w[0].x : t == 1 ? qd2.w[0].y : t == 2 ? qd2.w[0].z : qd2.w[0].w;
+    const uint32_t w2 = t == 0 ? qd3.w[0].x : t == 1 ? qd3.w[0].y : t == 2 ? qd3.w[0].z : qd3.w[0].w;
+    const v8i B0 = decode_binary_reg(w0, sign_mask, one_bits);
+    const v8i B1 = decode_binary_reg(w1, sign_mask, one_bits);
+    const v8i B2 = decode_binary_reg(w2, sign_mask, one_bits);
+    const v4f c0 = t == 0 ? mfma_group<0>(A, B0, (int)se) : t == 1 ? mfma_group<1>(A, B0, (int)se)
+                 : t == 2 ? mfma_group<2>(A, B0, (int)se) : mfma_group<3>(A, B0, (int)se);
+    const v4f c1 = t == 0 ? mfma_group<0>(A, B1, (int)se) : t == 1 ? mfma_group<1>(A, B1, (int)se)
+                 : t == 2 ? mfma_group<2>(A, B1, (int)se) : mfma_group<3>(A, B1, (int)se);
+    const v4f c2 = t == 0 ? mfma_group<0>(A, B2, (int)se) : t == 1 ? mfma_group<1>(A, B2, (int)se)
+                 : t == 2 ? mfma_group<2>(A, B2, (int)se) : mfma_group<3>(A, B2, (int)se);
+    if (t > 0) {
+      float s0 = cp0[0], s1 = cp1[0], s2 = cp2[0];
+#pragma unroll
+      for (int i = 1; i < R; i++) {
+        s0 += cp0[i];
+        s1 += cp1[i];
+        s2 += cp2[i];
+      }
+      acc0 = fmaf(sp0, s0, acc0);
+      acc1 = fmaf(sp1, s1, acc1);
+      acc2 = fmaf(sp2, s2, acc2);
+    }
+    cp0 = c0;
+    cp1 = c1;
+    cp2 = c2;
+    sp0 = quad_scale<1>(qd, t);
+    sp1 = quad_scale<1>(qd2, t);
+    sp2 = quad_scale<1>(qd3, t);
+  }
+  float s0 = cp0[0], s1 = cp1[0], s2 = cp2[0];
+#pragma unroll
+  for (int i = 1; i < R; i++) {
+    s0 += cp0[i];
+    s1 += cp1[i];
+    s2 += cp2[i];
+  }
+  acc0 = fmaf(sp0, s0, acc0);
+  acc1 = fmaf(sp1, s1, acc1);
+  acc2 = fmaf(sp2, s2, acc2);
 }
 
 // Output of an item: direct stores, or (several K-slices) coherent partial
@@ -1008,15 +1126,16 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 // lane group lg keeps rows (4 / R) lg .. (4 / R) lg + 4 / R - 1 of its
 // output row.
 //
-// RB = 2 (binary, one row): every wave holds two row-blocks, whose MFMAs
-// share each A operand read (row groups of 128 rows, two workgroups per CU
-// keep as many bytes in flight as four of one row-block each).
+// RB = 3 (binary, one row): every wave holds three row-blocks, whose MFMAs
+// share each A operand read (row groups of 192 rows, two workgroups per CU),
+// so that two waves per SIMD keep as many bytes in flight as three ternary
+// waves do; RB = 2 where a stage's codes are too long for buffer offsets.
 template <int FMT, int XK, int YK, int QM, bool MR, int RB>
 __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 && !MR && RB == 1 ? 4 : 2))) void gemv_stream(ChainArgs c) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   constexpr int MX = MR ? 4 / R : 1;  // accumulator rows per lane
   constexpr int NACC = MR ? MX : RB;  // accumulators per lane
-  static_assert(RB == 1 || (FMT == 1 && !MR), "two row-blocks per wave: binary, one row");
+  static_assert(RB == 1 || (FMT == 1 && !MR), "several row-blocks per wave: binary, one row");
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab ufirst = (I64Tab)c.ufirst;
@@ -1166,20 +1285,27 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     bool more = next(s, u, rg, ks, a, sn, un, rgn, ksn);
     FArgs an = load_args(args, sn);
     Item itn = item_at<FMT, RB>(an, rgn, ksn);
-    QuadPtr pn = quad_ptr<FMT, RB>(an, itn);
+    QuadPtr pn = quad_ptr<FMT, RB == 3 ? 1 : RB>(an, itn);
+    QuadBuf bn;
+    if constexpr (RB == 3) bn = quad_buf3(an, itn);
+    const int vc = 16 * (threadIdx.x & 63), vs = 8 * (threadIdx.x & 15);
     // the current slice's codes quad by quad with the next slice's
     // activations after quad kWriteAfter - 1: the order the loop issues them
     // in, kept by scheduling barriers, so that the wait counts in the loop
     // (the stricter of loop entry and back edge) leave a whole slice of loads
     // in flight
     Quad<FMT> qd[QM];
-    Quad<FMT> qd2[RB == 2 ? QM : 1];
+    Quad<FMT> qd2[RB >= 2 ? QM : 1];
+    Quad<FMT> qd3[RB == 3 ? QM : 1];
     {
-      const QuadPtr p0 = quad_ptr<FMT, RB>(a, it);
+      const QuadPtr p0 = quad_ptr<FMT, RB == 3 ? 1 : RB>(a, it);
+      QuadBuf b0;
+      if constexpr (RB == 3) b0 = quad_buf3(a, it);
 #pragma unroll
       for (int q = 0; q < QM; q++) {
         if (q == kWriteAfter) XLD(an, sn, ksn, itn.nq);
-        if constexpr (RB == 2) load_quad_p2(p0, q, qd[q], qd2[q]);
+        if constexpr (RB == 3) load_quad_b3(b0, q, vc, vs, qd[q], qd2[q], qd3[q]);
+        else if constexpr (RB == 2) load_quad_p2(p0, q, qd[q], qd2[q]);
         else load_quad_p<FMT>(p0, q, qd[q]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1253,12 +1379,16 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         if (it.live && q < it.nq) {
           if constexpr (MR)
             quad_mfma<FMT, XK, MX, 2>(a, lq, q, qd[q], acc, iacc);
+          else if constexpr (RB == 3)
+            quad_mfma_m1x3<XK>(arow, erow, q, qd[q], qd2[q], qd3[q], sign_mask, one_bits, acc[0], acc[1],
+                               acc[NACC - 1]);
           else if constexpr (RB == 2)
             quad_mfma_m1x2<XK>(arow, erow, q, qd[q], qd2[q], sign_mask, one_bits, acc[0], acc[1]);
           else
             quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
         }
-        if constexpr (RB == 2) load_quad_p2(pn, q, qd[q], qd2[q]);
+        if constexpr (RB == 3) load_quad_b3(bn, q, vc, vs, qd[q], qd2[q], qd3[q]);
+        else if constexpr (RB == 2) load_quad_p2(pn, q, qd[q], qd2[q]);
         else load_quad_p<FMT>(pn, q, qd[q]);
       }
       // done reading slice j's image
@@ -1312,7 +1442,8 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       more = more2;
       an = load_args(args, sn);
       itn = item_at<FMT, RB>(an, rgn, ksn);
-      pn = quad_ptr<FMT, RB>(an, itn);
+      if constexpr (RB == 3) bn = quad_buf3(an, itn);
+      else pn = quad_ptr<FMT, RB>(an, itn);
       j++;
     }
   }
@@ -1460,6 +1591,9 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
                : (const void*)gemv_chain<FMT, XK, YK_F32, QM, true>;
   }
   if constexpr (FMT == 1 && XK == XK_BF16) {
+    if (M == 1 && rb == 3)
+      return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 3>
+                 : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 3>;
     if (M == 1 && rb == 2)
       return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 2>
                  : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 2>;
@@ -1495,8 +1629,12 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   const int R = split_terms(xkind);
   const bool wide = M * R <= 10;
   const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : wide ? kQuadsMultiWide : kQuadsMulti);
-  // binary, one bf16 row, no waits: two row-blocks per wave
-  const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? 2 : 1;
+  // binary, one bf16 row, no waits: three row-blocks per wave (buffer
+  // addressing: every stage's codes shorter than 2^31 bytes), else two
+  bool buf_ok = true;
+  for (int i = 0; i < S; i++)
+    buf_ok = buf_ok && cdiv(st[i].N, 16) * cdiv(st[i].K / kGroup, 4) * 1024 < (int64_t(1) << 31);
+  const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? (buf_ok ? 3 : 2) : 1;
   size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : wide ? 10 : 16) * 33 + 48 + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
