@@ -915,10 +915,12 @@ __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, 
 // are device-coherent; WAIT: the weight loads go out first, then the
 // workgroup waits until `wait_cnt` reaches `wait_target` -- the previous
 // product is complete -- and reads its activations with coherent loads).
+// stage false: the workgroup's previous item was the same product and
+// K-slice, so the activation image in LDS is this item's already.
 template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
 __device__ __attribute__((always_inline)) inline void gemv_item(
     const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
-    uint32_t* err) {
+    uint32_t* err, bool stage = true) {
   constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   const Item it = item_of<FMT>(a, blk);
   const Lds l = lds_of(a, smem, it.nq);
@@ -927,7 +929,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   XRegs xr;
   if constexpr (!WAIT) {
     // activation loads of the first staging rounds go out first
-    stage_load_rounds<XK, false>(a, it, xr);
+    if (stage) stage_load_rounds<XK, false>(a, it, xr);
   }
   // every code and scale of the wave is requested before anything else
   Quad<FMT> qd[QM];
@@ -955,7 +957,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     __syncthreads();
     stage_load_rounds<XK, true>(a, it, xr);
   }
-  stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
+  if (stage) stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
   __syncthreads();
 
   float acc[MX];
@@ -1063,17 +1065,25 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
   const I64Tab first = (I64Tab)c.first;
   const I32Tab waitf = (I32Tab)c.wait;
   const int64_t total = first[c.S];
-  int s = 0;
+  int s = 0, s_last = -1;
+  int64_t ks_last = -1;
   for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
     while (i >= first[s + 1]) s++;
     const FArgs a = load_args(args, s);
-    const bool wt = s > 0 && waitf[s] != 0;
+    // a second item of the same product and K-slice (products with more
+    // items than workgroups): its wait is met and its activations are staged
+    const int64_t ks = (i - first[s]) % a.KS;
+    const bool again = s == s_last && ks == ks_last;
+    s_last = s;
+    ks_last = ks;
+    const bool wt = s > 0 && waitf[s] != 0 && !again;
     __syncthreads();  // the previous item's LDS reads are over
     if (wt)
       gemv_item<FMT, XK, MX, YK, QM, true, true, !MR>(a, i - first[s], smem, c.done + 256 * (s - 1),
                                                       (uint32_t)(first[s] - first[s - 1]), c.err);
     else
-      gemv_item<FMT, XK, MX, YK, QM, true, false, !MR>(a, i - first[s], smem, nullptr, 0u, c.err);
+      gemv_item<FMT, XK, MX, YK, QM, true, false, !MR>(a, i - first[s], smem, nullptr, 0u, c.err,
+                                                       !again);
     __builtin_amdgcn_s_waitcnt(0);  // this item's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
