@@ -24,6 +24,7 @@ Prints one JSON line (see --help for options).
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -54,10 +55,15 @@ GEMV_SOURCES = [os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", f)
 
 
 def gemv_source_hash():
+    """sha256 of the decode kernel's sources with comments and blank space
+    removed: an edit of a comment leaves the kernel, and its counters, valid."""
     h = hashlib.sha256()
     for path in GEMV_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,8 +34,9 @@ def make(fmt, N, K, tid):
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("wait", [0, 1])
 def test_chain_matches_separate_calls(fmt, wait):
-    # (48, 20480): four K-slices per row group and an odd number of row-blocks
-    # (the binary streaming kernel gives each wave two row-blocks)
+    # (48, 20480): four K-slices per row group; the binary streaming kernel
+    # gives each wave three row-blocks, so 100 and 3000 rows leave a last
+    # wave with one and with two live row-blocks
     shapes = [(640, 1024), (100, 5120), (256, 17408), (5120, 5120), (48, 128), (3000, 2560),
               (48, 20480)]
     mats, xs, ys, refs = [], [], [], []

@@ -1125,10 +1125,10 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 }
 
 // Binary weights carry half the bytes of 2-bit ternary per quad, so a
-// binary wave needs twice the work in flight: with bf16 activations it holds
-// two row-blocks (RB = 2, below); otherwise the binary kernel is held to 128
-// registers (one MFMA group in flight per step) to run four workgroups per
-// CU.
+// binary wave needs more work in flight: with bf16 activations it holds
+// three row-blocks (RB = 3, below); otherwise the binary kernel is held to
+// 128 registers (one MFMA group in flight per step) to run four workgroups
+// per CU.
 //
 // MR: chains of small-M products (M activation rows, M R <= 16, all stages
 // alike, e.g. a verification pass over drafted tokens): the slice images
