@@ -17,4 +17,5 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     device_codes,
     device_scales,
+    device_u32,
 )

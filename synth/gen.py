@@ -17,6 +17,7 @@ From r:
                     z = sqrt(-2 ln u1) cos(2 pi u2) in fp64, then fp32, then
                     bf16 (nearest even) where bf16 is used
     sign bit        b = r >> 31
+    raw word        w = r(i)   (packed binary codes: every bit is a fair sign)
 
 The host side uses numpy; codes and scales also have a device side written
 with torch integer / fp64 tensor operations (no HIP code), so that multi-GB
@@ -182,3 +183,18 @@ def device_scales(seed, tensor_id, N, G, device):
     t = 0.09 * u
     v = 0.01 + t
     return v.to(torch.float32).to(torch.float16).reshape(N, G)
+
+
+def device_u32(seed, tensor_id, n, device, chunk=1 << 26):
+    """The raw words r(0) .. r(n - 1) on `device` as an int32 tensor (the
+    same bits as rand_u32), n <= 2^32."""
+    import torch
+    if n > (1 << 32):
+        raise ValueError("more words than one tensor id holds")
+    out = torch.empty(n, dtype=torch.int32, device=device)
+    for i0 in range(0, n, chunk):
+        i1 = min(n, i0 + chunk)
+        idx = torch.arange(i0, i1, dtype=torch.int64, device=device)
+        r = _rand_t(seed, tensor_id, idx)
+        out[i0:i1] = (r - ((r >> 31) << 32)).to(torch.int32)
+    return out

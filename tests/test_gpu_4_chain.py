@@ -282,3 +282,35 @@ def test_chain_rows_rejects():
     with pytest.raises(lb.LowbitError) as e:  # the SiLU-mul epilogue is single-row
         lb.Chain([(2, 64, 256, pc, ps, x, y, 0, lb.EPI_SILU_MUL)], rows=2)
     assert e.value.status == lb.E_SHAPE
+
+
+@pytest.mark.parametrize("N", [32752, 32768])
+def test_chain_binary_codes_near_2_gib(N):
+    """A binary stage of K = 524288 whose packed codes come to 2^31 - 2^20
+    bytes (three row-blocks per streaming wave, 32-bit buffer offsets close
+    to their limit) and to exactly 2^31 bytes (the two-row-block variant
+    with 64-bit addresses).  The packed codes are raw counter words, every
+    bit a fair sign, so no unpacked copy is made; sampled row-blocks are
+    unpacked by the oracle and checked against its product."""
+    K = 524288
+    GQ, NB = K // 512, N // 16
+    print(f"chain binary N={N} K={K}: {NB * GQ * 1024} code bytes", flush=True)
+    pc = synth.device_u32(SEED, 301, NB * GQ * 256, "cuda").view(torch.uint8)
+    ps = synth.device_scales(SEED, 302, N, K // 128, "cuda").reshape(-1)  # in packed order
+    xh = synth.normal_bf16(SEED, 303, 1, K)
+    x = dev(xh.view(np.int16)).view(torch.bfloat16)[0]
+    y = torch.full((N,), float("nan"), device="cuda")
+    chain = lb.Chain([(1, N, K, pc, ps, x, y, 0)], x_dtype=lb.BF16, y_dtype=lb.F32)
+    chain.run()
+    torch.cuda.synchronize()
+    assert chain.failed_waits() == 0
+    chain.close()
+    yc = y.cpu().numpy()
+    assert not np.isnan(yc).any()
+    for rb in (0, 1, NB // 2 + 1, NB - 2, NB - 1):
+        pcb = pc[rb * GQ * 1024:(rb + 1) * GQ * 1024].cpu().numpy()
+        psb = ps[rb * GQ * 64:(rb + 1) * GQ * 64].cpu().numpy().view(np.uint16)
+        codes, scales, bad = O.unpack(1, 16, K, pcb, psb)
+        assert bad == 0
+        yref, absY = O.matmul(codes, scales, O.X_BF16, xh)
+        assert_within(yc[None, 16 * rb:16 * (rb + 1)], yref, absY, what=f"row-block {rb}")

@@ -16,6 +16,9 @@ def test_torch_and_numpy_generators_agree_on_cpu():
     s1 = synth.group_scales(1001, 8, 33, 5)
     s2 = synth.device_scales(1001, 8, 33, 5, "cpu").numpy().view(np.uint16)
     assert np.array_equal(s1, s2)
+    w1 = synth.rand_u32(1001, 9, np.arange(1000, dtype=np.uint64))
+    w2 = synth.device_u32(1001, 9, 1000, "cpu", chunk=77).numpy().view(np.uint32)
+    assert np.array_equal(np.asarray(w1, np.uint32), w2)
 
 
 def test_row_subsets_regenerate_the_same_rows():
