@@ -8,7 +8,8 @@ layers are regenerated on the host from their tensor ids and must meet the
 oracle tolerance.  Sequential decode (waits, gate/up with the SiLU-mul
 epilogue feeding the down projection, bf16 outputs; bench.chain_for): the
 last layer's outputs are final and are checked, down against the oracle
-applied to the GPU's own z."""
+applied to the GPU's own z.  Also the five-row verification pass and the
+256 one-product launches replayed as a HIP graph."""
 import numpy as np
 import pytest
 import torch
@@ -113,3 +114,75 @@ def test_decode_step_dependent_sampled(fmt):
     codes, scales = weights_rows(fmt, last, DN, rows)
     yref, absY = O.matmul(codes, scales, O.X_BF16, zbits)
     assert_within(to_np(outs[DN])[rows][None], yref, absY, bf16_out=True, what="down")
+
+
+def test_verify_pass_sampled():
+    """bench.py's verification pass: five bf16 activation rows through all
+    256 ternary products of the step in one chain (rows = 5)."""
+    print("decode step: verification pass, 5 rows", flush=True)
+    M, fmt = 5, 2
+    W = bench.build_model(lb, synth, torch, fmt, bench.LAYERS)
+    xvh = [synth.normal_bf16(bench.SEED, 950 + j, M, K) for j, (_, _, K) in enumerate(bench.MATS)]
+    xv = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in xvh]
+    yv = [[torch.full((M, N), float("nan"), device="cuda") for _, N, _ in bench.MATS]
+          for _ in range(bench.LAYERS)]
+    stages = [(fmt, N, K, W[l][j][0], W[l][j][1], xv[j], yv[l][j], 0)
+              for l in range(bench.LAYERS) for j, (_, N, K) in enumerate(bench.MATS)]
+    chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32, rows=M)
+    chain.run()
+    torch.cuda.synchronize()
+    assert chain.failed_waits() == 0
+    chain.close()
+    for l in (0, bench.LAYERS - 1):
+        for j, (name, N, K) in enumerate(bench.MATS):
+            assert not torch.isnan(yv[l][j]).any(), f"layer {l} {name}: outputs not written"
+            rows = sample_rows(N, 13 * l + j)
+            codes, scales = weights_rows(fmt, l, j, rows)
+            yref, absY = O.matmul(codes, scales, O.X_BF16, xvh[j])
+            assert_within(yv[l][j].cpu().numpy()[:, rows], yref, absY, what=f"layer {l} {name}")
+
+
+def test_separate_launches_graph_replays():
+    """bench.py's `separate` mode: one lowbit_gemv launch per product, the
+    step captured as one HIP graph.  Every replay (with eager launches and
+    synchronisations between them) equals the eager run bit for bit, and a
+    sample of the eager run meets the oracle."""
+    print("decode step: 256 launches as one HIP graph", flush=True)
+    fmt = 2
+    W = bench.build_model(lb, synth, torch, fmt, bench.LAYERS)
+    xh, xs = step_inputs()
+    ys = [[torch.empty(N, device="cuda") for _, N, _ in bench.MATS] for _ in range(bench.LAYERS)]
+
+    def step():
+        for l in range(bench.LAYERS):
+            for j, (_, N, K) in enumerate(bench.MATS):
+                lb.gemv(fmt, N, K, W[l][j][0], W[l][j][1], xs[j], y=ys[l][j], y_dtype=lb.F32)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()  # eager (allocates the split-K workspace outside the capture)
+    torch.cuda.synchronize()
+    eager = [[y.clone() for y in layer] for layer in ys]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for layer in ys:
+            for y in layer:
+                y.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        for l in range(bench.LAYERS):
+            for j in range(len(bench.MATS)):
+                assert torch.equal(ys[l][j], eager[l][j]), f"replay {rep} layer {l} product {j}"
+        with torch.cuda.stream(stream):  # eager work between replays
+            lb.gemv(fmt, 5120, 5120, W[0][1][0], W[0][1][1], xs[1], y_dtype=lb.F32)
+        torch.cuda.synchronize()
+    del graph
+    for j, (name, N, K) in enumerate(bench.MATS):
+        rows = sample_rows(N, 7 + j)
+        codes, scales = weights_rows(fmt, bench.LAYERS - 1, j, rows)
+        yref, absY = O.matmul(codes, scales, O.X_BF16, xh[j])
+        assert_within(eager[-1][j].cpu().numpy()[rows][None], yref, absY, what=f"last layer {name}")
