@@ -354,10 +354,8 @@ __device__ __attribute__((always_inline)) inline Item item_at(const FArgs& a, in
 struct QuadPtr {
   const uint8_t* c;
   const uint8_t* s;
-  const uint8_t* c2;  // binary waves of two or three row-blocks: the second one's codes and scales
+  const uint8_t* c2;  // binary waves of two row-blocks: the second one's codes and scales
   const uint8_t* s2;
-  const uint8_t* c3;  // (three: the third one's)
-  const uint8_t* s3;
   int nq;
   bool p1_last;  // 2-bit: the last quad's second word block is clamped onto its first
 };
@@ -376,22 +374,14 @@ __device__ __attribute__((always_inline)) inline QuadPtr quad_ptr(const FArgs& a
   }
   const uint8_t* sb = a.pscales ? (const uint8_t*)a.pscales : a.pcodes;
   p.s = sb + ((rbc * a.GQ + it.q0) * 16 + (L & 15)) * 8;
-  if constexpr (RB >= 2) {
-    static_assert(FMT == 1, "several row-blocks per wave: binary only");
+  if constexpr (RB == 2) {
+    static_assert(FMT == 1, "two row-blocks per wave: binary only");
     const int64_t rbc2 = it.rb + 1 < a.NB ? it.rb + 1 : rbc;  // past the end: a dummy re-read
     p.c2 = a.pcodes + (rbc2 * a.GQ + it.q0) * 1024 + 16 * L;
     p.s2 = sb + ((rbc2 * a.GQ + it.q0) * 16 + (L & 15)) * 8;
   } else {
     p.c2 = p.c;
     p.s2 = p.s;
-  }
-  if constexpr (RB == 3) {
-    const int64_t rbc3 = it.rb + 2 < a.NB ? it.rb + 2 : rbc;
-    p.c3 = a.pcodes + (rbc3 * a.GQ + it.q0) * 1024 + 16 * L;
-    p.s3 = sb + ((rbc3 * a.GQ + it.q0) * 16 + (L & 15)) * 8;
-  } else {
-    p.c3 = p.c2;
-    p.s3 = p.s2;
   }
   p.nq = it.nq;
   p.p1_last = 2 * (it.q0 + it.nq - 1) + 1 >= a.GP;
