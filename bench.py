@@ -430,6 +430,8 @@ def main():
     ap.add_argument("--modes", default="chain,chain_dep,separate",
                     help="decode-step modes to time, headline first (chain, chain_dep, separate)")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-other-format", action="store_true",
+                    help="skip the decode step in the other weight format")
     ap.add_argument("--verify-rows", type=int, default=5,
                     help="rows of the small-M verification pass through the whole step (0: skip)")
     args = ap.parse_args()
@@ -451,6 +453,19 @@ def main():
     ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
     roof["measured_read_gb_s"] = round(read_gbs, 1)
     roof["frac_of_measured_read"] = round(roof["achieved"] / read_gbs, 4)
+    # the same step with the other weight format (the workload has binary and
+    # ternary variants): streaming and sequential chains
+    other = None
+    if not args.no_other_format:
+        a2 = argparse.Namespace(**vars(args))
+        a2.fmt = 1 if args.fmt == 2 else 2
+        a2.modes = "chain,chain_dep"
+        a2.verify_rows = 0
+        oms, ogbs, obytes, oroof, _, omodes = bench_decode(a2, lb, synth, torch, np)
+        other = {"format": FMT_NAMES[a2.fmt], "mode": "chain", "ms_per_step": round(oms, 4),
+                 "gb_s": round(ogbs, 1), "pct_hbm_peak": round(100 * ogbs / HBM_PEAK_GBS, 1),
+                 "tok_s": round(1000.0 / oms, 2), "bytes_per_step": obytes,
+                 "kernel": oroof["kernel"], "decode_modes": omodes}
 
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",
@@ -475,6 +490,8 @@ def main():
                    "decode_modes": modes_out},
         "roofline": roof,
     }
+    if other is not None:
+        out["config"]["decode_" + other["format"].split("-")[0]] = other
     if not args.no_gemm:
         pp = {}
         for xk, peak in (("bf16", MFMA_PEAK_F16_TFLOPS), ("i8", MFMA_PEAK_I8_TOPS)):
