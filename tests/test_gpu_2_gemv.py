@@ -118,8 +118,9 @@ def test_int8_activations(fmt, N, K):
     assert_within(yf.cpu().numpy()[None], yref, absY, what="i8 float")
 
 
+# (20480, 5120): two waves of five quads per row-block (rounds of five loads)
 @pytest.mark.parametrize("N,K", [(37, 384), (256, 1024), (5120, 5120), (300, 17408), (16, 128),
-                                 (48, 640), (16, 393216)])
+                                 (48, 640), (16, 393216), (20480, 5120)])
 def test_sign_activations_xor_popcount(N, K):
     codes, scales, pc, ps = make(1, N, K, tid=51)
     xb = synth.sign_bits(SEED, 53, 1, K)

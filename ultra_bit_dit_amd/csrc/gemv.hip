@@ -1791,9 +1791,8 @@ struct SArgs {
 // at bit offsets base and base + 32 of the group (base = 64 (q & 1) +
 // 16 (q >> 1)); bit b of the word holds slot 8 (3 - (b & 3)) + (b >> 2),
 // a 4 x 8 bit transpose of the slot-ordered word.
-__device__ inline uint32_t sign_word(const uint8_t* xbits, int64_t g, int q) {
+__device__ inline uint32_t sign_word(const uint8_t* gp, int q) {
   const int base = 64 * (q & 1) + 16 * (q >> 1);
-  const uint8_t* gp = xbits + g * (kGroup / 8);
   const uint32_t v = (uint32_t)*(const uint16_t*)(gp + base / 8) |
                      ((uint32_t)*(const uint16_t*)(gp + base / 8 + 4) << 16);
   uint32_t w = 0;
@@ -1804,9 +1803,10 @@ __device__ inline uint32_t sign_word(const uint8_t* xbits, int64_t g, int q) {
   return w;
 }
 
-constexpr int kSignQB = 8;  // quads of codes a wave holds in registers per round
-
-template <int YK>
+// QB: quads of codes a wave loads per round (every load of a round is issued
+// before any of it is used; loads past the wave's range are clamped onto its
+// last quad, so the launch picks QB to fit the wave's quad count)
+template <int YK, int QB>
 __global__ __launch_bounds__(1024) void gemv_sign(SArgs a) {
   __shared__ float red_f[kMaxWaves][64];
   __shared__ int red_i[kMaxWaves][64];
@@ -1819,33 +1819,45 @@ __global__ __launch_bounds__(1024) void gemv_sign(SArgs a) {
   const uint2* ps2 = (const uint2*)a.pscales;
   // the first round's codes and scales go out before the row's sign words
   // are built (they do not depend on x)
-  u4 cw[kSignQB];
-  uint2 sc[kSignQB];
+  u4 cw[QB];
+  uint2 sc[QB];
   auto load_round = [&](int64_t base) {
 #pragma unroll
-    for (int i = 0; i < kSignQB; i++) {
+    for (int i = 0; i < QB; i++) {
       const int64_t gq = min<int64_t>(base + i, q1 - 1);  // clamped into the wave's range
       cw[i] = __builtin_nontemporal_load(&pc4[(rb * a.GQ + gq) * 64 + L]);
       sc[i] = a.pscales ? ps2[(rb * a.GQ + gq) * 16 + r] : make_uint2(0x3C003C00u, 0x3C003C00u);
     }
   };
   if (q0 < q1) load_round(q0);
-  // this row's sign words, built once per workgroup
-  for (int64_t i = threadIdx.x; i < a.GQ * 16; i += blockDim.x) {
-    const int t = (int)(i & 3), qq = (int)((i >> 2) & 3);
-    const int64_t g = 4 * (i >> 4) + t;
-    xw_lds[i] = g < a.G ? sign_word(a.xbits, g, qq) : 0u;
+  // this row's sign words, built once per workgroup: the raw sign bits (16
+  // bytes per group) are copied into the words' LDS area with 16-byte loads,
+  // then 16 lanes of one wave rebuild each quad's 16 words in place (a quad's
+  // words depend only on its own 64 raw bytes, and a wave's reads of them
+  // complete before its writes)
+  {
+    const uint4* xg = (const uint4*)a.xbits;
+    uint4* xl = (uint4*)xw_lds;
+    for (int64_t i = threadIdx.x; i < 4 * a.GQ; i += blockDim.x)
+      xl[i] = i < a.G ? xg[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  for (int64_t qb = 4 * (int64_t)w + q; qb < a.GQ; qb += 4 * (int64_t)S) {
+    const int t = r & 3, qq = r >> 2;
+    const int64_t g = 4 * qb + t;
+    const uint32_t v = g < a.G ? sign_word((const uint8_t*)xw_lds + 16 * g, qq) : 0u;
+    xw_lds[qb * 16 + r] = v;
   }
   __syncthreads();
   const uint4* xw4 = (const uint4*)xw_lds;
   float acc = 0.f;
   int iacc = 0;
-  // up to kSignQB quads per round: every load of a round is issued before
+  // up to QB quads per round: every load of a round is issued before
   // any of it is used
-  for (int64_t base = q0; base < q1; base += kSignQB) {
+  for (int64_t base = q0; base < q1; base += QB) {
     if (base != q0) load_round(base);
 #pragma unroll
-    for (int i = 0; i < kSignQB; i++) {
+    for (int i = 0; i < QB; i++) {
       const int64_t gq = base + i;
       if (gq < q1) {
         const uint4 xv = xw4[gq * 4 + q];
@@ -1883,6 +1895,25 @@ __global__ __launch_bounds__(1024) void gemv_sign(SArgs a) {
   }
 }
 
+// quads per load round for waves of `qpw` quads: as few rounds as rounds of
+// 8 allow (each round waits for its loads), then the smallest round that
+// still covers the quads in that many (fewest clamped duplicate loads)
+int pick_sign_round(int64_t qpw) {
+  const int64_t rounds = cdiv(qpw < 1 ? 1 : qpw, (int64_t)8);
+  const int64_t need = cdiv(qpw < 1 ? 1 : qpw, rounds);
+  for (int qb : {2, 4, 5, 8})
+    if (qb >= need) return qb;
+  return 8;
+}
+
+template <int QB>
+hipError_t launch_sign_qb(int ykind, dim3 grid, dim3 block, size_t lds, hipStream_t s, const SArgs& k) {
+  if (ykind == YK_F32) hipLaunchKernelGGL((gemv_sign<YK_F32, QB>), grid, block, lds, s, k);
+  else if (ykind == YK_BF16) hipLaunchKernelGGL((gemv_sign<YK_BF16, QB>), grid, block, lds, s, k);
+  else hipLaunchKernelGGL((gemv_sign<YK_I32, QB>), grid, block, lds, s, k);
+  return hipGetLastError();
+}
+
 int pick_waves(int64_t NB, int64_t GQ) {
   const int64_t target = 2560;  // resident waves wanted across the chip
   int64_t S = cdiv(target, NB);
@@ -1910,10 +1941,11 @@ hipError_t launch_gemv_sign(const SignArgs& g, hipStream_t s) {
   if (g.K > kSignMaxK || lds > 48 * 1024) return hipErrorInvalidValue;
   int S = pick_waves(NB, k.GQ);
   dim3 grid((unsigned)NB), block(64 * S);
-  if (g.ykind == YK_F32) hipLaunchKernelGGL(gemv_sign<YK_F32>, grid, block, lds, s, k);
-  else if (g.ykind == YK_BF16) hipLaunchKernelGGL(gemv_sign<YK_BF16>, grid, block, lds, s, k);
-  else hipLaunchKernelGGL(gemv_sign<YK_I32>, grid, block, lds, s, k);
-  return hipGetLastError();
+  const int QB = pick_sign_round(cdiv(k.GQ, (int64_t)S));
+  if (QB == 2) return launch_sign_qb<2>(g.ykind, grid, block, lds, s, k);
+  if (QB == 4) return launch_sign_qb<4>(g.ykind, grid, block, lds, s, k);
+  if (QB == 5) return launch_sign_qb<5>(g.ykind, grid, block, lds, s, k);
+  return launch_sign_qb<8>(g.ykind, grid, block, lds, s, k);
 }
 
 }  // namespace lowbit
