@@ -105,6 +105,8 @@ struct FArgs {
   float x_scale;
   int xkind;
   int epi;        // 1: SiLU-mul epilogue (chains, M = 1)
+  const uint8_t* xst;  // one-product kernel, M > 1: the slice images staged once
+                       // per call (else null: each workgroup stages its slice)
 };
 
 // Staging of quads [q0, q1) of the M activation rows into LDS by all threads
@@ -900,6 +902,26 @@ __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, 
   }
 }
 
+// The one-product kernel with several activation rows: item `it`'s slice
+// image, staged once per call into a.xst (slices qmax quads apart), copied
+// into LDS with direct global -> LDS copies (1 KiB per wave instruction)
+// and waited for.
+template <int FMT>
+__device__ __attribute__((always_inline)) inline void copy_image(const FArgs& a, const Item& it,
+                                                                 const Lds& l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+  const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
+  const int64_t bytes = (int64_t)it.nq * 16 * a.MA * 33;
+  const uint8_t* src = a.xst + it.ks * qmax * 16 * a.MA * 33;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
+  for (int64_t off = 1024 * (int64_t)w; off < bytes; off += 1024 * (int64_t)W)
+    if (off + 16 * lane < bytes)
+      __builtin_amdgcn_global_load_lds(src + off + 16 * lane, (lds_u8_t*)(l.xa + off), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+#endif
+}
+
 // One work item, loads issued all at once: the body of the one-product
 // kernel (CHAIN false) and of the chain kernel with waits (CHAIN: outputs
 // are device-coherent; WAIT: the weight loads go out first, then the
@@ -917,9 +939,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   lds_init<FMT>(l);
 
   XRegs xr;
+  const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
   if constexpr (!WAIT) {
     // activation loads of the first staging rounds go out first
-    if (stage) stage_load_rounds<XK, false>(a, it, xr);
+    if (stage && !pre) stage_load_rounds<XK, false>(a, it, xr);
   }
   // every code and scale of the wave is requested before anything else
   Quad<FMT> qd[QM];
@@ -947,7 +970,8 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     __syncthreads();
     stage_load_rounds<XK, true>(a, it, xr);
   }
-  if (stage) stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
+  if (pre) copy_image<FMT>(a, it, l);
+  else if (stage) stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
   __syncthreads();
 
   float acc[MX];
@@ -978,6 +1002,22 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     }
   }
   item_output<XK, MX, YK, CHAIN>(a, it, acc, iacc);
+}
+
+// Slice images of a one-product call with several activation rows, staged
+// once into xst (slice ks at ks * qmax quads): block (rd, ks) converts
+// round rd of slice ks, the units and lanes of the in-workgroup staging.
+template <int FMT, int XK>
+__global__ __launch_bounds__(256) void stage_images(FArgs a, uint8_t* xst) {
+  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  const int64_t ks = blockIdx.y, rd = blockIdx.x;
+  const Item it = item_at<FMT>(a, 0, ks);
+  const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
+  uint8_t* xa = xst + ks * qmax * 16 * a.MA * 33;
+  uint8_t* xe = xa + (int64_t)it.nq * 16 * a.MA * 32;
+  uint4 r0, r1;
+  stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
+  stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe);
 }
 
 template <int FMT, int XK, int MX, int YK, int QM>
@@ -1043,6 +1083,7 @@ __device__ __attribute__((always_inline)) inline FArgs load_args(FArgsTab t, int
   a.x_scale = t[s].x_scale;
   a.xkind = t[s].xkind;
   a.epi = t[s].epi;
+  a.xst = nullptr;
   return a;
 }
 
@@ -1531,8 +1572,16 @@ hipError_t launch_x(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, si
 
 }  // namespace
 
+// bytes of the slice images a one-product call with M > 1 stages once
+size_t image_bytes(const Plan& p, int fmt, int64_t M) {
+  if (M <= 1) return 0;
+  const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
+  return align256((size_t)(p.KS * qmax * 16 * p.MA * 33));
+}
+
 size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
-  return make_plan(fmt, N, K, M, xkind).bytes;
+  const Plan p = make_plan(fmt, N, K, M, xkind);
+  return p.bytes + image_bytes(p, fmt, M);
 }
 
 hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
@@ -1559,6 +1608,26 @@ hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
   k.x_scale = g.x_scale;
   k.xkind = g.xkind;
   k.epi = 0;
+  k.xst = nullptr;
+  if (g.M > 1) {
+    // several rows: the slice images are staged once, then copied by every
+    // workgroup (instead of each converting M x K activations itself)
+    k.xst = (const uint8_t*)g.ws + p.bytes;
+    const int64_t qmax = g.fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
+    const dim3 sgrid((unsigned)cdiv(qmax * 64 * g.M, (int64_t)256), (unsigned)p.KS);
+    uint8_t* xst = (uint8_t*)g.ws + p.bytes;
+    const bool f32 = g.xkind == XK_F32, i8 = g.xkind == XK_I8;
+#define STAGE_IMG(F)                                                                          \
+  {                                                                                           \
+    if (f32) hipLaunchKernelGGL((stage_images<F, XK_F32>), sgrid, dim3(256), 0, s, k, xst);   \
+    else if (i8) hipLaunchKernelGGL((stage_images<F, XK_I8>), sgrid, dim3(256), 0, s, k, xst); \
+    else hipLaunchKernelGGL((stage_images<F, XK_BF16>), sgrid, dim3(256), 0, s, k, xst);      \
+  }
+    if (g.fmt == 1) STAGE_IMG(1)
+    else if (g.fmt == 2) STAGE_IMG(2)
+    else STAGE_IMG(3)
+#undef STAGE_IMG
+  }
   const dim3 grid((unsigned)(p.NRG * p.KS)), block((unsigned)(64 * p.W));
   if (g.fmt == 1) return launch_x<1, kQuadsBinary>(g, k, grid, block, p.lds, s);
   if (g.fmt == 2) return launch_x<2, kQuadsTernary>(g, k, grid, block, p.lds, s);
@@ -1672,6 +1741,7 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
     k.x_scale = 1.0f;
     k.xkind = xkind;
     k.epi = st[i].epi;
+    k.xst = nullptr;
   }
   if (first[S] > 0x7FFFFFFF || cnt_words > 0x7FFFFFFF) return hipErrorInvalidValue;
   // layout of the one allocation
