@@ -223,3 +223,50 @@ def test_quantize_act_i8_paths(K, offset):
     assert np.array_equal(sx.cpu().numpy(), sx_ref)
     assert sx_ref[2] == 0 and not q_ref[2].any()
     assert q_ref[3][:8].tolist() == [127, 2, -4, 0, 2, 0, -126, 64]
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_small_m_graph_replays(fmt):
+    """Small-M products (M = 5: the slice images staged once per call, then
+    the product) captured as one HIP graph: every replay, with eager
+    launches and synchronisations between replays, equals the eager run bit
+    for bit; the eager run meets the oracle.  Two shapes, one with K-slices."""
+    M = 5
+    shapes = [(2048, 5120), (640, 17408)]
+    mats, Xs, Ys, refs = [], [], [], []
+    for j, (N, K) in enumerate(shapes):
+        codes, scales, pc, ps = make(fmt, N, K, tid=95 + 2 * j)
+        X = synth.normal_bf16(SEED, 99 + j, M, K)
+        mats.append((pc, ps))
+        Xs.append(dev(X.view(np.int16)).view(torch.bfloat16))
+        Ys.append(torch.empty((M, N), device="cuda"))
+        refs.append((X, codes, scales))
+    stream = torch.cuda.Stream()
+
+    def step():
+        for j, (N, K) in enumerate(shapes):
+            lb.gemm(fmt, M, N, K, mats[j][0], mats[j][1], Xs[j], Y=Ys[j])
+
+    with torch.cuda.stream(stream):
+        step()  # eager (sizes the workspace outside the capture)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in Ys]
+    for j, (X, codes, scales) in enumerate(refs):
+        yref, absY = O.matmul(codes, scales, O.X_BF16, X)
+        assert_within(eager[j].cpu().numpy(), yref, absY, what=f"shape {j}")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in Ys:
+            y.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        for j in range(len(shapes)):
+            assert torch.equal(Ys[j], eager[j]), f"replay {rep} shape {j}"
+        with torch.cuda.stream(stream):  # eager work between replays
+            lb.gemm(fmt, M, 2048, 5120, mats[0][0], mats[0][1], Xs[0])
+        torch.cuda.synchronize()
+    del graph
