@@ -71,28 +71,6 @@ __device__ inline uint32_t bf16_rne(float f) {
 //   xa[((ql * 16 + t * 4 + kb) * MA + a) * 32 + e]   fp8 bytes (group t of the quad)
 //   xe[((ql * 4 + b) * MA + a) * 4 + t]             E8M0 exponents
 
-__device__ inline void load8(int xkind, const void* X, int64_t idx, float (&v)[8]) {
-  if (xkind == XK_BF16) {
-    const uint4 w = *(const uint4*)((const uint16_t*)X + idx);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v[2 * j] = __uint_as_float(u[j] << 16);
-      v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-    }
-  } else if (xkind == XK_F32) {
-    const float4 a = *(const float4*)((const float*)X + idx);
-    const float4 b = *(const float4*)((const float*)X + idx + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint2 w = *(const uint2*)((const int8_t*)X + idx);
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-      v[j] = (float)(int8_t)(((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFF);
-  }
-}
-
 struct FArgs {
   const uint8_t* pcodes;
   const uint16_t* pscales;

@@ -24,10 +24,6 @@
 namespace lowbit {
 namespace {
 
-__device__ __forceinline__ double bf16_f64(uint16_t b) {
-  return (double)__uint_as_float((uint32_t)b << 16);
-}
-
 // fp64 -> binary16 bits, round to nearest even, from the bit pattern
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
   const uint64_t b = (uint64_t)__double_as_longlong(x);
