@@ -942,7 +942,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
           if (L == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
-        __builtin_amdgcn_s_sleep(10);
+        __builtin_amdgcn_s_sleep(2);
       }
     }
     __syncthreads();
