@@ -170,9 +170,13 @@ int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
  *   only for x_dtype I8 / SIGN1 with pscales == NULL: y = exact integer
  *   sum_k code * q (or the signed bit agreement count), x_scale ignored.
  * Alignment: pcodes, pscales, x 16 bytes; y 4 bytes.  Uses a per-stream
- * device workspace owned by the library (allocated on first use on a stream;
- * calls on one stream are ordered, calls on different streams do not share
- * it). */
+ * device workspace owned by the library (allocated on first use on a stream
+ * and grown, after synchronizing that stream, when a call needs more; calls
+ * on one stream are ordered, calls on different streams do not share it).
+ * While the stream is being captured into a graph the workspace cannot
+ * grow: such a call returns LOWBIT_E_NOMEM unless an earlier call on the
+ * stream already needed as much (run the captured calls once eagerly
+ * first). */
 int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* x, float x_scale,
                 int y_dtype, void* y, void* stream);
