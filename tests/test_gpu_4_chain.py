@@ -198,8 +198,17 @@ def test_chain_epilogue_rejects():
 def test_chain_rows(fmt, wait, rows):
     """Chains of small-M products (every stage takes rows x K activations):
     each row of each stage within the oracle tolerance, on ragged N, K from
-    one group to 136 groups, and on repeated runs."""
+    one group to 136 groups, and on repeated runs.  Ternary rows with bf16
+    activations take three split terms each, so at most five rows."""
     shapes = [(640, 1024), (100, 5120), (256, 17408), (48, 128), (3000, 2560)]
+    if fmt != 1 and rows > 5:
+        _, _, pc, ps = make(fmt, 64, 256, tid=498)
+        x = torch.zeros((rows, 256), dtype=torch.bfloat16, device="cuda")
+        y = torch.zeros((rows, 64), device="cuda")
+        with pytest.raises(lb.LowbitError) as e:
+            lb.Chain([(fmt, 64, 256, pc, ps, x, y, wait)], x_dtype=lb.BF16, rows=rows)
+        assert e.value.status == lb.E_SHAPE
+        return
     mats, xs, ys, refs = [], [], [], []
     for j, (N, K) in enumerate(shapes):
         codes, scales, pc, ps = make(fmt, N, K, tid=500 + 2 * j)
@@ -253,7 +262,7 @@ def test_chain_rows_rejects():
     _, _, pc, ps = make(2, 64, 256, tid=600)
     x = torch.zeros((9, 256), dtype=torch.bfloat16, device="cuda")
     y = torch.zeros((9, 64), device="cuda")
-    for rows, xdt in ((9, lb.BF16), (5, lb.F32), (0, lb.BF16)):
+    for rows, xdt in ((6, lb.BF16), (9, lb.BF16), (5, lb.F32), (0, lb.BF16)):
         with pytest.raises(lb.LowbitError) as e:
             lb.Chain([(2, 64, 256, pc, ps, x, y, 0)], x_dtype=xdt, rows=rows)
         assert e.value.status == lb.E_SHAPE

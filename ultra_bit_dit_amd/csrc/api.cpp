@@ -121,7 +121,9 @@ int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const
   return hip_status(launch_gemm(g, s));
 }
 
-int max_small_m(int x_dtype) { return x_dtype == LOWBIT_F32 ? 16 / kSplitF32 : 16 / kSplitBF16; }
+// activation rows the batch-1 kernels take at once: 16 rows of A over the
+// split terms of one row
+int max_small_m(int fmt, int x_dtype) { return 16 / split_terms(fmt, x_dtype); }
 
 }  // namespace
 
@@ -241,7 +243,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
       !aligned(Y, 16) || (x_scales && !aligned(x_scales, 4)))
     return LOWBIT_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (!sign && M <= max_small_m(x_dtype))
+  if (!sign && M <= max_small_m(fmt, x_dtype))
     return run_gemv_mfma(fmt, M, N, K, pcodes, pscales, x_dtype, X, 1.0f,
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
@@ -259,9 +261,9 @@ int lowbit_chain_create_rows(int n_stages, const lowbit_gemv_stage* stages, int6
   if (n_stages < 1) return LOWBIT_E_SHAPE;
   if (x_dtype != LOWBIT_F32 && x_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
   if (y_dtype != LOWBIT_F32 && y_dtype != LOWBIT_BF16) return LOWBIT_E_UNSUPPORTED;
-  if (rows < 1 || rows > max_small_m(x_dtype)) return LOWBIT_E_SHAPE;
   const int fmt = stages[0].fmt;
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (rows < 1 || rows > max_small_m(fmt, x_dtype)) return LOWBIT_E_SHAPE;
   std::vector<ChainStage> st(n_stages);
   for (int i = 0; i < n_stages; i++) {
     const lowbit_gemv_stage& g = stages[i];

@@ -34,12 +34,23 @@ __device__ inline float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
 }
 
-// x staging parameters for the MFMA GEMV: number of fp8 split terms per
-// activation row and the exponent step between terms
-constexpr int kSplitBF16 = 2;
-constexpr int kSplitF32 = 4;
-constexpr int kSplitI8 = 2;
-constexpr int kSplitShift = 4;  // each term is scaled 2^-4 relative to the previous
+// Activation operand scheme of the batch-1 / small-M kernels.  Activations
+// enter v_mfma_scale_f32_16x16x128_f8f6f4 as R low-precision split terms per
+// element, one row of A per term, each 32-element block with its own E8M0
+// exponent: E puts the block maximum in [2^kTop, 2^(kTop+1)) and term r
+// carries exponent E - kShift r.
+//   * ternary weights, bf16 activations: three e5m2 terms (3 significant bits
+//     each; exact for every element within 2^30 of its block maximum);
+//   * binary weights, bf16: two e4m3 terms (exact within 2^13 of the block
+//     maximum; smaller elements err by at most 2^-21 of it, and a binary row
+//     always weighs the maximum, so the error stays far inside the bound);
+//   * fp32: four e4m3 terms (16 significant bits);
+//   * int8 q: 16 (q >> 4) + (q & 15), exact.
+// Inputs the terms do not carry accurately enough are detected while staging
+// and their products are recomputed exactly (see the kernels).
+constexpr int split_terms(int fmt, int xkind) {
+  return xkind == 1 /* F32 */ ? 4 : (xkind == 2 /* BF16 */ && fmt != 1) ? 3 : 2;
+}
 
 enum XKind { XK_F32 = 1, XK_BF16 = 2, XK_I8 = 3, XK_SIGN1 = 4 };
 enum YKind { YK_F32 = 1, YK_BF16 = 2, YK_I32 = 5 };

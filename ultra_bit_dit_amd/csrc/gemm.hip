@@ -36,7 +36,8 @@ struct KArgs {
   void* y;
   float* part;              // split-K partial tiles
   uint32_t* cnt;            // zero-initialised arrival counters
-  int64_t M, N, G, GQ, GP, NB, MT, NT;
+  const uint16_t* x;        // the bf16 activations (exact recomputation of overflowed lists)
+  int64_t M, N, K, G, GQ, GP, NB, MT, NT;
   int KS;
   int row_fast;             // tile order: row tile fastest (else column tile fastest)
 };
@@ -157,10 +158,24 @@ __device__ __forceinline__ bool split_reduce(const KArgs& a, int64_t tile, int k
 // partial is scaled by the fp16 group scale in fp32 (int8 with unit scales:
 // exact integer per group).
 constexpr int kRT = 16;                  // activation rows per A-tile (one term each)
+constexpr int kSplitShift = 4;           // binades between the two e4m3 terms
 constexpr int kATBytes = 64 * 32 + 64;   // one A-tile of one group: fp8 bytes + exponents
 constexpr int kF8BM = 64;                // activation rows per workgroup tile (4 x 2 A-tiles)
 constexpr int kF8Threads = 512;          // 8 waves: 2 (rows) x 4 (columns)
-constexpr int kF8Img = (kF8BM / kRT) * 2 * kATBytes;  // staged bytes of one workgroup tile and group
+constexpr int kF8Tiles = (kF8BM / kRT) * 2 * kATBytes;  // the 8 A-tiles of one workgroup tile and group
+// Correction lists (ternary weights, bf16 activations).  Two e4m3 terms carry
+// a bf16 element exactly when it lies within 2^13 of its 32-element block's
+// maximum; a ternary row may weigh only the smaller elements of a block, so
+// every element the terms miss is listed with its exact residual rho =
+// x - (term 0 + term 1) (an fp32 number), and the GEMM adds code x rho x
+// scale for it after the group's MFMAs.  One region per 16-row tile of the
+// image: a count, then up to kEntries entries {slot position, rho}.  N(0,1)
+// activations list about one element per 64-row tile and group; a region
+// that overflows sends its wave to an exact recomputation of its outputs.
+constexpr int kEntries = 15;
+constexpr int kRegionBytes = 8 + 8 * kEntries;  // 128
+constexpr int kHdrBytes = (kF8BM / kRT) * kRegionBytes;  // 512
+constexpr int kF8Img = kF8Tiles + kHdrBytes;  // staged bytes of one workgroup tile and group
 
 // Staging: one thread per (row m, group g, hardware block b).  Block b of a
 // group holds k = 128 g + kmap(b, i), i = 0..31 (two runs of 16); A lane
@@ -172,8 +187,11 @@ constexpr int kF8Img = (kF8BM / kRT) * 2 * kATBytes;  // staged bytes of one wor
 // then 64 exponent bytes (by lane): each 16-byte LDS read of the 64 lanes is
 // one contiguous KiB (no bank conflicts).
 // A-tile 2 rt + u holds term u of rows 16 rt .. 16 rt + 15 (A row = row % 16).
-// Rows >= M are staged as zeros.
-template <int XK>
+// Rows >= M are staged as zeros.  LIST (ternary weights, bf16): region rt of
+// the header at kF8Tiles receives the correction list of rows 16 rt ..
+// 16 rt + 15: word 0 the number of elements the terms miss, then entries
+// {row % 16 | block << 4 | slot << 6, rho bits} in (row, block, slot) order.
+template <int XK, bool LIST>
 __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t K, int64_t G,
                                                 const void* __restrict__ X,
                                                 uint8_t* __restrict__ xs) {
@@ -212,13 +230,13 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
   }
   float t0[32], t1[32];
   int e0, e1;
+  int E = 0;
   if constexpr (XK == XK_BF16) {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
     // E puts the block maximum in [128, 256) x 2^E, clamped so that both
     // terms' exponents stay representable
-    int E = 0;
     if (amax != 0.0f) {
       int ex;
       (void)frexpf(amax, &ex);
@@ -274,6 +292,55 @@ __global__ __launch_bounds__(256) void stage_f8(int64_t M, int64_t Mpad, int64_t
   }
   blk0[2048 + r + 16 * b] = (uint8_t)e0;
   blk1[2048 + r + 16 * b] = (uint8_t)e1;
+  if constexpr (LIST && XK == XK_BF16) {
+    // rho = v - (term 0 2^E + term 1 2^(E-4)), all exact in fp32 (the terms
+    // and the powers of two are exact; their sum spans few enough binades)
+    const float p0 = ldexpf(1.0f, E), p1 = ldexpf(1.0f, E - kSplitShift);
+    float rho[32];
+    uint32_t miss = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        const int i = 4 * j + h;
+        const float d0 = h == 0 ? __builtin_amdgcn_cvt_f32_fp8(w0[j], 0)
+                       : h == 1 ? __builtin_amdgcn_cvt_f32_fp8(w0[j], 1)
+                       : h == 2 ? __builtin_amdgcn_cvt_f32_fp8(w0[j], 2)
+                                : __builtin_amdgcn_cvt_f32_fp8(w0[j], 3);
+        const float d1 = h == 0 ? __builtin_amdgcn_cvt_f32_fp8(w1[j], 0)
+                       : h == 1 ? __builtin_amdgcn_cvt_f32_fp8(w1[j], 1)
+                       : h == 2 ? __builtin_amdgcn_cvt_f32_fp8(w1[j], 2)
+                                : __builtin_amdgcn_cvt_f32_fp8(w1[j], 3);
+        rho[i] = v[i] - (d0 * p0 + d1 * p1);
+        miss |= (rho[i] != 0.0f ? 1u : 0u) << i;
+      }
+    }
+    // this lane's entries follow those of the lanes before it in the
+    // wavefront (16 rows x 4 blocks of one 16-row tile and group)
+    const int lane = threadIdx.x & 63;
+    const int cnt = __popc(miss);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    uint8_t* region = xs + ((m / kF8BM) * G + g) * (int64_t)kF8Img + kF8Tiles + rt * kRegionBytes;
+    if (lane == 0) *(uint32_t*)region = (uint32_t)total;
+    if (miss) {
+      int idx = incl - cnt;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        if ((miss >> i) & 1u) {
+          if (idx < kEntries)
+            *(uint2*)(region + 8 + 8 * idx) =
+                make_uint2((uint32_t)(r | (b << 4) | (i << 6)), __float_as_uint(rho[i]));
+          idx++;
+        }
+      }
+    }
+  }
 }
 
 // ------------------------------------------------- sign activations (fp4 A)
@@ -367,6 +434,41 @@ __device__ __forceinline__ void lds_read_a(uint32_t pa, uint32_t pe, v4u (&A0)[4
       : "memory");
 }
 static_assert(kATBytes == 2112, "A-tile offsets in the LDS reads");
+
+// lds_read_a plus the entry counts of the wave's two correction regions (at
+// ph and ph + kRegionBytes), with the same wait
+__device__ __forceinline__ void lds_read_a_cnt(uint32_t pa, uint32_t pe, uint32_t ph, v4u (&A0)[4],
+                                               v4u (&A1)[4], uint32_t (&se)[4], uint32_t (&cnt)[2]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %14\n\t"
+      "ds_read_b128 %4, %14 offset:1024\n\t"
+      "ds_read_u8 %8, %15\n\t"
+      "ds_read_b128 %1, %14 offset:2112\n\t"
+      "ds_read_b128 %5, %14 offset:3136\n\t"
+      "ds_read_u8 %9, %15 offset:2112\n\t"
+      "ds_read_b128 %2, %14 offset:4224\n\t"
+      "ds_read_b128 %6, %14 offset:5248\n\t"
+      "ds_read_u8 %10, %15 offset:4224\n\t"
+      "ds_read_b128 %3, %14 offset:6336\n\t"
+      "ds_read_b128 %7, %14 offset:7360\n\t"
+      "ds_read_u8 %11, %15 offset:6336\n\t"
+      "ds_read_b32 %12, %16\n\t"
+      "ds_read_b32 %13, %16 offset:128\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A0[2]), "=&v"(A0[3]), "=&v"(A1[0]), "=&v"(A1[1]),
+        "=&v"(A1[2]), "=&v"(A1[3]), "=&v"(se[0]), "=&v"(se[1]), "=&v"(se[2]), "=&v"(se[3]),
+        "=&v"(cnt[0]), "=&v"(cnt[1])
+      : "v"(pa), "v"(pe), "v"(ph)
+      : "memory");
+}
+static_assert(kRegionBytes == 128, "region offset in the count read");
+
+// one 8-byte correction entry from LDS, waited for
+__device__ __forceinline__ uint2 lds_read_entry(uint32_t addr) {
+  uint2 v;
+  __asm__ volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return v;
+}
 
 // fp4 A operands of two consecutive sign A-tiles (1 KiB apart) at pa
 __device__ __forceinline__ void lds_read_s1(uint32_t pa, v4u (&A)[2]) {
@@ -509,6 +611,94 @@ struct CodeLds {
 // expcnt at its maximum
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 
+// Code (-1 / 0 / +1) of slot i (uniform) of group T of a quad, for this
+// lane's quarter, with few registers: 2-bit from the raw P0 / P1 words
+// (slot i = 8 j + p: z at bit 4 p + 1 - (j & 1), s two bits above it),
+// base-3 through the trit table.
+template <int FMT, int T>
+__device__ __forceinline__ int code_at(const Quad<FMT>& qd, int i, const uint32_t* t3) {
+  if constexpr (FMT == 2) {
+    const u4 c4 = qd.w[T >> 1];
+    const uint32_t p0 = (T & 1) ? c4.z : c4.x, p1 = (T & 1) ? c4.w : c4.y;
+    const int jx = i >> 3, zp = 4 * (i & 7) + 1 - (jx & 1);
+    const uint32_t w = jx < 2 ? p0 : p1;
+    const int z = (w >> zp) & 1, sg = (w >> (zp + 2)) & 1;
+    return z ? (sg ? -1 : 1) : 0;
+  } else {
+    const v8i B = decode_group<FMT>(qd, T, t3);
+    const int wi = i >> 3;
+    const uint32_t wd = (uint32_t)(wi == 0 ? B[0] : wi == 1 ? B[1] : wi == 2 ? B[2] : B[3]);
+    const uint32_t nib = (wd >> (4 * (i & 7))) & 0xFu;
+    return nib == 0x2u ? 1 : nib == 0xAu ? -1 : 0;
+  }
+}
+
+// fp4 operand B of group t of a quad, t chosen at run time
+template <int FMT>
+__device__ __forceinline__ v8i decode_group_rt(const Quad<FMT>& qd, int t, const uint32_t* t3) {
+  return t == 0 ? decode_group<FMT>(qd, 0, t3) : t == 1 ? decode_group<FMT>(qd, 1, t3)
+       : t == 2 ? decode_group<FMT>(qd, 2, t3) : decode_group<FMT>(qd, 3, t3);
+}
+
+// Exact recomputation, on the VALU, of one wave's outputs over groups
+// [g0, g1) (bf16 activations): lane L = r + 16 q multiplies quarter q of row
+// 16 rb + r by the activations of each of the wave's rows (products of
+// +-1 / 0 are exact), the quarters are added, and each group's sum is scaled
+// by its fp32 scale.  The slow path of a workgroup whose correction list
+// overflowed; the results go through LDS (ex, 2 RBW 4 words per lane) so
+// that the loops stay rolled.
+template <int FMT, int RBW>
+__device__ __attribute__((always_inline)) inline void exact_wave(const KArgs& a, int64_t mt, int wm, int64_t rb0,
+                                                     int g0, int g1, const uint32_t* t3, float* ex) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  for (int j = 0; j < RBW; j++) {
+    const int64_t rbc = rb0 + j < a.NB ? rb0 + j : a.NB - 1;
+    for (int rt = 0; rt < 2; rt++) {
+      float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+      for (int g = g0; g < g1; g++) {
+        Quad<FMT> qd;
+        load_quad_at<FMT>(a.pcodes, a.pscales, rbc, g >> 2, a.GQ, a.GP, lane, qd);
+        const v8i B = decode_group_rt<FMT>(qd, g & 3, t3);
+        const float sc = quad_scale<FMT>(qd, g & 3);
+        const int64_t k0 = (int64_t)g * kGroup + 64 * (q & 1) + 16 * (q >> 1);
+        for (int mm = 0; mm < 16; mm++) {
+          const int64_t m = mt * kF8BM + 32 * wm + 16 * rt + mm;
+          float part = 0.f;
+          if (m < a.M) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {  // slots 16 h .. 16 h + 15: k0 + 32 h + (i & 15)
+              const v4u* src = (const v4u*)(a.x + m * a.K + k0 + 32 * h);
+              const v4u w0 = src[0], w1 = src[1];
+#pragma unroll
+              for (int i = 0; i < 16; i++) {
+                const uint32_t wd = i < 8 ? w0[i >> 1] : w1[(i - 8) >> 1];
+                const float xv = __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+                const int slot = 16 * h + i;
+                const uint32_t nib = ((uint32_t)B[slot >> 3] >> (4 * (slot & 7))) & 0xFu;
+                part += nib == 0x2u ? xv : nib == 0xAu ? -xv : 0.0f;
+              }
+            }
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          if (q == (mm >> 2)) {
+            const int e = mm & 3;
+            if (e == 0) e0 = fmaf(sc, part, e0);
+            else if (e == 1) e1 = fmaf(sc, part, e1);
+            else if (e == 2) e2 = fmaf(sc, part, e2);
+            else e3 = fmaf(sc, part, e3);
+          }
+        }
+      }
+      float* o = ex + ((rt * RBW + j) * 4) * 64 + lane;
+      o[0] = e0;
+      o[64] = e1;
+      o[128] = e2;
+      o[192] = e3;
+    }
+  }
+}
+
 template <int FMT, int XK, int YK, bool SCALED, int RBW>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_f8(KArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space code: device pass only
@@ -524,6 +714,8 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     return (lds_u8*)(t == 0 ? xb0 : t == 1 ? xb1 : t == 2 ? xb2 : xb3);
   };
   constexpr bool INT = (XK == XK_I8 || S1) && !SCALED;
+  // ternary weights with bf16 activations: per-group correction lists
+  constexpr bool LIST = FMT != 1 && XK == XK_BF16;
   // wave-uniform values are kept in scalar registers (the copy addresses
   // below are then a scalar base plus a fixed per-lane offset)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -544,11 +736,11 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   // ---- copies.  Per-lane offsets stay in the same registers for the whole
   // loop (a copy's address registers must not change while it is in flight).
   const uint8_t* xs = a.xt + mt * a.G * (int64_t)IMG;
-  static_assert(kF8Img == 16 * 1024 + 512, "image = 16 KiB + 8 x 64 bytes");
+  static_assert(kF8Img == 16 * 1024 + 1024, "image = 16 KiB + 8 x 128 bytes");
   const uint32_t vo0 = 1024 * wave + 16 * lane, vo1 = vo0 + 8192;
-  const uint32_t vo2 = 16384 + 64 * wave + 16 * lane;
+  const uint32_t vo2 = 16384 + 128 * wave + 16 * lane;
   // image of group g into ring buffer t: 1 KiB chunks w and w + 8, and
-  // 64 bytes of the 512-byte tail (lanes 0..3)
+  // 128 bytes of the 1 KiB tail (lanes 0..7: exponents, correction lists)
   // (sign images: 512 bytes per wave, lanes 0..31)
   const uint32_t vs = 512 * wave + 16 * lane;
   auto xissue = [&](int g, int t) {
@@ -559,7 +751,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     } else {
       __builtin_amdgcn_global_load_lds(src + vo0, dst + 1024 * wave, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(src + vo1, dst + 1024 * (wave + 8), 16, 0, 0);
-      if (lane < 4) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 64 * wave, 16, 0, 0);
+      if (lane < 8) __builtin_amdgcn_global_load_lds(src + vo2, dst + 16384 + 128 * wave, 16, 0, 0);
     }
   };
   // this wave copies row-blocks RBW wn + HR wm .. + HR - 1 of the tile
@@ -651,6 +843,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   for (int t = 0; t < 3; t++) xissue(g0 + t < g1 ? g0 + t : g1 - 1, t);
 
   Quad<FMT> qd[RBW];
+  bool overflow = false;  // (LIST) one of the wave's correction lists overflowed
   for (int q = q0; q < q1; q++) {
 #pragma unroll
     for (int t = 0; t < 4; t++) {
@@ -671,15 +864,60 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         v8i At[4];
         uint32_t se[4];
         v4u As[2];
+        uint32_t ncorr[2] = {0u, 0u};  // (LIST) entries in the wave's two regions
         if constexpr (S1) {
           lds_read_s1((uint32_t)(uintptr_t)(ring(t) + 2 * wm * 1024) + 16 * lane, As);
         } else {
           v4u A0[4], A1[4];
-          aread(t, A0, A1, se);
+          if constexpr (LIST) {
+            const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
+            const uint32_t ph = (uint32_t)(uintptr_t)(ring(t) + kF8Tiles + 2 * wm * kRegionBytes);
+            lds_read_a_cnt(base + 16 * lane, base + 2048 + lane, ph, A0, A1, se, ncorr);
+          } else {
+            aread(t, A0, A1, se);
+          }
 #pragma unroll
           for (int i = 0; i < 4; i++)
             At[i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
                         (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+        }
+        if constexpr (LIST) {
+          // the elements the two terms miss: acc[row][col] += s code rho
+          // (added before the group's MFMA results, while few registers are live).
+          // Lane 16 b + r holds block b's codes of row r (its quarter), lane
+          // 16 lg + r the outputs of rows 4 lg .. 4 lg + 3 of the row tile.
+          const uint32_t n0 = __builtin_amdgcn_readfirstlane(ncorr[0]);
+          const uint32_t n1 = __builtin_amdgcn_readfirstlane(ncorr[1]);
+          if (n0 | n1) {
+            if (n0 > (uint32_t)kEntries || n1 > (uint32_t)kEntries) {
+              overflow = true;
+            } else {
+              const uint32_t ph = (uint32_t)(uintptr_t)(ring(t) + kF8Tiles + 2 * wm * kRegionBytes);
+#pragma unroll
+              for (int rt = 0; rt < 2; rt++) {
+                const uint32_t ne = rt == 0 ? n0 : n1;
+#pragma unroll 1
+                for (uint32_t ei = 0; ei < ne; ei++) {
+                  const uint2 ent = lds_read_entry(ph + rt * kRegionBytes + 8 + 8 * ei);
+                  const uint32_t pos = __builtin_amdgcn_readfirstlane(ent.x);
+                  const float rho = __uint_as_float(__builtin_amdgcn_readfirstlane(ent.y));
+                  const int row16 = pos & 15, b = (pos >> 4) & 3, i = (pos >> 6) & 31;
+                  const int src = 16 * b + (lane & 15);
+                  const bool dst = (lane >> 4) == (row16 >> 2);
+                  const int ev = row16 & 3;
+#pragma unroll
+                  for (int j = 0; j < RBW; j++) {
+                    const int cd = t == 0 ? code_at<FMT, 0>(qd[j], i, t3) : t == 1 ? code_at<FMT, 1>(qd[j], i, t3)
+                                 : t == 2 ? code_at<FMT, 2>(qd[j], i, t3) : code_at<FMT, 3>(qd[j], i, t3);
+                    const float cr = cd > 0 ? rho : cd < 0 ? -rho : 0.0f;
+                    const float moved = __shfl(quad_scale<FMT>(qd[j], t) * cr, src);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[rt][j][e] += (dst && ev == e) ? moved : 0.0f;
+                  }
+                }
+              }
+            }
+          }
         }
         // row-blocks four at a time: decode, then per row-tile rt (16 rows)
         // term 0 (A-tile 2 rt) and term 1 (2 rt + 1) accumulate into one MFMA
@@ -724,6 +962,21 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+  if constexpr (LIST) {
+    // more missed elements than a list holds: the workgroup's outputs
+    // exactly (every wave; the LDS buffers are free once all have left the loop)
+    if (__syncthreads_or(overflow ? 1 : 0)) {
+      float* ex = wave < 4 ? (float*)ring(wave) : (float*)((lds_u8*)cbuf + (wave - 4) * 2 * RBW * 4 * 64 * 4);
+      exact_wave<FMT, RBW>(a, mt, wm, rb0, g0, g1, t3, ex);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < RBW; j++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[i][j][e] = ex[((i * RBW + j) * 4 + e) * 64 + lane];
+    }
+  }
 
   constexpr int NV = 2 * RBW * 4;
   uint32_t v[NV];
@@ -822,6 +1075,8 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.y = g.y;
   k.part = (float*)(ws + p.part_off);
   k.cnt = (uint32_t*)ws;
+  k.x = (const uint16_t*)g.x;
+  k.K = g.K;
   k.M = g.M;
   k.N = g.N;
   k.G = p.G;
@@ -837,7 +1092,7 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   const dim3 sgrid((unsigned)cdiv(units, 256));
   const dim3 grid((unsigned)(p.MT * p.NT * p.KS)), block(kF8Threads);
   if (g.xkind == XK_BF16) {
-    hipLaunchKernelGGL(stage_f8<XK_BF16>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
+    hipLaunchKernelGGL((stage_f8<XK_BF16, FMT != 1>), sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                        (uint8_t*)k.xt);
     if (g.ykind == YK_BF16)
       hipLaunchKernelGGL((gemm_f8<FMT, XK_BF16, YK_BF16, false, RBW>), grid, block, 0, s, k);
@@ -856,7 +1111,7 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
       hipLaunchKernelGGL((gemm_f8<FMT, XK_SIGN1, YK_F32, true, RBW>), grid, block, 0, s, k);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(stage_f8<XK_I8>, sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
+  hipLaunchKernelGGL((stage_f8<XK_I8, false>), sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                      (uint8_t*)k.xt);
   if (g.ykind == YK_I32)
     hipLaunchKernelGGL((gemm_f8<FMT, XK_I8, YK_I32, false, RBW>), grid, block, 0, s, k);

@@ -36,12 +36,57 @@ constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
 constexpr int kQuadsMulti = 4;      // quads per slice of the several-row streaming kernel
 constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
 
-template <int T>
+// Operand scheme of the activations for weight format FMT and activation kind
+// XK (split_terms): R terms, kShift binades apart, the block maximum scaled
+// into [2^kTop, 2^(kTop+1)), A format kFmtA (0 = fp8 e4m3, 1 = bf8 e5m2).
+// kCheck: how staging verifies that the terms carry the activations
+// accurately enough -- 0: not needed (int8 is exact; binary rows with bf16
+// are within 2^-21 of the block maximum, which every binary row weighs),
+// 1: per element (ternary rows may weigh any subset of a block, so every
+// element must be within 2^-12 of itself), 2: per block (binary, fp32: the
+// block's summed error within 2^-14 of its maximum).
+template <int FMT, int XK>
+struct XSplit {
+  static constexpr bool kBF8 = XK == XK_BF16 && FMT != 1;
+  static constexpr int R = split_terms(FMT, XK);
+  static constexpr int kShift = kBF8 ? 3 : 4;
+  static constexpr int kTop = kBF8 ? 14 : 7;
+  static constexpr int kFmtA = kBF8 ? 1 : 0;
+  static constexpr int kCheck = XK == XK_I8 ? 0 : FMT != 1 ? 1 : XK == XK_F32 ? 2 : 0;
+};
+constexpr float kStageEps = 1.0f / 4096.0f;  // 2^-12: staging error allowed per element
+
+// two floats -> two fp8 / bf8 bytes (round to nearest even) in half HI of old
+template <int FA, bool HI>
+__device__ __attribute__((always_inline)) inline uint32_t cvt_pk8(float a, float b, uint32_t old) {
+  if constexpr (FA == 0) return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+  else return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+}
+// the four fp8 / bf8 bytes of w as floats (exact)
+template <int FA>
+__device__ __attribute__((always_inline)) inline void cvt_f32x4(uint32_t w, float* d) {
+  if constexpr (FA == 0) {
+    d[0] = __builtin_amdgcn_cvt_f32_fp8(w, 0); d[1] = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    d[2] = __builtin_amdgcn_cvt_f32_fp8(w, 2); d[3] = __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  } else {
+    d[0] = __builtin_amdgcn_cvt_f32_bf8(w, 0); d[1] = __builtin_amdgcn_cvt_f32_bf8(w, 1);
+    d[2] = __builtin_amdgcn_cvt_f32_bf8(w, 2); d[3] = __builtin_amdgcn_cvt_f32_bf8(w, 3);
+  }
+}
+
+template <int T, int FA = 0>
 __device__ inline v4f mfma_group(const v8i& A, const v8i& B, int sa) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // A: fp8 e4m3 (0), B: fp4 e2m1 (4); byte T of sa is the A block exponent,
-  // B is unscaled (E8M0 127 = 2^0)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, T, sa, 0, 127);
+  // A: fp8 e4m3 (0) or bf8 e5m2 (1), B: fp4 e2m1 (4); byte T of sa is the A
+  // block exponent, B is unscaled (E8M0 127 = 2^0)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, FA, 4, T, sa, 0, 127);
+}
+
+// mfma_group for a run-time group index t
+template <int FA>
+__device__ __attribute__((always_inline)) inline v4f mfma_group_t(int t, const v8i& A, const v8i& B, int sa) {
+  return t == 0 ? mfma_group<0, FA>(A, B, sa) : t == 1 ? mfma_group<1, FA>(A, B, sa)
+       : t == 2 ? mfma_group<2, FA>(A, B, sa) : mfma_group<3, FA>(A, B, sa);
 }
 
 __device__ inline uint32_t bf16_rne(float f) {
@@ -51,15 +96,21 @@ __device__ inline uint32_t bf16_rne(float f) {
 
 // ------------------------------------------------------- activation staging
 // The MFMA multiplies fp4 weights (exactly +-1 / 0) by activations given as
-// fp8 e4m3 split terms.  For each 32-element hardware block, E is chosen so
-// the block maximum scaled by 2^-E lies in [128, 256); term 0 is
-// rne_e4m3(v), each next term is rne_e4m3 of 16 x the remaining residual,
-// and term r carries the E8M0 block exponent E - 4r, applied inside the
-// MFMA.  Two terms reproduce a bf16 value exactly for elements within 2^13 of
-// the block maximum (smaller ones keep an error below 2^-21 x the maximum);
-// four terms give fp32 inputs 16 significant bits.  int8 values q are split
-// exactly as 16 * (q >> 4) + (q & 15).  The conversions use the hardware
-// v_cvt_pk_fp8_f32 / v_cvt_f32_fp8 (OCP e4m3, round to nearest even).
+// fp8 split terms (XSplit).  For each 32-element hardware block, E is chosen
+// so the block maximum scaled by 2^-E lies in [2^kTop, 2^(kTop+1)); term 0
+// is the round-to-nearest-even fp8 (e4m3) or bf8 (e5m2) value of v, each
+// next term that of 2^kShift x the remaining residual, and term r carries
+// the E8M0 block exponent E - kShift r, applied inside the MFMA.  int8
+// values q are split exactly as 16 * (q >> 4) + (q & 15).  The conversions
+// use the hardware v_cvt_pk_{fp8,bf8}_f32 / v_cvt_f32_{fp8,bf8} (OCP
+// formats, round to nearest even, subnormals kept).
+//
+// Staging also reconstructs every element from its terms (exact in fp32) and
+// flags the slice when an element misses the accuracy XSplit::kCheck asks
+// for: a block spanning more than the terms' range (a large element beside
+// much smaller ones that a ternary row may weigh alone).  A flagged slice is
+// recomputed exactly on the VALU (exact_slice), so every finite input meets
+// the product bound; N(0,1) activations never raise the flag.
 //
 // Hardware block b of a group covers MFMA positions h = 32b + i; position h
 // pairs with fp4 weight slot i of quarter b (activation k = 128g +
@@ -70,6 +121,9 @@ __device__ inline uint32_t bf16_rne(float f) {
 // of A, ql = quad index inside the slice):
 //   xa[((ql * 16 + t * 4 + kb) * MA + a) * 32 + e]   fp8 bytes (group t of the quad)
 //   xe[((ql * 4 + b) * MA + a) * 4 + t]             E8M0 exponents
+// (A row a = m R + r holds term r of activation row m.)  Images staged into
+// global memory are followed by flag words (image_flag_bytes): nonzero when
+// the slice must be recomputed exactly.
 
 struct FArgs {
   const uint8_t* pcodes;
@@ -149,13 +203,17 @@ __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a
   }
 }
 
-// convert one round of units into fp8 terms and exponents in LDS
-template <int R, int XK>
-__device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs& a, int64_t q0,
+// Convert one round of units into split terms and exponents in LDS (or a
+// global image).  Returns true when one of the unit's elements misses the
+// accuracy XSplit::kCheck asks for (never for units past the end).
+template <int FMT, int XK>
+__device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs& a, int64_t q0,
                                                                      int64_t nq, int64_t rd,
                                                                      uint4 ra, uint4 rb,
                                                                      uint8_t* xa, uint8_t* xe) {
-  if (rd * blockDim.x >= nq * 64 * a.M) return;  // uniform: round past the end
+  using S = XSplit<FMT, XK>;
+  constexpr int R = S::R, FA = S::kFmtA;
+  if (rd * blockDim.x >= nq * 64 * a.M) return false;  // uniform: round past the end
   const int64_t c = rd * blockDim.x + threadIdx.x;
   int ch, b, t;
   int64_t ql, m, g;
@@ -188,25 +246,34 @@ __device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs
   for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[j]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));  // the 4 units of a block
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  if (!inside) return;
+  if (!inside) return false;
   int E = 0;
   if (XK != XK_I8 && amax != 0.0f) {
     int ex;
     frexpf(amax, &ex);
-    E = (ex - 1) - 7;
-    const int lo = -127 + kSplitShift * (R - 1);
+    E = (ex - 1) - S::kTop;
+    const int lo = -127 + S::kShift * (R - 1);  // every term's exponent representable
     if (E < lo) E = lo;
   }
   const int kb = 2 * (b & 1) + (ch >> 1), e = 16 * (b >> 1) + 8 * (ch & 1);
-  float tv[8];
+  // tv: the part of v (scaled by 2^-E) the terms still have to carry, times
+  // 2^(kShift r) before term r; t0: tv before term 0, for the accuracy check
+  float tv[8], t0[8];
+  uint32_t lost = 0;  // elements whose scaling by 2^-E underflowed to zero
+  float amax_s = 0.f;
   if constexpr (XK == XK_I8) {
 #pragma unroll
     for (int j = 0; j < 8; j++) tv[j] = v[j];
   } else {
-    // exact power of two: E is clamped to [-127 + 4(R-1), 120]
+    // exact power of two: E is clamped to [-127 + kShift (R-1), 127 - kTop]
     const float sc = ldexpf(1.0f, -E);
 #pragma unroll
-    for (int j = 0; j < 8; j++) tv[j] = v[j] * sc;
+    for (int j = 0; j < 8; j++) {
+      tv[j] = v[j] * sc;
+      if (S::kCheck == 1) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
+      t0[j] = tv[j];
+    }
+    amax_s = amax * sc;
   }
 #pragma unroll
   for (int r = 0; r < R; r++) {
@@ -219,31 +286,46 @@ __device__ __attribute__((always_inline)) inline void stage_convert1(const FArgs
         const int q = (int)tv[j];
         p[j] = (float)(r == 0 ? (q >> 4) : (q & 15));
       }
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w0, true);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], w1, true);
+      w0 = cvt_pk8<0, false>(p[0], p[1], 0);
+      w0 = cvt_pk8<0, true>(p[2], p[3], w0);
+      w1 = cvt_pk8<0, false>(p[4], p[5], 0);
+      w1 = cvt_pk8<0, true>(p[6], p[7], w1);
       Er = r == 0 ? 4 : 0;
     } else {
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[0], tv[1], 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[2], tv[3], w0, true);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[4], tv[5], 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tv[6], tv[7], w1, true);
-      if (r + 1 < R) {  // residual for the next term, exact in fp32
-        const float d[8] = {
-            __builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
-            __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3),
-            __builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
-            __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
+      w0 = cvt_pk8<FA, false>(tv[0], tv[1], 0);
+      w0 = cvt_pk8<FA, true>(tv[2], tv[3], w0);
+      w1 = cvt_pk8<FA, false>(tv[4], tv[5], 0);
+      w1 = cvt_pk8<FA, true>(tv[6], tv[7], w1);
+      Er = E - S::kShift * r;
+      if (S::kCheck != 0 || r + 1 < R) {
+        float d[8];
+        cvt_f32x4<FA>(w0, d);
+        cvt_f32x4<FA>(w1, d + 4);
+        // residual, exact in fp32: the next term's input (scaled by
+        // 2^kShift), or after the last term what the terms miss
 #pragma unroll
-        for (int j = 0; j < 8; j++) tv[j] = (tv[j] - d[j]) * 16.0f;
+        for (int j = 0; j < 8; j++) tv[j] = r + 1 < R ? (tv[j] - d[j]) * (float)(1 << S::kShift) : tv[j] - d[j];
       }
-      Er = E - kSplitShift * r;
     }
     const int64_t arow = m * R + r;
     *(uint2*)(xa + ((ql * 16 + t * 4 + kb) * a.MA + arow) * 32 + e) = make_uint2(w0, w1);
     if (ch == 0) xe[((ql * 4 + b) * a.MA + arow) * 4 + t] = (uint8_t)(127 + Er);
   }
+  // tv is now the error in units of the last term's scale, 2^(kShift (R-1))
+  // below v's scale: exact comparisons with powers of two
+  constexpr float kEpsR = kStageEps * (float)(1 << (S::kShift * (R - 1)));
+  bool bad = false;
+  if constexpr (S::kCheck == 1) {
+    bad = lost != 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) bad = bad || fabsf(tv[j]) > kEpsR * fabsf(t0[j]);
+  } else if constexpr (S::kCheck == 2) {
+    float err = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) err += fabsf(tv[j]);
+    bad = err > 0.25f * kEpsR * amax_s;  // the block's four units: at most eps x its maximum
+  }
+  return bad;
 }
 
 // --------------------------------------------------------------- MFMA GEMV
@@ -452,20 +534,34 @@ __device__ __attribute__((always_inline)) inline void load_quad_b3(const QuadBuf
   o3.sc = make_uint2(s3.x, s3.y);
 }
 
-// LDS of an item: staged activations, a zero block, the base-3 table
+// LDS of an item: staged activations (and, when copied from a global image,
+// its flag words), a zero block with per-wave staging flags, the base-3 table
 struct Lds {
   uint8_t* xa;
   uint8_t* xe;
-  uint8_t* zblk;
+  uint8_t* zblk;   // 32 zero bytes, a word of unit exponents, then wflag
+  uint32_t* wflag;  // [kMaxW]: the wave's last staging found an inaccurate element
   uint32_t* t3;
 };
 
-__device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint8_t* smem, int nq) {
+// bytes of the zero block and flags ahead of the base-3 table
+constexpr int kZeroBlock = 64;
+
+// bytes of the flag words that follow a slice image staged into global memory
+// by `rounds` staging rounds (one word per round, padded to 16 bytes)
+__host__ __device__ inline int64_t image_flag_bytes(int64_t rounds) { return (4 * rounds + 15) / 16 * 16; }
+
+// staging rounds of a slice of nq quads and M rows (256 threads)
+__host__ __device__ inline int64_t slice_rounds(int64_t nq, int64_t M) { return (nq * 64 * M + 255) / 256; }
+
+__device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint8_t* smem, int nq,
+                                                            int64_t extra = 0) {
   Lds l;
   l.xa = smem;
   l.xe = smem + (int64_t)nq * 16 * a.MA * 32;
-  l.zblk = l.xe + (int64_t)nq * 16 * a.MA;
-  l.t3 = (uint32_t*)(l.zblk + 48);
+  l.zblk = l.xe + (int64_t)nq * 16 * a.MA + extra;
+  l.wflag = (uint32_t*)(l.zblk + 48);
+  l.t3 = (uint32_t*)(l.zblk + kZeroBlock);
   return l;
 }
 
@@ -479,15 +575,33 @@ __device__ __attribute__((always_inline)) inline void lds_init(const Lds& l) {
   if constexpr (FMT == 3) fill_trit_table(l.t3);
 }
 
+// this wave's staging flag: lane 0 writes whether any lane saw an inaccurate element
+__device__ __attribute__((always_inline)) inline void put_wave_flag(uint32_t* wflag, bool bad) {
+  const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if ((threadIdx.x & 63) == 0) wflag[threadIdx.x >> 6] = any ? 1u : 0u;
+}
+
+// OR of the W waves' flags (after a barrier), uniform
+__device__ __attribute__((always_inline)) inline bool get_flags(const uint32_t* w, int n) {
+  uint32_t f = 0;
+  for (int i = 0; i < n; i++) f |= w[i];
+  return __builtin_amdgcn_readfirstlane(f) != 0;
+}
+
 // the 4 groups of quad q: operands first, then 4 independent MFMAs, then the
-// per-group scale epilogues (padding groups have zero activations)
-// (BATCH groups at a time: 4 gives the most independent MFMAs, 2 fewer live
-// registers)
-template <int FMT, int XK, int MX, int BATCH = 4>
+// per-group scale epilogues (padding groups have zero activations).  Several
+// activation rows (MM > 1): each lane keeps one accumulator per A row it
+// receives (rows 4 lg .. 4 lg + 3) and gather_rows adds the R term rows of
+// every activation row afterwards.  One row (MM = 1): the R term rows sit in
+// the lane's first R slots and are added before the scale is applied, in
+// the order quad_mfma_m1 uses (the chains and the one-product kernel agree
+// bit for bit).  (BATCH groups at a time: 4 gives the most independent
+// MFMAs, 2 fewer live registers)
+template <int FMT, int XK, int MM, int BATCH = 4>
 __device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, const Lds& l, int q,
                                                                 const Quad<FMT>& qd,
-                                                                float (&acc)[MX], int (&iacc)[MX]) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+                                                                float (&acc)[4], int (&iacc)[4]) {
+  constexpr int FA = XSplit<FMT, XK>::kFmtA;
   constexpr bool INTC = XK == XK_I8;
   const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
   const bool arow = r < a.MA;
@@ -506,27 +620,127 @@ __device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, 
     }
     v4f c[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; u++) {
-      const int t = t0 + u;
-      c[u] = t == 0 ? mfma_group<0>(A[u], B[u], (int)se)
-           : t == 1 ? mfma_group<1>(A[u], B[u], (int)se)
-           : t == 2 ? mfma_group<2>(A[u], B[u], (int)se)
-                    : mfma_group<3>(A[u], B[u], (int)se);
-    }
+    for (int u = 0; u < BATCH; u++) c[u] = mfma_group_t<FA>(t0 + u, A[u], B[u], (int)se);
 #pragma unroll
     for (int u = 0; u < BATCH; u++) {
       const int t = t0 + u;
       const float s = unit_scales ? 1.0f : f16_bits_to_f32((t < 2 ? qd.sc.x : qd.sc.y) >> (16 * (t & 1)));
+      if constexpr (MM == 1) {
+        constexpr int R = XSplit<FMT, XK>::R;
+        float tsum = c[u][0];
 #pragma unroll
-      for (int j = 0; j < MX; j++) {
-        float tsum = c[u][R * j];
+        for (int i = 1; i < R; i++) tsum += c[u][i];
+        acc[0] = fmaf(s, tsum, acc[0]);
+        if (INTC) iacc[0] += __float2int_rn(tsum);
+      } else {
 #pragma unroll
-        for (int i = 1; i < R; i++) tsum += c[u][R * j + i];
-        acc[j] = fmaf(s, tsum, acc[j]);
-        if (INTC) iacc[j] += __float2int_rn(tsum);
+        for (int v = 0; v < 4; v++) {
+          acc[v] = fmaf(s, c[u][v], acc[v]);
+          if (INTC) iacc[v] += __float2int_rn(c[u][v]);
+        }
       }
     }
   }
+}
+
+// Activation row m's value from per-A-row accumulators (quad_mfma): the sum,
+// in term order, of A rows m R .. m R + R - 1, which lane group (m R + r) / 4
+// holds in slot (m R + r) % 4.  Every lane calls it; the result is valid in
+// lanes 0..15 (lane r = output row r of the row-block).
+template <int R, int MM, typename T>
+__device__ __attribute__((always_inline)) inline void gather_rows(const T (&acc)[4], T (&ym)[MM]) {
+  if constexpr (MM == 1) {  // one row: quad_mfma added its terms already
+    ym[0] = acc[0];
+    return;
+  }
+#pragma unroll
+  for (int m = 0; m < MM; m++) ym[m] = 0;
+#pragma unroll
+  for (int ar = 0; ar < MM * R; ar++) {
+    const int v = ar & 3, lgs = ar >> 2;
+    const T val = lgs == 0 ? acc[v] : __shfl_down(acc[v], 16 * lgs);
+    ym[ar / R] += val;
+  }
+}
+
+// 16 consecutive activations of row m from k0 as floats; COH: device-coherent
+// 16-byte loads (activations another workgroup may just have written; the
+// row block must lie within the first 2^31 bytes of x)
+template <int XK>
+__device__ __attribute__((always_inline)) inline void load_x16(const FArgs& a, int64_t m, int64_t k0,
+                                                               bool coh, float (&o)[16]) {
+  const int64_t idx = m * a.K + k0;
+  if constexpr (XK == XK_BF16) {
+    uint4 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      w[h] = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 2), (uint32_t)(idx * 2 + 16 * h))
+                 : ((const uint4*)((const uint16_t*)a.x + idx))[h];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint32_t u[4] = {w[h].x, w[h].y, w[h].z, w[h].w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        o[8 * h + 2 * j] = __uint_as_float(u[j] << 16);
+        o[8 * h + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    uint4 w[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++)
+      w[h] = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 4), (uint32_t)(idx * 4 + 16 * h))
+                 : ((const uint4*)((const float*)a.x + idx))[h];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      o[4 * h] = __uint_as_float(w[h].x);
+      o[4 * h + 1] = __uint_as_float(w[h].y);
+      o[4 * h + 2] = __uint_as_float(w[h].z);
+      o[4 * h + 3] = __uint_as_float(w[h].w);
+    }
+  }
+}
+
+// Exact value of an item's slice (quads [q0, q0 + nq)) for row-block rb and
+// activation row m, computed on the VALU: lane L = r + 16 q multiplies its
+// quarter's 32 weights of every group (decoded from the packed words) by the
+// activations (products of +-1 / 0 are exact), sums each group in fp32,
+// scales it by the group's fp32 scale, and the four quarters are added.
+// The slow path for slices whose staging was flagged; every lane returns the
+// value of row r.
+template <int FMT, int XK>
+__device__ __attribute__((always_inline)) inline float exact_slice(const FArgs& a, int64_t rb, int64_t q0, int nq,
+                                                       int64_t m, bool coh, const uint32_t* t3) {
+  const int L = threadIdx.x & 63, qtr = L >> 4;
+  const int64_t rbc = rb < a.NB ? rb : a.NB - 1;
+  float acc = 0.f;
+  for (int ql = 0; ql < nq; ql++) {
+    Quad<FMT> qd;
+    load_quad_at<FMT>(a.pcodes, a.pscales, rbc, q0 + ql, a.GQ, a.GP, L, qd);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {  // unrolled: the quad's registers are indexed statically
+      const int64_t g = 4 * (q0 + ql) + t;
+      if (g >= a.G) continue;
+      const v8i B = decode_group<FMT>(qd, t, t3);
+      const int64_t k0 = g * kGroup + 64 * (qtr & 1) + 16 * (qtr >> 1);
+      float part = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {  // slots 16 h .. 16 h + 15: k0 + 32 h + (i & 15)
+        float xv[16];
+        load_x16<XK>(a, m, k0 + 32 * h, coh, xv);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int slot = 16 * h + i;
+          const uint32_t nib = ((uint32_t)B[slot >> 3] >> (4 * (slot & 7))) & 0xFu;
+          part += nib == 0x2u ? xv[i] : nib == 0xAu ? -xv[i] : 0.0f;
+        }
+      }
+      acc = fmaf(a.pscales ? quad_scale<FMT>(qd, t) : 1.0f, part, acc);
+    }
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  return acc;
 }
 
 // fp4 operand B of binary group t with the two masks held in registers
@@ -558,7 +772,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
                                                                    const uint32_t* t3,
                                                                    uint32_t sign_mask,
                                                                    uint32_t one_bits, float& acc) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr int R = XSplit<FMT, XK>::R, FA = XSplit<FMT, XK>::kFmtA;
   const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
   uint4 xa[4][2];
   if constexpr (AHEAD) {
@@ -587,10 +801,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
     } else {
       B = decode_group<FMT>(qd, t, t3);
     }
-    const v4f c = t == 0 ? mfma_group<0>(A, B, (int)se)
-                : t == 1 ? mfma_group<1>(A, B, (int)se)
-                : t == 2 ? mfma_group<2>(A, B, (int)se)
-                         : mfma_group<3>(A, B, (int)se);
+    const v4f c = mfma_group_t<FA>(t, A, B, (int)se);
     if (t > 0) {
       float tsum = cp[0];
 #pragma unroll
@@ -627,7 +838,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1x2(const uint8
                                                                      uint32_t sign_mask,
                                                                      uint32_t one_bits, float& acc0,
                                                                      float& acc1) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr int R = XSplit<1, XK>::R;
   const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
   v4f cp0, cp1;
   float sp0 = 0.f, sp1 = 0.f;
@@ -675,7 +886,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1x3(
     const uint8_t* arow, const uint8_t* erow, int q, const Quad<1>& qd, const Quad<1>& qd2,
     const Quad<1>& qd3, uint32_t sign_mask, uint32_t one_bits, float& acc0, float& acc1,
     float& acc2) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr int R = XSplit<1, XK>::R;
   const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
   v4f cp0, cp1, cp2;
   float sp0 = 0.f, sp1 = 0.f, sp2 = 0.f;
@@ -729,12 +940,13 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1x3(
 
 // Output of an item: direct stores, or (several K-slices) coherent partial
 // sums and, in the last workgroup of the row group to arrive, their sum in
-// slice order.  COH: the outputs themselves are device-coherent stores.
-template <int XK, int MX, int YK, bool COH>
+// slice order.  ym[m] / yi[m] hold activation row m's values in lanes 0..15
+// (lane r = row 16 rb + r).  COH: the outputs themselves are device-coherent
+// stores.
+template <int XK, int MM, int YK, bool COH>
 __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a, const Item& it,
-                                                                  const float (&acc)[MX],
-                                                                  const int (&iacc)[MX]) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+                                                                  const float (&ym)[MM],
+                                                                  const int (&yi)[MM]) {
   constexpr bool INTC = XK == XK_I8;
   __shared__ uint32_t s_last;
   const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
@@ -758,28 +970,30 @@ __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a
   };
   constexpr bool IPART = INTC && YK == YK_I32;
   const int64_t n = 16 * it.rb + r;
+  const bool mine = it.live && lg == 0;  // the lanes that hold the outputs
   if (a.KS == 1 && a.epi) {
-    const float z = silu_mul_lanes(acc[0]);
-    if (it.live && lg == 0 && r < 8) store(0, 8 * it.rb + r, z, 0);
+    const float z = silu_mul_lanes(ym[0]);
+    if (mine && r < 8) store(0, 8 * it.rb + r, z, 0);
     return;
   }
   if (a.KS == 1) {
+    if (mine && n < a.N) {
 #pragma unroll
-    for (int j = 0; j < MX; j++) {
-      const int64_t m = (int64_t)lg * (4 / R) + j;
-      if (it.live && m < a.M && n < a.N) store(m, n, acc[j], iacc[j]);
+      for (int m = 0; m < MM; m++)
+        if (m < a.M) store(m, n, ym[m], yi[m]);
     }
     return;
   }
   // partials: write-through (agent-coherent) stores, completed before the
   // workgroup's arrival is counted
+  if (mine) {
 #pragma unroll
-  for (int j = 0; j < MX; j++) {
-    const int64_t m = (int64_t)lg * (4 / R) + j;
-    if (it.live && m < a.M) {
-      float* dst = a.part + (it.ks * a.M + m) * a.Npad + n;
-      if (IPART) __hip_atomic_store((int*)dst, iacc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int m = 0; m < MM; m++) {
+      if (m < a.M) {
+        float* dst = a.part + (it.ks * a.M + m) * a.Npad + n;
+        if (IPART) __hip_atomic_store((int*)dst, yi[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_store(dst, ym[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -791,27 +1005,28 @@ __device__ __attribute__((always_inline)) inline void item_output(const FArgs& a
   // last arrival: add the slices in order (coherent loads) and store
   if (a.epi) {
     float f = 0.f;
-    if (it.live && lg == 0)
+    if (mine)
       for (int64_t k2 = 0; k2 < a.KS; k2++)
         f += __hip_atomic_load(a.part + k2 * a.Npad + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float z = silu_mul_lanes(f);
-    if (it.live && lg == 0 && r < 8) store(0, 8 * it.rb + r, z, 0);
+    if (mine && r < 8) store(0, 8 * it.rb + r, z, 0);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.cnt + 16 + it.rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
+  if (mine && n < a.N) {
 #pragma unroll
-  for (int j = 0; j < MX; j++) {
-    const int64_t m = (int64_t)lg * (4 / R) + j;
-    if (it.live && m < a.M && n < a.N) {
-      float f = 0.f;
-      int iv = 0;
-      for (int64_t k2 = 0; k2 < a.KS; k2++) {
-        float* src = a.part + (k2 * a.M + m) * a.Npad + n;
-        if (IPART) iv += __hip_atomic_load((int*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else f += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int m = 0; m < MM; m++) {
+      if (m < a.M) {
+        float f = 0.f;
+        int iv = 0;
+        for (int64_t k2 = 0; k2 < a.KS; k2++) {
+          float* src = a.part + (k2 * a.M + m) * a.Npad + n;
+          if (IPART) iv += __hip_atomic_load((int*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else f += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        store(m, n, f, iv);
       }
-      store(m, n, f, iv);
     }
   }
   if (threadIdx.x == 0)
@@ -850,18 +1065,20 @@ __device__ __attribute__((always_inline)) inline void stage_load_rounds(const FA
   if constexpr (K + 1 < kStageRounds) stage_load_rounds<XK, COH, K + 1>(a, it, x);
 }
 
-template <int R, int XK, int K = 0>
-__device__ __attribute__((always_inline)) inline void stage_convert_rounds(const FArgs& a,
+template <int FMT, int XK, int K = 0>
+__device__ __attribute__((always_inline)) inline bool stage_convert_rounds(const FArgs& a,
                                                                            const Item& it,
                                                                            const Lds& l, XRegs& x) {
-  stage_convert1<R, XK>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe);
-  if constexpr (K + 1 < kStageRounds) stage_convert_rounds<R, XK, K + 1>(a, it, l, x);
+  bool bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe);
+  if constexpr (K + 1 < kStageRounds) bad = stage_convert_rounds<FMT, XK, K + 1>(a, it, l, x) || bad;
+  return bad;
 }
 
-template <int R, int XK, int SB>
-__device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, const Item& it,
+// every staging round of an item; true if this thread saw an inaccurate element
+template <int FMT, int XK, int SB>
+__device__ __attribute__((always_inline)) inline bool stage_all(const FArgs& a, const Item& it,
                                                                 const Lds& l, XRegs& x, bool coh) {
-  stage_convert_rounds<R, XK>(a, it, l, x);
+  bool bad = stage_convert_rounds<FMT, XK>(a, it, l, x);
   // remaining rounds (small-M products with long slices): SB rounds' loads
   // go out together, then their conversions
   const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
@@ -876,22 +1093,30 @@ __device__ __attribute__((always_inline)) inline void stage_all(const FArgs& a, 
     }
 #pragma unroll
     for (int u = 0; u < SB; u++)
-      if (rd + u < rounds) stage_convert1<R, XK>(a, it.q0, it.nq, rd + u, r0[u], r1[u], l.xa, l.xe);
+      if (rd + u < rounds)
+        bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, rd + u, r0[u], r1[u], l.xa, l.xe) || bad;
   }
+  return bad;
+}
+
+// Byte stride of the slice images a one-product call with several activation
+// rows stages once into xst: the image of qmax quads and its flag words.
+__host__ __device__ inline int64_t image_stride(int64_t qmax, int64_t MA, int64_t M) {
+  return qmax * 16 * MA * 33 + image_flag_bytes(slice_rounds(qmax, M));
 }
 
 // The one-product kernel with several activation rows: item `it`'s slice
-// image, staged once per call into a.xst (slices qmax quads apart), copied
-// into LDS with direct global -> LDS copies (1 KiB per wave instruction)
-// and waited for.
+// image and flag words, staged once per call into a.xst, copied into LDS
+// with direct global -> LDS copies (1 KiB per wave instruction) and waited
+// for.
 template <int FMT>
 __device__ __attribute__((always_inline)) inline void copy_image(const FArgs& a, const Item& it,
                                                                  const Lds& l) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
   const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
-  const int64_t bytes = (int64_t)it.nq * 16 * a.MA * 33;
-  const uint8_t* src = a.xst + it.ks * qmax * 16 * a.MA * 33;
+  const int64_t bytes = (int64_t)it.nq * 16 * a.MA * 33 + image_flag_bytes(slice_rounds(it.nq, a.M));
+  const uint8_t* src = a.xst + it.ks * image_stride(qmax, a.MA, a.M);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
   for (int64_t off = 1024 * (int64_t)w; off < bytes; off += 1024 * (int64_t)W)
     if (off + 16 * lane < bytes)
@@ -906,18 +1131,21 @@ __device__ __attribute__((always_inline)) inline void copy_image(const FArgs& a,
 // workgroup waits until `wait_cnt` reaches `wait_target` -- the previous
 // product is complete -- and reads its activations with coherent loads).
 // stage false: the workgroup's previous item was the same product and
-// K-slice, so the activation image in LDS is this item's already.
-template <int FMT, int XK, int MX, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
+// K-slice, so the activation image (and its staging flags) in LDS is this
+// item's already.  MM: activation rows the kernel handles at most.
+template <int FMT, int XK, int MM, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
 __device__ __attribute__((always_inline)) inline void gemv_item(
     const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
     uint32_t* err, bool stage = true) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  using S = XSplit<FMT, XK>;
+  constexpr int R = S::R;
   const Item it = item_of<FMT>(a, blk);
-  const Lds l = lds_of(a, smem, it.nq);
+  const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
+  const int64_t nflag = pre ? image_flag_bytes(slice_rounds(it.nq, a.M)) : 0;
+  const Lds l = lds_of(a, smem, it.nq, nflag);
   lds_init<FMT>(l);
 
   XRegs xr;
-  const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
   if constexpr (!WAIT) {
     // activation loads of the first staging rounds go out first
     if (stage && !pre) stage_load_rounds<XK, false>(a, it, xr);
@@ -948,21 +1176,27 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     __syncthreads();
     stage_load_rounds<XK, true>(a, it, xr);
   }
-  if (pre) copy_image<FMT>(a, it, l);
-  else if (stage) stage_all<R, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
-  __syncthreads();
-
-  float acc[MX];
-  int iacc[MX];
-#pragma unroll
-  for (int j = 0; j < MX; j++) {
-    acc[j] = 0.f;
-    iacc[j] = 0;
+  if (pre) {
+    copy_image<FMT>(a, it, l);
+  } else if (stage) {
+    const bool bad = stage_all<FMT, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
+    put_wave_flag(l.wflag, bad);
   }
-  if (it.live) {
-    if constexpr (CHAIN && ONE) {
-      // chains of one activation row, with scales: the single-row routine
-      const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
+  __syncthreads();
+  // the slice must be recomputed exactly (a staged element is not accurate enough)
+  const bool exact = S::kCheck != 0 &&
+                     (pre ? get_flags((const uint32_t*)(l.xa + (int64_t)it.nq * 16 * a.MA * 33),
+                                      (int)slice_rounds(it.nq, a.M))
+                          : get_flags(l.wflag, blockDim.x >> 6));
+
+  float ym[MM];
+  int yi[MM];
+  if constexpr (CHAIN && ONE) {
+    // chains of one activation row, with scales: the single-row routine
+    static_assert(MM == 1, "the single-row routine keeps one row");
+    float acc = 0.f;
+    if (it.live) {
+      const int lane = threadIdx.x & 63, rr = (lane & 15) % R, lg = lane >> 4;
       const uint8_t* arow = l.xa + (lg * R + rr) * 32;
       const uint8_t* erow = l.xe + (lg * R + rr) * 4;
       uint32_t sign_mask = 0x88888888u, one_bits = 0x22222222u;
@@ -972,36 +1206,57 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma_m1<FMT, XK, true>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc[0]);
-    } else {
+        if (q < it.nq) quad_mfma_m1<FMT, XK, true>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+    }
+    ym[0] = acc;
+    yi[0] = 0;
+  } else {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int iacc[4] = {0, 0, 0, 0};
+    if (it.live) {
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma<FMT, XK, MX>(a, l, q, qd[q], acc, iacc);
+        if (q < it.nq) quad_mfma<FMT, XK, MM>(a, l, q, qd[q], acc, iacc);
+    }
+    gather_rows<R, MM>(acc, ym);
+    gather_rows<R, MM>(iacc, yi);
+  }
+  if constexpr (S::kCheck != 0) {
+    if (exact) {
+      for (int m = 0; m < (int)a.M; m++) {  // rolled: one copy of the slow path
+        const float v = exact_slice<FMT, XK>(a, it.rb, it.q0, it.nq, m, WAIT, l.t3);
+#pragma unroll
+        for (int mm = 0; mm < MM; mm++)
+          if (mm == m) ym[mm] = v;
+      }
     }
   }
-  item_output<XK, MX, YK, CHAIN>(a, it, acc, iacc);
+  item_output<XK, MM, YK, CHAIN>(a, it, ym, yi);
 }
 
 // Slice images of a one-product call with several activation rows, staged
-// once into xst (slice ks at ks * qmax quads): block (rd, ks) converts
-// round rd of slice ks, the units and lanes of the in-workgroup staging.
+// once into xst (slice ks at ks * image_stride): block (rd, ks) converts
+// round rd of slice ks, the units and lanes of the in-workgroup staging, and
+// writes the round's flag word.
 template <int FMT, int XK>
 __global__ __launch_bounds__(256) void stage_images(FArgs a, uint8_t* xst) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
   const int64_t ks = blockIdx.y, rd = blockIdx.x;
   const Item it = item_at<FMT>(a, 0, ks);
   const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
-  uint8_t* xa = xst + ks * qmax * 16 * a.MA * 33;
+  uint8_t* xa = xst + ks * image_stride(qmax, a.MA, a.M);
   uint8_t* xe = xa + (int64_t)it.nq * 16 * a.MA * 32;
   uint4 r0, r1;
   stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
-  stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe);
+  const bool bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe);
+  const int flagged = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0 && rd < slice_rounds(it.nq, a.M))
+    ((uint32_t*)(xa + (int64_t)it.nq * 16 * a.MA * 33))[rd] = flagged ? 1u : 0u;
 }
 
-template <int FMT, int XK, int MX, int YK, int QM>
+template <int FMT, int XK, int MM, int YK, int QM>
 __global__ __launch_bounds__(64 * kMaxW) void gemv_mfma(FArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  gemv_item<FMT, XK, MX, YK, QM, false, false>(a, blockIdx.x, smem, nullptr, 0, nullptr);
+  gemv_item<FMT, XK, MM, YK, QM, false, false>(a, blockIdx.x, smem, nullptr, 0, nullptr);
 }
 
 // Persistent kernel over a chain of batch-1 products (items of product s
@@ -1068,7 +1323,7 @@ __device__ __attribute__((always_inline)) inline FArgs load_args(FArgsTab t, int
 // MR: several activation rows per product (lane group lg keeps 4 / R rows)
 template <int FMT, int XK, int YK, int QM, bool MR>
 __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2))) void gemv_chain(ChainArgs c) {
-  constexpr int MX = MR ? 4 / (XK == XK_F32 ? kSplitF32 : kSplitBF16) : 1;
+  constexpr int MX = MR ? 16 / XSplit<FMT, XK>::R : 1;  // activation rows at most
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab first = (I64Tab)c.first;
@@ -1127,10 +1382,12 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
 // the slice after) are
 // already in flight, so every wave keeps a full slice of loads outstanding
 // across slice, row-group and product boundaries.
+// (Slice images of the streaming kernel: the image, then one 16-byte flag
+// word -- nonzero when the slice must be recomputed exactly.)
 template <int FMT>
 __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArgs& a) {
   const int64_t qmax = FMT == 3 ? 2 * cdiv(cdiv(a.GQ, 2), a.KS) : cdiv(a.GQ, a.KS);
-  return qmax * 16 * a.MA * 33;
+  return qmax * 16 * a.MA * 33 + 16;
 }
 
 // Binary weights carry half the bytes of 2-bit ternary per quad, so a
@@ -1141,9 +1398,9 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 //
 // MR: chains of small-M products (M activation rows, M R <= 16, all stages
 // alike, e.g. a verification pass over drafted tokens): the slice images
-// hold M R rows of A, the quads go through the generic quad routine, and
-// lane group lg keeps rows (4 / R) lg .. (4 / R) lg + 4 / R - 1 of its
-// output row.
+// hold M R rows of A, the quads go through the generic quad routine (one
+// accumulator per A row), and each slice's rows are gathered into lanes
+// 0..15 (gather_rows) before they are added up over the row's slices.
 //
 // RB = 3 (binary, one row): every wave holds three row-blocks, whose MFMAs
 // share each A operand read (row groups of 192 rows, two workgroups per CU),
@@ -1151,10 +1408,13 @@ __device__ __attribute__((always_inline)) inline int64_t slice_stride(const FArg
 // waves do; RB = 2 where a stage's codes are too long for buffer offsets.
 template <int FMT, int XK, int YK, int QM, bool MR, int RB>
 __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT == 1 && XK == XK_BF16 && !MR && RB == 1 ? 4 : 2))) void gemv_stream(ChainArgs c) {
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
-  constexpr int MX = MR ? 4 / R : 1;  // accumulator rows per lane
-  constexpr int NACC = MR ? MX : RB;  // accumulators per lane
+  using S = XSplit<FMT, XK>;
+  constexpr int R = S::R;
+  constexpr int MM = MR ? 16 / R : 1;  // activation rows at most
+  constexpr int NACC = MR ? 4 : RB;   // accumulators per lane (MR: one per A row)
+  constexpr int NTOT = MR ? MM : RB;  // row sums per lane
   static_assert(RB == 1 || (FMT == 1 && !MR), "several row-blocks per wave: binary, one row");
+  static_assert(RB == 1 || S::kCheck == 0, "binary bf16 rows never need the exact recomputation");
   extern __shared__ __align__(16) uint8_t smem[];
   const FArgsTab args = (FArgsTab)c.args;
   const I64Tab ufirst = (I64Tab)c.ufirst;
@@ -1173,11 +1433,15 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       uint8_t* xa = c.xst + xoff[s] + ks * slice_stride<FMT>(a);
       uint8_t* xe = xa + (int64_t)it.nq * 16 * a.MA * 32;
       const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
+      bool bad = false;
       for (int64_t rd = 0; rd < rounds; rd++) {
         uint4 r0, r1;
         stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
-        stage_convert1<R, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe);
+        bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe) || bad;
       }
+      // the slice's flag word after its image
+      const int flagged = __syncthreads_or(bad ? 1 : 0);
+      if (threadIdx.x == 0) *(uint32_t*)(xa + (int64_t)it.nq * 16 * a.MA * 33) = flagged ? 1u : 0u;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1207,17 +1471,18 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // rows of A an image may hold: several-row chains use 6-quad slices up to
   // 10 rows of A and 4-quad slices up to 16
   constexpr int MAX_MA = MR ? (QM == kQuadsMultiWide ? 10 : 16) : R;
-  constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
+  // (an image is followed by its 16-byte flag word)
+  constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
   constexpr int kWriteAfter = 3;  // quads computed before the next image is written
   static_assert(QM > kWriteAfter, "the next image is written part-way through a slice");
-  const int64_t bufsz = (int64_t)QM * 16 * MAX_MA * 33;
+  const int64_t bufsz = (int64_t)QM * 16 * MAX_MA * 33 + 16;
   // rows of A of every stage (one M per chain)
   const int64_t MAc = MR ? args[0].MA : R;
   auto xbuf = [&](uint32_t b) { return smem + b * bufsz; };
   Lds lfix;
   lfix.zblk = smem + 2 * bufsz;
-  lfix.t3 = (uint32_t*)(lfix.zblk + 48);
-  uint32_t* filled = (uint32_t*)(lfix.zblk + 48 + 1024);
+  lfix.t3 = (uint32_t*)(lfix.zblk + kZeroBlock);
+  uint32_t* filled = (uint32_t*)(lfix.zblk + kZeroBlock + 1024);
   uint32_t* consumed = filled + 2;
   lds_init<FMT>(lfix);
   if (threadIdx.x < 4) filled[threadIdx.x] = 0;
@@ -1239,7 +1504,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     Item it = item_at<FMT, RB>(a, rg, 0);
     // staged activations of a slice, XR 16-byte pieces per thread
     auto xsrc = [&](const FArgs& f, int sidx, int64_t kslice, int nq, int k) {
-      const int64_t nb = (int64_t)nq * 16 * f.MA * 33 / 16;
+      const int64_t nb = (int64_t)nq * 16 * f.MA * 33 / 16 + 1;  // image and flag word
       const int64_t piece = min<int64_t>((int64_t)k * 64 * kMaxW + tid, nb - 1);
       return (const uint4*)(c.xst + xoff[sidx] + kslice * slice_stride<FMT>(f)) + piece;
     };
@@ -1261,7 +1526,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   }
 #define XPUT(DST, NQ)                                                                        \
   {                                                                                          \
-    const int64_t nb_ = (int64_t)(NQ) * 16 * MAc * 33 / 16;                                  \
+    const int64_t nb_ = (int64_t)(NQ) * 16 * MAc * 33 / 16 + 1;                              \
     uint4* d_ = (uint4*)(DST);                                                               \
     constexpr int T_ = 64 * kMaxW;                                                           \
     if (tid < nb_) d_[tid] = x0;                                                             \
@@ -1329,14 +1594,15 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float acc[NACC], tot[NACC];  // tot: slices added in slice order, as the split-K reduction does
+    float acc[NACC], tot[NTOT];  // tot: slices added in slice order, as the split-K reduction does
     int iacc[NACC];
 #pragma unroll
     for (int m = 0; m < NACC; m++) {
       acc[m] = 0.f;
-      tot[m] = 0.f;
       iacc[m] = 0;
     }
+#pragma unroll
+    for (int m = 0; m < NTOT; m++) tot[m] = 0.f;
     uint32_t j = 0;   // slice number of this workgroup
 
     auto wait_ge = [&](uint32_t* ctr, uint32_t target) {
@@ -1370,7 +1636,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       if (j > 0) wait_ge(filled + b, 4u * ((j + 1) >> 1));
       // this lane's A row and exponent word in the slice image (one row), or
       // the image as the generic quad routine reads it (several rows)
-      const int lane = threadIdx.x & 63, rr = (lane & 15) & (R - 1), lg = lane >> 4;
+      const int lane = threadIdx.x & 63, rr = (lane & 15) % R, lg = lane >> 4;
       const uint8_t* arow = xbuf(b) + (lg * R + rr) * 32;
       const uint8_t* erow = xbuf(b) + it.nq * 16 * R * 32 + (lg * R + rr) * 4;
       Lds lq = lfix;
@@ -1397,7 +1663,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         }
         if (it.live && q < it.nq) {
           if constexpr (MR)
-            quad_mfma<FMT, XK, MX, 2>(a, lq, q, qd[q], acc, iacc);
+            quad_mfma<FMT, XK, MM, 2>(a, lq, q, qd[q], acc, iacc);
           else if constexpr (RB == 3)
             quad_mfma_m1x3<XK>(arow, erow, q, qd[q], qd2[q], qd3[q], sign_mask, one_bits, acc[0], acc[1],
                                acc[NACC - 1]);
@@ -1414,24 +1680,33 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
       __builtin_amdgcn_s_waitcnt(0xC07F);
       if ((threadIdx.x & 63) == 0)
         __hip_atomic_fetch_add(consumed + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if constexpr (MR) {
+        // this slice's value of every activation row, in lanes 0..15
+        float ys[MM];
+        gather_rows<R, MM>(acc, ys);
 #pragma unroll
-      for (int m = 0; m < NACC; m++) {
-        tot[m] = a.KS == 1 ? acc[m] : tot[m] + acc[m];
-        acc[m] = 0.f;
+        for (int m = 0; m < MM; m++) tot[m] = a.KS == 1 ? ys[m] : tot[m] + ys[m];
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[v] = 0.f;
+      } else {
+#pragma unroll
+        for (int m = 0; m < NACC; m++) {
+          tot[m] = a.KS == 1 ? acc[m] : tot[m] + acc[m];
+          acc[m] = 0.f;
+        }
       }
       if (ks == a.KS - 1) {
-        // row group complete: one output per row (lanes of the first row of A)
+        // row group complete: one output per row (lanes 0..15)
         const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
         const int64_t n = 16 * it.rb + r;
         if constexpr (MR) {
 #pragma unroll
-          for (int jj = 0; jj < MX; jj++) {
-            const int64_t m = (int64_t)lg * (4 / R) + jj;
-            if (it.live && m < a.M && n < a.N) {
-              if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = tot[jj];
-              else ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(tot[jj]);
+          for (int m = 0; m < MM; m++) {
+            if (it.live && lg == 0 && m < a.M && n < a.N) {
+              if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = tot[m];
+              else ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(tot[m]);
             }
-            tot[jj] = 0.f;
+            tot[m] = 0.f;
           }
         } else {
 #pragma unroll
@@ -1467,6 +1742,47 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     }
   }
 
+  // ---- exact recomputation of the row groups of products with a flagged
+  // slice (a staged activation not accurate enough; never for N(0,1)
+  // inputs): each workgroup redoes its own row groups on the VALU, after its
+  // main loop so that the streaming loop keeps its registers, and overwrites
+  // the outputs it wrote.
+  if constexpr (S::kCheck != 0) {
+    int sf = 0;
+    for (int64_t uf = blockIdx.x; uf < total; uf += gridDim.x) {
+      while (uf >= ufirst[sf + 1]) sf++;
+      const FArgs a = load_args(args, sf);
+      bool flagged = false;
+      for (int64_t k2 = 0; k2 < a.KS; k2++) {
+        const Item itk = item_at<FMT>(a, 0, k2);
+        const uint8_t* img = c.xst + xoff[sf] + k2 * slice_stride<FMT>(a);
+        flagged = flagged || *(const uint32_t*)(img + (int64_t)itk.nq * 16 * a.MA * 33) != 0;
+      }
+      if (!__builtin_amdgcn_readfirstlane(flagged ? 1 : 0)) continue;
+      const int64_t rgf = uf - ufirst[sf];
+      const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
+      for (int64_t m = 0; m < a.M; m++) {
+        float y = 0.f;
+        Item itk;
+        for (int64_t k2 = 0; k2 < a.KS; k2++) {  // slices in order, as the main loop adds them
+          itk = item_at<FMT, RB>(a, rgf, k2);
+          y += exact_slice<FMT, XK>(a, itk.rb, itk.q0, itk.nq, m, false, lfix.t3);
+        }
+        const int64_t n = 16 * itk.rb + r;
+        if (a.epi) {
+          const float z = silu_mul_lanes(y);
+          if (itk.live && lg == 0 && r < 8) {
+            if (YK == YK_F32) ((float*)a.y)[8 * itk.rb + r] = z;
+            else ((uint16_t*)a.y)[8 * itk.rb + r] = (uint16_t)bf16_rne(z);
+          }
+        } else if (itk.live && lg == 0 && n < a.N) {
+          if (YK == YK_F32) ((float*)a.y)[m * a.N + n] = y;
+          else ((uint16_t*)a.y)[m * a.N + n] = (uint16_t)bf16_rne(y);
+        }
+      }
+    }
+  }
+
 #undef XLD
 #undef XPUT
   // ---- the last workgroup to finish resets the barrier
@@ -1487,8 +1803,6 @@ struct Plan {
   size_t lds, part_off, bytes;
 };
 
-int split_terms(int xkind) { return xkind == XK_F32 ? kSplitF32 : kSplitBF16; }
-
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 constexpr int kQuadsBinary = 16;   // quads a wave keeps in registers (binary)
@@ -1496,7 +1810,7 @@ constexpr int kQuadsTernary = 10;  // (2-bit ternary: twice the code bytes)
 
 Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 0, int rb = 1) {
   Plan p;
-  p.R = split_terms(xkind);
+  p.R = split_terms(fmt, xkind);
   p.MA = M * p.R;
   p.NB = cdiv(N, 16);
   p.G = K / kGroup;
@@ -1518,34 +1832,45 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   p.W = kMaxW;
   p.NRG = cdiv(p.NB, p.W * rb);  // rb row-blocks per wave (the binary streaming kernel: 2)
   const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
-  p.lds = (size_t)qmax * 16 * p.MA * 32 + (size_t)qmax * 16 * p.MA + 48 + (fmt == 3 ? 1024 : 0);
+  // LDS of the one-product kernel: the slice image (with its flag words when
+  // it is copied from the images staged once per call, M > 1), the zero
+  // block and flags, the base-3 table
+  p.lds = (size_t)qmax * 16 * p.MA * 33 + (M > 1 ? (size_t)image_flag_bytes(slice_rounds(qmax, M)) : 0) +
+          kZeroBlock + (fmt == 3 ? 1024 : 0);
   p.Npad = p.NRG * p.W * rb * 16;
   p.part_off = kCounterBytes;
   p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
   return p;
 }
 
-template <int FMT, int XK, int MX, int QM>
+template <int FMT, int XK, int MM, int QM>
 hipError_t launch_y(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, size_t lds,
                     hipStream_t s) {
   if (g.ykind == YK_F32)
-    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_F32, QM>), grid, block, lds, s, k);
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MM, YK_F32, QM>), grid, block, lds, s, k);
   else if (g.ykind == YK_BF16)
-    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_BF16, QM>), grid, block, lds, s, k);
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MM, YK_BF16, QM>), grid, block, lds, s, k);
   else
-    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MX, YK_I32, QM>), grid, block, lds, s, k);
+    hipLaunchKernelGGL((gemv_mfma<FMT, XK, MM, YK_I32, QM>), grid, block, lds, s, k);
   return hipGetLastError();
+}
+
+// one activation row, or up to 16 / R of them
+template <int FMT, int XK, int QM>
+hipError_t launch_m(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, size_t lds,
+                    hipStream_t s) {
+  constexpr int MM = 16 / split_terms(FMT, XK);
+  if (g.M > MM) return hipErrorInvalidValue;
+  return g.M == 1 ? launch_y<FMT, XK, 1, QM>(g, k, grid, block, lds, s)
+                  : launch_y<FMT, XK, MM, QM>(g, k, grid, block, lds, s);
 }
 
 template <int FMT, int QM>
 hipError_t launch_x(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, size_t lds,
                     hipStream_t s) {
-  if (g.xkind == XK_F32) return launch_y<FMT, XK_F32, 1, QM>(g, k, grid, block, lds, s);
-  if (g.xkind == XK_I8)
-    return g.M == 1 ? launch_y<FMT, XK_I8, 1, QM>(g, k, grid, block, lds, s)
-                    : launch_y<FMT, XK_I8, 2, QM>(g, k, grid, block, lds, s);
-  return g.M == 1 ? launch_y<FMT, XK_BF16, 1, QM>(g, k, grid, block, lds, s)
-                  : launch_y<FMT, XK_BF16, 2, QM>(g, k, grid, block, lds, s);
+  if (g.xkind == XK_F32) return launch_m<FMT, XK_F32, QM>(g, k, grid, block, lds, s);
+  if (g.xkind == XK_I8) return launch_m<FMT, XK_I8, QM>(g, k, grid, block, lds, s);
+  return launch_m<FMT, XK_BF16, QM>(g, k, grid, block, lds, s);
 }
 
 }  // namespace
@@ -1554,7 +1879,7 @@ hipError_t launch_x(const GemvArgs& g, const FArgs& k, dim3 grid, dim3 block, si
 size_t image_bytes(const Plan& p, int fmt, int64_t M) {
   if (M <= 1) return 0;
   const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
-  return align256((size_t)(p.KS * qmax * 16 * p.MA * 33));
+  return align256((size_t)(p.KS * image_stride(qmax, p.MA, M)));
 }
 
 size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind) {
@@ -1648,7 +1973,7 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
   if (M == 1)
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 1>;
-  constexpr int R = XK == XK_F32 ? kSplitF32 : kSplitBF16;
+  constexpr int R = XSplit<FMT, XK>::R;
   if (M * R <= 10)
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMultiWide, true, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMultiWide, true, 1>;
@@ -1660,8 +1985,9 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
 
 hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int ykind, void** out) {
   *out = nullptr;
-  if (S < 1 || M < 1 || M * split_terms(xkind) > 16) return hipErrorInvalidValue;
+  if (S < 1 || M < 1) return hipErrorInvalidValue;
   const int fmt = st[0].fmt;
+  if (M * split_terms(fmt, xkind) > 16) return hipErrorInvalidValue;
   std::vector<FArgs> args(S);
   std::vector<int64_t> first(S + 1, 0);
   std::vector<int32_t> wait(S, 0);
@@ -1673,7 +1999,7 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   // the streaming kernel keeps kQuadsTernary quads of every format in flight
   // (kQuadsMulti with several activation rows); its two image buffers are
   // sized for the most rows of A it handles (R, or 16)
-  const int R = split_terms(xkind);
+  const int R = split_terms(fmt, xkind);
   const bool wide = M * R <= 10;
   const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : wide ? kQuadsMultiWide : kQuadsMulti);
   // binary, one bf16 row, no waits: three row-blocks per wave (buffer
@@ -1682,7 +2008,9 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   for (int i = 0; i < S; i++)
     buf_ok = buf_ok && cdiv(st[i].N, 16) * cdiv(st[i].K / kGroup, 4) * 1024 < (int64_t(1) << 31);
   const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? (buf_ok ? 3 : 2) : 1;
-  size_t lds = waits ? 0 : 2 * (size_t)quads * 16 * (M == 1 ? R : wide ? 10 : 16) * 33 + 48 + 1024 + 16;
+  // streaming kernel: two image buffers (image + flag word), the zero block,
+  // the base-3 table and four counters
+  size_t lds = waits ? 0 : 2 * ((size_t)quads * 16 * (M == 1 ? R : wide ? 10 : 16) * 33 + 16) + kZeroBlock + 1024 + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
     if (st[i].epi && M != 1) return hipErrorInvalidValue;
@@ -1694,7 +2022,7 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
     sfirst[i + 1] = sfirst[i] + p.KS;
     xoff[i] = xst_bytes;
     const int64_t qmax = fmt == 3 ? 2 * cdiv(cdiv(p.GQ, 2), p.KS) : cdiv(p.GQ, p.KS);
-    xst_bytes += p.KS * qmax * 16 * p.MA * 33;
+    xst_bytes += p.KS * (qmax * 16 * p.MA * 33 + 16);  // slice_stride
     wait[i] = st[i].wait_prev ? 1 : 0;
     cnt_off[i] = cnt_words;
     cnt_words += p.NRG;
