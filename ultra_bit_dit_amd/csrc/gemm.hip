@@ -611,25 +611,23 @@ struct CodeLds {
 // expcnt at its maximum
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 
-// Code (-1 / 0 / +1) of slot i (uniform) of group T of a quad, for this
-// lane's quarter, with few registers: 2-bit from the raw P0 / P1 words
-// (slot i = 8 j + p: z at bit 4 p + 1 - (j & 1), s two bits above it),
-// base-3 through the trit table.
-template <int FMT, int T>
-__device__ __forceinline__ int code_at(const Quad<FMT>& qd, int i, const uint32_t* t3) {
+// Code of slot i of group T of a quad, for this lane's quarter, as three bits
+// (bit 0: nonzero, bit 2: negative), with few registers.  2-bit: slot
+// i = 8 j + p has its z bit at 4 p + 1 - (j & 1) of word P0 (j < 2) or P1
+// and its s bit two above; the caller passes HI = (j >= 2) and the bit
+// position zp.  Base-3: through the trit table (fp4 nibble: +1 = 0x2,
+// -1 = 0xA, 0 = 0x0, so bits 1 and 3 of the nibble).
+template <int FMT, int T, bool HI>
+__device__ __forceinline__ uint32_t code3_at(const Quad<FMT>& qd, int i, int zp, const uint32_t* t3) {
   if constexpr (FMT == 2) {
     const u4 c4 = qd.w[T >> 1];
-    const uint32_t p0 = (T & 1) ? c4.z : c4.x, p1 = (T & 1) ? c4.w : c4.y;
-    const int jx = i >> 3, zp = 4 * (i & 7) + 1 - (jx & 1);
-    const uint32_t w = jx < 2 ? p0 : p1;
-    const int z = (w >> zp) & 1, sg = (w >> (zp + 2)) & 1;
-    return z ? (sg ? -1 : 1) : 0;
+    const uint32_t w = HI ? ((T & 1) ? c4.w : c4.y) : ((T & 1) ? c4.z : c4.x);
+    return (w >> zp) & 5u;
   } else {
     const v8i B = decode_group<FMT>(qd, T, t3);
     const int wi = i >> 3;
     const uint32_t wd = (uint32_t)(wi == 0 ? B[0] : wi == 1 ? B[1] : wi == 2 ? B[2] : B[3]);
-    const uint32_t nib = (wd >> (4 * (i & 7))) & 0xFu;
-    return nib == 0x2u ? 1 : nib == 0xAu ? -1 : 0;
+    return (wd >> (4 * (i & 7) + 1)) & 5u;
   }
 }
 
@@ -889,7 +887,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
           const uint32_t n0 = __builtin_amdgcn_readfirstlane(ncorr[0]);
           const uint32_t n1 = __builtin_amdgcn_readfirstlane(ncorr[1]);
           if (n0 | n1) {
-            if (n0 > (uint32_t)kEntries || n1 > (uint32_t)kEntries) {
+            if (__builtin_expect(n0 > (uint32_t)kEntries || n1 > (uint32_t)kEntries, 0)) {
               overflow = true;
             } else {
               const uint32_t ph = (uint32_t)(uintptr_t)(ring(t) + kF8Tiles + 2 * wm * kRegionBytes);
@@ -902,17 +900,40 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
                   const uint32_t pos = __builtin_amdgcn_readfirstlane(ent.x);
                   const float rho = __uint_as_float(__builtin_amdgcn_readfirstlane(ent.y));
                   const int row16 = pos & 15, b = (pos >> 4) & 3, i = (pos >> 6) & 31;
-                  const int src = 16 * b + (lane & 15);
+                  // the lanes of quarter b pack the slot's code of every
+                  // row-block (three bits each); one lane move brings them to
+                  // the lanes that hold row16's outputs
+                  const int zp = 4 * (i & 7) + 1 - ((i >> 3) & 1);
+                  uint32_t packed = 0;
+                  auto pack = [&](auto hi) {
+#pragma unroll
+                    for (int j = 0; j < RBW; j++) {
+                      const uint32_t c3 = t == 0 ? code3_at<FMT, 0, decltype(hi)::value>(qd[j], i, zp, t3)
+                                        : t == 1 ? code3_at<FMT, 1, decltype(hi)::value>(qd[j], i, zp, t3)
+                                        : t == 2 ? code3_at<FMT, 2, decltype(hi)::value>(qd[j], i, zp, t3)
+                                                 : code3_at<FMT, 3, decltype(hi)::value>(qd[j], i, zp, t3);
+                      packed |= c3 << (3 * j);
+                    }
+                  };
+                  if (i >= 16) pack(std::true_type());  // uniform
+                  else pack(std::false_type());
+                  packed = (uint32_t)__shfl((int)packed, 16 * b + (lane & 15));
                   const bool dst = (lane >> 4) == (row16 >> 2);
                   const int ev = row16 & 3;
+                  const float nrho = -rho;
+                  float val[RBW];
 #pragma unroll
                   for (int j = 0; j < RBW; j++) {
-                    const int cd = t == 0 ? code_at<FMT, 0>(qd[j], i, t3) : t == 1 ? code_at<FMT, 1>(qd[j], i, t3)
-                                 : t == 2 ? code_at<FMT, 2>(qd[j], i, t3) : code_at<FMT, 3>(qd[j], i, t3);
-                    const float cr = cd > 0 ? rho : cd < 0 ? -rho : 0.0f;
-                    const float moved = __shfl(quad_scale<FMT>(qd[j], t) * cr, src);
+                    const uint32_t c3 = dst ? (packed >> (3 * j)) & 5u : 0u;
+                    const float cr = c3 == 1u ? rho : c3 == 5u ? nrho : 0.0f;
+                    val[j] = quad_scale<FMT>(qd[j], t) * cr;
+                  }
 #pragma unroll
-                    for (int e = 0; e < 4; e++) acc[rt][j][e] += (dst && ev == e) ? moved : 0.0f;
+                  for (int e = 0; e < 4; e++) {
+                    if (ev == e) {  // uniform
+#pragma unroll
+                      for (int j = 0; j < RBW; j++) acc[rt][j][e] += val[j];
+                    }
                   }
                 }
               }
@@ -965,7 +986,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   if constexpr (LIST) {
     // more missed elements than a list holds: the workgroup's outputs
     // exactly (every wave; the LDS buffers are free once all have left the loop)
-    if (__syncthreads_or(overflow ? 1 : 0)) {
+    if (__builtin_expect(__syncthreads_or(overflow ? 1 : 0), 0)) {
       float* ex = wave < 4 ? (float*)ring(wave) : (float*)((lds_u8*)cbuf + (wave - 4) * 2 * RBW * 4 * 64 * 4);
       exact_wave<FMT, RBW>(a, mt, wm, rb0, g0, g1, t3, ex);
       __builtin_amdgcn_wave_barrier();

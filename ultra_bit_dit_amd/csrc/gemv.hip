@@ -41,10 +41,10 @@ constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
 // into [2^kTop, 2^(kTop+1)), A format kFmtA (0 = fp8 e4m3, 1 = bf8 e5m2).
 // kCheck: how staging verifies that the terms carry the activations
 // accurately enough -- 0: not needed (int8 is exact; binary rows with bf16
-// are within 2^-21 of the block maximum, which every binary row weighs),
-// 1: per element (ternary rows may weigh any subset of a block, so every
-// element must be within 2^-12 of itself), 2: per block (binary, fp32: the
-// block's summed error within 2^-14 of its maximum).
+// are within 2^-21 of the block maximum, which every binary row weighs);
+// ternary rows may weigh any subset of a block, so every element must be
+// carried: 1 (bf16) exactly, 3 (fp32) within 2^-12 of itself; 2 (binary,
+// fp32): the block's summed error within 2^-14 of its maximum.
 template <int FMT, int XK>
 struct XSplit {
   static constexpr bool kBF8 = XK == XK_BF16 && FMT != 1;
@@ -52,7 +52,7 @@ struct XSplit {
   static constexpr int kShift = kBF8 ? 3 : 4;
   static constexpr int kTop = kBF8 ? 14 : 7;
   static constexpr int kFmtA = kBF8 ? 1 : 0;
-  static constexpr int kCheck = XK == XK_I8 ? 0 : FMT != 1 ? 1 : XK == XK_F32 ? 2 : 0;
+  static constexpr int kCheck = XK == XK_I8 ? 0 : FMT != 1 ? (XK == XK_F32 ? 3 : 1) : XK == XK_F32 ? 2 : 0;
 };
 constexpr float kStageEps = 1.0f / 4096.0f;  // 2^-12: staging error allowed per element
 
@@ -257,7 +257,7 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   }
   const int kb = 2 * (b & 1) + (ch >> 1), e = 16 * (b >> 1) + 8 * (ch & 1);
   // tv: the part of v (scaled by 2^-E) the terms still have to carry, times
-  // 2^(kShift r) before term r; t0: tv before term 0, for the accuracy check
+  // 2^(kShift r) before term r; t0: tv before term 0 (relative check only)
   float tv[8], t0[8];
   uint32_t lost = 0;  // elements whose scaling by 2^-E underflowed to zero
   float amax_s = 0.f;
@@ -270,8 +270,8 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       tv[j] = v[j] * sc;
-      if (S::kCheck == 1) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
-      t0[j] = tv[j];
+      if (S::kCheck == 1 || S::kCheck == 3) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
+      if (S::kCheck == 3) t0[j] = tv[j];
     }
     amax_s = amax * sc;
   }
@@ -316,6 +316,10 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   constexpr float kEpsR = kStageEps * (float)(1 << (S::kShift * (R - 1)));
   bool bad = false;
   if constexpr (S::kCheck == 1) {
+    bad = lost != 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) bad = bad || tv[j] != 0.0f;
+  } else if constexpr (S::kCheck == 3) {
     bad = lost != 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) bad = bad || fabsf(tv[j]) > kEpsR * fabsf(t0[j]);
@@ -663,40 +667,32 @@ __device__ __attribute__((always_inline)) inline void gather_rows(const T (&acc)
   }
 }
 
-// 16 consecutive activations of row m from k0 as floats; COH: device-coherent
-// 16-byte loads (activations another workgroup may just have written; the
-// row block must lie within the first 2^31 bytes of x)
+// 8 consecutive activations of row m from k0 as floats (bf16: one 16-byte
+// load, fp32: two); COH: device-coherent loads (activations another
+// workgroup may just have written; the row must lie within the first 2^31
+// bytes of x)
 template <int XK>
-__device__ __attribute__((always_inline)) inline void load_x16(const FArgs& a, int64_t m, int64_t k0,
-                                                               bool coh, float (&o)[16]) {
+__device__ __attribute__((always_inline)) inline void load_x8(const FArgs& a, int64_t m, int64_t k0,
+                                                              bool coh, float (&o)[8]) {
   const int64_t idx = m * a.K + k0;
   if constexpr (XK == XK_BF16) {
-    uint4 w[2];
+    const uint4 w = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 2), (uint32_t)(idx * 2))
+                        : *(const uint4*)((const uint16_t*)a.x + idx);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int h = 0; h < 2; h++)
-      w[h] = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 2), (uint32_t)(idx * 2 + 16 * h))
-                 : ((const uint4*)((const uint16_t*)a.x + idx))[h];
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const uint32_t u[4] = {w[h].x, w[h].y, w[h].z, w[h].w};
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        o[8 * h + 2 * j] = __uint_as_float(u[j] << 16);
-        o[8 * h + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 4; j++) {
+      o[2 * j] = __uint_as_float(u[j] << 16);
+      o[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
     }
   } else {
-    uint4 w[4];
 #pragma unroll
-    for (int h = 0; h < 4; h++)
-      w[h] = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 4), (uint32_t)(idx * 4 + 16 * h))
-                 : ((const uint4*)((const float*)a.x + idx))[h];
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      o[4 * h] = __uint_as_float(w[h].x);
-      o[4 * h + 1] = __uint_as_float(w[h].y);
-      o[4 * h + 2] = __uint_as_float(w[h].z);
-      o[4 * h + 3] = __uint_as_float(w[h].w);
+    for (int h = 0; h < 2; h++) {
+      const uint4 w = coh ? coh_load16(a.x, (uint32_t)(a.M * a.K * 4), (uint32_t)(idx * 4 + 16 * h))
+                          : ((const uint4*)((const float*)a.x + idx))[h];
+      o[4 * h] = __uint_as_float(w.x);
+      o[4 * h + 1] = __uint_as_float(w.y);
+      o[4 * h + 2] = __uint_as_float(w.z);
+      o[4 * h + 3] = __uint_as_float(w.w);
     }
   }
 }
@@ -706,37 +702,36 @@ __device__ __attribute__((always_inline)) inline void load_x16(const FArgs& a, i
 // quarter's 32 weights of every group (decoded from the packed words) by the
 // activations (products of +-1 / 0 are exact), sums each group in fp32,
 // scales it by the group's fp32 scale, and the four quarters are added.
-// The slow path for slices whose staging was flagged; every lane returns the
-// value of row r.
+// The slow path for slices whose staging was flagged (kept small in
+// registers: it sits in kernels whose main loops need them); every lane
+// returns the value of row r.
 template <int FMT, int XK>
 __device__ __attribute__((always_inline)) inline float exact_slice(const FArgs& a, int64_t rb, int64_t q0, int nq,
                                                        int64_t m, bool coh, const uint32_t* t3) {
   const int L = threadIdx.x & 63, qtr = L >> 4;
   const int64_t rbc = rb < a.NB ? rb : a.NB - 1;
   float acc = 0.f;
-  for (int ql = 0; ql < nq; ql++) {
+#pragma unroll 1
+  for (int64_t g = 4 * q0; g < 4 * (q0 + nq) && g < a.G; g++) {
     Quad<FMT> qd;
-    load_quad_at<FMT>(a.pcodes, a.pscales, rbc, q0 + ql, a.GQ, a.GP, L, qd);
+    load_quad_at<FMT>(a.pcodes, a.pscales, rbc, g >> 2, a.GQ, a.GP, L, qd);
+    const int t = (int)(g & 3);
+    const v8i B = t == 0 ? decode_group<FMT>(qd, 0, t3) : t == 1 ? decode_group<FMT>(qd, 1, t3)
+                : t == 2 ? decode_group<FMT>(qd, 2, t3) : decode_group<FMT>(qd, 3, t3);
+    const int64_t k0 = g * kGroup + 64 * (qtr & 1) + 16 * (qtr >> 1);
+    float part = 0.f;
+#pragma unroll 1
+    for (int c = 0; c < 4; c++) {  // slots 8 c .. 8 c + 7: k0 + 32 (c >> 1) + 8 (c & 1) + i
+      float xv[8];
+      load_x8<XK>(a, m, k0 + 32 * (c >> 1) + 8 * (c & 1), coh, xv);
+      const uint32_t w = (uint32_t)(c == 0 ? B[0] : c == 1 ? B[1] : c == 2 ? B[2] : B[3]);
 #pragma unroll
-    for (int t = 0; t < 4; t++) {  // unrolled: the quad's registers are indexed statically
-      const int64_t g = 4 * (q0 + ql) + t;
-      if (g >= a.G) continue;
-      const v8i B = decode_group<FMT>(qd, t, t3);
-      const int64_t k0 = g * kGroup + 64 * (qtr & 1) + 16 * (qtr >> 1);
-      float part = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; h++) {  // slots 16 h .. 16 h + 15: k0 + 32 h + (i & 15)
-        float xv[16];
-        load_x16<XK>(a, m, k0 + 32 * h, coh, xv);
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int slot = 16 * h + i;
-          const uint32_t nib = ((uint32_t)B[slot >> 3] >> (4 * (slot & 7))) & 0xFu;
-          part += nib == 0x2u ? xv[i] : nib == 0xAu ? -xv[i] : 0.0f;
-        }
+      for (int i = 0; i < 8; i++) {
+        const uint32_t nib = (w >> (4 * i)) & 0xFu;
+        part += nib == 0x2u ? xv[i] : nib == 0xAu ? -xv[i] : 0.0f;
       }
-      acc = fmaf(a.pscales ? quad_scale<FMT>(qd, t) : 1.0f, part, acc);
     }
+    acc = fmaf(a.pscales ? quad_scale<FMT>(qd, t) : 1.0f, part, acc);
   }
   acc += __shfl_xor(acc, 16);
   acc += __shfl_xor(acc, 32);
@@ -1058,31 +1053,34 @@ __device__ __attribute__((always_inline)) inline uint4& xb_reg(XRegs& x) {
   else return x.b4;
 }
 
-template <int XK, bool COH, int K = 0>
+// NR <= kStageRounds rounds hoisted (one-row items need only as many as
+// their largest slice has: 3 for 10-quad slices, 4 for 16)
+template <int XK, bool COH, int NR, int K = 0>
 __device__ __attribute__((always_inline)) inline void stage_load_rounds(const FArgs& a,
                                                                         const Item& it, XRegs& x) {
   stage_load1<XK, COH>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x));
-  if constexpr (K + 1 < kStageRounds) stage_load_rounds<XK, COH, K + 1>(a, it, x);
+  if constexpr (K + 1 < NR) stage_load_rounds<XK, COH, NR, K + 1>(a, it, x);
 }
 
-template <int FMT, int XK, int K = 0>
+template <int FMT, int XK, int NR, int K = 0>
 __device__ __attribute__((always_inline)) inline bool stage_convert_rounds(const FArgs& a,
                                                                            const Item& it,
                                                                            const Lds& l, XRegs& x) {
   bool bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe);
-  if constexpr (K + 1 < kStageRounds) bad = stage_convert_rounds<FMT, XK, K + 1>(a, it, l, x) || bad;
+  if constexpr (K + 1 < NR) bad = stage_convert_rounds<FMT, XK, NR, K + 1>(a, it, l, x) || bad;
   return bad;
 }
 
-// every staging round of an item; true if this thread saw an inaccurate element
-template <int FMT, int XK, int SB>
+// every staging round of an item (the first NR hoisted); true if this thread
+// saw an inaccurate element
+template <int FMT, int XK, int SB, int NR>
 __device__ __attribute__((always_inline)) inline bool stage_all(const FArgs& a, const Item& it,
                                                                 const Lds& l, XRegs& x, bool coh) {
-  bool bad = stage_convert_rounds<FMT, XK>(a, it, l, x);
+  bool bad = stage_convert_rounds<FMT, XK, NR>(a, it, l, x);
   // remaining rounds (small-M products with long slices): SB rounds' loads
   // go out together, then their conversions
   const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
-  for (int64_t rd = kStageRounds; rd < rounds; rd += SB) {
+  for (int64_t rd = NR; rd < rounds; rd += SB) {
     uint4 r0[SB], r1[SB];
 #pragma unroll
     for (int u = 0; u < SB; u++) {
@@ -1139,6 +1137,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     uint32_t* err, bool stage = true) {
   using S = XSplit<FMT, XK>;
   constexpr int R = S::R;
+  // staging rounds whose loads go out before the weight loads: a one-row
+  // slice of QM quads needs QM 64 / 256 of them
+  constexpr int NR = MM == 1 ? (QM * 64 + 255) / 256 : kStageRounds;
+  static_assert(NR <= kStageRounds, "hoisted staging rounds");
   const Item it = item_of<FMT>(a, blk);
   const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
   const int64_t nflag = pre ? image_flag_bytes(slice_rounds(it.nq, a.M)) : 0;
@@ -1148,7 +1150,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   XRegs xr;
   if constexpr (!WAIT) {
     // activation loads of the first staging rounds go out first
-    if (stage && !pre) stage_load_rounds<XK, false>(a, it, xr);
+    if (stage && !pre) stage_load_rounds<XK, false, NR>(a, it, xr);
   }
   // every code and scale of the wave is requested before anything else
   Quad<FMT> qd[QM];
@@ -1174,12 +1176,12 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
     }
     __syncthreads();
-    stage_load_rounds<XK, true>(a, it, xr);
+    stage_load_rounds<XK, true, NR>(a, it, xr);
   }
   if (pre) {
     copy_image<FMT>(a, it, l);
   } else if (stage) {
-    const bool bad = stage_all<FMT, XK, ONE || !CHAIN ? 1 : 4>(a, it, l, xr, WAIT);
+    const bool bad = stage_all<FMT, XK, ONE || !CHAIN ? 1 : 4, NR>(a, it, l, xr, WAIT);
     put_wave_flag(l.wflag, bad);
   }
   __syncthreads();
@@ -1191,8 +1193,9 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
 
   float ym[MM];
   int yi[MM];
-  if constexpr (CHAIN && ONE) {
-    // chains of one activation row, with scales: the single-row routine
+  if constexpr ((CHAIN && ONE) || (MM == 1 && XK != XK_I8)) {
+    // one activation row with scales (float activations always have them):
+    // the single-row routine
     static_assert(MM == 1, "the single-row routine keeps one row");
     float acc = 0.f;
     if (it.live) {
@@ -1206,7 +1209,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma_m1<FMT, XK, true>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+        if (q < it.nq) quad_mfma_m1<FMT, XK, CHAIN>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
     }
     ym[0] = acc;
     yi[0] = 0;
@@ -1222,7 +1225,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     gather_rows<R, MM>(iacc, yi);
   }
   if constexpr (S::kCheck != 0) {
-    if (exact) {
+    if (__builtin_expect(exact, 0)) {  // the slice recomputed exactly
       for (int m = 0; m < (int)a.M; m++) {  // rolled: one copy of the slow path
         const float v = exact_slice<FMT, XK>(a, it.rb, it.q0, it.nq, m, WAIT, l.t3);
 #pragma unroll
@@ -1283,6 +1286,7 @@ struct ChainArgs {
   const int64_t* xoff;     // [S] byte offset of product s's staged activations in xst
   uint8_t* xst;            // staged activations of every product and K-slice
   uint32_t* bar;           // grid barrier arrivals, zero between launches
+  uint32_t* flagged;       // some staged slice was flagged, zero between launches
   int S;
 };
 
@@ -1439,9 +1443,12 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         stage_load1<XK, false>(a, it.q0, it.nq, rd, r0, r1);
         bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, rd, r0, r1, xa, xe) || bad;
       }
-      // the slice's flag word after its image
+      // the slice's flag word after its image, and the launch's summary flag
       const int flagged = __syncthreads_or(bad ? 1 : 0);
-      if (threadIdx.x == 0) *(uint32_t*)(xa + (int64_t)it.nq * 16 * a.MA * 33) = flagged ? 1u : 0u;
+      if (threadIdx.x == 0) {
+        *(uint32_t*)(xa + (int64_t)it.nq * 16 * a.MA * 33) = flagged ? 1u : 0u;
+        if (flagged) __hip_atomic_fetch_or(c.flagged, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1459,6 +1466,13 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     }
     __syncthreads();
   }
+
+  // some slice of the launch was flagged (written before the grid barrier;
+  // read now, so that the load's latency is spent under the main loop)
+  bool any = false;
+  if constexpr (S::kCheck != 0)
+    any = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(c.flagged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
 
   // ---- main loop
   // LDS: two buffers, each the image of one staged slice (slice j uses
@@ -1749,7 +1763,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // the outputs it wrote.
   if constexpr (S::kCheck != 0) {
     int sf = 0;
-    for (int64_t uf = blockIdx.x; uf < total; uf += gridDim.x) {
+    for (int64_t uf = __builtin_expect(any, 0) ? (int64_t)blockIdx.x : total; uf < total; uf += gridDim.x) {
       while (uf >= ufirst[sf + 1]) sf++;
       const FArgs a = load_args(args, sf);
       bool flagged = false;
@@ -1792,6 +1806,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         __hip_atomic_fetch_add(c.finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == gridDim.x - 1) {
       __hip_atomic_store(c.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(c.flagged, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(c.finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -2111,6 +2126,7 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   c->args.finished = (uint32_t*)(m + o_fin);
   c->args.err = (uint32_t*)(m + o_fin) + 1;
   c->args.bar = (uint32_t*)(m + o_fin) + 2;
+  c->args.flagged = (uint32_t*)(m + o_fin) + 3;
   c->args.ufirst = (const int64_t*)(m + o_uf);
   c->args.sfirst = (const int64_t*)(m + o_sf);
   c->args.xoff = (const int64_t*)(m + o_xo);
