@@ -2,20 +2,30 @@
  * lowbit.h -- C ABI of liblowbit: matrix products over group-scaled binary
  * {-1,+1} and ternary {-1,0,+1} weights on AMD Instinct MI355X (gfx950).
  *
- * What is computed (sources):
+ * Pages cited, by title (a citation names the page's tag and a section of it
+ * in the page's own words):
+ *   [RM] richmindsetzone.com: "瀏覽器生圖技術內幕：1-bit diffusion 點樣將 3GB
+ *        模型塞入 WebGPU？"
+ *   [KC] kongchang.com: "三值权重压缩：27B模型缩至6GB，可在浏览器本地运行"
+ *   [OB] ainewscove.com: "我开源了 OpenBonsai：把你自己的 BF16 模型与微调压缩成约
+ *        2 GB 的三值 GGUF"
+ *   [XH] best.xiaohu.ai: "PrismMLが27BモデルをiPhoneに押し込んだ。しかも頭の良さは
+ *        ほぼ落ちていない"
+ *
+ * What is computed:
  *   - Each weight is a sign (binary) or one of {-1,0,+1} (ternary), and every
- *     group of weights shares one FP16 scale ("1-bit 嘅數學" section of the
- *     richmindsetzone.com page "瀏覽器生圖技術內幕：1-bit diffusion 點樣將 3GB
- *     模型塞入 WebGPU？"; effective widths 1.125 bits binary, 1.71 ternary).
- *   - The group holds 128 weights, one FP16 scale each (method list of the
- *     ainewscove.com OpenBonsai post).
- *   - Multiplying by -1/0/+1 is an add or a sign flip ("精度保留了多少"
- *     section of the kongchang.com Ternary Bonsai 2 article); a binary
- *     product can be done with XOR + popcount (same section of the
- *     richmindsetzone.com page, the paragraph comparing binary and ternary).
+ *     group of weights shares one FP16 scale ([RM] section "1-bit 嘅數學：
+ *     點解唔爆鑊？"; effective widths 1.125 bits binary, 1.71 ternary).
+ *   - The group holds 128 weights, one FP16 scale each ([OB], the method list
+ *     of the paragraph "工作原理").
+ *   - Multiplying by -1/0/+1 is an add or a sign flip ([KC] section
+ *     "精度保留了多少"); a binary product can be done with XOR + popcount
+ *     ([RM] section "1-bit 嘅數學：點解唔爆鑊？", the paragraph comparing
+ *     binary and ternary).
  *   - Batch-1 decode streams every weight once per token and is bound by
- *     memory bandwidth; prefill is a dense contraction (best.xiaohu.ai Bonsai
- *     27B article, sections "ローカル27Bを阻む第一の壁" and "速度は二層").
+ *     memory bandwidth; prefill is a dense contraction ([XH] sections
+ *     "ローカル27Bを阻む第一の壁：「1語生成するたびに全身を運び直す」" and
+ *     "速度は二層：低ビット搬送と、CUDA上の草稿加速").
  *
  * Dense (unpacked) meaning of the operands, shared by every entry point:
  *   W       [N][K] weights, row n = output feature, k = reduction index.
@@ -28,8 +38,27 @@
  *
  * Every pointer is caller-owned device memory unless stated.  Every call is
  * asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
- * stream).  Argument errors are returned synchronously before any HIP call.
- * A launch failure returns LOWBIT_E_HIP.  No entry point synchronizes.
+ * stream) on the current device.  Argument errors are returned synchronously
+ * before any HIP call.  A launch failure returns LOWBIT_E_HIP.  No entry
+ * point waits for the GPU except lowbit_chain_status, lowbit_chain_destroy
+ * and lowbit_release_workspaces, which say so.
+ *
+ * Streams, workspaces and graphs.  lowbit_gemv and lowbit_gemm use a device
+ * workspace that the library owns, one per (device, stream).  Calls on one
+ * stream are ordered and share it; calls on different streams never share
+ * one.  A call that needs more than its stream's workspace holds allocates a
+ * larger one (hipMalloc, which may synchronize the device as HIP does) and
+ * keeps the smaller one allocated until lowbit_release_workspaces, because
+ * kernels already queued, and graphs captured earlier, may still use it; no
+ * call waits on the stream.  A stream that is being captured into a HIP graph
+ * cannot grow its workspace: such a call returns LOWBIT_E_NOMEM, so reserve
+ * the workspace first (lowbit_workspace_bytes + lowbit_reserve_workspace, or
+ * one eager call of the largest captured product on that stream).  A captured
+ * graph keeps the workspace address it was captured with; replaying it is
+ * valid until lowbit_release_workspaces.  Replays of graphs captured on one
+ * stream must run in order on one stream (they share its workspace).  The
+ * kernels leave the workspace's counters as they found them, so a replay
+ * needs no reset.  No call records a memset into a capture.
  *
  * =====================  PACKED LAYOUT (gfx950)  ===========================
  * Rows are tiled in row-blocks of 16 (NB = ceil(N/16), rows >= N are padding
@@ -95,7 +124,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 2
+#define LOWBIT_ABI_VERSION 3
 
 enum lowbit_status {
   LOWBIT_OK = 0,
@@ -123,20 +152,24 @@ enum lowbit_dtype {
   LOWBIT_I32 = 5    /* int32 output of the exact integer paths               */
 };
 
-/* ABI version of the loaded library (LOWBIT_ABI_VERSION). */
+/* ABI version of the loaded library (LOWBIT_ABI_VERSION).  Library
+ * bookkeeping; no passage of the pages. */
 int lowbit_abi_version(void);
 
-/* Static text for a status code; never NULL. */
+/* Static text for a status code; never NULL.  Library bookkeeping. */
 const char* lowbit_status_str(int status);
 
 /* Bytes of the packed code and scale buffers for an N x K matrix in `fmt`
- * (layout above).  Host-only, no HIP call.  Errors: E_NULL, E_SHAPE,
- * E_UNSUPPORTED. */
+ * (layout above; storage of [RM] section "1-bit 嘅數學：點解唔爆鑊？" and
+ * the ternary width of [KC] section "精度保留了多少").  Host-only, no HIP
+ * call.  Errors: E_NULL, E_SHAPE, E_UNSUPPORTED. */
 int lowbit_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes,
                         size_t* scale_bytes);
 
 /* Pack dense codes [N][K] (int8) and scales [N][G] (fp16 bits) into the
  * layout above, writing every byte of pcodes/pscales (padding included).
+ * Group-scaled weights of [RM] section "1-bit 嘅數學：點解唔爆鑊？" with the
+ * group of 128 of [OB] paragraph "工作原理".
  * pcodes and pscales must be 16-byte aligned.  Codes outside the format's
  * value set are counted into *bad_code_count (device int32, atomically
  * added; pass NULL to skip); their packed value is unspecified.  The count is
@@ -145,7 +178,8 @@ int lowbit_pack(int fmt, int64_t N, int64_t K, const int8_t* codes,
                 const uint16_t* scales, void* pcodes, void* pscales,
                 int32_t* bad_code_count, void* stream);
 
-/* Inverse of lowbit_pack: writes codes [N][K] and scales [N][G].  A weight
+/* Inverse of lowbit_pack (same passages): writes codes [N][K] and scales
+ * [N][G].  A weight
  * decoded from a reserved 2-bit pattern or an out-of-range base-3 byte is
  * written as 0 and counted (one per weight) into *bad_code_count (device
  * int32, atomically added, nullable). */
@@ -153,14 +187,19 @@ int lowbit_unpack(int fmt, int64_t N, int64_t K, const void* pcodes,
                   const void* pscales, int8_t* codes, uint16_t* scales,
                   int32_t* bad_code_count, void* stream);
 
-/* Per-row absmax int8 quantization of bf16 X [M][K] (fp32 arithmetic, no
+/* Per-row absmax int8 quantization of bf16 X [M][K] (the pages fix no
+ * activation format; an 8-bit activation is the plainest reading of the
+ * integer product of [KC] section "精度保留了多少".  fp32 arithmetic, no
  * fused operations): a = max_k |x|; if a == 0 then q = 0 and s_x = 0, else
  * inv = 127.0f / a, q = clamp(rint(x * inv), -127, 127) with ties to even,
  * s_x = a / 127.0f.  Writes Q [M][K] and s_x [M]. */
 int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
                            int8_t* Q, float* s_x, void* stream);
 
-/* Batch-1 product y[n] = sum_k W[n][k] * x[k] for n < N.
+/* Batch-1 product y[n] = sum_k W[n][k] * x[k] for n < N: the per-token
+ * product of decode ([XH] section "ローカル27Bを阻む第一の壁：「1語生成する
+ * たびに全身を運び直す」") over the weights of [RM] section "1-bit 嘅數學：
+ * 點解唔爆鑊？".
  *   x_dtype F32 / BF16: x holds K values.
  *   x_dtype I8: x holds K int8 q; the result is multiplied by x_scale.
  *   x_dtype SIGN1 (binary weights only, K <= 393216): x holds K/8 bytes of
@@ -169,19 +208,18 @@ int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
  *   y_dtype F32 or BF16 (round to nearest even).  y_dtype I32 is allowed
  *   only for x_dtype I8 / SIGN1 with pscales == NULL: y = exact integer
  *   sum_k code * q (or the signed bit agreement count), x_scale ignored.
- * Alignment: pcodes, pscales, x 16 bytes; y 4 bytes.  Uses a per-stream
- * device workspace owned by the library (allocated on first use on a stream
- * and grown, after synchronizing that stream, when a call needs more; calls
- * on one stream are ordered, calls on different streams do not share it).
- * While the stream is being captured into a graph the workspace cannot
- * grow: such a call returns LOWBIT_E_NOMEM unless an earlier call on the
- * stream already needed as much (run the captured calls once eagerly
- * first). */
+ * Alignment: pcodes, pscales, x 16 bytes; y 4 bytes.  Uses the stream's
+ * workspace (see "Streams, workspaces and graphs" above; E_NOMEM if it must
+ * grow during capture or cannot be allocated). */
 int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* x, float x_scale,
                 int y_dtype, void* y, void* stream);
 
-/* Product Y[m][n] = sum_k W[n][k] * X[m][k] for m < M, n < N.
+/* Product Y[m][n] = sum_k W[n][k] * X[m][k] for m < M, n < N: the dense
+ * contraction of prefill and of a denoising step ([XH] section "速度は二層：
+ * 低ビット搬送と、CUDA上の草稿加速"; [RM] section "1-bit 嘅數學：點解唔爆鑊？").
+ * M <= 16 / (activation split terms) runs the small-M GEMV path (8 rows for
+ * binary bf16, 5 for ternary bf16, 8 for int8).
  *   x_dtype BF16: X bf16 [M][K], fp32 accumulation.
  *   x_dtype I8: X int8 [M][K] (e.g. from lowbit_quantize_act_i8) with
  *     x_scales[M] (device fp32); per 128-group integer sums are exact in int32
@@ -192,21 +230,37 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
  *     x_scales[M] the per-row magnitude alpha_m (device fp32), so that
  *     x[m][k] = alpha_m (-1)^bit.  Per group D[m][n][g] = sum_k code * sign
  *     is an exact integer (for binary weights 128 - 2 popcount(w XOR x) per
- *     group, the XOR + popcount product of the "1-bit 嘅數學" section of the
- *     richmindsetzone.com page) and Y = alpha_m sum_g scale[n][g] D[m][n][g];
+ *     group, the XOR + popcount product of [RM] section "1-bit 嘅數學：點解唔爆鑊？") and Y = alpha_m sum_g scale[n][g] D[m][n][g];
  *     y_dtype I32 requires pscales == NULL and returns sum_g D (x_scales
  *     ignored).
  *   y_dtype F32 or BF16 (or I32 as above).
  * K <= 2^36 (E_SHAPE beyond).  Alignment: pcodes, pscales, X, Y 16 bytes.
- * Uses the per-stream workspace described for lowbit_gemv. */
+ * Uses the stream's workspace as lowbit_gemv does. */
 int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* X,
                 const float* x_scales, int y_dtype, void* Y, void* stream);
 
+/* Workspace management (library bookkeeping, no passage of the pages).
+ * lowbit_workspace_bytes: host-only; *bytes = the workspace a lowbit_gemm
+ *   call with these arguments needs (M = 1: also bounds lowbit_gemv's).
+ *   Errors: E_NULL, E_UNSUPPORTED, E_SHAPE.
+ * lowbit_reserve_workspace: makes the stream's workspace on the current
+ *   device hold at least `bytes` (grows it as a product call would; E_NOMEM
+ *   during capture or when hipMalloc fails).  Call before capturing.
+ * lowbit_release_workspaces: waits for each device that holds one, then frees
+ *   every workspace, current and retired, of every stream and device.  Call
+ *   it only when no queued kernel and no graph that will be replayed uses one;
+ *   later calls allocate afresh.  Errors: E_HIP. */
+int lowbit_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int x_dtype,
+                           size_t* bytes);
+int lowbit_reserve_workspace(size_t bytes, void* stream);
+int lowbit_release_workspaces(void);
+
 /* ---- chains of batch-1 products in one persistent launch ------------------
  * Batch-1 decode streams every weight of every layer once per token and is
  * bound by memory bandwidth, so the cost that matters is the one paid per
- * token (speed section of the prismml.com Ternary Bonsai 2 announcement).
+ * token ([XH] sections "ローカル27Bを阻む第一の壁：「1語生成するたびに全身を運び
+ * 直す」" and "速度は二層：低ビット搬送と、CUDA上の草稿加速").
  * A chain runs a fixed list of batch-1 products of one weight format as one
  * cooperative launch whose workgroups stream the weights of later products
  * while earlier ones finish.  Stage i with wait_prev != 0 reads its x only
@@ -214,7 +268,7 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
  * computed from, an earlier stage's y); its weights may be read earlier.
  * Outputs are written with device-coherent stores. */
 typedef struct lowbit_gemv_stage {
-  int fmt;              /* LOWBIT_BINARY or LOWBIT_TERNARY_2BIT, equal for all stages */
+  int fmt;              /* any lowbit_format, equal for all stages                */
   int64_t N, K;         /* W is N x K, K % 128 == 0                                */
   const void* pcodes;   /* packed codes (16-byte aligned)                          */
   const void* pscales;  /* packed fp16 scales (16-byte aligned)                    */
@@ -229,8 +283,7 @@ typedef struct lowbit_gemv_stage {
 
 /* Stage epilogues.  LOWBIT_EPI_SILU_MUL: the stage is a fused gate/up
  * product of a gated FFN (the compressed models keep their base model's
- * architecture: kongchang.com Ternary Bonsai 2 article, model-card
- * paragraph) whose N rows (N % 16 == 0) are ordered so that in every 16-row
+ * architecture: [KC] section "三值权重（Ternary）到底做了什么") whose N rows (N % 16 == 0) are ordered so that in every 16-row
  * block rows 0..7 are gate rows 8b..8b+7 and rows 8..15 the up rows
  * 8b..8b+7; y then receives N/2 values z[i] = silu(g[i]) u[i],
  * silu(v) = v / (1 + e^-v), computed in fp32 from the fp32 products and
@@ -253,9 +306,9 @@ int lowbit_chain_create(int n_stages, const lowbit_gemv_stage* stages, int x_dty
 /* The same with `rows` activation rows per product (1 <= rows <= 8 for BF16 x,
  * <= 4 for F32 x; every stage takes rows x K activations and writes rows x N
  * outputs): a small-M chain such as one pass that verifies rows - 1 drafted
- * tokens and the next one through every product of a model (speed section
- * of the Japanese Bonsai 27B article: drafts are checked by the target model
- * in one pass).  The SiLU-mul epilogue needs rows == 1.  Errors as
+ * tokens and the next one through every product of a model ([XH] section
+ * "速度は二層：低ビット搬送と、CUDA上の草稿加速": drafts are checked by the
+ * target model in one pass).  The SiLU-mul epilogue needs rows == 1.  Errors as
  * lowbit_chain_create (E_SHAPE for rows out of range). */
 int lowbit_chain_create_rows(int n_stages, const lowbit_gemv_stage* stages, int64_t rows,
                              int x_dtype, int y_dtype, lowbit_chain** chain);
@@ -269,12 +322,13 @@ int lowbit_chain_run(lowbit_chain* chain, void* stream);
  * meaningful).  Never expected when runs do not overlap. */
 int lowbit_chain_status(lowbit_chain* chain, int* failed_waits);
 
-/* Frees the chain's device memory (synchronizes the device first). */
+/* Frees the chain's device memory (synchronizes the device first).  Library
+ * bookkeeping. */
 int lowbit_chain_destroy(lowbit_chain* chain);
 
 /* Data-free quantizer front end (the signed Hadamard rotation and the
- * FP16 scale per 128 weights of the method list, section 工作原理, of the
- * ainewscove.com OpenBonsai post; its calibrated GPTQ step needs data and is
+ * FP16 scale per 128 weights of the method list of [OB] paragraph
+ * "工作原理"; its calibrated GPTQ step needs data and is
  * not part of it).  From bf16 weights W [N][K] writes dense codes [N][K]
  * (int8, the input of lowbit_pack) and fp16 scales [N][K/128].  Per row and
  * group of 128: v = W * d (signs d[K], int8 +-1; signs == NULL: no
@@ -291,7 +345,8 @@ int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf1
                             const int8_t* signs, int8_t* codes, uint16_t* scales,
                             void* stream);
 
-/* Activations for rotated weights: per row of bf16 X [M][K] and block of 128,
+/* Activations for rotated weights ([OB] paragraph "工作原理", the signed
+ * Hadamard rotation): per row of bf16 X [M][K] and block of 128,
  * X_rot = H (d * x) / sqrt(128) in fp32 (signs as given to
  * lowbit_quantize_weights), so that products with the rotated weights
  * equal those with the original ones.  Output fp32 [M][K].
@@ -299,7 +354,9 @@ int lowbit_quantize_weights(int fmt, int64_t N, int64_t K, const uint16_t* W_bf1
 int lowbit_rotate_act(int64_t M, int64_t K, const uint16_t* X_bf16, const int8_t* signs,
                       float* X_rot, void* stream);
 
-/* Measurement helper, not part of the matrix-product path: reads the
+/* Measurement helper, not part of the matrix-product path (the bandwidth
+ * bound of [XH] section "ローカル27Bを阻む第一の壁：「1語生成するたびに全身を
+ * 運び直す」"): reads the
  * `bytes` (a positive multiple of 16) at src once with 16-byte streaming
  * loads spread over the whole device and XORs the data into *out (device
  * uint32, caller-initialised), so the sustained HBM read rate can be timed

@@ -10,10 +10,11 @@
  *       is a sign, a group of weights shares one FP16 scale, ternary adds a
  *       zero state; effective widths 1.125 and 1.71 bits; a binary GEMM can
  *       be computed with XOR + popcount.
- *  [R3] kongchang.com, "三值权重压缩：27B模型缩至6GB…", section
+ *  [R3] kongchang.com, "三值权重压缩：27B模型缩至6GB，可在浏览器本地运行", section
  *       "精度保留了多少": ternary values need about log2(3) bits and a
  *       product with -1/0/+1 reduces to additions and sign flips.
- *  [R4] ainewscove.com OpenBonsai post, method list ("工作原理"): one FP16
+ *  [R4] ainewscove.com, "我开源了 OpenBonsai：把你自己的 BF16 模型与微调压缩
+ *       成约 2 GB 的三值 GGUF", method list of the paragraph "工作原理": one FP16
  *       scale per 128 weights; a signed Hadamard rotation to reduce weight
  *       outliers before the weights are quantized.
  *  The byte layout is the one written in the layout specification of the
@@ -533,8 +534,9 @@ int orc_rotate_rows(int64_t N, int64_t K, const uint16_t* W_bf16, const int8_t* 
 /* Gated FFN activation feeding the down projection: z[k] = silu(g[k]) u[k],
  * silu(v) = v / (1 + e^-v), in fp64.  The pages state that the compressed
  * models keep their base model's architecture and change only how weights
- * are stored (kongchang.com Ternary Bonsai 2 article, model-card paragraph;
- * the Japanese Bonsai 27B article, section on the base network); the gated
+ * are stored ([R3] section "三值权重（Ternary）到底做了什么"; page
+ * "PrismMLが27BモデルをiPhoneに押し込んだ。しかも頭の良さはほぼ落ちていない",
+ * section "土台は依然Qwen3.6-27B。Bonsaiが網全体を極限ビットに押し込む"); the gated
  * SiLU FFN is that base family's, which the pages do not print. */
 int orc_silu_mul(int64_t K, const double* g, const double* u, double* z) {
   if (K < 0 || (K && (!g || !u || !z))) return -2;

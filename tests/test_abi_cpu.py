@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lb.lib().lowbit_abi_version() == 2
+    assert lb.lib().lowbit_abi_version() == 3
     for st in range(-8, 1):
         assert isinstance(lb.status_str(st), str) and lb.status_str(st)
 
@@ -108,3 +108,42 @@ def test_quantizer_validation_without_gpu():
     assert f(2, 4, 128, A16, A4, A16, A16, None) == lb.E_ALIGN
     assert f(2, 4, 128, A16, None, A4, A16, None) == lb.E_ALIGN
     assert f(2, 4, 128, A16, None, A16, A1, None) == lb.E_ALIGN
+
+
+def test_workspace_bytes_contract():
+    """lowbit_workspace_bytes is host-only: argument errors, the F32 rule of
+    lowbit_gemm, and sizes that grow with the product (no GPU needed)."""
+    L = lb.lib()
+    b = ctypes.c_size_t(7)
+    assert L.lowbit_workspace_bytes(1, 1, 16, 128, lb.BF16, None) == lb.E_NULL
+    assert L.lowbit_workspace_bytes(9, 1, 16, 128, lb.BF16, ctypes.byref(b)) == lb.E_UNSUPPORTED
+    assert b.value == 0
+    assert L.lowbit_workspace_bytes(1, 1, 16, 128, 9, ctypes.byref(b)) == lb.E_UNSUPPORTED
+    assert L.lowbit_workspace_bytes(1, 1, 16, 100, lb.BF16, ctypes.byref(b)) == lb.E_SHAPE
+    assert L.lowbit_workspace_bytes(1, 0, 16, 128, lb.BF16, ctypes.byref(b)) == lb.E_SHAPE
+    # lowbit_gemm takes no fp32 activations for M > 1
+    assert L.lowbit_workspace_bytes(2, 2, 16, 128, lb.F32, ctypes.byref(b)) == lb.E_UNSUPPORTED
+    for fmt in (1, 2, 3):
+        for xd in (lb.BF16, lb.I8, lb.SIGN1):
+            for M in (1, 4, 64, 512):
+                v = lb.workspace_bytes(fmt, M, 5120, 5120, xd)
+                assert v >= 0
+                assert lb.workspace_bytes(fmt, M, 5120, 5120 * 4, xd) >= v
+        assert lb.workspace_bytes(fmt, 1, 5120, 5120, lb.F32) > 0
+
+
+def test_chain_del_at_finalization_does_nothing():
+    """Chain.__del__ leaves the chain alone while the interpreter shuts down
+    (the HIP runtime may be gone then)."""
+    import sys
+    c = lb.Chain.__new__(lb.Chain)
+    c._h = ctypes.c_void_p(0x1234)  # never passed to the library here
+    c._keep = []
+    real = sys.is_finalizing
+    try:
+        sys.is_finalizing = lambda: True
+        c.__del__()
+    finally:
+        sys.is_finalizing = real
+    assert c._h.value == 0x1234
+    c._h = None

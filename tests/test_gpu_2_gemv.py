@@ -270,3 +270,59 @@ def test_small_m_graph_replays(fmt):
             lb.gemm(fmt, M, 2048, 5120, mats[0][0], mats[0][1], Xs[0])
         torch.cuda.synchronize()
     del graph
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured on a stream keeps its workspace after a larger eager
+    call on the same stream grows the stream's workspace: replays before and
+    after the growth equal the eager result bit for bit.  Capturing a product
+    on a stream whose workspace is too small fails with E_NOMEM."""
+    fmt, M, N, K = 2, 5, 640, 5120
+    print("graph workspace growth", flush=True)
+    codes, scales, pc, ps = make(fmt, N, K, tid=121)
+    X = synth.normal_bf16(SEED, 123, M, K)
+    Xt = dev(X.view(np.int16)).view(torch.bfloat16)
+    Y = torch.empty((M, N), device="cuda")
+    ref = lb.gemm(fmt, M, N, K, pc, ps, Xt)  # eager, on the default stream
+    torch.cuda.synchronize()
+    yref, absY = O.matmul(codes, scales, O.X_BF16, X)
+    assert_within(ref.cpu().numpy(), yref, absY, what="eager")
+
+    stream = torch.cuda.Stream()
+    need = lb.workspace_bytes(fmt, M, N, K, lb.BF16)
+    assert need > 0
+    lb.reserve_workspace(need, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        lb.gemm(fmt, M, N, K, pc, ps, Xt, Y=Y)
+    torch.cuda.synchronize()
+
+    # a larger product on the same stream grows its workspace
+    Nb, Kb, Mb = 2048, 17408, 300
+    _, _, pcb, psb = make(fmt, Nb, Kb, tid=125)
+    Xb = torch.randn((Mb, Kb), device="cuda").to(torch.bfloat16)
+    assert lb.workspace_bytes(fmt, Mb, Nb, Kb, lb.BF16) > need
+    for rep in range(3):
+        Y.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            graph.replay()
+            if rep == 0:
+                lb.gemm(fmt, Mb, Nb, Kb, pcb, psb, Xb)  # grows while the replay may run
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref), f"replay {rep}"
+    del graph
+
+    # no reserve: the capture cannot grow the fresh stream's workspace
+    fresh = torch.cuda.Stream()
+    g2 = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(g2, stream=fresh):
+        Y.fill_(0.0)
+        try:
+            lb.gemm(fmt, M, N, K, pc, ps, Xt, Y=Y)
+        except lb.LowbitError as e:
+            err = e
+    torch.cuda.synchronize()
+    assert err is not None and err.status == lb.E_NOMEM
+    del g2

@@ -1,7 +1,8 @@
 """Pins for the oracle's data-free weight quantizer (signed Hadamard rotation
 per 128-group, absmean fp16 scale, rounding to binary / ternary codes; the
-rotation and the per-128 FP16 scale come from the OpenBonsai post's method
-list, section 工作原理).  None of these compares the oracle with itself: the
+rotation and the per-128 FP16 scale come from the method list of the
+paragraph "工作原理" of the page "我开源了 OpenBonsai：把你自己的 BF16 模型与微调
+压缩成约 2 GB 的三值 GGUF").  None of these compares the oracle with itself: the
 fp16 encoder against numpy's correctly rounded float16, the rotation against
 scipy's Sylvester Hadamard matrix, the scale against a numerical L2
 minimisation, and hand-worked groups from tests/golden."""

@@ -2,6 +2,7 @@
 // workspace.  Every check runs on the host before any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -30,17 +31,22 @@ bool shape_ok(int64_t N, int64_t K) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_E_HIP; }
 
-// ---- per-(device, stream) workspace, grown on demand.  Growing waits for the
-// stream (the old buffer may still be read by queued kernels), so a stream
-// being captured into a graph must already hold a large enough workspace.
-// Its first kCounterBytes hold the fused GEMV's counters (zeroed here once;
-// every launch leaves them zero).
+// ---- per-(device, stream) workspace, grown on demand.  A grown workspace
+// serves the stream's later calls; the smaller one it replaces is retired,
+// not freed, because kernels queued before the growth, and HIP graphs
+// captured on the stream, may still use it.  Nothing waits for the stream.
+// A stream being captured cannot grow its workspace (reserve it first).
+// Retired and current workspaces are freed by lowbit_release_workspaces.
+// The first kCounterBytes of a workspace hold the kernels' arrival counters
+// (zeroed on the stream when the workspace is allocated; every launch leaves
+// them zero).
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;  // (device, workspace)
 
 int workspace(hipStream_t s, size_t need, void** out) {
   int dev = 0;
@@ -51,19 +57,16 @@ int workspace(hipStream_t s, size_t need, void** out) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return LOWBIT_E_HIP;
     if (cs != hipStreamCaptureStatusNone) return LOWBIT_E_NOMEM;
-    if (w.ptr) {
-      if (hipStreamSynchronize(s) != hipSuccess) return LOWBIT_E_HIP;
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    size_t sz = need < (1u << 20) ? (1u << 20) : need + need / 4;
-    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
-      w.ptr = nullptr;
-      return LOWBIT_E_NOMEM;
-    }
+    const size_t sz = need < (1u << 20) ? (1u << 20) : need + need / 4;
+    void* p = nullptr;
+    if (hipMalloc(&p, sz) != hipSuccess) return LOWBIT_E_NOMEM;
     // the counter block must start at zero; kernels leave it zero
-    if (hipMemsetAsync(w.ptr, 0, kCounterBytes, s) != hipSuccess) return LOWBIT_E_HIP;
+    if (hipMemsetAsync(p, 0, kCounterBytes, s) != hipSuccess) {
+      (void)hipFree(p);
+      return LOWBIT_E_HIP;
+    }
+    if (w.ptr) g_retired.push_back({dev, w.ptr});
+    w.ptr = p;
     w.bytes = sz;
   }
   *out = w.ptr;
@@ -125,6 +128,15 @@ int run_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const
 // split terms of one row
 int max_small_m(int fmt, int x_dtype) { return 16 / split_terms(fmt, x_dtype); }
 
+// Workspace bytes a product needs: the path lowbit_gemm (or lowbit_gemv when
+// M = 1) takes for these arguments.  Sign activations: the GEMM's need (the
+// batch-1 sign GEMV of lowbit_gemv uses none, so this bounds both).
+size_t product_workspace(int fmt, int64_t M, int64_t N, int64_t K, int x_dtype) {
+  if (x_dtype != LOWBIT_SIGN1 && M <= max_small_m(fmt, x_dtype))
+    return gemv_workspace_bytes(fmt, N, K, M, x_dtype);
+  return gemm_workspace_bytes(fmt, x_dtype, M, N, K);
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,7 +152,7 @@ const char* lowbit_status_str(int status) {
     case LOWBIT_E_UNSUPPORTED: return "unsupported format / dtype combination";
     case LOWBIT_E_BADCODE: return "invalid code";
     case LOWBIT_E_HIP: return "HIP runtime error";
-    case LOWBIT_E_NOMEM: return "workspace allocation failed";
+    case LOWBIT_E_NOMEM: return "workspace allocation failed (or needed growth during graph capture)";
   }
   return "unknown status";
 }
@@ -248,6 +260,48 @@ int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, co
                          x_dtype == LOWBIT_I8 && y_dtype != LOWBIT_I32 ? x_scales : nullptr,
                          y_dtype, Y, s);
   return run_gemm(fmt, M, N, K, pcodes, pscales, x_dtype, X, x_scales, y_dtype, Y, s);
+}
+
+int lowbit_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int x_dtype, size_t* bytes) {
+  if (!bytes) return LOWBIT_E_NULL;
+  *bytes = 0;
+  if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
+  if (x_dtype < LOWBIT_F32 || x_dtype > LOWBIT_SIGN1) return LOWBIT_E_UNSUPPORTED;
+  if (!shape_ok(N, K) || M < 1 || M > (int64_t(1) << 31) || K > (int64_t(1) << 36))
+    return LOWBIT_E_SHAPE;
+  if (M > 1 && x_dtype == LOWBIT_F32) return LOWBIT_E_UNSUPPORTED;  // lowbit_gemm takes no F32
+  *bytes = product_workspace(fmt, M, N, K, x_dtype);
+  return LOWBIT_OK;
+}
+
+int lowbit_reserve_workspace(size_t bytes, void* stream) {
+  void* ws = nullptr;
+  return workspace((hipStream_t)stream, bytes, &ws);
+}
+
+int lowbit_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int rc = LOWBIT_OK;
+  int cur = 0;
+  if (!g_ws.empty() || !g_retired.empty())
+    if (hipGetDevice(&cur) != hipSuccess) return LOWBIT_E_HIP;
+  std::vector<int> devs;
+  for (auto& kv : g_ws) devs.push_back(kv.first.first);
+  for (auto& r : g_retired) devs.push_back(r.first);
+  std::sort(devs.begin(), devs.end());
+  devs.erase(std::unique(devs.begin(), devs.end()), devs.end());
+  for (int d : devs)  // queued kernels may still use a workspace
+    if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = LOWBIT_E_HIP;
+  auto release = [&](int dev, void* p) {
+    if (hipSetDevice(dev) != hipSuccess || hipFree(p) != hipSuccess) rc = LOWBIT_E_HIP;
+  };
+  for (auto& kv : g_ws)
+    if (kv.second.ptr) release(kv.first.first, kv.second.ptr);
+  for (auto& r : g_retired) release(r.first, r.second);
+  g_ws.clear();
+  g_retired.clear();
+  if (rc == LOWBIT_OK && hipSetDevice(cur) != hipSuccess) rc = LOWBIT_E_HIP;
+  return rc;
 }
 
 struct lowbit_chain {

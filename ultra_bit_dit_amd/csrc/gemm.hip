@@ -1,8 +1,8 @@
 // Large-M products Y[M][N] = X[M][K] . W[N][K]^T over packed binary or
 // ternary weights (2-bit or base-3) with one fp16 scale per 128-weight group
-// (the group-scaled matmul of the "1-bit 嘅數學" section of the ultra_bit_dit
-// page; prefill and diffusion-transformer blocks run it as a dense
-// contraction).
+// (the group-scaled matmul of section "1-bit 嘅數學：點解唔爆鑊？" of the page
+// "瀏覽器生圖技術內幕：1-bit diffusion 點樣將 3GB 模型塞入 WebGPU？"; prefill
+// and diffusion-transformer blocks run it as a dense contraction).
 //
 // One MFMA kernel for every format: gfx950's block-scaled
 // v_mfma_scale_f32_16x16x128_f8f6f4 with fp8 e4m3 activations (two exact

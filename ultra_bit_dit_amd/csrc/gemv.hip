@@ -14,13 +14,13 @@
 // Per 16 rows x 128 weights a wave issues one 16-byte vector load of codes
 // (per 4 groups), one MFMA and ~10 VALU ops; the kernel is bound by HBM
 // bandwidth.  Multiplications by -1 / 0 / +1 are exact in the MFMA (ternary
-// products reduce to adds and sign flips: "精度保留了多少" section of the
-// kongchang.com Ternary Bonsai 2 article).
+// products reduce to adds and sign flips: section "精度保留了多少" of the
+// page "三值权重压缩：27B模型缩至6GB，可在浏览器本地运行").
 //
 // Sign path (binary weights x sign activations): per 32 weights one XOR and
 // one popcount give the exact signed agreement 32 - 2 * popcount(w ^ x)
-// (the XOR + popcount remark of the "1-bit 嘅數學" section of the
-// richmindsetzone.com 1-bit diffusion page).
+// (the XOR + popcount remark of section "1-bit 嘅數學：點解唔爆鑊？" of the
+// page "瀏覽器生圖技術內幕：1-bit diffusion 點樣將 3GB 模型塞入 WebGPU？").
 #include <algorithm>
 #include <vector>
 

@@ -1,7 +1,8 @@
 // Data-free quantizer front end: bf16 weights -> binary / ternary codes and
 // one fp16 scale per 128-weight group, with an optional signed Hadamard
 // rotation of each group (the rotation and the per-128 FP16 scale of the
-// method list, section 工作原理, of the ainewscove.com OpenBonsai post; its
+// method list of the paragraph "工作原理" of the page "我开源了 OpenBonsai：
+// 把你自己的 BF16 模型与微调压缩成约 2 GB 的三值 GGUF"; its
 // calibrated GPTQ step needs data and is not part of this front end), and
 // the matching rotation of activations.
 //

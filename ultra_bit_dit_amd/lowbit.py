@@ -7,6 +7,7 @@ no fallback.
 """
 import ctypes
 import os
+import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "liblowbit.so")
@@ -19,6 +20,7 @@ EPI_NONE, EPI_SILU_MUL = 0, 1
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
            "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
+           "lowbit_workspace_bytes", "lowbit_reserve_workspace", "lowbit_release_workspaces",
            "lowbit_chain_create", "lowbit_chain_create_rows", "lowbit_chain_run", "lowbit_chain_status",
            "lowbit_chain_destroy",
            "lowbit_hbm_read_probe", "lowbit_quantize_weights", "lowbit_rotate_act")
@@ -59,6 +61,9 @@ def lib():
         L.lowbit_quantize_act_i8.argtypes = [i64, i64, vp, vp, vp, vp]
         L.lowbit_gemv.argtypes = [i32, i64, i64, vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
         L.lowbit_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i32, vp, vp, i32, vp, vp]
+        L.lowbit_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.lowbit_reserve_workspace.argtypes = [ctypes.c_size_t, vp]
+        L.lowbit_release_workspaces.argtypes = []
         L.lowbit_chain_create.argtypes = [i32, ctypes.POINTER(GemvStage), i32, i32,
                                           ctypes.POINTER(vp)]
         L.lowbit_chain_create_rows.argtypes = [i32, ctypes.POINTER(GemvStage), i64, i32, i32,
@@ -174,6 +179,24 @@ def gemm(fmt, M, N, K, pcodes, pscales, X, x_scales=None, y_dtype=F32, Y=None, x
     return Y
 
 
+def workspace_bytes(fmt, M, N, K, x_dtype):
+    """Workspace bytes lowbit_gemm (or lowbit_gemv, M = 1) needs for these arguments."""
+    b = ctypes.c_size_t()
+    _check("lowbit_workspace_bytes",
+           lib().lowbit_workspace_bytes(fmt, M, N, K, x_dtype, ctypes.byref(b)))
+    return b.value
+
+
+def reserve_workspace(nbytes, stream=None):
+    """Grow the stream's workspace to at least nbytes (do it before capturing a graph)."""
+    _check("lowbit_reserve_workspace", lib().lowbit_reserve_workspace(int(nbytes), _stream(stream)))
+
+
+def release_workspaces():
+    """Wait for the devices, then free every workspace (no graph using one may be replayed after)."""
+    _check("lowbit_release_workspaces", lib().lowbit_release_workspaces())
+
+
 def quantize_weights(fmt, W, signs=None, stream=None):
     """Dense (codes int8 [N][K], scales int16 fp16 bits [N][K/128]) from bf16
     weights W [N][K] (see lowbit_quantize_weights); signs int8 [K] or None."""
@@ -242,6 +265,10 @@ class Chain:
             self._keep = []
 
     def __del__(self):
+        # at interpreter exit the HIP runtime may already be torn down: leave
+        # the chain's memory to the process exit then
+        if sys is None or sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
