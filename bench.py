@@ -47,7 +47,7 @@ DIT = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("out", 3072, 30
        ("up", 9216, 3072), ("down", 3072, 9216)]
 FMT_NAMES = {1: "binary", 2: "ternary-2bit", 3: "ternary-base3"}
 SEED = 1002  # decode-step workload
-PP_SEED, DIT_SEED = 1003, 1004
+C0_SEED, C1_SEED, PP_SEED, DIT_SEED = 1000, 1001, 1003, 1004
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "{kernel}_decode_step_pmc.txt")
 # sources the decode kernels are built from (their hash ties a counter summary to them)
 GEMV_SOURCES = [os.path.join(ROOT, "ultra_bit_dit_amd", "csrc", f)
@@ -109,20 +109,34 @@ def run_step(lb, fmt, W, xs, ys, layers):
             lb.gemv(fmt, N, K, pc, ps, xs[j], y=ys[j], y_dtype=lb.F32)
 
 
-def time_region(torch, stream, fn, steps, warmup):
+def time_region(torch, stream, fn, steps, warmup, per_step=None):
     """Warm-up, then `steps` calls bracketed by synchronisations; HIP events
-    on `stream` (the stream every launch goes to).  Returns ms per call."""
+    on `stream` (the stream every launch goes to).  Returns ms per call (the
+    mean over the bracketed region).  With `per_step` (a list) an event is
+    also recorded between consecutive calls and the per-call durations are
+    appended to it."""
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True)
+              for _ in range(steps + 1 if per_step is not None else 2)]
+        ev[0].record(stream)
+        for i in range(steps):
             fn()
-        e1.record(stream)
+            if per_step is not None:
+                ev[i + 1].record(stream)
+        ev[-1].record(stream)
         torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 def pmc_traffic(launch_bytes, kernel):
@@ -206,6 +220,17 @@ def chain_for(lb, fmt, W, xs, ys, layers, wait, torch=None):
     return ch
 
 
+GEMM_LEGS = ("pp512_bf16", "pp512_i8", "dit_bf16", "dit_sign", "gemv_products", "quantizer")
+
+MODE_WHAT = {
+    "chain": "the step as specified (fixed x per shape, products independent): one persistent "
+             "launch streams every product's weights; the streaming bound",
+    "chain_dep": "sequential decode: every product waits for the previous one, gate/up's "
+                 "SiLU-mul output feeds down (bf16 activations); one persistent launch",
+    "separate": "one launch per product, the step captured as one HIP graph",
+}
+
+
 def bench_decode(args, lb, synth, torch, np):
     """Times the decode step three ways (see --modes):
     chain      one persistent launch per step streams all 4 x layers products
@@ -226,13 +251,14 @@ def bench_decode(args, lb, synth, torch, np):
     stream = torch.cuda.Stream()
     res = {}
     for mode in modes:
+        per = []
         if mode in ("chain", "chain_dep"):
             ch = chain_for(lb, fmt, W, xs, ys, layers, 1 if mode == "chain_dep" else 0, torch)
-            ms = time_region(torch, stream, lambda: ch.run(stream), args.steps, args.warmup)
+            ms = time_region(torch, stream, lambda: ch.run(stream), args.steps, args.warmup, per)
             if ch.failed_waits():
                 raise RuntimeError("chain wait gave up")
             ch.close()
-            res[mode] = (ms, 1)
+            res[mode] = (ms, 1, median(per))
         elif mode == "separate":
             with torch.cuda.stream(stream):
                 run_step(lb, fmt, W, xs, ys, layers)  # eager warm-up (allocates the workspace)
@@ -241,21 +267,21 @@ def bench_decode(args, lb, synth, torch, np):
             with torch.cuda.graph(graph, stream=stream):
                 run_step(lb, fmt, W, xs, ys, layers)
             torch.cuda.synchronize()
-            ms = time_region(torch, stream, graph.replay, args.steps, args.warmup)
+            ms = time_region(torch, stream, graph.replay, args.steps, args.warmup, per)
             del graph
-            res[mode] = (ms, len(MATS) * layers)
+            res[mode] = (ms, len(MATS) * layers, median(per))
         else:
             raise SystemExit(f"unknown mode {mode}")
         log(f"decode [{mode}] {ms:.3f} ms/step, {step_bytes / ms / 1e6:.0f} GB/s, "
             f"{1000 / ms:.1f} tok/s")
     head = modes[0]
-    ms, launches = res[head]
+    ms, launches, _ = res[head]
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launch_bytes = step_bytes / launches
     launch_us = ms * 1e3 / launches
     kbase = {"chain": "gemv_stream", "chain_dep": "gemv_chain", "separate": "gemv_mfma"}[head]
     traffic, tnote = pmc_traffic(launch_bytes, kbase)
-    kname = kbase + (" (ternary 2-bit" if fmt == 2 else " (binary") + ", bf16 x, fp32 y)"
+    kname = kbase + f" ({FMT_NAMES[fmt]}, bf16 x, fp32 y)"
     roof = {"bound": "hbm", "kernel": kname,
             "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(launch_bytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -264,8 +290,10 @@ def bench_decode(args, lb, synth, torch, np):
             "avg_launch_us": round(launch_us, 3),
             "note": f"{launches} launch(es) per step, durations from HIP events over the timed "
                     f"region; traffic: {tnote}"}
-    modes_out = {m: {"ms_per_step": round(v[0], 4), "gb_s": round(step_bytes / v[0] / 1e6, 1),
-                     "tok_s": round(1000.0 / v[0], 2), "launches_per_step": v[1]}
+    modes_out = {m: {"ms_per_step": round(v[0], 4), "median_ms_per_step": round(v[2], 4),
+                     "gb_s": round(step_bytes / v[0] / 1e6, 1),
+                     "tok_s": round(1000.0 / v[0], 2), "launches_per_step": v[1],
+                     "what": MODE_WHAT[m]}
                  for m, v in res.items()}
     if args.verify_rows > 1:
         # one pass of `verify_rows` activation rows through every product of
@@ -322,20 +350,25 @@ def bench_gemm_pass(lb, synth, torch, np, fmt, M, shapes, seed, xkind, reps):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
-def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
-    """One product per launch over `copies` distinct weight matrices (more
-    packed bytes than the 256 MB last-level cache, so every launch streams
-    from HBM), the launches replayed as one HIP graph.  mode "sign": batch-1
-    binary weights x sign activations (XOR + popcount, lowbit_gemv SIGN1);
-    "m<M>": M bf16 activation rows (M = 5: the small-M verification pass).
-    Returns (us per product, GB/s of packed weight bytes)."""
-    mats = build_mats(lb, synth, fmt, SEED + 10, 0, [("w", N, K)] * copies)
+def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps, launches=None,
+                       seed=SEED + 10):
+    """One product per launch, the launches cycling over `copies` distinct
+    weight matrices (more packed bytes than the 256 MB last-level cache: every
+    launch streams from HBM; one copy: the weights stay cache-resident),
+    `launches` of them (default one per copy) replayed as one HIP graph.
+    mode "sign": batch-1 binary weights x sign activations (XOR + popcount,
+    lowbit_gemv SIGN1); "m<M>": M bf16 activation rows (M = 1: lowbit_gemv,
+    M = 5: the small-M verification pass).  Returns (us per product, GB/s of
+    packed weight bytes)."""
+    launches = launches or copies
+    mats = build_mats(lb, synth, fmt, seed, 0, [("w", N, K)] * copies)
+    order = [mats[i % copies] for i in range(launches)]
     if mode == "sign":
         xb = torch.from_numpy(synth.sign_bits(SEED + 10, 850, 1, K)).cuda()[0]
         y = torch.empty(N, dtype=torch.float32, device="cuda")
 
         def one():
-            for pc, ps in mats:
+            for pc, ps in order:
                 lb.gemv(1, N, K, pc, ps, xb, x_scale=1.0, y=y, x_dtype=lb.SIGN1)
     else:
         M = int(mode[1:])  # "m<rows>"
@@ -344,7 +377,7 @@ def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
         Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
         def one():
-            for pc, ps in mats:
+            for pc, ps in order:
                 if M == 1:
                     lb.gemv(fmt, N, K, pc, ps, X[0], y=Y[0])
                 else:
@@ -358,10 +391,78 @@ def bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, mode, reps):
         one()
     torch.cuda.synchronize()
     ms = time_region(torch, stream, graph.replay, reps, 2)
-    nbytes = packed_bytes(lb, fmt, [("w", N, K)]) * copies
-    del graph, mats
+    nbytes = packed_bytes(lb, fmt, [("w", N, K)]) * launches
+    del graph, mats, order
     torch.cuda.synchronize()
-    return ms * 1e3 / copies, nbytes / (ms * 1e-3) / 1e9
+    return ms * 1e3 / launches, nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_c0_latency(lb, synth, torch, np, reps=200):
+    """The binary GEMV correctness configuration (N = 256, K = 1024, fp32 x and
+    y): 36,864 packed bytes, far below the cache, so the figure is latency.
+    Reports the median of `reps` single calls, each bracketed by its own
+    events on an idle stream, and the per-call time of 100 calls replayed as
+    one HIP graph."""
+    N, K = 256, 1024
+    codes = synth.device_codes(False, C0_SEED, 0, N, K, "cuda")
+    scales = synth.device_scales(C0_SEED, 1, N, K // 128, "cuda")
+    pc, ps = lb.pack(1, codes, scales)
+    x = torch.from_numpy(synth.normal_f32(C0_SEED, 2, 1, K)).cuda()[0]
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    one = lambda: lb.gemv(1, N, K, pc, ps, x, y=y)  # noqa: E731
+    single = []
+    with torch.cuda.stream(stream):
+        for _ in range(10):
+            one()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one()
+            e1.record(stream)
+            e1.synchronize()
+            single.append(e0.elapsed_time(e1) * 1e3)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(100):
+            one()
+    torch.cuda.synchronize()
+    gms = time_region(torch, stream, graph.replay, 20, 2)
+    del graph
+    torch.cuda.synchronize()
+    return {"us_single_call_median": round(median(single), 2),
+            "us_single_call_min": round(min(single), 2),
+            "us_per_call_in_graph": round(gms * 1e3 / 100, 3),
+            "packed_bytes": packed_bytes(lb, 1, [("w", N, K)]),
+            "what": "binary GEMV N=256 K=1024, fp32 x, fp32 y (C0); latency-bound"}
+
+
+def bench_c1(lb, synth, torch, np, reps):
+    """The ternary 5120 x 5120 GEMV (bf16 x, fp32 y) in both packings: cold,
+    the launches rotating over enough distinct copies (>= 512 MB) that every
+    launch streams from HBM, and hot, 100 launches on one cache-resident
+    matrix.  Each labelled."""
+    out = {}
+    N = K = 5120
+    for fmt in (2, 3):
+        nb = packed_bytes(lb, fmt, [("w", N, K)])
+        copies = max(80, -(-(512 << 20) // nb))
+        us, gb = bench_gemv_product(lb, synth, torch, np, fmt, N, K, copies, "m1", reps,
+                                    seed=C1_SEED)
+        uh, gh = bench_gemv_product(lb, synth, torch, np, fmt, N, K, 1, "m1", reps, launches=100,
+                                    seed=C1_SEED)
+        name = FMT_NAMES[fmt]
+        log(f"C1 {name}: cold {us:.2f} us ({gb:.0f} GB/s), hot {uh:.2f} us ({gh:.0f} GB/s)")
+        out[name] = {
+            "packed_bytes": nb,
+            "cold": {"us_per_product": round(us, 3), "gb_s": round(gb, 1),
+                     "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1),
+                     "what": f"rotated over {copies} copies ({copies * nb / 1e6:.0f} MB), "
+                             "each launch streams from HBM"},
+            "hot": {"us_per_product": round(uh, 3), "gb_s": round(gh, 1),
+                    "what": "one matrix, 100 launches: cache-resident (not an HBM figure)"}}
+    return out
 
 
 def bench_quantizer(lb, synth, torch, np, N, K, reps):
@@ -386,43 +487,183 @@ def bench_quantizer(lb, synth, torch, np, N, K, reps):
     return ms, nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(fmt, budget_s):
-    """The oracle, as it stands, on a bounded sample: 64-row slices of the four
-    layer matrices (regenerated bit-exactly on the host), timed over as many
-    calls as fit the budget and scaled to tokens per second."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Threads for the multi-threaded oracle runs: the CPUs this process may
+    run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_time(O, calls, threads):
+    """Wall seconds for the oracle products `calls` (tuples codes, scales,
+    xkind, X), each split by weight rows over `threads` threads (the
+    oracle's C library runs without the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
+    for codes, scales, xk, X in calls:
+        N = codes.shape[0]
+        step = -(-N // threads)
+        for r in range(0, N, step):
+            jobs.append((codes[r:r + step], scales[r:r + step], xk, X))
+    t0 = time.perf_counter()
+    if threads == 1:
+        for c, sc, xk, X in jobs:
+            O.matmul(c, sc, xk, X, with_abs=False)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda a: O.matmul(a[0], a[1], a[2], a[3], with_abs=False), jobs))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(fmt, step_bytes, budget_s, device_gen=None):
+    """The oracle, as it stands, timed on the host: fp64 dequantize-then-
+    multiply (plain C, -O2), once on 1 thread and once on T threads.  Inputs
+    are the same seeded synthetic tensors, regenerated bit-exactly on the host.
+      C0   binary GEMV N=256 K=1024 (fp32 x), timed in full;
+      C1   ternary GEMV 5120 x 5120 (bf16 x), timed in full (dequantize-
+           multiply only; the oracle's unpacker is timed on its own);
+      C2   decode step: a row sample of the four layer matrices (64 rows on
+           1 thread; the full layer on T threads when it fits the budget),
+           extrapolated per weight to 64 layers;
+      C3   pp512: 512 rows x 8 weight rows of each layer matrix, extrapolated
+           to one layer and to 64 layers;
+      C4   DiT block M=4608: 256 activation rows x 4 weight rows of each block
+           matrix, extrapolated to the block.
+    `value` is the T-thread decode rate in the headline's unit (packed-weight
+    bytes of one step / seconds per step); tok/s beside it.  device_gen (not
+    None: a GPU is present) lets whole inputs be generated on the device."""
     import numpy as np
     import synth
     from oracle import oracle as O
+    T = cpu_threads()
     gen = synth.ternary_codes if fmt != 1 else synth.binary_codes
-    rows = np.arange(64)
-    sample = []
-    for j, (name, N, K) in enumerate(MATS):
-        sample.append((gen(SEED, 2 * j, N, K, rows=rows),
-                       synth.group_scales(SEED, 2 * j + 1, N, K // 128, rows=rows),
-                       synth.normal_bf16(SEED, 900 + j, 1, K), K))
-    macs_done, t_used, calls = 0, 0.0, 0
-    while t_used < budget_s:
-        codes, scales, x, K = sample[calls % len(sample)]
-        t0 = time.perf_counter()
-        O.matmul(codes, scales, O.X_BF16, x, with_abs=False)
-        t_used += time.perf_counter() - t0
-        macs_done += len(rows) * K
-        calls += 1
+    out = {"kind": "oracle", "cores": T, "cpu_model": cpu_model(), "threads_available": T}
     layer_macs = sum(N * K for _, N, K in MATS)
-    sec_per_token = t_used / macs_done * layer_macs * LAYERS
-    return {"value": 1.0 / sec_per_token, "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} oracle calls on 64-row slices of the four layer-0 matrices "
-                      f"({macs_done / 1e6:.0f}M weight MACs, {t_used:.1f}s, 1 thread), scaled to "
-                      f"{layer_macs * LAYERS / 1e9:.2f}G MACs per token"}
+
+    # C0 and C1 in full
+    c0 = (synth.binary_codes(C0_SEED, 0, 256, 1024), synth.group_scales(C0_SEED, 1, 256, 8),
+          O.X_F32, synth.normal_f32(C0_SEED, 2, 1, 1024))
+    t_c0 = min(oracle_time(O, [c0], 1) for _ in range(5))
+    c1 = (synth.ternary_codes(C1_SEED, 0, 5120, 5120), synth.group_scales(C1_SEED, 1, 5120, 40),
+          O.X_BF16, synth.normal_bf16(C1_SEED, 2, 1, 5120))
+    t_c1_1 = oracle_time(O, [c1], 1)
+    t_c1_T = oracle_time(O, [c1], T)
+    pc, ps, _ = O.pack(2, c1[0], c1[1])
+    t0 = time.perf_counter()
+    O.unpack(2, 5120, 5120, pc, ps)
+    t_unpack = time.perf_counter() - t0
+    out["c0_binary_gemv"] = {"us_1_thread": round(t_c0 * 1e6, 1), "measured": "in full"}
+    out["c1_ternary_gemv"] = {"ms_1_thread": round(t_c1_1 * 1e3, 2), f"ms_{T}_threads":
+                              round(t_c1_T * 1e3, 2), "unpack_2bit_ms_1_thread":
+                              round(t_unpack * 1e3, 2), "measured": "in full"}
+
+    # C2: 1-thread row sample, T-thread full layer (or the largest sample that fits)
+    full_layer = None
+    if device_gen is not None:
+        # whole matrices generated on the device (the same values as the host
+        # generators, much faster) and copied to the host once
+        full_layer = []
+        for j, (name, N, K) in enumerate(MATS):
+            full_layer.append(
+                (synth.device_codes(fmt != 1, SEED, 2 * j, N, K, "cuda").cpu().numpy(),
+                 synth.device_scales(SEED, 2 * j + 1, N, K // 128, "cuda").cpu().numpy()
+                 .view(np.uint16)))
+
+    def layer_calls(rows):
+        calls = []
+        for j, (name, N, K) in enumerate(MATS):
+            if full_layer is not None:
+                codes, scales = full_layer[j][0][:rows], full_layer[j][1][:rows]
+            else:
+                r = np.arange(min(rows, N))
+                codes = gen(SEED, 2 * j, N, K, rows=r)
+                scales = synth.group_scales(SEED, 2 * j + 1, N, K // 128, rows=r)
+            calls.append((codes, scales, O.X_BF16, synth.normal_bf16(SEED, 900 + j, 1, K)))
+        return calls
+
+    # rows of each matrix: 64 to probe the rate, then as many as a quarter of
+    # the budget allows on 1 thread and half of it on T threads (up to the
+    # whole layer); host-generated inputs stay small
+    probe = layer_calls(64)
+    rate_1 = sum(c[0].size for c in probe) / oracle_time(O, probe, 1)
+    cap = max(N for _, N, _ in MATS) if full_layer is not None else 256
+    rows_1 = int(min(cap, max(64, budget_s * 0.25 * rate_1 / 32768)))
+    s1 = layer_calls(rows_1)
+    t1 = oracle_time(O, s1, 1)
+    macs1 = sum(c[0].size for c in s1)
+    sec_tok_1 = t1 / macs1 * layer_macs * LAYERS
+    rows_T = int(min(cap, max(64, budget_s * 0.5 * rate_1 * T / 32768)))
+    sT = layer_calls(rows_T)
+    tT = oracle_time(O, sT, T)
+    macsT = sum(c[0].size for c in sT)
+    full = macsT == layer_macs
+    sec_tok_T = tT / macsT * layer_macs * LAYERS
+    del sT, s1, full_layer
+    out["value"] = round(step_bytes / sec_tok_T / 1e9, 4)
+    out["unit"] = "GB/s"
+    out["tok_s"] = round(1.0 / sec_tok_T, 6)
+    out["sample"] = (f"decode step ({FMT_NAMES[fmt]}): {'one full layer' if full else f'{rows_T} rows of each layer matrix'} "
+                     f"({macsT / 1e6:.0f}M weight MACs) in {tT:.2f}s on {T} threads, "
+                     f"extrapolated per weight to {LAYERS} layers ({layer_macs * LAYERS / 1e9:.2f}G MACs); "
+                     f"value = packed bytes of one step / seconds per step")
+    out["single_thread"] = {"tok_s": round(1.0 / sec_tok_1, 6),
+                            "gb_s": round(step_bytes / sec_tok_1 / 1e9, 4),
+                            "sample": f"{rows_1} rows of each layer matrix ({macs1 / 1e6:.0f}M MACs) "
+                                      f"in {t1:.2f}s, extrapolated to {LAYERS} layers"}
+
+    # C3: pp512 layer sample (T threads)
+    c3 = []
+    for j, (name, N, K) in enumerate(MATS):
+        r = np.arange(8)
+        c3.append((synth.ternary_codes(PP_SEED, 2 * j, N, K, rows=r),
+                   synth.group_scales(PP_SEED, 2 * j + 1, N, K // 128, rows=r),
+                   O.X_BF16, synth.normal_bf16(PP_SEED, 700 + j, 512, K)))
+    t3 = oracle_time(O, c3, min(T, 8))
+    m3 = sum(512 * c[0].size for c in c3)
+    s_layer = t3 / m3 * 512 * layer_macs
+    out["c3_pp512"] = {"s_per_layer": round(s_layer, 2), "s_per_pass_64_layers": round(s_layer * LAYERS, 1),
+                       "gflop_s": round(2 * m3 / t3 / 1e9, 3), "threads": min(T, 8),
+                       "measured": f"512 rows x 8 weight rows of each layer matrix ({m3 / 1e6:.0f}M MACs, "
+                                   f"{t3:.2f}s); extrapolated"}
+    # C4: DiT block sample (T threads)
+    c4 = []
+    for j, (name, N, K) in enumerate(DIT):
+        r = np.arange(4)
+        c4.append((synth.binary_codes(DIT_SEED, 2 * j, N, K, rows=r),
+                   synth.group_scales(DIT_SEED, 2 * j + 1, N, K // 128, rows=r),
+                   O.X_BF16, synth.normal_bf16(DIT_SEED, 700 + j, 256, K)))
+    t4 = oracle_time(O, c4, min(T, 4))
+    m4 = sum(256 * c[0].size for c in c4)
+    block_macs = 4608 * sum(N * K for _, N, K in DIT)
+    out["c4_dit_block_4608"] = {"s_per_block": round(t4 / m4 * block_macs, 1),
+                                "gflop_s": round(2 * m4 / t4 / 1e9, 3), "threads": min(T, 4),
+                                "measured": f"256 activation rows x 4 weight rows of each block "
+                                            f"matrix ({m4 / 1e6:.0f}M MACs, {t4:.2f}s); extrapolated"}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--fmt", type=int, default=2, choices=[1, 2])
+    ap.add_argument("--fmt", type=int, default=2, choices=[1, 2, 3],
+                    help="headline weight format: 1 binary, 2 ternary 2-bit, 3 ternary base-3")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--gemm-reps", type=int, default=10)
@@ -430,8 +671,12 @@ def main():
     ap.add_argument("--modes", default="chain,chain_dep,separate",
                     help="decode-step modes to time, headline first (chain, chain_dep, separate)")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--gemm-legs", default=",".join(GEMM_LEGS),
+                    help="legs after the decode step (comma list of " + ", ".join(GEMM_LEGS) + ")")
     ap.add_argument("--no-other-format", action="store_true",
-                    help="skip the decode step in the other weight format")
+                    help="skip the decode step in the other weight formats")
+    ap.add_argument("--no-c01", action="store_true",
+                    help="skip the C0 latency and C1 single-product legs")
     ap.add_argument("--verify-rows", type=int, default=5,
                     help="rows of the small-M verification pass through the whole step (0: skip)")
     args = ap.parse_args()
@@ -453,19 +698,22 @@ def main():
     ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
     roof["measured_read_gb_s"] = round(read_gbs, 1)
     roof["frac_of_measured_read"] = round(roof["achieved"] / read_gbs, 4)
-    # the same step with the other weight format (the workload has binary and
-    # ternary variants): streaming and sequential chains
-    other = None
+    # the same step in the other weight formats (binary, and both ternary
+    # packings): streaming and sequential chains
+    others = []
     if not args.no_other_format:
-        a2 = argparse.Namespace(**vars(args))
-        a2.fmt = 1 if args.fmt == 2 else 2
-        a2.modes = "chain,chain_dep"
-        a2.verify_rows = 0
-        oms, ogbs, obytes, oroof, _, omodes = bench_decode(a2, lb, synth, torch, np)
-        other = {"format": FMT_NAMES[a2.fmt], "mode": "chain", "ms_per_step": round(oms, 4),
-                 "gb_s": round(ogbs, 1), "pct_hbm_peak": round(100 * ogbs / HBM_PEAK_GBS, 1),
-                 "tok_s": round(1000.0 / oms, 2), "bytes_per_step": obytes,
-                 "kernel": oroof["kernel"], "decode_modes": omodes}
+        for ofmt in (1, 2, 3):
+            if ofmt == args.fmt:
+                continue
+            a2 = argparse.Namespace(**vars(args))
+            a2.fmt = ofmt
+            a2.modes = "chain,chain_dep"
+            a2.verify_rows = 0
+            oms, ogbs, obytes, oroof, _, omodes = bench_decode(a2, lb, synth, torch, np)
+            others.append({"format": FMT_NAMES[ofmt], "mode": "chain", "ms_per_step": round(oms, 4),
+                           "gb_s": round(ogbs, 1), "pct_hbm_peak": round(100 * ogbs / HBM_PEAK_GBS, 1),
+                           "tok_s": round(1000.0 / oms, 2), "bytes_per_step": obytes,
+                           "kernel": oroof["kernel"], "decode_modes": omodes})
 
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",
@@ -484,23 +732,34 @@ def main():
                                "(qkv 15360x5120, o 5120x5120, gate/up 34816x5120, down 5120x17408), "
                                "group-128 fp16 scales, bf16 activations, batch 1",
                    "tok_s": round(1000.0 / ms, 2),
+                   "tok_s_sequential": modes_out.get("chain_dep", {}).get("tok_s"),
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                    "bytes_per_step": step_bytes,
                    "mode": head,
                    "decode_modes": modes_out},
         "roofline": roof,
     }
-    if other is not None:
-        out["config"]["decode_" + other["format"].split("-")[0]] = other
-    if not args.no_gemm:
-        pp = {}
-        for xk, peak in (("bf16", MFMA_PEAK_F16_TFLOPS), ("i8", MFMA_PEAK_I8_TOPS)):
-            pms, tf = bench_gemm_pass(lb, synth, torch, np, 2, 512, MATS, PP_SEED, xk, args.gemm_reps)
-            log(f"pp512 {xk}: {pms:.3f} ms per layer, {tf:.1f} TFLOP/s")
-            pp[xk] = {"ms_per_layer": round(pms, 4), "tflops": round(tf, 1),
-                      "pct_mfma_peak": round(100 * tf / peak, 1),
-                      "tok_s_64_layers": round(512 / (pms * LAYERS * 1e-3), 1)}
+    for o in others:
+        out["config"]["decode_" + o["format"].replace("-", "_")] = o
+    if not args.no_c01:
+        out["config"]["c0_binary_gemv_latency"] = bench_c0_latency(lb, synth, torch, np)
+        log(f"C0: {out['config']['c0_binary_gemv_latency']}")
+        out["config"]["c1_ternary_gemv_5120"] = bench_c1(lb, synth, torch, np, args.gemm_reps)
+    legs = set() if args.no_gemm else set(l for l in args.gemm_legs.split(",") if l)
+    if legs - set(GEMM_LEGS):
+        raise SystemExit(f"unknown legs {sorted(legs - set(GEMM_LEGS))}")
+    pp = {}
+    for xk, peak in (("bf16", MFMA_PEAK_F16_TFLOPS), ("i8", MFMA_PEAK_I8_TOPS)):
+        if "pp512_" + xk not in legs:
+            continue
+        pms, tf = bench_gemm_pass(lb, synth, torch, np, 2, 512, MATS, PP_SEED, xk, args.gemm_reps)
+        log(f"pp512 {xk}: {pms:.3f} ms per layer, {tf:.1f} TFLOP/s")
+        pp[xk] = {"ms_per_layer": round(pms, 4), "tflops": round(tf, 1),
+                  "pct_mfma_peak": round(100 * tf / peak, 1),
+                  "tok_s_64_layers": round(512 / (pms * LAYERS * 1e-3), 1)}
+    if pp:
         out["config"]["pp512_ternary"] = pp
+    if "dit_bf16" in legs:
         dit = {}
         for M in (4608, 18432):
             dms, tf = bench_gemm_pass(lb, synth, torch, np, 1, M, DIT, DIT_SEED, "bf16",
@@ -509,6 +768,7 @@ def main():
             dit[str(M)] = {"ms_per_block": round(dms, 4), "tflops": round(tf, 1),
                            "pct_mfma_peak": round(100 * tf / MFMA_PEAK_F16_TFLOPS, 1)}
         out["config"]["dit_block_binary_bf16"] = dit
+    if "dit_sign" in legs:
         # the same blocks with sign activations (binary x binary on the fp4 MFMA)
         sg = {}
         for M in (4608, 18432):
@@ -518,6 +778,7 @@ def main():
             sg[str(M)] = {"ms_per_block": round(dms, 4), "tops": round(tf, 1),
                           "pct_mfma_peak_fp4": round(100 * tf / MFMA_PEAK_F4_TOPS, 1)}
         out["config"]["dit_block_binary_sign"] = sg
+    if "gemv_products" in legs:
         # batch-1 XOR + popcount and the five-row verification pass, gate/up shape
         gv = {}
         us, gb = bench_gemv_product(lb, synth, torch, np, 1, 34816, 5120, 16, "sign", args.gemm_reps)
@@ -529,14 +790,19 @@ def main():
         gv["m5_ternary_34816x5120"] = {"us_per_product": round(us, 2), "gb_s": round(gb, 1),
                                        "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
         out["config"]["gemv_products"] = gv
+    if "quantizer" in legs:
         # data-free quantizer front end on the gate/up matrix (rotated, ternary)
         qms, qgbs = bench_quantizer(lb, synth, torch, np, 34816, 5120, args.gemm_reps)
         log(f"quantizer 34816x5120: {qms:.3f} ms, {qgbs:.0f} GB/s")
         out["config"]["quantizer_gate_up"] = {"ms": round(qms, 4), "gb_s": round(qgbs, 1),
                                               "pct_hbm_peak": round(100 * qgbs / HBM_PEAK_GBS, 1),
                                               "bytes": "bf16 in + int8 codes + fp16 scales out"}
+    # nothing of the library's may outlive the process's GPU work: every
+    # chain and graph is closed above; free the per-stream workspaces
+    torch.cuda.synchronize()
+    lb.release_workspaces()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.fmt, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(args.fmt, step_bytes, args.cpu_budget, device_gen=True)
     print(json.dumps(out), flush=True)
 
 
