@@ -134,7 +134,9 @@ enum lowbit_status {
   LOWBIT_E_UNSUPPORTED = -4, /* format / dtype combination not provided       */
   LOWBIT_E_BADCODE = -5,     /* reserved for callers that check the flag     */
   LOWBIT_E_HIP = -6,         /* a HIP runtime call or launch failed           */
-  LOWBIT_E_NOMEM = -7        /* the library could not allocate its workspace  */
+  LOWBIT_E_NOMEM = -7,       /* the library could not allocate its workspace  */
+  LOWBIT_E_TOO_LARGE = -8    /* lowbit_gemv_noalloc: the product needs more
+                                scratch than the library's static array       */
 };
 
 enum lowbit_format {
@@ -214,6 +216,25 @@ int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16,
 int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes,
                 const void* pscales, int x_dtype, const void* x, float x_scale,
                 int y_dtype, void* y, void* stream);
+
+/* Allocation-free lowbit_gemv, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors as lowbit_gemv, which it
+ * equals bit for bit (the same kernels), plus LOWBIT_E_TOO_LARGE.  Instead of
+ * the per-stream workspace it uses a static device array of 4 MiB per GPU
+ * (held until the process ends), enough for every product whose workspace
+ * (lowbit_workspace_bytes with M = 1) is at most 4 MiB -- every N <= 65536
+ * with K <= 65536, and the 27B-class layer shapes; larger products return
+ * LOWBIT_E_TOO_LARGE before any launch.  It calls no hipMalloc or hipFree.
+ * The first call on a device looks the array up and clears its counter
+ * block with a small kernel on `stream`.  All calls on one GPU share the
+ * array: calls that may overlap in time on one GPU (different streams, or
+ * replays of graphs holding this call on different streams) race and give
+ * wrong results; order them on one stream.  Sign activations (SIGN1) use no
+ * scratch. */
+int lowbit_gemv_noalloc(int fmt, int64_t N, int64_t K, const void* pcodes,
+                        const void* pscales, int x_dtype, const void* x, float x_scale,
+                        int y_dtype, void* y, void* stream);
 
 /* Product Y[m][n] = sum_k W[n][k] * X[m][k] for m < M, n < N: the dense
  * contraction of prefill and of a denoising step ([XH] section "速度は二層：

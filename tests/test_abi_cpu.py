@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     assert lb.lib().lowbit_abi_version() == 3
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert isinstance(lb.status_str(st), str) and lb.status_str(st)
 
 
@@ -147,3 +147,21 @@ def test_chain_del_at_finalization_does_nothing():
         sys.is_finalizing = real
     assert c._h.value == 0x1234
     c._h = None
+
+
+def test_gemv_noalloc_validation_without_gpu():
+    """The allocation-free GEMV checks its arguments as lowbit_gemv does and
+    rejects products that need more than its static scratch before any HIP
+    call."""
+    L = lb.lib()
+    f = L.lowbit_gemv_noalloc
+    assert f(1, 16, 128, None, A16, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_NULL
+    assert f(1, 16, 100, A16, A16, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_SHAPE
+    assert f(7, 16, 128, A16, A16, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_UNSUPPORTED
+    assert f(2, 16, 128, A16, A16, lb.SIGN1, A16, 1.0, lb.F32, A16, None) == lb.E_UNSUPPORTED
+    assert f(1, 16, 128, A16, A16, lb.BF16, A16, 1.0, lb.F32, A1, None) == lb.E_ALIGN
+    for fmt in (1, 2, 3):
+        N, K = 1 << 17, 1 << 16
+        assert lb.workspace_bytes(fmt, 1, N, K, lb.BF16) > 4 << 20
+        assert f(fmt, N, K, A16, A16, lb.BF16, A16, 1.0, lb.F32, A16, None) == lb.E_TOO_LARGE
+    assert "scratch" in lb.status_str(lb.E_TOO_LARGE)

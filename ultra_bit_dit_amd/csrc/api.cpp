@@ -75,14 +75,49 @@ int workspace(hipStream_t s, size_t need, void** out) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ---- the allocation-free GEMV's scratch: one static device array per GPU,
+// shared by every lowbit_gemv_noalloc call on that GPU.  Host code uses only
+// the device address hipGetSymbolAddress returns for the current device
+// (taken once per device, under g_scratch_mutex); the array's name on the
+// host is not a device address.  Its first kCounterBytes hold the fused
+// GEMV's arrival counters: zero when the code object is loaded (static
+// storage), cleared again by a fill kernel on the first call's stream, and
+// left zero by every launch.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static_assert(kScratchBytes >= (size_t)kCounterBytes, "counters must fit the scratch");
+
+__global__ void fill_zero_u32(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+std::mutex g_scratch_mutex;
+std::map<int, void*> g_scratch;  // device -> address of `scratch` on it
+
+int scratch_for_device(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LOWBIT_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LOWBIT_E_HIP;
+    hipLaunchKernelGGL(fill_zero_u32, dim3(64), dim3(256), 0, s, (uint32_t*)ptr,
+                       (int64_t)(kCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return LOWBIT_E_HIP;
+    it = g_scratch.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return LOWBIT_OK;
+}
+
 // small-M product through the fused MFMA GEMV kernel (M * R <= 16 rows of A)
-int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
-                  const void* pscales, int x_dtype, const void* x, float x_scale,
-                  const float* x_scales, int y_dtype, void* y, hipStream_t s) {
-  if (cdiv(N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
-  void* ws = nullptr;
-  int rc = workspace(s, gemv_workspace_bytes(fmt, N, K, M, x_dtype), &ws);
-  if (rc) return rc;
+// with the workspace `ws` (counters first, zero)
+int gemv_mfma_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
+                 const void* pscales, int x_dtype, const void* x, float x_scale,
+                 const float* x_scales, int y_dtype, void* y, void* ws, hipStream_t s) {
   GemvArgs g;
   g.fmt = fmt;
   g.N = N;
@@ -98,6 +133,17 @@ int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
   g.y = y;
   g.ws = ws;
   return hip_status(launch_gemv_mfma(g, s));
+}
+
+int run_gemv_mfma(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes,
+                  const void* pscales, int x_dtype, const void* x, float x_scale,
+                  const float* x_scales, int y_dtype, void* y, hipStream_t s) {
+  if (cdiv(N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
+  void* ws = nullptr;
+  int rc = workspace(s, gemv_workspace_bytes(fmt, N, K, M, x_dtype), &ws);
+  if (rc) return rc;
+  return gemv_mfma_ws(fmt, M, N, K, pcodes, pscales, x_dtype, x, x_scale, x_scales, y_dtype, y,
+                      ws, s);
 }
 
 // large-M product through the staged-tile MFMA GEMM
@@ -153,6 +199,7 @@ const char* lowbit_status_str(int status) {
     case LOWBIT_E_BADCODE: return "invalid code";
     case LOWBIT_E_HIP: return "HIP runtime error";
     case LOWBIT_E_NOMEM: return "workspace allocation failed (or needed growth during graph capture)";
+    case LOWBIT_E_TOO_LARGE: return "product needs more scratch than the allocation-free call holds";
   }
   return "unknown status";
 }
@@ -202,8 +249,11 @@ int lowbit_quantize_act_i8(int64_t M, int64_t K, const uint16_t* X_bf16, int8_t*
   return hip_status(launch_quantize_i8(M, K, X_bf16, Q, s_x, (hipStream_t)stream));
 }
 
-int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
-                int x_dtype, const void* x, float x_scale, int y_dtype, void* y, void* stream) {
+namespace {
+
+// argument checks of lowbit_gemv (and its allocation-free variant)
+int gemv_check(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+               int x_dtype, const void* x, int y_dtype, void* y) {
   if (!pcodes || !x || !y) return LOWBIT_E_NULL;
   if (!valid_fmt(fmt)) return LOWBIT_E_UNSUPPORTED;
   if (!shape_ok(N, K)) return LOWBIT_E_SHAPE;
@@ -217,23 +267,51 @@ int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* p
   if (!aligned(pcodes, 16) || (pscales && !aligned(pscales, 16)) || !aligned(x, 16) ||
       !aligned(y, 4))
     return LOWBIT_E_ALIGN;
+  if (x_dtype == LOWBIT_SIGN1 && K > kSignMaxK) return LOWBIT_E_SHAPE;  // sign words in LDS
+  if (x_dtype != LOWBIT_SIGN1 && cdiv(N, 16) > kMaxRowGroups) return LOWBIT_E_SHAPE;
+  return LOWBIT_OK;
+}
+
+int gemv_sign(int64_t N, int64_t K, const void* pcodes, const void* pscales, const void* x,
+              float x_scale, int y_dtype, void* y, hipStream_t s) {
+  SignArgs a;
+  a.N = N;
+  a.K = K;
+  a.M = 1;
+  a.pcodes = pcodes;
+  a.pscales = (const uint16_t*)pscales;
+  a.xbits = (const uint8_t*)x;
+  a.alpha = x_scale;
+  a.ykind = y_dtype;
+  a.y = y;
+  return hip_status(launch_gemv_sign(a, s));
+}
+
+}  // namespace
+
+int lowbit_gemv(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+                int x_dtype, const void* x, float x_scale, int y_dtype, void* y, void* stream) {
+  const int rc = gemv_check(fmt, N, K, pcodes, pscales, x_dtype, x, y_dtype, y);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (x_dtype == LOWBIT_SIGN1) {
-    if (K > kSignMaxK) return LOWBIT_E_SHAPE;  // the row's sign words live in LDS
-    SignArgs a;
-    a.N = N;
-    a.K = K;
-    a.M = 1;
-    a.pcodes = pcodes;
-    a.pscales = (const uint16_t*)pscales;
-    a.xbits = (const uint8_t*)x;
-    a.alpha = x_scale;
-    a.ykind = y_dtype;
-    a.y = y;
-    return hip_status(launch_gemv_sign(a, s));
-  }
+  if (x_dtype == LOWBIT_SIGN1) return gemv_sign(N, K, pcodes, pscales, x, x_scale, y_dtype, y, s);
   return run_gemv_mfma(fmt, 1, N, K, pcodes, pscales, x_dtype, x, x_scale, nullptr, y_dtype, y,
                        s);
+}
+
+int lowbit_gemv_noalloc(int fmt, int64_t N, int64_t K, const void* pcodes, const void* pscales,
+                        int x_dtype, const void* x, float x_scale, int y_dtype, void* y,
+                        void* stream) {
+  const int rc = gemv_check(fmt, N, K, pcodes, pscales, x_dtype, x, y_dtype, y);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (x_dtype == LOWBIT_SIGN1) return gemv_sign(N, K, pcodes, pscales, x, x_scale, y_dtype, y, s);
+  if (gemv_workspace_bytes(fmt, N, K, 1, x_dtype) > kScratchBytes) return LOWBIT_E_TOO_LARGE;
+  void* ws = nullptr;
+  const int r2 = scratch_for_device(s, &ws);
+  if (r2) return r2;
+  return gemv_mfma_ws(fmt, 1, N, K, pcodes, pscales, x_dtype, x, x_scale, nullptr, y_dtype, y, ws,
+                      s);
 }
 
 int lowbit_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* pcodes, const void* pscales,

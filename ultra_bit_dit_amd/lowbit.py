@@ -13,6 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "liblowbit.so")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_BADCODE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+E_TOO_LARGE = -8
 BINARY, TERNARY_2BIT, TERNARY_BASE3 = 1, 2, 3
 F32, BF16, I8, SIGN1, I32 = 1, 2, 3, 4, 5
 EPI_NONE, EPI_SILU_MUL = 0, 1
@@ -20,7 +21,7 @@ EPI_NONE, EPI_SILU_MUL = 0, 1
 # every symbol the public header declares
 EXPORTS = ("lowbit_abi_version", "lowbit_status_str", "lowbit_packed_bytes", "lowbit_pack",
            "lowbit_unpack", "lowbit_quantize_act_i8", "lowbit_gemv", "lowbit_gemm",
-           "lowbit_workspace_bytes", "lowbit_reserve_workspace", "lowbit_release_workspaces",
+           "lowbit_gemv_noalloc", "lowbit_workspace_bytes", "lowbit_reserve_workspace", "lowbit_release_workspaces",
            "lowbit_chain_create", "lowbit_chain_create_rows", "lowbit_chain_run", "lowbit_chain_status",
            "lowbit_chain_destroy",
            "lowbit_hbm_read_probe", "lowbit_quantize_weights", "lowbit_rotate_act")
@@ -60,6 +61,7 @@ def lib():
         L.lowbit_unpack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
         L.lowbit_quantize_act_i8.argtypes = [i64, i64, vp, vp, vp, vp]
         L.lowbit_gemv.argtypes = [i32, i64, i64, vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
+        L.lowbit_gemv_noalloc.argtypes = [i32, i64, i64, vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
         L.lowbit_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i32, vp, vp, i32, vp, vp]
         L.lowbit_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.lowbit_reserve_workspace.argtypes = [ctypes.c_size_t, vp]
@@ -165,6 +167,16 @@ def gemv(fmt, N, K, pcodes, pscales, x, x_scale=1.0, y_dtype=F32, y=None, x_dtyp
         y = torch.empty(N, dtype=_ytorch(y_dtype), device=pcodes.device)
     _check("lowbit_gemv", lib().lowbit_gemv(fmt, N, K, _ptr(pcodes), _ptr(pscales), _xdt(x, x_dtype),
                                             _ptr(x), float(x_scale), y_dtype, _ptr(y), _stream(stream)))
+    return y
+
+
+def gemv_noalloc(fmt, N, K, pcodes, pscales, x, y, x_scale=1.0, y_dtype=F32, x_dtype=None,
+                 stream=None):
+    """lowbit_gemv through the allocation-free entry point (lowbit_gemv_noalloc):
+    the caller passes the output y; nothing is allocated."""
+    _check("lowbit_gemv_noalloc",
+           lib().lowbit_gemv_noalloc(fmt, N, K, _ptr(pcodes), _ptr(pscales), _xdt(x, x_dtype),
+                                     _ptr(x), float(x_scale), y_dtype, _ptr(y), _stream(stream)))
     return y
 
 
