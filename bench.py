@@ -139,7 +139,7 @@ def median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
-def pmc_traffic(launch_bytes, kernel):
+def pmc_traffic(launch_bytes, kernel, fmt=2):
     """HBM bytes per launch of the decode kernel from the committed rocprofv3
     counter summary, scaled by the same counters read on a plain copy of
     known size; None when the summary is missing or the kernel source changed
@@ -153,6 +153,8 @@ def pmc_traffic(launch_bytes, kernel):
                     kv[k.strip()] = v.strip()
         if kv.get("gemv_source_sha256_16") != gemv_source_hash() or kv.get("kernel") != kernel:
             return None, "kernel changed since the counters were taken"
+        if kv.get("format", FMT_NAMES[2]) != FMT_NAMES[fmt]:
+            return None, f"counters taken for {kv.get('format')}, not {FMT_NAMES[fmt]}"
         copy_bytes = float(kv["copy_bytes_each_way"])
         f_scale = copy_bytes / (float(kv["copy_FETCH_SIZE_KiB"]) * 1024.0)
         w_scale = copy_bytes / (float(kv["copy_WRITE_SIZE_KiB"]) * 1024.0)
@@ -280,7 +282,7 @@ def bench_decode(args, lb, synth, torch, np):
     launch_bytes = step_bytes / launches
     launch_us = ms * 1e3 / launches
     kbase = {"chain": "gemv_stream", "chain_dep": "gemv_chain", "separate": "gemv_mfma"}[head]
-    traffic, tnote = pmc_traffic(launch_bytes, kbase)
+    traffic, tnote = pmc_traffic(launch_bytes, kbase, fmt)
     kname = kbase + f" ({FMT_NAMES[fmt]}, bf16 x, fp32 y)"
     roof = {"bound": "hbm", "kernel": kname,
             "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
@@ -656,6 +658,212 @@ def cpu_baseline(fmt, step_bytes, budget_s, device_gen=None):
     return out
 
 
+# ------------------------------------------------------------------ profiles
+# Summaries of rocprofv3 output for profiles/: `python bench.py --summarize
+# KIND --prof-dir DIR [--prof-dir2 DIR2] --out FILE --cmd "..."`.
+
+def _csv_rows(d, suffix):
+    """Rows of every `*<suffix>` CSV rocprofv3 wrote under directory d."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def _demangle(names):
+    import subprocess
+    try:
+        out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True,
+                             timeout=60).stdout.split("\n")
+        return [o.replace("lowbit::(anonymous namespace)::", "") for o in out[:len(names)]]
+    except (OSError, subprocess.SubprocessError):
+        return list(names)
+
+
+def _dispatches(d):
+    """Per dispatch of a --pmc run: {"id", "kernel", "grid", "counters": {...}} in
+    dispatch order (counter values of one dispatch summed over their rows)."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        did = int(_col(r, "Dispatch_Id", "Dispatch_ID"))
+        e = acc.setdefault(did, {"id": did, "kernel": _col(r, "Kernel_Name"),
+                                 "grid": _col(r, "Grid_Size", "Grid_Size_X"), "counters": {}})
+        c = _col(r, "Counter_Name")
+        e["counters"][c] = e["counters"].get(c, 0.0) + float(_col(r, "Counter_Value"))
+    out = [acc[k] for k in sorted(acc)]
+    dm = _demangle([e["kernel"] for e in out])
+    for e, n in zip(out, dm):
+        e["kernel"] = n
+    return out
+
+
+def _trace(d):
+    """Per dispatch of a --kernel-trace run: (kernel, duration ns) in order."""
+    rows = _csv_rows(d, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(_col(r, "Dispatch_Id", "Dispatch_ID")))
+    names = _demangle([_col(r, "Kernel_Name") for r in rows])
+    return [(n, int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")))
+            for n, r in zip(names, rows)]
+
+
+def _kbase(name):
+    return name.split("<", 1)[0].split("(", 1)[0].strip()
+
+
+def summarize_stats(d, out, cmd):
+    """Kernel-trace statistics (rocprofv3 --stats): every kernel's calls and
+    average / min / max duration."""
+    rows = _csv_rows(d, "kernel_stats.csv")
+    names = _demangle([_col(r, "Name", "Kernel_Name") for r in rows])
+    lines = ["# rocprofv3 kernel statistics (--kernel-trace --stats)", f"# command: {cmd}",
+             "# kernel | calls | total ms | average us | min us | max us"]
+    for n, r in sorted(zip(names, rows), key=lambda t: -float(_col(t[1], "TotalDurationNs"))):
+        lines.append(f"{n[:150]} | {_col(r, 'Calls')} | {float(_col(r, 'TotalDurationNs')) / 1e6:.3f} | "
+                     f"{float(_col(r, 'AverageNs')) / 1e3:.3f} | {float(_col(r, 'MinNs')) / 1e3:.3f} | "
+                     f"{float(_col(r, 'MaxNs')) / 1e3:.3f}")
+    _write(out, lines)
+
+
+def summarize_hbm(dfetch, dwrite, out, cmd, fmt, layers):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of the streaming decode kernel and
+    of the copy it is scaled by, in the key = value form pmc_traffic reads."""
+    from ultra_bit_dit_amd import lowbit as lb
+    name = f"gemv_stream<{fmt},"
+
+    def pick(d, counter):
+        ds = _dispatches(d)
+        g = [e["counters"][counter] for e in ds if e["kernel"].startswith(name)]
+        c = [e["counters"][counter] for e in ds if "neg" in e["kernel"]]
+        if not g or not c:
+            raise SystemExit(f"no {name} or copy dispatch with {counter} under {d}")
+        return sum(g) / len(g), max(c), len(g)
+
+    gf, cf, nf = pick(dfetch, "FETCH_SIZE")
+    gw, cw, nw = pick(dwrite, "WRITE_SIZE")
+    lines = [
+        "# rocprofv3 HBM byte counters of the decode GEMV kernel (gemv_stream)",
+        f"# FETCH_SIZE command: {cmd.replace('@PMC@', 'FETCH_SIZE')}",
+        f"# WRITE_SIZE command: {cmd.replace('@PMC@', 'WRITE_SIZE')}",
+        "# copy reference: torch.neg over 64 Mi fp32 (256 MiB read, 256 MiB written)",
+        f"# gemv dispatches counted: {nf} (FETCH), {nw} (WRITE); per-dispatch KiB averaged",
+        "kernel = gemv_stream",
+        f"format = {FMT_NAMES[fmt]}",
+        "# hash of the code of gemv.hip + fp4.hpp + common.hpp (the sources the kernel is built "
+        "from; comments and blank space removed)",
+        f"gemv_source_sha256_16 = {gemv_source_hash()}",
+        f"profiled_algorithmic_bytes_per_dispatch = {packed_bytes(lb, fmt, MATS) * layers}",
+        f"gemv_FETCH_SIZE_KiB_per_dispatch = {gf:.1f}",
+        f"gemv_WRITE_SIZE_KiB_per_dispatch = {gw:.1f}",
+        f"copy_bytes_each_way = {256 << 20}",
+        f"copy_FETCH_SIZE_KiB = {cf:.1f}",
+        f"copy_WRITE_SIZE_KiB = {cw:.1f}",
+    ]
+    _write(out, lines)
+
+
+def gemm_dispatch_labels(legs, reps):
+    """The (leg, M, product, timed) label of every gemm_f8 dispatch of a bench
+    run over `legs` with --gemm-reps `reps`, in launch order (two warm-up
+    passes, then the timed ones, per bench_gemm_pass call)."""
+    out = []
+    for leg in [l for l in GEMM_LEGS if l in legs]:
+        if leg.startswith("pp512"):
+            runs = [(512, MATS, reps)]
+        elif leg.startswith("dit"):
+            runs = [(M, DIT, max(2, reps // (M // 4608))) for M in (4608, 18432)]
+        else:
+            continue
+        for M, shapes, r in runs:
+            for p in range(2 + r):
+                for name, N, K in shapes:
+                    out.append((leg, M, name, N, K, p >= 2))
+    return out
+
+
+def summarize_mfma(dpmc, dtrace, out, cmd_pmc, cmd_trace, legs, reps):
+    """MFMA counters and durations per GEMM product (pp512 and DiT legs).
+    Dispatches are matched to products by launch order."""
+    labels = gemm_dispatch_labels(legs, reps)
+    pm = [e for e in _dispatches(dpmc) if _kbase(e["kernel"]) == "gemm_f8"]
+    tr = [t for t in _trace(dtrace) if _kbase(t[0]) == "gemm_f8"]
+    if len(pm) != len(labels) or len(tr) != len(labels):
+        raise SystemExit(f"{len(pm)} counted / {len(tr)} traced gemm_f8 dispatches, "
+                         f"{len(labels)} expected")
+    groups = {}
+    for lab, e, t in zip(labels, pm, tr):
+        g = groups.setdefault(lab[:5], {"n": 0, "c": {}, "dur": [], "kernel": e["kernel"]})
+        g["n"] += 1
+        for k, v in e["counters"].items():
+            g["c"][k] = g["c"].get(k, 0.0) + v
+        if lab[5]:
+            g["dur"].append(t[1])
+    lines = ["# rocprofv3 MFMA counters of the GEMM kernel (gemm_f8), per product",
+             f"# counters: {cmd_pmc}", f"# durations: {cmd_trace}",
+             "# dispatches matched to products by launch order; durations: median over the "
+             "timed passes of the trace run; counters: mean per dispatch",
+             "# flop = 2 M N K; mfma_ops = SQ_INSTS_VALU_MFMA_MOPS_* x 512 (operations the "
+             "MFMA pipe executed, split terms and padding included)",
+             "# busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES x 4 SIMDs); "
+             "cycles_per_mfma = SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA"]
+    for (leg, M, name, N, K), g in groups.items():
+        c = {k: v / g["n"] for k, v in g["c"].items()}
+        dur = median(g["dur"]) if g["dur"] else float("nan")
+        flop = 2.0 * M * N * K
+        mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS")) * 512
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+        cu = c.get("SQ_BUSY_CU_CYCLES", float("nan"))
+        nm = c.get("SQ_INSTS_MFMA", float("nan"))
+        lines.append(
+            f"{leg} M={M} {name} {N}x{K}: {dur / 1e3:.2f} us, {flop / dur / 1e3:.1f} TFLOP/s "
+            f"({100 * flop / dur / 1e3 / (MFMA_PEAK_F16_TFLOPS if leg.endswith('bf16') else MFMA_PEAK_I8_TOPS if leg.endswith('i8') else MFMA_PEAK_F4_TOPS):.1f}% of the "
+            f"{'bf16' if leg.endswith('bf16') else 'int8' if leg.endswith('i8') else 'fp4'} peak); "
+            f"mfma_ops/flop {mops / flop:.2f}; mfma_ops rate {mops / dur / 1e3:.1f} T/s; "
+            f"busy_frac {busy / (4 * cu):.3f}; cycles_per_mfma {busy / nm:.1f}; "
+            + "; ".join(f"{k} {v:.4g}" for k, v in sorted(c.items())))
+    lines.append(f"# kernel instances: {sorted(set(g['kernel'][:120] for g in groups.values()))}")
+    _write(out, lines)
+
+
+def summarize_valu(d, out, cmd, fmt, layers):
+    """Instruction counters of the streaming decode kernel per weight."""
+    ds = [e for e in _dispatches(d) if e["kernel"].startswith(f"gemv_stream<{fmt},")]
+    if not ds:
+        raise SystemExit(f"no gemv_stream<{fmt}, dispatch under {d}")
+    c = {}
+    for e in ds:
+        for k, v in e["counters"].items():
+            c[k] = c.get(k, 0.0) + v / len(ds)
+    weights = sum(N * K for _, N, K in MATS) * layers
+    lines = [f"# rocprofv3 instruction counters of the decode GEMV kernel (gemv_stream, "
+             f"{FMT_NAMES[fmt]}), mean per dispatch", f"# command: {cmd}",
+             f"# one dispatch = {layers} layers = {weights} weights; SQ_INSTS_* count wave "
+             "instructions (64 lanes each)"]
+    for k, v in sorted(c.items()):
+        lines.append(f"{k} = {v:.6g}")
+    for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS"):
+        if k in c:
+            lines.append(f"{k}_per_1k_weights = {1000 * c[k] / weights:.4f}")
+    if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
+        lines.append(f"wait_inst_any_frac_of_wave_cycles = {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.4f}")
+    _write(out, lines)
+
+
+def _write(path, lines):
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -679,7 +887,28 @@ def main():
                     help="skip the C0 latency and C1 single-product legs")
     ap.add_argument("--verify-rows", type=int, default=5,
                     help="rows of the small-M verification pass through the whole step (0: skip)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode step (and the streaming-read probe)")
+    ap.add_argument("--summarize", choices=["stats", "hbm", "mfma", "valu"],
+                    help="write a profiles/ summary of rocprofv3 output instead of benchmarking")
+    ap.add_argument("--prof-dir", action="append", default=[])
+    ap.add_argument("--out")
+    ap.add_argument("--cmd", action="append", default=[],
+                    help="the rocprofv3 command(s) the summary states")
     args = ap.parse_args()
+    if args.summarize:
+        legs = [l for l in args.gemm_legs.split(",") if l]
+        if args.summarize == "stats":
+            summarize_stats(args.prof_dir[0], args.out, args.cmd[0])
+        elif args.summarize == "hbm":
+            summarize_hbm(args.prof_dir[0], args.prof_dir[1], args.out, args.cmd[0], args.fmt,
+                          args.layers)
+        elif args.summarize == "mfma":
+            summarize_mfma(args.prof_dir[0], args.prof_dir[1], args.out, args.cmd[0], args.cmd[1],
+                           legs, args.gemm_reps)
+        else:
+            summarize_valu(args.prof_dir[0], args.out, args.cmd[0], args.fmt, args.layers)
+        return
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the "
               "kernels run on one device's share; multi-GPU sharding is not implemented)",
@@ -693,36 +922,14 @@ def main():
     from ultra_bit_dit_amd import lowbit as lb
 
     copy_calibration(torch)
-    read_gbs = hbm_read_rate(lb, torch)
-    log(f"streaming read of 4 GiB: {read_gbs:.0f} GB/s")
-    ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
-    roof["measured_read_gb_s"] = round(read_gbs, 1)
-    roof["frac_of_measured_read"] = round(roof["achieved"] / read_gbs, 4)
-    # the same step in the other weight formats (binary, and both ternary
-    # packings): streaming and sequential chains
-    others = []
-    if not args.no_other_format:
-        for ofmt in (1, 2, 3):
-            if ofmt == args.fmt:
-                continue
-            a2 = argparse.Namespace(**vars(args))
-            a2.fmt = ofmt
-            a2.modes = "chain,chain_dep"
-            a2.verify_rows = 0
-            oms, ogbs, obytes, oroof, _, omodes = bench_decode(a2, lb, synth, torch, np)
-            others.append({"format": FMT_NAMES[ofmt], "mode": "chain", "ms_per_step": round(oms, 4),
-                           "gb_s": round(ogbs, 1), "pct_hbm_peak": round(100 * ogbs / HBM_PEAK_GBS, 1),
-                           "tok_s": round(1000.0 / oms, 2), "bytes_per_step": obytes,
-                           "kernel": oroof["kernel"], "decode_modes": omodes})
-
     out = {
         "metric": "decode GEMV HBM GB/s (% peak) & tok/s; pp512 GEMM TFLOP/s (% MFMA peak)",
-        "value": round(gbs, 1),
+        "value": None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -730,15 +937,41 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"27B-class decode step, {FMT_NAMES[args.fmt]}: {args.layers} layers x "
                                "(qkv 15360x5120, o 5120x5120, gate/up 34816x5120, down 5120x17408), "
-                               "group-128 fp16 scales, bf16 activations, batch 1",
-                   "tok_s": round(1000.0 / ms, 2),
-                   "tok_s_sequential": modes_out.get("chain_dep", {}).get("tok_s"),
-                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                   "bytes_per_step": step_bytes,
-                   "mode": head,
-                   "decode_modes": modes_out},
-        "roofline": roof,
+                               "group-128 fp16 scales, bf16 activations, batch 1"},
     }
+    others = []
+    step_bytes = packed_bytes(lb, args.fmt, MATS) * args.layers
+    if not args.no_decode:
+        read_gbs = hbm_read_rate(lb, torch)
+        log(f"streaming read of 4 GiB: {read_gbs:.0f} GB/s")
+        ms, gbs, step_bytes, roof, head, modes_out = bench_decode(args, lb, synth, torch, np)
+        roof["measured_read_gb_s"] = round(read_gbs, 1)
+        roof["frac_of_measured_read"] = round(roof["achieved"] / read_gbs, 4)
+        out["value"] = round(gbs, 1)
+        out["ms_per_step"] = round(ms, 4)
+        out["config"].update({"tok_s": round(1000.0 / ms, 2),
+                              "tok_s_sequential": modes_out.get("chain_dep", {}).get("tok_s"),
+                              "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                              "bytes_per_step": step_bytes,
+                              "mode": head,
+                              "decode_modes": modes_out})
+        out["roofline"] = roof
+        # the same step in the other weight formats (binary, and both ternary
+        # packings): streaming and sequential chains
+        if not args.no_other_format:
+            for ofmt in (1, 2, 3):
+                if ofmt == args.fmt:
+                    continue
+                a2 = argparse.Namespace(**vars(args))
+                a2.fmt = ofmt
+                a2.modes = "chain,chain_dep"
+                a2.verify_rows = 0
+                oms, ogbs, obytes, oroof, _, omodes = bench_decode(a2, lb, synth, torch, np)
+                others.append({"format": FMT_NAMES[ofmt], "mode": "chain",
+                               "ms_per_step": round(oms, 4), "gb_s": round(ogbs, 1),
+                               "pct_hbm_peak": round(100 * ogbs / HBM_PEAK_GBS, 1),
+                               "tok_s": round(1000.0 / oms, 2), "bytes_per_step": obytes,
+                               "kernel": oroof["kernel"], "decode_modes": omodes})
     for o in others:
         out["config"]["decode_" + o["format"].replace("-", "_")] = o
     if not args.no_c01:
