@@ -685,9 +685,10 @@ def _demangle(names):
     try:
         out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True,
                              timeout=60).stdout.split("\n")
-        return [o.replace("lowbit::(anonymous namespace)::", "") for o in out[:len(names)]]
     except (OSError, subprocess.SubprocessError):
-        return list(names)
+        out = list(names)
+    out = [o.replace("lowbit::(anonymous namespace)::", "") for o in out[:len(names)]]
+    return [o[5:] if o.startswith("void ") else o for o in out]
 
 
 def _dispatches(d):
@@ -697,7 +698,8 @@ def _dispatches(d):
     for r in _csv_rows(d, "counter_collection.csv"):
         did = int(_col(r, "Dispatch_Id", "Dispatch_ID"))
         e = acc.setdefault(did, {"id": did, "kernel": _col(r, "Kernel_Name"),
-                                 "grid": _col(r, "Grid_Size", "Grid_Size_X"), "counters": {}})
+                                 "grid": _col(r, "Grid_Size", "Grid_Size_X"), "counters": {},
+                                 "ns": int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))})
         c = _col(r, "Counter_Name")
         e["counters"][c] = e["counters"].get(c, 0.0) + float(_col(r, "Counter_Value"))
     out = [acc[k] for k in sorted(acc)]
@@ -801,8 +803,9 @@ def summarize_mfma(dpmc, dtrace, out, cmd_pmc, cmd_trace, legs, reps):
                          f"{len(labels)} expected")
     groups = {}
     for lab, e, t in zip(labels, pm, tr):
-        g = groups.setdefault(lab[:5], {"n": 0, "c": {}, "dur": [], "kernel": e["kernel"]})
+        g = groups.setdefault(lab[:5], {"n": 0, "c": {}, "dur": [], "kernel": e["kernel"], "pns": 0})
         g["n"] += 1
+        g["pns"] += e["ns"]
         for k, v in e["counters"].items():
             g["c"][k] = g["c"].get(k, 0.0) + v
         if lab[5]:
@@ -813,23 +816,31 @@ def summarize_mfma(dpmc, dtrace, out, cmd_pmc, cmd_trace, legs, reps):
              "timed passes of the trace run; counters: mean per dispatch",
              "# flop = 2 M N K; mfma_ops = SQ_INSTS_VALU_MFMA_MOPS_* x 512 (operations the "
              "MFMA pipe executed, split terms and padding included)",
-             "# busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES x 4 SIMDs); "
-             "cycles_per_mfma = SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA"]
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs): "
+             "the fraction of SIMD cycles the MFMA pipe was busy while the kernel ran; "
+             "clock = GRBM_GUI_ACTIVE / 8 / dispatch time of the counter run; "
+             "cycles_per_mfma = SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA (32: the 16x16x128 "
+             "fp8 x fp4 MFMA at the fp8 rate; 16: fp4 x fp4)",
+             "# product: time | TFLOP/s (2MNK) | % of the dtype's dense peak | MFMA ops executed / "
+             "2MNK | mfma_busy | clock GHz | cycles_per_mfma | VALU instructions per MFMA"]
     for (leg, M, name, N, K), g in groups.items():
         c = {k: v / g["n"] for k, v in g["c"].items()}
+        pns = g["pns"] / g["n"]
         dur = median(g["dur"]) if g["dur"] else float("nan")
         flop = 2.0 * M * N * K
         mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS")) * 512
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
-        cu = c.get("SQ_BUSY_CU_CYCLES", float("nan"))
+        gui = c.get("GRBM_GUI_ACTIVE", float("nan")) / 8
         nm = c.get("SQ_INSTS_MFMA", float("nan"))
+        peak = (MFMA_PEAK_F16_TFLOPS if leg.endswith("bf16") else MFMA_PEAK_I8_TOPS
+                if leg.endswith("i8") else MFMA_PEAK_F4_TOPS)
+        pname = "bf16" if leg.endswith("bf16") else "int8" if leg.endswith("i8") else "fp4"
         lines.append(
-            f"{leg} M={M} {name} {N}x{K}: {dur / 1e3:.2f} us, {flop / dur / 1e3:.1f} TFLOP/s "
-            f"({100 * flop / dur / 1e3 / (MFMA_PEAK_F16_TFLOPS if leg.endswith('bf16') else MFMA_PEAK_I8_TOPS if leg.endswith('i8') else MFMA_PEAK_F4_TOPS):.1f}% of the "
-            f"{'bf16' if leg.endswith('bf16') else 'int8' if leg.endswith('i8') else 'fp4'} peak); "
-            f"mfma_ops/flop {mops / flop:.2f}; mfma_ops rate {mops / dur / 1e3:.1f} T/s; "
-            f"busy_frac {busy / (4 * cu):.3f}; cycles_per_mfma {busy / nm:.1f}; "
-            + "; ".join(f"{k} {v:.4g}" for k, v in sorted(c.items())))
+            f"{leg} M={M} {name} {N}x{K}: {dur / 1e3:.2f} us | {flop / dur / 1e3:.1f} | "
+            f"{100 * flop / dur / 1e3 / peak:.1f}% {pname} | {mops / flop:.2f} | "
+            f"{busy / (1024 * gui):.3f} | {gui / pns:.2f} | {busy / nm:.1f} | "
+            f"{c.get('SQ_INSTS_VALU', float('nan')) / nm:.1f}")
+        lines.append("    raw: " + "; ".join(f"{k} {v:.6g}" for k, v in sorted(c.items())))
     lines.append(f"# kernel instances: {sorted(set(g['kernel'][:120] for g in groups.values()))}")
     _write(out, lines)
 
