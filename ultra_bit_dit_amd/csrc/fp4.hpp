@@ -58,20 +58,38 @@ __device__ __attribute__((always_inline)) inline void load_quad_at(const uint8_t
 }
 
 // base-3: byte value -> its 5 trits as fp4 nibbles (trit 0 -> -1 = 0xA,
-// 1 -> 0, 2 -> +1 = 0x2), nibble e = trit e (least significant first);
-// threads 0..242 of the block fill the 243 entries
-__device__ __attribute__((always_inline)) inline void fill_trit_table(uint32_t* t3) {
-  if (threadIdx.x < 243) {
-    uint32_t v = threadIdx.x, nib = 0;
+// 1 -> 0, 2 -> +1 = 0x2), nibble e = trit e (least significant first)
+__device__ __attribute__((always_inline)) inline uint32_t trit_nibbles(uint32_t v) {
+  uint32_t nib = 0;
 #pragma unroll
-    for (int e = 0; e < 5; e++) {
-      const uint32_t t = v % 3;
-      v /= 3;
-      nib |= (t == 0 ? 0xAu : t == 2 ? 0x2u : 0u) << (4 * e);
+  for (int e = 0; e < 5; e++) {
+    const uint32_t t = v % 3;
+    v /= 3;
+    nib |= (t == 0 ? 0xAu : t == 2 ? 0x2u : 0u) << (4 * e);
+  }
+  return nib;
+}
+
+// The table of trit_nibbles in LDS, TS copies interleaved: entry v of copy c
+// at word TS v + c.  Lane L reads copy L % TS, so a wave's 64 random lookups
+// spread over the banks instead of colliding on the 243 words of a single
+// copy.  Threads of a block of `nthreads` fill it together.
+template <int TS = 1>
+__device__ __attribute__((always_inline)) inline void fill_trit_table(uint32_t* t3, int nthreads = 256) {
+  static_assert(TS == 1 || TS % 4 == 0, "copies are written four at a time");
+  for (int e = threadIdx.x; e < 243; e += nthreads) {
+    const uint32_t nib = trit_nibbles((uint32_t)e);
+    if constexpr (TS == 1) {
+      t3[e] = nib;
+    } else {
+#pragma unroll
+      for (int c = 0; c < TS; c += 4) *(uint4*)(t3 + TS * e + c) = make_uint4(nib, nib, nib, nib);
     }
-    t3[threadIdx.x] = nib;
   }
 }
+
+// bytes of the LDS table with TS copies
+constexpr int trit_table_bytes(int ts) { return 243 * 4 * ts <= 1024 ? 1024 : 243 * 4 * ts; }
 
 // fp16 scale of group t of a quad
 template <int FMT>
@@ -79,8 +97,9 @@ __device__ __attribute__((always_inline)) inline float quad_scale(const Quad<FMT
   return f16_bits_to_f32((t < 2 ? qd.sc.x : qd.sc.y) >> (16 * (t & 1)));
 }
 
-// fp4 operand B of group t of a quad
-template <int FMT>
+// fp4 operand B of group t of a quad (base-3: t3 is the lane's copy of a
+// table with TS interleaved copies, i.e. the table plus L % TS)
+template <int FMT, int TS = 1>
 __device__ __attribute__((always_inline)) inline v8i decode_group(const Quad<FMT>& qd, int t,
                                                                   const uint32_t* t3) {
   uint32_t d0, d1, d2, d3;
@@ -102,9 +121,9 @@ __device__ __attribute__((always_inline)) inline v8i decode_group(const Quad<FMT
 #pragma unroll
     for (int i = 0; i < 6; i++) {
       const int byte = 6 * t + i;
-      nb[i] = t3[(word(byte >> 2) >> (8 * (byte & 3))) & 0xFFu];
+      nb[i] = t3[TS * ((word(byte >> 2) >> (8 * (byte & 3))) & 0xFFu)];
     }
-    const uint32_t tl = (t3[(qd.t3 >> (8 * (t >> 1))) & 0xFFu] >> (8 * (t & 1))) & 0xFFu;
+    const uint32_t tl = (t3[TS * ((qd.t3 >> (8 * (t >> 1))) & 0xFFu)] >> (8 * (t & 1))) & 0xFFu;
     // slot s -> nibble s of d0..d3 (5 slots per byte)
     const uint64_t lo = (uint64_t)nb[0] | ((uint64_t)nb[1] << 20) | ((uint64_t)nb[2] << 40) |
                         ((uint64_t)nb[3] << 60);

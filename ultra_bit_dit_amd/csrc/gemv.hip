@@ -35,6 +35,13 @@ constexpr uint32_t kChainSpinLimit = 1u << 24;  // sleeps before a chain wait gi
 constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
 constexpr int kQuadsMulti = 4;      // quads per slice of the several-row streaming kernel
 constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
+// rows of A the image buffers of a several-row streaming kernel with QM-quad
+// slices hold (a slice image travels in at most nine 16-byte registers per
+// thread)
+constexpr int multi_max_ma(int qm) { return qm == kQuadsMultiWide ? 10 : 16; }
+// dynamic LDS of the one-product kernel and the waiting chain: two
+// workgroups per CU fit in the 160 KiB of a gfx950 CU
+constexpr size_t kLdsCap = 80 * 1024;
 
 // Operand scheme of the activations for weight format FMT and activation kind
 // XK (split_terms): R terms, kShift binades apart, the block maximum scaled
@@ -48,6 +55,12 @@ constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
 template <int FMT, int XK>
 struct XSplit {
   static constexpr bool kBF8 = XK == XK_BF16 && FMT != 1;
+  // kCheck 1: three round-to-nearest-even bf8 terms, 3 binades apart, carry
+  // every bf16 value of scaled magnitude 2^-13 or more exactly (checked over
+  // every 8-bit significand at every exponent; the bound holds whether or not
+  // the conversion keeps subnormal results), so a scaled magnitude below it
+  // is what staging flags
+  static constexpr float kMinExact = 0x1p-13f;
   static constexpr int R = split_terms(FMT, XK);
   static constexpr int kShift = kBF8 ? 3 : 4;
   static constexpr int kTop = kBF8 ? 14 : 7;
@@ -259,7 +272,8 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   // tv: the part of v (scaled by 2^-E) the terms still have to carry, times
   // 2^(kShift r) before term r; t0: tv before term 0 (relative check only)
   float tv[8], t0[8];
-  uint32_t lost = 0;  // elements whose scaling by 2^-E underflowed to zero
+  uint32_t lost = 0;  // kCheck 3: elements whose scaling by 2^-E underflowed to zero
+  bool small = false;  // kCheck 1: a nonzero element below kMinExact
   float amax_s = 0.f;
   if constexpr (XK == XK_I8) {
 #pragma unroll
@@ -270,7 +284,8 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       tv[j] = v[j] * sc;
-      if (S::kCheck == 1 || S::kCheck == 3) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
+      if (S::kCheck == 1) small = small || (v[j] != 0.0f && fabsf(tv[j]) < S::kMinExact);
+      if (S::kCheck == 3) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
       if (S::kCheck == 3) t0[j] = tv[j];
     }
     amax_s = amax * sc;
@@ -297,7 +312,7 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
       w1 = cvt_pk8<FA, false>(tv[4], tv[5], 0);
       w1 = cvt_pk8<FA, true>(tv[6], tv[7], w1);
       Er = E - S::kShift * r;
-      if (S::kCheck != 0 || r + 1 < R) {
+      if (S::kCheck >= 2 || r + 1 < R) {
         float d[8];
         cvt_f32x4<FA>(w0, d);
         cvt_f32x4<FA>(w1, d + 4);
@@ -316,9 +331,7 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   constexpr float kEpsR = kStageEps * (float)(1 << (S::kShift * (R - 1)));
   bool bad = false;
   if constexpr (S::kCheck == 1) {
-    bad = lost != 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) bad = bad || tv[j] != 0.0f;
+    bad = small;
   } else if constexpr (S::kCheck == 3) {
     bad = lost != 0;
 #pragma unroll
@@ -573,11 +586,18 @@ __device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint
 // activation row: their A operand is zero); base-3: byte value -> its 5
 // trits as fp4 nibbles (trit 0 -> -1 = 0xA, 1 -> 0, 2 -> +1 = 0x2), nibble e
 // = trit e (least significant first)
-template <int FMT>
+template <int FMT, int TS = 1>
 __device__ __attribute__((always_inline)) inline void lds_init(const Lds& l) {
   if (threadIdx.x < 9) ((uint32_t*)l.zblk)[threadIdx.x] = threadIdx.x < 8 ? 0u : 0x7F7F7F7Fu;
-  if constexpr (FMT == 3) fill_trit_table(l.t3);
+  if constexpr (FMT == 3) fill_trit_table<TS>(l.t3, (int)blockDim.x);
 }
+
+// copies of the base-3 table: the one-row kernels keep one per bank
+// (lookups spread over the banks) in the LDS their small slice images leave
+// free (16 copies: three workgroups of the streaming kernel still fit a CU)
+constexpr int kTritCopies = 16;
+template <int FMT, bool ONE_ROW>
+constexpr int trit_copies() { return FMT == 3 && ONE_ROW ? kTritCopies : 1; }
 
 // this wave's staging flag: lane 0 writes whether any lane saw an inaccurate element
 __device__ __attribute__((always_inline)) inline void put_wave_flag(uint32_t* wflag, bool bad) {
@@ -601,13 +621,14 @@ __device__ __attribute__((always_inline)) inline bool get_flags(const uint32_t* 
 // the order quad_mfma_m1 uses (the chains and the one-product kernel agree
 // bit for bit).  (BATCH groups at a time: 4 gives the most independent
 // MFMAs, 2 fewer live registers)
-template <int FMT, int XK, int MM, int BATCH = 4>
+template <int FMT, int XK, int MM, int BATCH = 4, int TS = 1>
 __device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, const Lds& l, int q,
                                                                 const Quad<FMT>& qd,
                                                                 float (&acc)[4], int (&iacc)[4]) {
   constexpr int FA = XSplit<FMT, XK>::kFmtA;
   constexpr bool INTC = XK == XK_I8;
   const int L = threadIdx.x & 63, r = L & 15, lg = L >> 4;
+  const uint32_t* t3 = l.t3 + L % TS;
   const bool arow = r < a.MA;
   const uint32_t se = *(const uint32_t*)(arow ? l.xe + ((q * 4 + lg) * a.MA + r) * 4 : l.zblk + 32);
   const bool unit_scales = a.pscales == nullptr;
@@ -620,7 +641,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma(const FArgs& a, 
       const uint4* src = (const uint4*)(arow ? l.xa + ((q * 16 + t * 4 + lg) * a.MA + r) * 32 : l.zblk);
       const uint4 x0 = src[0], x1 = src[1];
       A[u] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      B[u] = decode_group<FMT>(qd, t, l.t3);
+      B[u] = decode_group<FMT, TS>(qd, t, t3);
     }
     v4f c[BATCH];
 #pragma unroll
@@ -705,10 +726,11 @@ __device__ __attribute__((always_inline)) inline void load_x8(const FArgs& a, in
 // The slow path for slices whose staging was flagged (kept small in
 // registers: it sits in kernels whose main loops need them); every lane
 // returns the value of row r.
-template <int FMT, int XK>
+template <int FMT, int XK, int TS = 1>
 __device__ __attribute__((always_inline)) inline float exact_slice(const FArgs& a, int64_t rb, int64_t q0, int nq,
-                                                       int64_t m, bool coh, const uint32_t* t3) {
+                                                       int64_t m, bool coh, const uint32_t* t3tab) {
   const int L = threadIdx.x & 63, qtr = L >> 4;
+  const uint32_t* t3 = t3tab + L % TS;
   const int64_t rbc = rb < a.NB ? rb : a.NB - 1;
   float acc = 0.f;
 #pragma unroll 1
@@ -716,8 +738,8 @@ __device__ __attribute__((always_inline)) inline float exact_slice(const FArgs& 
     Quad<FMT> qd;
     load_quad_at<FMT>(a.pcodes, a.pscales, rbc, g >> 2, a.GQ, a.GP, L, qd);
     const int t = (int)(g & 3);
-    const v8i B = t == 0 ? decode_group<FMT>(qd, 0, t3) : t == 1 ? decode_group<FMT>(qd, 1, t3)
-                : t == 2 ? decode_group<FMT>(qd, 2, t3) : decode_group<FMT>(qd, 3, t3);
+    const v8i B = t == 0 ? decode_group<FMT, TS>(qd, 0, t3) : t == 1 ? decode_group<FMT, TS>(qd, 1, t3)
+                : t == 2 ? decode_group<FMT, TS>(qd, 2, t3) : decode_group<FMT, TS>(qd, 3, t3);
     const int64_t k0 = g * kGroup + 64 * (qtr & 1) + 16 * (qtr >> 1);
     float part = 0.f;
 #pragma unroll 1
@@ -760,14 +782,15 @@ __device__ __attribute__((always_inline)) inline v8i decode_binary_reg(uint32_t 
 // operands of all four groups are read from LDS first (eight more live
 // registers per group), for callers with few waves per SIMD to hide the
 // LDS latency behind.
-template <int FMT, int XK, bool AHEAD = false>
+template <int FMT, int XK, bool AHEAD = false, int TS = 1>
 __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t* arow,
                                                                    const uint8_t* erow, int q,
                                                                    const Quad<FMT>& qd,
-                                                                   const uint32_t* t3,
+                                                                   const uint32_t* t3tab,
                                                                    uint32_t sign_mask,
                                                                    uint32_t one_bits, float& acc) {
   constexpr int R = XSplit<FMT, XK>::R, FA = XSplit<FMT, XK>::kFmtA;
+  const uint32_t* t3 = t3tab + (threadIdx.x & 63) % TS;
   const uint32_t se = *(const uint32_t*)(erow + q * 4 * R * 4);
   uint4 xa[4][2];
   if constexpr (AHEAD) {
@@ -794,7 +817,7 @@ __device__ __attribute__((always_inline)) inline void quad_mfma_m1(const uint8_t
       const uint32_t wv = t == 0 ? qd.w[0].x : t == 1 ? qd.w[0].y : t == 2 ? qd.w[0].z : qd.w[0].w;
       B = decode_binary_reg(wv, sign_mask, one_bits);
     } else {
-      B = decode_group<FMT>(qd, t, t3);
+      B = decode_group<FMT, TS>(qd, t, t3);
     }
     const v4f c = mfma_group_t<FA>(t, A, B, (int)se);
     if (t > 0) {
@@ -1144,8 +1167,9 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   const Item it = item_of<FMT>(a, blk);
   const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
   const int64_t nflag = pre ? image_flag_bytes(slice_rounds(it.nq, a.M)) : 0;
+  constexpr int TS = trit_copies<FMT, MM == 1>();
   const Lds l = lds_of(a, smem, it.nq, nflag);
-  lds_init<FMT>(l);
+  lds_init<FMT, TS>(l);
 
   XRegs xr;
   if constexpr (!WAIT) {
@@ -1209,7 +1233,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma_m1<FMT, XK, CHAIN>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+        if (q < it.nq) quad_mfma_m1<FMT, XK, CHAIN, TS>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
     }
     ym[0] = acc;
     yi[0] = 0;
@@ -1219,7 +1243,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
     if (it.live) {
 #pragma unroll
       for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma<FMT, XK, MM>(a, l, q, qd[q], acc, iacc);
+        if (q < it.nq) quad_mfma<FMT, XK, MM, 4, TS>(a, l, q, qd[q], acc, iacc);
     }
     gather_rows<R, MM>(acc, ym);
     gather_rows<R, MM>(iacc, yi);
@@ -1227,7 +1251,7 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   if constexpr (S::kCheck != 0) {
     if (__builtin_expect(exact, 0)) {  // the slice recomputed exactly
       for (int m = 0; m < (int)a.M; m++) {  // rolled: one copy of the slow path
-        const float v = exact_slice<FMT, XK>(a, it.rb, it.q0, it.nq, m, WAIT, l.t3);
+        const float v = exact_slice<FMT, XK, TS>(a, it.rb, it.q0, it.nq, m, WAIT, l.t3);
 #pragma unroll
         for (int mm = 0; mm < MM; mm++)
           if (mm == m) ym[mm] = v;
@@ -1484,7 +1508,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // no workgroup barrier in the loop).
   // rows of A an image may hold: several-row chains use 6-quad slices up to
   // 10 rows of A and 4-quad slices up to 16
-  constexpr int MAX_MA = MR ? (QM == kQuadsMultiWide ? 10 : 16) : R;
+  constexpr int MAX_MA = MR ? multi_max_ma(QM) : R;
   // (an image is followed by its 16-byte flag word)
   constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
   constexpr int kWriteAfter = 3;  // quads computed before the next image is written
@@ -1495,10 +1519,11 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   auto xbuf = [&](uint32_t b) { return smem + b * bufsz; };
   Lds lfix;
   lfix.zblk = smem + 2 * bufsz;
+  constexpr int TS = trit_copies<FMT, !MR>();
   lfix.t3 = (uint32_t*)(lfix.zblk + kZeroBlock);
-  uint32_t* filled = (uint32_t*)(lfix.zblk + kZeroBlock + 1024);
+  uint32_t* filled = (uint32_t*)(lfix.zblk + kZeroBlock + trit_table_bytes(TS));
   uint32_t* consumed = filled + 2;
-  lds_init<FMT>(lfix);
+  lds_init<FMT, TS>(lfix);
   if (threadIdx.x < 4) filled[threadIdx.x] = 0;
   // binary decode masks, in registers (opaque to constant folding)
   uint32_t sign_mask = 0x88888888u, one_bits = 0x22222222u;
@@ -1684,7 +1709,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
           else if constexpr (RB == 2)
             quad_mfma_m1x2<XK>(arow, erow, q, qd[q], qd2[q], sign_mask, one_bits, acc[0], acc[1]);
           else
-            quad_mfma_m1<FMT, XK>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
+            quad_mfma_m1<FMT, XK, false, TS>(arow, erow, q, qd[q], lfix.t3, sign_mask, one_bits, acc[0]);
         }
         if constexpr (RB == 3) load_quad_b3(bn, q, vc, vs, qd[q], qd2[q], qd3[q]);
         else if constexpr (RB == 2) load_quad_p2(pn, q, qd[q], qd2[q]);
@@ -1780,7 +1805,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
         Item itk;
         for (int64_t k2 = 0; k2 < a.KS; k2++) {  // slices in order, as the main loop adds them
           itk = item_at<FMT, RB>(a, rgf, k2);
-          y += exact_slice<FMT, XK>(a, itk.rb, itk.q0, itk.nq, m, false, lfix.t3);
+          y += exact_slice<FMT, XK, TS>(a, itk.rb, itk.q0, itk.nq, m, false, lfix.t3);
         }
         const int64_t n = 16 * itk.rb + r;
         if (a.epi) {
@@ -1832,9 +1857,10 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   p.GQ = cdiv(p.G, 4);
   p.GP = cdiv(p.G, 2);
   p.QM = quads > 0 ? quads : fmt == 1 ? kQuadsBinary : kQuadsTernary;
-  // staged activations of a slice stay within 56 KiB of LDS (small-M
-  // products of 10 rows of A keep a 5120-long row in one slice)
-  int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (56 * 1024) / (16 * p.MA * 33)));
+  // staged activations of a slice stay within 78 KiB of LDS (small-M
+  // products of up to 15 rows of A keep a 5120-long row in one slice; two
+  // workgroups still fit a CU)
+  int64_t qcap = std::min<int64_t>(p.QM, std::max<int64_t>(1, (78 * 1024) / (16 * p.MA * 33)));
   if (fmt == 3) {
     // base-3 slices are whole octets (pairs of quads)
     qcap = std::max<int64_t>(2, qcap & ~int64_t(1));
@@ -1851,7 +1877,7 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   // it is copied from the images staged once per call, M > 1), the zero
   // block and flags, the base-3 table
   p.lds = (size_t)qmax * 16 * p.MA * 33 + (M > 1 ? (size_t)image_flag_bytes(slice_rounds(qmax, M)) : 0) +
-          kZeroBlock + (fmt == 3 ? 1024 : 0);
+          kZeroBlock + (fmt == 3 ? trit_table_bytes(M == 1 ? kTritCopies : 1) : 0);
   p.Npad = p.NRG * p.W * rb * 16;
   p.part_off = kCounterBytes;
   p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
@@ -1904,7 +1930,7 @@ size_t gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M, int xkind)
 
 hipError_t launch_gemv_mfma(const GemvArgs& g, hipStream_t s) {
   const Plan p = make_plan(g.fmt, g.N, g.K, g.M, g.xkind);
-  if (p.NRG > kMaxRowGroups || p.lds > 64 * 1024) return hipErrorInvalidValue;
+  if (p.NRG > kMaxRowGroups || p.lds > kLdsCap) return hipErrorInvalidValue;
   FArgs k;
   k.pcodes = (const uint8_t*)g.pcodes;
   k.pscales = g.pscales;
@@ -1989,7 +2015,7 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsTernary, false, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsTernary, false, 1>;
   constexpr int R = XSplit<FMT, XK>::R;
-  if (M * R <= 10)
+  if (M * R <= multi_max_ma(kQuadsMultiWide))
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMultiWide, true, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMultiWide, true, 1>;
   return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true, 1>
@@ -2015,8 +2041,10 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   // (kQuadsMulti with several activation rows); its two image buffers are
   // sized for the most rows of A it handles (R, or 16)
   const int R = split_terms(fmt, xkind);
-  const bool wide = M * R <= 10;
-  const int quads = waits ? 0 : (M == 1 ? kQuadsTernary : wide ? kQuadsMultiWide : kQuadsMulti);
+  const int quads = waits ? 0
+                  : M == 1 ? kQuadsTernary
+                  : M * R <= multi_max_ma(kQuadsMultiWide) ? kQuadsMultiWide
+                  : kQuadsMulti;
   // binary, one bf16 row, no waits: three row-blocks per wave (buffer
   // addressing: every stage's codes shorter than 2^31 bytes), else two
   bool buf_ok = true;
@@ -2025,12 +2053,13 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   const int rb = !waits && M == 1 && fmt == 1 && xkind == XK_BF16 ? (buf_ok ? 3 : 2) : 1;
   // streaming kernel: two image buffers (image + flag word), the zero block,
   // the base-3 table and four counters
-  size_t lds = waits ? 0 : 2 * ((size_t)quads * 16 * (M == 1 ? R : wide ? 10 : 16) * 33 + 16) + kZeroBlock + 1024 + 16;
+  size_t lds = waits ? 0 : 2 * ((size_t)quads * 16 * (M == 1 ? R : multi_max_ma(quads)) * 33 + 16) + kZeroBlock +
+                          trit_table_bytes(fmt == 3 && M == 1 ? kTritCopies : 1) + 16;
   for (int i = 0; i < S; i++) {
     if (st[i].fmt != fmt) return hipErrorInvalidValue;
     if (st[i].epi && M != 1) return hipErrorInvalidValue;
     const Plan p = make_plan(fmt, st[i].N, st[i].K, M, xkind, quads, rb);
-    if (p.lds > 64 * 1024) return hipErrorInvalidValue;
+    if (p.lds > kLdsCap) return hipErrorInvalidValue;
     if (waits) lds = std::max(lds, p.lds);
     first[i + 1] = first[i] + p.NRG * p.KS;
     ufirst[i + 1] = ufirst[i] + p.NRG;
