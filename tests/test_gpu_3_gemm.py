@@ -173,8 +173,10 @@ def test_pp512_ternary_bf16_sampled(N, K):
     sample_check(2, 512, N, K, tid=150 + (N + K) % 7)
 
 
-@pytest.mark.parametrize("N,K", [(5120, 5120), (5120, 17408)])
+@pytest.mark.parametrize("N,K", [(5120, 5120), (5120, 17408), (34816, 5120)])
 def test_pp512_ternary_int8_sampled(N, K):
+    # 34816 x 5120: 544 tiles of 64 x 512, two whole rounds of the 256 compute
+    # units and 32 tiles split eight ways along K (exact int32 either way)
     print(f"pp512 ternary int8 N={N} K={K}", flush=True)
     sample_check(2, 512, N, K, tid=160 + (N + K) % 7, int8=True)
 

@@ -38,33 +38,60 @@ struct KArgs {
   uint32_t* cnt;            // zero-initialised arrival counters
   const uint16_t* x;        // the bf16 activations (exact recomputation of overflowed lists)
   int64_t M, N, K, G, GQ, GP, NB, MT, NT;
+  int64_t F;                // tiles (in tile order) run whole; the others are split KS ways
   int KS;
   int row_fast;             // tile order: row tile fastest (else column tile fastest)
 };
 
-// Workgroup -> (split, row tile, column tile).  Workgroups are dealt to the
-// 8 XCDs round-robin; each XCD gets a contiguous run of the tile order.  With
-// the column tile fastest the workgroups resident on one XCD share their
-// activation tiles in that XCD's L2 and every XCD streams all the weights;
-// with the row tile fastest (products whose packed weights outweigh their
-// staged activations, e.g. 512-token prefill) each XCD keeps its share of
-// the weights in L2 and streams the activation tiles instead.
-__device__ inline void tile_of(const KArgs& a, int64_t& mt, int64_t& nt, int& ks) {
-  const int64_t T = a.MT * a.NT * a.KS;
+// Workgroup -> (split, row tile, column tile).  The first F tiles of the
+// tile order run whole (one workgroup each); the other TT tiles are split
+// KS ways along K (split ks of tail tile j is workgroup F + ks TT + j).
+// Workgroups are dealt to the 8 XCDs round-robin; each XCD gets a
+// contiguous run of that order -- F / 8 whole tiles, then (TT KS) / 8 split
+// ones, so that every XCD gets the same share of the work when both divide
+// by 8.  With the column tile fastest the workgroups resident on one XCD
+// share their activation tiles in that XCD's L2 and every XCD streams all
+// the weights; with the row tile fastest (products whose packed weights
+// outweigh their staged activations, e.g. 512-token prefill) each XCD keeps
+// its share of the weights in L2 and streams the activation tiles instead.
+// nks: the splits of this workgroup's tile (1 or KS); tail: the tile's index
+// among the split ones (their partial sums and counters).
+__device__ inline void tile_of(const KArgs& a, int64_t& mt, int64_t& nt, int& ks, int& nks,
+                               int64_t& tail) {
+  const int64_t TT = a.MT * a.NT - a.F;
+  const int64_t T = a.F + TT * a.KS;
   const int64_t bid = blockIdx.x;
   int64_t id = bid;
   if (T >= 8) {
-    const int64_t base = T / 8, rem = T % 8, x = bid % 8, loc = bid / 8;
-    id = x * base + min(x, rem) + loc;
+    const int64_t x = bid % 8, loc = bid / 8;
+    if (a.F % 8 == 0 && (TT * a.KS) % 8 == 0) {
+      const int64_t fl = a.F / 8, tl = TT * a.KS / 8;
+      id = loc < fl ? x * fl + loc : a.F + x * tl + (loc - fl);
+    } else {
+      const int64_t base = T / 8, rem = T % 8;
+      id = x * base + min(x, rem) + loc;
+    }
+  }
+  int64_t ti;
+  if (id < a.F) {
+    ti = id;
+    ks = 0;
+    nks = 1;
+    tail = 0;
+  } else {
+    const int64_t j = id - a.F;
+    tail = j % TT;
+    ti = a.F + tail;
+    ks = (int)(j / TT);
+    nks = a.KS;
   }
   if (a.row_fast) {
-    mt = id % a.MT;
-    nt = (id / a.MT) % a.NT;
+    mt = ti % a.MT;
+    nt = (ti / a.MT) % a.NT;
   } else {
-    nt = id % a.NT;
-    mt = (id / a.NT) % a.MT;
+    nt = ti % a.NT;
+    mt = (ti / a.NT) % a.MT;
   }
-  ks = (int)(id / (a.NT * a.MT));
 }
 
 __device__ __forceinline__ float bf16_rne(float v) {
@@ -718,15 +745,17 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
   // below are then a scalar base plus a fixed per-lane offset)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  int64_t mt, nt;
-  int ks;
-  tile_of(a, mt, nt, ks);
+  int64_t mt, nt, tail;
+  int ks, nks;
+  tile_of(a, mt, nt, ks, nks, tail);
   mt = uniform64(mt);
   nt = uniform64(nt);
+  tail = uniform64(tail);
   ks = __builtin_amdgcn_readfirstlane(ks);
+  nks = __builtin_amdgcn_readfirstlane(nks);
   // group and quad indices fit 32 bits (K < 2^38)
-  const int q0 = __builtin_amdgcn_readfirstlane((int)(a.GQ * ks / a.KS));
-  const int q1 = __builtin_amdgcn_readfirstlane((int)(a.GQ * (ks + 1) / a.KS));
+  const int q0 = __builtin_amdgcn_readfirstlane((int)(a.GQ * ks / nks));
+  const int q1 = __builtin_amdgcn_readfirstlane((int)(a.GQ * (ks + 1) / nks));
   const int g0 = 4 * q0, g1 = 4 * q1 < (int)a.G ? 4 * q1 : (int)a.G;
   const int64_t rb0 = nt * CL::kRows + RBW * wn;  // this wave's first row-block
   if constexpr (FMT == 3) fill_trit_table(t3);
@@ -1008,7 +1037,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int e = 0; e < 4; e++)
         v[(i * RBW + j) * 4 + e] = INT ? (uint32_t)iacc[i][j][e] : __float_as_uint(acc[i][j][e]);
-  if (a.KS > 1 && !split_reduce<NV, INT, kF8Threads>(a, mt * a.NT + nt, ks, wave, lane, v)) return;
+  if (nks > 1 && !split_reduce<NV, INT, kF8Threads>(a, tail, ks, wave, lane, v)) return;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -1033,7 +1062,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 
 // ---------------------------------------------------------------- planning
 struct GemmPlan {
-  int64_t MT, NT, G, KS;
+  int64_t MT, NT, G, KS, F;
   int RBW;
   int row_fast;  // tile order of the launch (see tile_of)
   size_t xt_off, rs_off, part_off, bytes;
@@ -1063,6 +1092,30 @@ int64_t pick_splits(int64_t tiles, int64_t GQ) {
   return best;
 }
 
+// Grids of whole rounds and a partial last one: the tiles of the last round
+// may be split along K (2, 4 or 8 ways) so that their work spreads over
+// every compute unit, when the round time saved (a round of whole tiles
+// estimated at ~1 PFLOP/s) outweighs the partial tiles' extra HBM traffic
+// (written once and read once, at ~5 TB/s).  Returns the split count (1: no
+// split); the whole rounds' tiles run unsplit.
+int64_t pick_tail_splits(int64_t tail, int64_t GQ, int64_t K, int RBW) {
+  const double round_s = 64.0 * 64 * RBW * (double)K * 2 * 256 / 1.0e15;
+  const double part_tile = 64.0 * 64 * RBW * 4;
+  int64_t best = 1;
+  double best_gain = 0.0;
+  for (int64_t ks = 2; ks <= 8 && ks <= GQ; ks *= 2) {
+    if ((tail * ks) % 8 != 0) continue;
+    const double saved = (1.0 - (double)cdiv(tail * ks, (int64_t)256) / (double)ks) * round_s;
+    // (with half again as much for the last arrival's reduction latency)
+    const double cost = 1.5 * 2.0 * (double)tail * ks * part_tile / 5.0e12;
+    if (saved - cost > best_gain) {
+      best = ks;
+      best_gain = saved - cost;
+    }
+  }
+  return best;
+}
+
 GemmPlan make_gemm_plan(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
   p.G = K / kGroup;
@@ -1072,7 +1125,14 @@ GemmPlan make_gemm_plan(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
   p.RBW = N >= 2048 && fmt != 3 ? 8 : 4;
   p.NT = cdiv(N, 64 * p.RBW);
   const int64_t tiles = p.MT * p.NT;
-  p.KS = tiles > kMaxRowGroups ? 1 : pick_splits(tiles, cdiv(p.G, 4));
+  if (tiles < 256) {  // less than one round: every tile split alike
+    p.F = 0;
+    p.KS = pick_splits(tiles, cdiv(p.G, 4));
+  } else {
+    const int64_t tail = tiles % 256;
+    p.KS = tail == 0 ? 1 : pick_tail_splits(tail, cdiv(p.G, 4), K, p.RBW);
+    p.F = p.KS > 1 ? tiles - tail : tiles;
+  }
   // packed weight bytes (codes and scales) against staged activation bytes
   const double wbytes = (double)N * K * (fmt == 1 ? 1.0 : fmt == 2 ? 2.0 : 1.625) / 8 + (double)N * p.G * 2;
   const double xbytes = (double)p.MT * p.G * (xkind == XK_SIGN1 ? kS1Img : kF8Img);
@@ -1081,7 +1141,7 @@ GemmPlan make_gemm_plan(int fmt, int xkind, int64_t M, int64_t N, int64_t K) {
   p.xt_off = p.rs_off;
   p.part_off = p.xt_off + align256((size_t)p.MT * p.G * (xkind == XK_SIGN1 ? kS1Img : kF8Img));
   const size_t part_tile = (size_t)kF8BM * 64 * p.RBW * 4;
-  p.bytes = p.part_off + (p.KS > 1 ? (size_t)p.KS * tiles * part_tile : 0);
+  p.bytes = p.part_off + (p.KS > 1 ? (size_t)p.KS * (tiles - p.F) * part_tile : 0);
   return p;
 }
 
@@ -1107,11 +1167,12 @@ hipError_t launch_fmt(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   k.MT = p.MT;
   k.NT = p.NT;
   k.KS = (int)p.KS;
+  k.F = p.F;
   k.row_fast = p.row_fast;
   const int64_t Mpad = p.MT * kF8BM;
   const int64_t units = Mpad * p.G * 4;
   const dim3 sgrid((unsigned)cdiv(units, 256));
-  const dim3 grid((unsigned)(p.MT * p.NT * p.KS)), block(kF8Threads);
+  const dim3 grid((unsigned)(p.F + (p.MT * p.NT - p.F) * p.KS)), block(kF8Threads);
   if (g.xkind == XK_BF16) {
     hipLaunchKernelGGL((stage_f8<XK_BF16, FMT != 1>), sgrid, dim3(256), 0, s, g.M, Mpad, g.K, p.G, g.x,
                        (uint8_t*)k.xt);
@@ -1163,7 +1224,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.xkind != XK_BF16 && (g.ykind == YK_I32) != (g.pscales == nullptr)) return hipErrorInvalidValue;
   if (g.xkind != XK_BF16 && g.ykind != YK_I32 && g.x_scales == nullptr) return hipErrorInvalidValue;
   const GemmPlan p = make_gemm_plan(g.fmt, g.xkind, g.M, g.N, g.K);
-  if (p.MT * p.NT * p.KS > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (p.F + (p.MT * p.NT - p.F) * p.KS > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (g.fmt == 1) return launch_rbw<1>(g, p, s);
   if (g.fmt == 2) return launch_rbw<2>(g, p, s);
   if (g.fmt == 3) return launch_rbw<3>(g, p, s);
