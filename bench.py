@@ -727,9 +727,12 @@ def summarize_stats(d, out, cmd):
     average / min / max duration."""
     rows = _csv_rows(d, "kernel_stats.csv")
     names = _demangle([_col(r, "Name", "Kernel_Name") for r in rows])
-    lines = ["# rocprofv3 kernel statistics (--kernel-trace --stats)", f"# command: {cmd}",
+    lines = ["# rocprofv3 kernel statistics (--kernel-trace --stats) of the library's kernels "
+             "(torch's input-generation kernels omitted)", f"# command: {cmd}",
              "# kernel | calls | total ms | average us | min us | max us"]
     for n, r in sorted(zip(names, rows), key=lambda t: -float(_col(t[1], "TotalDurationNs"))):
+        if n.startswith(("at::", "(anonymous namespace)::", "__amd_rocclr")):
+            continue
         lines.append(f"{n[:150]} | {_col(r, 'Calls')} | {float(_col(r, 'TotalDurationNs')) / 1e6:.3f} | "
                      f"{float(_col(r, 'AverageNs')) / 1e3:.3f} | {float(_col(r, 'MinNs')) / 1e3:.3f} | "
                      f"{float(_col(r, 'MaxNs')) / 1e3:.3f}")
