@@ -869,6 +869,11 @@ def summarize_valu(d, out, cmd, fmt, layers):
             lines.append(f"{k}_per_1k_weights = {1000 * c[k] / weights:.4f}")
     if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
         lines.append(f"wait_inst_any_frac_of_wave_cycles = {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.4f}")
+    if "GRBM_GUI_ACTIVE" in c:
+        ns = sum(e["ns"] for e in ds) / len(ds)
+        lines.append(f"dispatch_us = {ns / 1e3:.1f}")
+        # GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles
+        lines.append(f"sustained_clock_ghz = {c['GRBM_GUI_ACTIVE'] / 8 / ns:.3f}")
     _write(out, lines)
 
 
