@@ -34,11 +34,12 @@ constexpr int kMaxWaves = 16;  // waves per workgroup of the sign kernel
 constexpr uint32_t kChainSpinLimit = 1u << 24;  // sleeps before a chain wait gives up
 constexpr int kMaxW = 4;       // waves (row-blocks) per MFMA workgroup, at most
 constexpr int kQuadsMulti = 4;      // quads per slice of the several-row streaming kernel
+constexpr int kQuadsMultiMid = 5;   // (the same with at most 15 rows of A, not base-3)
 constexpr int kQuadsMultiWide = 6;  // (the same with at most 10 rows of A)
 // rows of A the image buffers of a several-row streaming kernel with QM-quad
-// slices hold (a slice image travels in at most nine 16-byte registers per
-// thread)
-constexpr int multi_max_ma(int qm) { return qm == kQuadsMultiWide ? 10 : 16; }
+// slices hold (a slice image travels in at most ten 16-byte registers per
+// thread; two workgroups' buffers fit a CU)
+constexpr int multi_max_ma(int qm) { return qm == kQuadsMultiWide ? 10 : qm == kQuadsMultiMid ? 15 : 16; }
 // dynamic LDS of the one-product kernel and the waiting chain: two
 // workgroups per CU fit in the 160 KiB of a gfx950 CU
 constexpr size_t kLdsCap = 80 * 1024;
@@ -1507,7 +1508,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
   // only ever held back by a wave more than about one slice behind (there is
   // no workgroup barrier in the loop).
   // rows of A an image may hold: several-row chains use 6-quad slices up to
-  // 10 rows of A and 4-quad slices up to 16
+  // 10 rows of A, 5-quad slices up to 15 and 4-quad slices up to 16
   constexpr int MAX_MA = MR ? multi_max_ma(QM) : R;
   // (an image is followed by its 16-byte flag word)
   constexpr int XR = (QM * 16 * MAX_MA * 33 + 16 + 16 * 64 * kMaxW - 1) / (16 * 64 * kMaxW);
@@ -1549,8 +1550,8 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     };
     // a slice image travels in up to nine 16-byte registers per thread (named
     // registers, not an array, so that they never live in scratch memory)
-    uint4 x0, x1, x2, x3, x4, x5, x6, x7, x8;
-    static_assert(XR <= 9, "slice image larger than nine 16-byte pieces per thread");
+    uint4 x0, x1, x2, x3, x4, x5, x6, x7, x8, x9;
+    static_assert(XR <= 10, "slice image larger than ten 16-byte pieces per thread");
 #define XLD(F, SI, KS_, NQ)                                                                  \
   {                                                                                          \
     x0 = *xsrc(F, SI, KS_, NQ, 0);                                                           \
@@ -1562,6 +1563,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     if (XR > 6) x6 = *xsrc(F, SI, KS_, NQ, 6);                                               \
     if (XR > 7) x7 = *xsrc(F, SI, KS_, NQ, 7);                                               \
     if (XR > 8) x8 = *xsrc(F, SI, KS_, NQ, 8);                                               \
+    if (XR > 9) x9 = *xsrc(F, SI, KS_, NQ, 9);                                               \
   }
 #define XPUT(DST, NQ)                                                                        \
   {                                                                                          \
@@ -1577,6 +1579,7 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(FMT 
     if (XR > 6 && 6 * T_ + tid < nb_) d_[6 * T_ + tid] = x6;                                 \
     if (XR > 7 && 7 * T_ + tid < nb_) d_[7 * T_ + tid] = x7;                                 \
     if (XR > 8 && 8 * T_ + tid < nb_) d_[8 * T_ + tid] = x8;                                 \
+    if (XR > 9 && 9 * T_ + tid < nb_) d_[9 * T_ + tid] = x9;                                 \
   }
     XLD(a, s, ks, it.nq);
     XPUT(xbuf(0), it.nq);
@@ -2018,6 +2021,11 @@ const void* chain_kernel(int ykind, bool waits, int64_t M, int rb) {
   if (M * R <= multi_max_ma(kQuadsMultiWide))
     return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMultiWide, true, 1>
                : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMultiWide, true, 1>;
+  // (base-3 slices are whole octets: an odd quad count would re-read a quad)
+  if constexpr (FMT != 3)
+    if (M * R <= multi_max_ma(kQuadsMultiMid))
+      return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMultiMid, true, 1>
+                 : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMultiMid, true, 1>;
   return b16 ? (const void*)gemv_stream<FMT, XK, YK_BF16, kQuadsMulti, true, 1>
              : (const void*)gemv_stream<FMT, XK, YK_F32, kQuadsMulti, true, 1>;
 }
@@ -2044,6 +2052,7 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
   const int quads = waits ? 0
                   : M == 1 ? kQuadsTernary
                   : M * R <= multi_max_ma(kQuadsMultiWide) ? kQuadsMultiWide
+                  : fmt != 3 && M * R <= multi_max_ma(kQuadsMultiMid) ? kQuadsMultiMid
                   : kQuadsMulti;
   // binary, one bf16 row, no waits: three row-blocks per wave (buffer
   // addressing: every stage's codes shorter than 2^31 bytes), else two
