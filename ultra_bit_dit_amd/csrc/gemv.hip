@@ -2153,7 +2153,13 @@ hipError_t chain_create(const ChainStage* st, int S, int64_t M, int xkind, int y
     delete c;
     return e;
   }
-  const int64_t want = (int64_t)per_cu * cus;
+  // The streaming 2-bit chain runs two workgroups per CU although three fit:
+  // fewer concurrent weight streams read HBM more efficiently (a plain
+  // read of the same row-group pattern: 7.0 TB/s at two workgroups of four
+  // waves per CU, 6.6 at three), and its per-wave work hides the rest.
+  // Base-3 keeps every resident workgroup (its table decode needs them).
+  const int64_t per = !waits && fmt == 2 ? std::min(per_cu, 2) : per_cu;
+  const int64_t want = per * cus;
   c->grid = dim3((unsigned)std::min<int64_t>(want, first[S]));
   c->block = dim3(64 * kMaxW);
   c->lds = lds;
