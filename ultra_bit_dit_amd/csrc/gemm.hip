@@ -436,59 +436,50 @@ __device__ __forceinline__ v4f mfma_f8f4(const v8i& A, const v8i& B, int se, con
 // LDS buffers apart and would wait for every copy); each block waits for its
 // own results.
 //
-// A operands of four consecutive A-tiles (kATBytes apart): this lane's two
-// 16-byte halves at LDS byte addresses pa and pa + 1024, and their exponents
-// at pe.
-__device__ __forceinline__ void lds_read_a(uint32_t pa, uint32_t pe, v4u (&A0)[4], v4u (&A1)[4],
-                                           uint32_t (&se)[4]) {
-  __asm__ volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %4, %12 offset:1024\n\t"
-      "ds_read_u8 %8, %13\n\t"
-      "ds_read_b128 %1, %12 offset:2112\n\t"
-      "ds_read_b128 %5, %12 offset:3136\n\t"
-      "ds_read_u8 %9, %13 offset:2112\n\t"
-      "ds_read_b128 %2, %12 offset:4224\n\t"
-      "ds_read_b128 %6, %12 offset:5248\n\t"
-      "ds_read_u8 %10, %13 offset:4224\n\t"
-      "ds_read_b128 %3, %12 offset:6336\n\t"
-      "ds_read_b128 %7, %12 offset:7360\n\t"
-      "ds_read_u8 %11, %13 offset:6336\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A0[2]), "=&v"(A0[3]), "=&v"(A1[0]), "=&v"(A1[1]),
-        "=&v"(A1[2]), "=&v"(A1[3]), "=&v"(se[0]), "=&v"(se[1]), "=&v"(se[2]), "=&v"(se[3])
-      : "v"(pa), "v"(pe)
-      : "memory");
+// A operands of two consecutive A-tiles (kATBytes apart: one row tile,
+// both terms): this lane's two 16-byte halves at LDS byte addresses pa and
+// pa + 1024, and their exponents at pe; when CNT also the entry counts of the
+// wave's two correction regions (at ph and ph + kRegionBytes).  The main
+// loop reads the second row tile's A-tiles while the first one's MFMAs run.
+template <bool CNT>
+__device__ __forceinline__ void lds_read_a2(uint32_t pa, uint32_t pe, uint32_t ph, v4u (&A0)[2],
+                                            v4u (&A1)[2], uint32_t (&se)[2], uint32_t (&cnt)[2]) {
+  if constexpr (CNT) {
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %2, %8 offset:1024\n\t"
+        "ds_read_u8 %4, %9\n\t"
+        "ds_read_b128 %1, %8 offset:2112\n\t"
+        "ds_read_b128 %3, %8 offset:3136\n\t"
+        "ds_read_u8 %5, %9 offset:2112\n\t"
+        "ds_read_b32 %6, %10\n\t"
+        "ds_read_b32 %7, %10 offset:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A1[0]), "=&v"(A1[1]), "=&v"(se[0]), "=&v"(se[1]),
+          "=&v"(cnt[0]), "=&v"(cnt[1])
+        : "v"(pa), "v"(pe), "v"(ph)
+        : "memory");
+  } else {
+    // (issued while MFMAs that read these registers as their accumulator
+    // input may still be in flight: wait states first, so that no returning
+    // load overwrites an operand an MFMA pass has yet to read)
+    __asm__ volatile(
+        "s_nop 7\n\t"
+        "s_nop 7\n\t"
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %2, %6 offset:1024\n\t"
+        "ds_read_u8 %4, %7\n\t"
+        "ds_read_b128 %1, %6 offset:2112\n\t"
+        "ds_read_b128 %3, %6 offset:3136\n\t"
+        "ds_read_u8 %5, %7 offset:2112\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A1[0]), "=&v"(A1[1]), "=&v"(se[0]), "=&v"(se[1])
+        : "v"(pa), "v"(pe)
+        : "memory");
+  }
 }
-static_assert(kATBytes == 2112, "A-tile offsets in the LDS reads");
 
-// lds_read_a plus the entry counts of the wave's two correction regions (at
-// ph and ph + kRegionBytes), with the same wait
-__device__ __forceinline__ void lds_read_a_cnt(uint32_t pa, uint32_t pe, uint32_t ph, v4u (&A0)[4],
-                                               v4u (&A1)[4], uint32_t (&se)[4], uint32_t (&cnt)[2]) {
-  __asm__ volatile(
-      "ds_read_b128 %0, %14\n\t"
-      "ds_read_b128 %4, %14 offset:1024\n\t"
-      "ds_read_u8 %8, %15\n\t"
-      "ds_read_b128 %1, %14 offset:2112\n\t"
-      "ds_read_b128 %5, %14 offset:3136\n\t"
-      "ds_read_u8 %9, %15 offset:2112\n\t"
-      "ds_read_b128 %2, %14 offset:4224\n\t"
-      "ds_read_b128 %6, %14 offset:5248\n\t"
-      "ds_read_u8 %10, %15 offset:4224\n\t"
-      "ds_read_b128 %3, %14 offset:6336\n\t"
-      "ds_read_b128 %7, %14 offset:7360\n\t"
-      "ds_read_u8 %11, %15 offset:6336\n\t"
-      "ds_read_b32 %12, %16\n\t"
-      "ds_read_b32 %13, %16 offset:128\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(A0[0]), "=&v"(A0[1]), "=&v"(A0[2]), "=&v"(A0[3]), "=&v"(A1[0]), "=&v"(A1[1]),
-        "=&v"(A1[2]), "=&v"(A1[3]), "=&v"(se[0]), "=&v"(se[1]), "=&v"(se[2]), "=&v"(se[3]),
-        "=&v"(cnt[0]), "=&v"(cnt[1])
-      : "v"(pa), "v"(pe), "v"(ph)
-      : "memory");
-}
-static_assert(kRegionBytes == 128, "region offset in the count read");
+static_assert(kATBytes == 2112 && kRegionBytes == 128, "LDS offsets of the A-tile reads");
 
 // one 8-byte correction entry from LDS, waited for
 __device__ __forceinline__ uint2 lds_read_entry(uint32_t addr) {
@@ -832,10 +823,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
     __asm__ volatile("" ::: "memory");
   };
   // ---- LDS reads (written out, see lds_read_a / lds_read_codes)
-  auto aread = [&](int t, v4u (&A0)[4], v4u (&A1)[4], uint32_t (&se)[4]) {
-    const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
-    lds_read_a(base + 16 * lane, base + 2048 + lane, A0, A1, se);
-  };
+
   // codes and scales of row-blocks RBW wn + j .. + 3 of the quad in the code buffer
   static_assert(RBW % 4 == 0, "code reads go four row-blocks at a time");
   static_assert(CL::kSlot == (FMT == 1 ? 1024 : FMT == 2 ? 2048 : 2304), "slot offsets of the code reads");
@@ -871,6 +859,12 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 
   Quad<FMT> qd[RBW];
   bool overflow = false;  // (LIST) one of the wave's correction lists overflowed
+  // binary decode masks in registers (VOP3 takes no literal): v_and_or_b32
+  uint32_t sign_mask = 0x88888888u, one_bits = 0x22222222u;
+  if constexpr (FMT == 1) {
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(sign_mask));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(one_bits));
+  }
   for (int q = q0; q < q1; q++) {
 #pragma unroll
     for (int t = 0; t < 4; t++) {
@@ -895,18 +889,19 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
         if constexpr (S1) {
           lds_read_s1((uint32_t)(uintptr_t)(ring(t) + 2 * wm * 1024) + 16 * lane, As);
         } else {
-          v4u A0[4], A1[4];
-          if constexpr (LIST) {
-            const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
-            const uint32_t ph = (uint32_t)(uintptr_t)(ring(t) + kF8Tiles + 2 * wm * kRegionBytes);
-            lds_read_a_cnt(base + 16 * lane, base + 2048 + lane, ph, A0, A1, se, ncorr);
-          } else {
-            aread(t, A0, A1, se);
-          }
+          // the first row tile's two A-tiles (and the correction counts of
+          // both regions) now, the second row tile's during the first one's MFMAs
+          v4u A0[2], A1[2];
+          uint32_t se2[2];
+          const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + 4 * wm * kATBytes);
+          const uint32_t ph = (uint32_t)(uintptr_t)(ring(t) + kF8Tiles + 2 * wm * kRegionBytes);
+          lds_read_a2<LIST>(base + 16 * lane, base + 2048 + lane, ph, A0, A1, se2, ncorr);
 #pragma unroll
-          for (int i = 0; i < 4; i++)
+          for (int i = 0; i < 2; i++) {
             At[i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
                         (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+            se[i] = se2[i];
+          }
         }
         if constexpr (LIST) {
           // the elements the two terms miss: acc[row][col] += s code rho
@@ -979,8 +974,15 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
           float sj[4];
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            B[j] = decode_group<FMT>(qd[h + j], t, t3);
-            sj[j] = a.pscales ? quad_scale<FMT>(qd[h + j], t) : 1.0f;
+            if constexpr (FMT == 1) {
+              const u4 c4 = qd[h + j].w[0];
+              B[j] = decode_binary_reg(t == 0 ? c4.x : t == 1 ? c4.y : t == 2 ? c4.z : c4.w, sign_mask,
+                                       one_bits);
+            } else {
+              B[j] = decode_group<FMT>(qd[h + j], t, t3);
+            }
+            // (the exact int32 product is the only one without scales)
+            sj[j] = INT ? 1.0f : quad_scale<FMT>(qd[h + j], t);
           }
 #pragma unroll
           for (int rt = 0; rt < 2; rt++) {
@@ -994,6 +996,20 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2)))
                 c[j] = mfma_f8f4(At[2 * rt], B[j], (int)se[2 * rt], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
               for (int j = 0; j < 4; j++) c[j] = mfma_f8f4(At[2 * rt + 1], B[j], (int)se[2 * rt + 1], c[j]);
+              if (h == 0 && rt == 0) {
+                // the second row tile's A-tiles, while these MFMAs run (before
+                // their results are read)
+                v4u A0[2], A1[2];
+                uint32_t se2[2], nc2[2];
+                const uint32_t base = (uint32_t)(uintptr_t)(ring(t) + (4 * wm + 2) * kATBytes);
+                lds_read_a2<false>(base + 16 * lane, base + 2048 + lane, 0u, A0, A1, se2, nc2);
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                  At[2 + i] = v8i{(int)A0[i].x, (int)A0[i].y, (int)A0[i].z, (int)A0[i].w,
+                                  (int)A1[i].x, (int)A1[i].y, (int)A1[i].z, (int)A1[i].w};
+                  se[2 + i] = se2[i];
+                }
+              }
             }
 #pragma unroll
             for (int j = 0; j < 4; j++) {

@@ -761,18 +761,6 @@ __device__ __attribute__((always_inline)) inline float exact_slice(const FArgs& 
   return acc;
 }
 
-// fp4 operand B of binary group t with the two masks held in registers
-// (a VOP3 instruction takes no literal here): one v_and_or_b32 for slot
-// register 0 and a shift plus v_and_or_b32 for each of the other three.
-__device__ __attribute__((always_inline)) inline v8i decode_binary_reg(uint32_t wv, uint32_t sign_mask,
-                                                                       uint32_t one_bits) {
-  const uint32_t d0 = (wv & sign_mask) | one_bits;
-  const uint32_t d1 = ((wv << 1) & sign_mask) | one_bits;
-  const uint32_t d2 = ((wv << 2) & sign_mask) | one_bits;
-  const uint32_t d3 = ((wv << 3) & sign_mask) | one_bits;
-  return v8i{(int)d0, (int)d1, (int)d2, (int)d3, 0, 0, 0, 0};
-}
-
 // quad_mfma for one activation row (M = 1, MA = R rows of A) with scales:
 // `arow` points at this lane's A row of group 0 of the slice image (lanes
 // with r >= R read row r mod R: their output rows are never used, and
