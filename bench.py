@@ -739,9 +739,12 @@ def summarize_stats(d, out, cmd):
     _write(out, lines)
 
 
-def summarize_hbm(dfetch, dwrite, out, cmd, fmt, layers):
+def summarize_hbm(dfetch, dwrite, out, cmds, fmt, layers):
     """FETCH_SIZE / WRITE_SIZE per dispatch of the streaming decode kernel and
-    of the copy it is scaled by, in the key = value form pmc_traffic reads."""
+    of the copy it is scaled by, in the key = value form pmc_traffic reads.
+    cmds: the two rocprofv3 commands, or one with @PMC@ for the counter."""
+    fcmd = cmds[0].replace("@PMC@", "FETCH_SIZE")
+    wcmd = cmds[1] if len(cmds) > 1 else cmds[0].replace("@PMC@", "WRITE_SIZE")
     from ultra_bit_dit_amd import lowbit as lb
     name = f"gemv_stream<{fmt},"
 
@@ -757,8 +760,8 @@ def summarize_hbm(dfetch, dwrite, out, cmd, fmt, layers):
     gw, cw, nw = pick(dwrite, "WRITE_SIZE")
     lines = [
         "# rocprofv3 HBM byte counters of the decode GEMV kernel (gemv_stream)",
-        f"# FETCH_SIZE command: {cmd.replace('@PMC@', 'FETCH_SIZE')}",
-        f"# WRITE_SIZE command: {cmd.replace('@PMC@', 'WRITE_SIZE')}",
+        f"# FETCH_SIZE command: {fcmd}",
+        f"# WRITE_SIZE command: {wcmd}",
         "# copy reference: torch.neg over 64 Mi fp32 (256 MiB read, 256 MiB written)",
         f"# gemv dispatches counted: {nf} (FETCH), {nw} (WRITE); per-dispatch KiB averaged",
         "kernel = gemv_stream",
@@ -920,7 +923,7 @@ def main():
         if args.summarize == "stats":
             summarize_stats(args.prof_dir[0], args.out, args.cmd[0])
         elif args.summarize == "hbm":
-            summarize_hbm(args.prof_dir[0], args.prof_dir[1], args.out, args.cmd[0], args.fmt,
+            summarize_hbm(args.prof_dir[0], args.prof_dir[1], args.out, args.cmd, args.fmt,
                           args.layers)
         elif args.summarize == "mfma":
             summarize_mfma(args.prof_dir[0], args.prof_dir[1], args.out, args.cmd[0], args.cmd[1],
