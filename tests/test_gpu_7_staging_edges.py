@@ -288,3 +288,49 @@ def test_gemm_split_k_lists(fmt):
     torch.cuda.synchronize()
     yref, absY = O.matmul(codes, scales, O.X_BF16, X)
     assert_within(Y.cpu().numpy(), yref, absY, what="split-K lists")
+
+
+def few_far_below(seed, tid, K, every=256, span=40):
+    """One bf16 row: N(0,1) values with one element per `every` scaled down
+    by 2^span, far beyond the range the split terms carry beside its block's
+    maximum (a few correction-list entries per slice, no overflow)."""
+    x = synth.normal_f32(seed, tid, 1, K).astype(np.float64)
+    rng = np.random.default_rng(tid)
+    cols = np.array([every * j + int(rng.integers(0, every)) for j in range(K // every)])
+    x[0, cols] *= 2.0 ** -span
+    return bf16_bits(x), cols
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_waiting_chain_correction_lists(fmt):
+    """Waiting chain, one row: the weights see only the elements far below
+    their blocks' maxima (codes zero elsewhere), so sum |w x| counts only
+    them and the result is what the correction lists add.  The second stage
+    has more row groups than the grid has workgroups, so some workgroups
+    run a second item on the same staged slice and its list."""
+    print(f"waiting chain correction lists fmt={fmt}", flush=True)
+    shapes = [(256, 2048), (33792, 1024), (512, 5120)]
+    stages, refs, ys = [], [], []
+    for j, (N, K) in enumerate(shapes):
+        X, cols = few_far_below(SEED, 601 + j, K)
+        full = codes_for(fmt, SEED, 611 + j, N, K)
+        codes = np.zeros_like(full)
+        codes[:, cols] = np.where(full[:, cols] == 0, 1, full[:, cols])
+        scales = synth.group_scales(SEED, 621 + j, N, K // 128)
+        pc, ps = pack(fmt, codes, scales)
+        y = torch.full((N,), float("nan"), device="cuda")
+        ys.append(y)
+        stages.append((fmt, N, K, pc, ps, bf16_dev(X)[0], y, 1 if j else 0))
+        refs.append(O.matmul(codes, scales, O.X_BF16, X))
+    chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        for j in range(len(shapes)):
+            yref, absY = refs[j]
+            assert np.all(absY > 0)
+            assert_within(ys[j].cpu().numpy()[None], yref, absY, what=f"stage {j} rep {rep}")
+    assert chain.failed_waits() == 0
+    chain.close()

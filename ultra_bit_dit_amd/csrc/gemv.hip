@@ -70,6 +70,17 @@ struct XSplit {
 };
 constexpr float kStageEps = 1.0f / 4096.0f;  // 2^-12: staging error allowed per element
 
+// Correction lists of the one-row kernels (ternary weights, bf16
+// activations): the split terms carry every element within 2^27 of its
+// block's maximum exactly; an element further below is listed with its
+// exact residual rho = x - (what the terms carry), and the item adds
+// scale x code x rho for it after its MFMAs.  Per wave a count word and up
+// to kListEntries entries {slot position, rho}; a wave whose list
+// overflows flags the slice for the exact recomputation.
+constexpr int kListEntries = 15;
+constexpr int kListWaveWords = 2 + 2 * kListEntries;  // 32
+constexpr int kListBytes = 4 * kListWaveWords * kMaxW;  // 512
+
 // two floats -> two fp8 / bf8 bytes (round to nearest even) in half HI of old
 template <int FA, bool HI>
 __device__ __attribute__((always_inline)) inline uint32_t cvt_pk8(float a, float b, uint32_t old) {
@@ -219,12 +230,15 @@ __device__ __attribute__((always_inline)) inline void stage_load1(const FArgs& a
 
 // Convert one round of units into split terms and exponents in LDS (or a
 // global image).  Returns true when one of the unit's elements misses the
-// accuracy XSplit::kCheck asks for (never for units past the end).
-template <int FMT, int XK>
+// accuracy XSplit::kCheck asks for (never for units past the end).  LIST
+// (one-row items, kCheck 1): such elements go to the wave's correction list
+// wlist instead, and only a full list returns true.
+template <int FMT, int XK, bool LIST = false>
 __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs& a, int64_t q0,
                                                                      int64_t nq, int64_t rd,
                                                                      uint4 ra, uint4 rb,
-                                                                     uint8_t* xa, uint8_t* xe) {
+                                                                     uint8_t* xa, uint8_t* xe,
+                                                                     uint32_t* wlist = nullptr) {
   using S = XSplit<FMT, XK>;
   constexpr int R = S::R, FA = S::kFmtA;
   if (rd * blockDim.x >= nq * 64 * a.M) return false;  // uniform: round past the end
@@ -275,6 +289,7 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   float tv[8], t0[8];
   uint32_t lost = 0;  // kCheck 3: elements whose scaling by 2^-E underflowed to zero
   bool small = false;  // kCheck 1: a nonzero element below kMinExact
+  uint32_t smallbits = 0;  // (LIST) which ones
   float amax_s = 0.f;
   if constexpr (XK == XK_I8) {
 #pragma unroll
@@ -285,12 +300,19 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       tv[j] = v[j] * sc;
-      if (S::kCheck == 1) small = small || (v[j] != 0.0f && fabsf(tv[j]) < S::kMinExact);
+      if constexpr (S::kCheck == 1 && LIST) {
+        const bool sj = v[j] != 0.0f && fabsf(tv[j]) < S::kMinExact;
+        small = small || sj;
+        smallbits |= (sj ? 1u : 0u) << j;
+      } else if constexpr (S::kCheck == 1) {
+        small = small || (v[j] != 0.0f && fabsf(tv[j]) < S::kMinExact);
+      }
       if (S::kCheck == 3) lost |= (tv[j] == 0.0f && v[j] != 0.0f) ? 1u : 0u;
       if (S::kCheck == 3) t0[j] = tv[j];
     }
     amax_s = amax * sc;
   }
+  uint32_t wr[LIST ? R : 1][2];  // (LIST) the terms' bytes
 #pragma unroll
   for (int r = 0; r < R; r++) {
     uint32_t w0, w1;
@@ -323,6 +345,10 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
         for (int j = 0; j < 8; j++) tv[j] = r + 1 < R ? (tv[j] - d[j]) * (float)(1 << S::kShift) : tv[j] - d[j];
       }
     }
+    if constexpr (LIST) {
+      wr[r][0] = w0;
+      wr[r][1] = w1;
+    }
     const int64_t arow = m * R + r;
     *(uint2*)(xa + ((ql * 16 + t * 4 + kb) * a.MA + arow) * 32 + e) = make_uint2(w0, w1);
     if (ch == 0) xe[((ql * 4 + b) * a.MA + arow) * 4 + t] = (uint8_t)(127 + Er);
@@ -331,7 +357,38 @@ __device__ __attribute__((always_inline)) inline bool stage_convert1(const FArgs
   // below v's scale: exact comparisons with powers of two
   constexpr float kEpsR = kStageEps * (float)(1 << (S::kShift * (R - 1)));
   bool bad = false;
-  if constexpr (S::kCheck == 1) {
+  if constexpr (S::kCheck == 1 && LIST) {
+    if (small) {  // rare: list the elements the terms may not carry exactly
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if ((smallbits >> j) & 1u) {
+          // what the terms carry, term by term (each term times its power
+          // of two is exact, and for such an element so are the sums)
+          float carried = 0.f;
+#pragma unroll
+          for (int r = 0; r < R; r++) {
+            const uint32_t w = wr[r][j >> 2];
+            const float d = (j & 3) == 0 ? __builtin_amdgcn_cvt_f32_bf8(w, 0)
+                          : (j & 3) == 1 ? __builtin_amdgcn_cvt_f32_bf8(w, 1)
+                          : (j & 3) == 2 ? __builtin_amdgcn_cvt_f32_bf8(w, 2)
+                                         : __builtin_amdgcn_cvt_f32_bf8(w, 3);
+            carried += d * ldexpf(1.0f, E - S::kShift * r);
+          }
+          const float rho = v[j] - carried;
+          if (rho != 0.0f) {
+            const uint32_t idx = atomicAdd(wlist, 1u);
+            if (idx < (uint32_t)kListEntries) {
+              const uint32_t pos = (uint32_t)(8 * ch + j) | ((uint32_t)b << 5) | ((uint32_t)t << 7) |
+                                   ((uint32_t)ql << 9);
+              *(uint2*)(wlist + 2 + 2 * idx) = make_uint2(pos, __float_as_uint(rho));
+            } else {
+              bad = true;
+            }
+          }
+        }
+      }
+    }
+  } else if constexpr (S::kCheck == 1) {
     bad = small;
   } else if constexpr (S::kCheck == 3) {
     bad = lost != 0;
@@ -557,6 +614,7 @@ __device__ __attribute__((always_inline)) inline void load_quad_b3(const QuadBuf
 struct Lds {
   uint8_t* xa;
   uint8_t* xe;
+  uint32_t* list;  // one-row ternary staging: the waves' correction lists
   uint8_t* zblk;   // 32 zero bytes, a word of unit exponents, then wflag
   uint32_t* wflag;  // [kMaxW]: the wave's last staging found an inaccurate element
   uint32_t* t3;
@@ -577,7 +635,8 @@ __device__ __attribute__((always_inline)) inline Lds lds_of(const FArgs& a, uint
   Lds l;
   l.xa = smem;
   l.xe = smem + (int64_t)nq * 16 * a.MA * 32;
-  l.zblk = l.xe + (int64_t)nq * 16 * a.MA + extra;
+  l.list = (uint32_t*)(l.xe + (int64_t)nq * 16 * a.MA + extra);
+  l.zblk = (uint8_t*)l.list + kListBytes;
   l.wflag = (uint32_t*)(l.zblk + 48);
   l.t3 = (uint32_t*)(l.zblk + kZeroBlock);
   return l;
@@ -1074,21 +1133,24 @@ __device__ __attribute__((always_inline)) inline void stage_load_rounds(const FA
   if constexpr (K + 1 < NR) stage_load_rounds<XK, COH, NR, K + 1>(a, it, x);
 }
 
-template <int FMT, int XK, int NR, int K = 0>
+template <int FMT, int XK, int NR, bool LIST, int K = 0>
 __device__ __attribute__((always_inline)) inline bool stage_convert_rounds(const FArgs& a,
                                                                            const Item& it,
-                                                                           const Lds& l, XRegs& x) {
-  bool bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe);
-  if constexpr (K + 1 < NR) bad = stage_convert_rounds<FMT, XK, NR, K + 1>(a, it, l, x) || bad;
+                                                                           const Lds& l, XRegs& x,
+                                                                           uint32_t* wlist) {
+  bool bad = stage_convert1<FMT, XK, LIST>(a, it.q0, it.nq, K, xa_reg<K>(x), xb_reg<K>(x), l.xa, l.xe,
+                                           wlist);
+  if constexpr (K + 1 < NR) bad = stage_convert_rounds<FMT, XK, NR, LIST, K + 1>(a, it, l, x, wlist) || bad;
   return bad;
 }
 
 // every staging round of an item (the first NR hoisted); true if this thread
-// saw an inaccurate element
-template <int FMT, int XK, int SB, int NR>
+// saw an inaccurate element (LIST: that its wave's correction list is full)
+template <int FMT, int XK, int SB, int NR, bool LIST = false>
 __device__ __attribute__((always_inline)) inline bool stage_all(const FArgs& a, const Item& it,
                                                                 const Lds& l, XRegs& x, bool coh) {
-  bool bad = stage_convert_rounds<FMT, XK, NR>(a, it, l, x);
+  uint32_t* wlist = LIST ? l.list + kListWaveWords * (threadIdx.x >> 6) : nullptr;
+  bool bad = stage_convert_rounds<FMT, XK, NR, LIST>(a, it, l, x, wlist);
   // remaining rounds (small-M products with long slices): SB rounds' loads
   // go out together, then their conversions
   const int64_t rounds = cdiv(it.nq * 64 * a.M, (int64_t)blockDim.x);
@@ -1104,7 +1166,7 @@ __device__ __attribute__((always_inline)) inline bool stage_all(const FArgs& a, 
 #pragma unroll
     for (int u = 0; u < SB; u++)
       if (rd + u < rounds)
-        bad = stage_convert1<FMT, XK>(a, it.q0, it.nq, rd + u, r0[u], r1[u], l.xa, l.xe) || bad;
+        bad = stage_convert1<FMT, XK, LIST>(a, it.q0, it.nq, rd + u, r0[u], r1[u], l.xa, l.xe, wlist) || bad;
   }
   return bad;
 }
@@ -1143,6 +1205,42 @@ __device__ __attribute__((always_inline)) inline void copy_image(const FArgs& a,
 // stage false: the workgroup's previous item was the same product and
 // K-slice, so the activation image (and its staging flags) in LDS is this
 // item's already.  MM: activation rows the kernel handles at most.
+// The correction-list entries of quad q (one-row items): entry {slot i of
+// quarter b of group t of quad ql, rho} adds scale x code x rho to the
+// outputs; lane r + 16 b holds row r's code and scale, the output of row r
+// is in lane r.
+template <int FMT, int TS>
+__device__ __attribute__((always_inline)) inline void list_quad(const Lds& l, int q, const Quad<FMT>& qd, float& acc) {
+  const uint32_t* t3 = l.t3 + (threadIdx.x & 63) % TS;
+  for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++) {
+    const uint32_t* wl = l.list + kListWaveWords * w2;
+    const uint32_t n = min(__builtin_amdgcn_readfirstlane(wl[0]), (uint32_t)kListEntries);
+    for (uint32_t e = 0; e < n; e++) {
+      const uint32_t pos = __builtin_amdgcn_readfirstlane(wl[2 + 2 * e]);
+      if ((int)(pos >> 9) != q) continue;  // uniform
+      const float rho = __uint_as_float(__builtin_amdgcn_readfirstlane(wl[3 + 2 * e]));
+      const int i = pos & 31, b = (pos >> 5) & 3, t = (pos >> 7) & 3;
+      uint32_t nib;  // the slot's fp4 code: +1 = 0x2, -1 = 0xA, 0 = 0x0
+      if constexpr (FMT == 2) {
+        // straight from the bit-sliced words: slot i is nibble i & 7 of
+        // P0 (i < 16) or P1, shifted left once for the odd eighths
+        const u4 c4 = (t >> 1) ? qd.w[1] : qd.w[0];
+        const uint32_t p0 = (t & 1) ? c4.z : c4.x, p1 = (t & 1) ? c4.w : c4.y;
+        const uint32_t wd = ((i < 16 ? p0 : p1) << ((i >> 3) & 1)) & 0xAAAAAAAAu;
+        nib = (wd >> (4 * (i & 7))) & 0xFu;
+      } else {
+        const v8i B = decode_group<FMT, TS>(qd, t, t3);
+        const int wi = i >> 3;
+        const uint32_t wd = (uint32_t)(wi == 0 ? B[0] : wi == 1 ? B[1] : wi == 2 ? B[2] : B[3]);
+        nib = (wd >> (4 * (i & 7))) & 0xFu;
+      }
+      const float c = nib == 0x2u ? rho : nib == 0xAu ? -rho : 0.0f;
+      const float val = quad_scale<FMT>(qd, t) * c;
+      acc += __shfl(val, (int)(threadIdx.x & 15) + 16 * b);
+    }
+  }
+}
+
 template <int FMT, int XK, int MM, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
 __device__ __attribute__((always_inline)) inline void gemv_item(
     const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
@@ -1155,6 +1253,9 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   static_assert(NR <= kStageRounds, "hoisted staging rounds");
   const Item it = item_of<FMT>(a, blk);
   const bool pre = !CHAIN && a.xst != nullptr;  // slice image staged once per call
+  // one activation row of ternary weights and bf16 activations: the elements
+  // the split terms may miss go to correction lists (applied after the MFMAs)
+  constexpr bool LISTED = S::kCheck == 1 && MM == 1 && CHAIN;
   const int64_t nflag = pre ? image_flag_bytes(slice_rounds(it.nq, a.M)) : 0;
   constexpr int TS = trit_copies<FMT, MM == 1>();
   const Lds l = lds_of(a, smem, it.nq, nflag);
@@ -1194,7 +1295,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   if (pre) {
     copy_image<FMT>(a, it, l);
   } else if (stage) {
-    const bool bad = stage_all<FMT, XK, ONE || !CHAIN ? 1 : 4, NR>(a, it, l, xr, WAIT);
+    // (each wave's list is cleared by its own lane 0 before its lanes append:
+    // one wave's LDS accesses take effect in order)
+    if (LISTED && (threadIdx.x & 63) == 0) l.list[kListWaveWords * (threadIdx.x >> 6)] = 0u;
+    const bool bad = stage_all<FMT, XK, ONE || !CHAIN ? 1 : 4, NR, LISTED>(a, it, l, xr, WAIT);
     put_wave_flag(l.wflag, bad);
   }
   __syncthreads();
@@ -1220,9 +1324,23 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
         asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(sign_mask));
         asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(one_bits));
       }
+      // (LISTED) the entries of the waves' correction lists: quad ql of an
+      // entry is applied right after that quad's MFMAs, while its codes are
+      // in registers
+      uint32_t nlist = 0;
+      if constexpr (LISTED) {
+        for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++)
+          nlist += min(__builtin_amdgcn_readfirstlane(l.list[kListWaveWords * w2]), (uint32_t)kListEntries);
+      }
 #pragma unroll
-      for (int q = 0; q < QM; q++)
-        if (q < it.nq) quad_mfma_m1<FMT, XK, CHAIN, TS>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+      for (int q = 0; q < QM; q++) {
+        if (q < it.nq) {
+          quad_mfma_m1<FMT, XK, CHAIN, TS>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+          if constexpr (LISTED) {
+            if (nlist != 0) list_quad<FMT, TS>(l, q, qd[q], acc);
+          }
+        }
+      }
     }
     ym[0] = acc;
     yi[0] = 0;
@@ -1868,7 +1986,7 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int64_t M, int xkind, int quads = 
   // it is copied from the images staged once per call, M > 1), the zero
   // block and flags, the base-3 table
   p.lds = (size_t)qmax * 16 * p.MA * 33 + (M > 1 ? (size_t)image_flag_bytes(slice_rounds(qmax, M)) : 0) +
-          kZeroBlock + (fmt == 3 ? trit_table_bytes(M == 1 ? kTritCopies : 1) : 0);
+          kListBytes + kZeroBlock + (fmt == 3 ? trit_table_bytes(M == 1 ? kTritCopies : 1) : 0);
   p.Npad = p.NRG * p.W * rb * 16;
   p.part_off = kCounterBytes;
   p.bytes = p.part_off + align256((size_t)(p.KS > 1 ? p.KS : 0) * M * p.Npad * 4);
