@@ -1205,20 +1205,23 @@ __device__ __attribute__((always_inline)) inline void copy_image(const FArgs& a,
 // stage false: the workgroup's previous item was the same product and
 // K-slice, so the activation image (and its staging flags) in LDS is this
 // item's already.  MM: activation rows the kernel handles at most.
-// The correction-list entries of quad q (one-row items): entry {slot i of
-// quarter b of group t of quad ql, rho} adds scale x code x rho to the
-// outputs; lane r + 16 b holds row r's code and scale, the output of row r
-// is in lane r.
+// The correction-list entries of a one-row item: entry {slot i of quarter b
+// of group t of quad ql, rho} adds scale x code x rho to the outputs.  Lane
+// r + 16 b reads row r's codes and scales of quad ql again (the item has
+// just read them: L2 hits; entries are rare, and keeping every quad's codes
+// in registers past the MFMAs would cost more), the output of row r is in
+// lane r.
 template <int FMT, int TS>
-__device__ __attribute__((always_inline)) inline void list_quad(const Lds& l, int q, const Quad<FMT>& qd, float& acc) {
+__device__ __attribute__((always_inline)) inline void list_fix(const FArgs& a, const Item& it, const Lds& l, float& acc) {
   const uint32_t* t3 = l.t3 + (threadIdx.x & 63) % TS;
   for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++) {
     const uint32_t* wl = l.list + kListWaveWords * w2;
     const uint32_t n = min(__builtin_amdgcn_readfirstlane(wl[0]), (uint32_t)kListEntries);
     for (uint32_t e = 0; e < n; e++) {
       const uint32_t pos = __builtin_amdgcn_readfirstlane(wl[2 + 2 * e]);
-      if ((int)(pos >> 9) != q) continue;  // uniform
       const float rho = __uint_as_float(__builtin_amdgcn_readfirstlane(wl[3 + 2 * e]));
+      Quad<FMT> qd;
+      load_quad<FMT>(a, it, (int)(pos >> 9), qd);
       const int i = pos & 31, b = (pos >> 5) & 3, t = (pos >> 7) & 3;
       uint32_t nib;  // the slot's fp4 code: +1 = 0x2, -1 = 0xA, 0 = 0x0
       if constexpr (FMT == 2) {
@@ -1324,22 +1327,14 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
         asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(sign_mask));
         asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(one_bits));
       }
-      // (LISTED) the entries of the waves' correction lists: quad ql of an
-      // entry is applied right after that quad's MFMAs, while its codes are
-      // in registers
-      uint32_t nlist = 0;
-      if constexpr (LISTED) {
-        for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++)
-          nlist += min(__builtin_amdgcn_readfirstlane(l.list[kListWaveWords * w2]), (uint32_t)kListEntries);
-      }
 #pragma unroll
-      for (int q = 0; q < QM; q++) {
-        if (q < it.nq) {
-          quad_mfma_m1<FMT, XK, CHAIN, TS>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
-          if constexpr (LISTED) {
-            if (nlist != 0) list_quad<FMT, TS>(l, q, qd[q], acc);
-          }
-        }
+      for (int q = 0; q < QM; q++)
+        if (q < it.nq) quad_mfma_m1<FMT, XK, CHAIN, TS>(arow, erow, q, qd[q], l.t3, sign_mask, one_bits, acc);
+      if constexpr (LISTED) {
+        // the entries of the waves' correction lists (rare)
+        uint32_t nlist = 0;
+        for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++) nlist |= l.list[kListWaveWords * w2];
+        if (__builtin_amdgcn_readfirstlane(nlist) != 0) list_fix<FMT, TS>(a, it, l, acc);
       }
     }
     ym[0] = acc;
