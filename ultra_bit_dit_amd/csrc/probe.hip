@@ -11,7 +11,7 @@ namespace {
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 4;  // 16-byte loads in flight per thread per step
+constexpr int kProbeUnroll = 8;  // 16-byte loads in flight per thread per step
 
 // Every 16-byte piece is read once with a nontemporal load in a grid-stride
 // loop; each workgroup XOR-folds what it read into *out (so no load can be
@@ -45,7 +45,11 @@ hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* out, hipStr
   const int64_t n16 = bytes / 16;
   const int64_t per_block = (int64_t)kProbeThreads * kProbeUnroll;
   const int64_t want = (n16 + per_block - 1) / per_block;
-  const int64_t grid = want < 8 * (int64_t)cus ? want : 8 * (int64_t)cus;
+  // one workgroup per CU with 8 loads in flight per thread (32 KiB per CU)
+  // reads fastest: measured 7.36 TB/s, against 7.23 at two workgroups with
+  // 4 loads and 6.1 at eight with 4 (more concurrent streams read HBM less
+  // efficiently)
+  const int64_t grid = want < (int64_t)cus ? want : (int64_t)cus;
   hipLaunchKernelGGL(hbm_read, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kProbeThreads), 0, s,
                      (const v4u*)src, n16, out);
   return hipGetLastError();
