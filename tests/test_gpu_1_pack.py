@@ -92,7 +92,7 @@ def test_unpack_counts_reserved_patterns():
     assert int(bad.item()) == 9 and not c2.cpu().numpy().any()
 
 
-@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 << 20])
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 << 20, (64 << 20) + 112])
 def test_hbm_read_probe_reads_every_byte(nbytes):
     """The streaming-read helper folds every 16-byte piece it reads into one
     XOR: equal to numpy's XOR of the same data (ragged tail included)."""
