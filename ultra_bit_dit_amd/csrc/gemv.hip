@@ -1244,10 +1244,43 @@ __device__ __attribute__((always_inline)) inline void list_fix(const FArgs& a, c
   }
 }
 
+// Warming loads for the workgroup's next item: one 4-byte load per 128-byte
+// line of this wave's codes (up to 24 KiB) and scales of item blk, so that
+// the lines are cached when that item runs.  The values are only consumed
+// (an empty asm statement), never used.
+template <int FMT>
+__device__ __attribute__((always_inline)) inline void warm_item(const FArgs& a, int64_t blk, uint32_t& w0,
+                                                                uint32_t& w1, uint32_t& w2, uint32_t& w3) {
+  const Item it = item_of<FMT>(a, blk);
+  if (it.nq <= 0) return;
+  const int L = threadIdx.x & 63;
+  const int64_t rbc = it.live ? it.rb : a.NB - 1;
+  int64_t c0, clen;
+  if constexpr (FMT == 1) {
+    c0 = (rbc * a.GQ + it.q0) * 1024;
+    clen = (int64_t)it.nq * 1024;
+  } else if constexpr (FMT == 2) {
+    c0 = (rbc * a.GP + 2 * it.q0) * 1024;
+    clen = (min<int64_t>(2 * (it.q0 + it.nq), a.GP) - 2 * it.q0) * 1024;
+  } else {
+    const int64_t o0 = it.q0 >> 1, o1 = (it.q0 + it.nq - 1) >> 1;
+    c0 = (rbc * ((a.GQ + 1) / 2) + o0) * 3328;
+    clen = (o1 - o0 + 1) * 3328;
+  }
+  const uint8_t* cb = a.pcodes + c0;
+  w0 = *(const uint32_t*)(cb + min<int64_t>(128 * L, clen - 4));
+  w1 = *(const uint32_t*)(cb + min<int64_t>(128 * L + 8192, clen - 4));
+  w2 = *(const uint32_t*)(cb + min<int64_t>(128 * L + 16384, clen - 4));
+  if (a.pscales) {
+    const uint8_t* sb = (const uint8_t*)a.pscales + (rbc * a.GQ + it.q0) * 128;
+    w3 = *(const uint32_t*)(sb + min<int64_t>(128 * L, (int64_t)it.nq * 128 - 4));
+  }
+}
+
 template <int FMT, int XK, int MM, int YK, int QM, bool CHAIN, bool WAIT, bool ONE = false>
 __device__ __attribute__((always_inline)) inline void gemv_item(
     const FArgs& a, int64_t blk, uint8_t* smem, const uint32_t* wait_cnt, uint32_t wait_target,
-    uint32_t* err, bool stage = true) {
+    uint32_t* err, bool stage = true, int64_t warm_blk = -1) {
   using S = XSplit<FMT, XK>;
   constexpr int R = S::R;
   // staging rounds whose loads go out before the weight loads: a one-row
@@ -1273,7 +1306,10 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
   Quad<FMT> qd[QM];
 #pragma unroll
   for (int q = 0; q < QM; q++) load_quad<FMT>(a, it, q, qd[q]);
+  uint32_t wm0 = 0, wm1 = 0, wm2 = 0, wm3 = 0;
   if constexpr (WAIT) {
+    // (warm_blk: the workgroup's next item, of this product and K-slice)
+    if (warm_blk >= 0) warm_item<FMT>(a, warm_blk, wm0, wm1, wm2, wm3);
     // the previous product must be complete before its outputs are read; the
     // weight loads above are already in flight
     if (threadIdx.x < 64) {
@@ -1360,6 +1396,9 @@ __device__ __attribute__((always_inline)) inline void gemv_item(
       }
     }
   }
+  // the warming loads have landed before the item's stores go out (the
+  // completion count that follows waits for the stores)
+  if constexpr (WAIT) asm volatile("" ::"v"(wm0), "v"(wm1), "v"(wm2), "v"(wm3));
   item_output<XK, MM, YK, CHAIN>(a, it, ym, yi);
 }
 
@@ -1472,9 +1511,14 @@ __global__ __launch_bounds__(64 * kMaxW) __attribute__((amdgpu_waves_per_eu(2)))
     ks_last = ks;
     const bool wt = s > 0 && waitf[s] != 0 && !again;
     __syncthreads();  // the previous item's LDS reads are over
+    // the workgroup's next item, when it is of the same product and K-slice
+    // (one-row chains: the several-row kernels have no registers to spare)
+    const int64_t nxt = i + gridDim.x;
+    const bool warm = !MR && nxt < first[s + 1] && (nxt - first[s]) % a.KS == ks;
     if (wt)
       gemv_item<FMT, XK, MX, YK, QM, true, true, !MR>(a, i - first[s], smem, c.done + 256 * (s - 1),
-                                                      (uint32_t)(first[s] - first[s - 1]), c.err);
+                                                      (uint32_t)(first[s] - first[s - 1]), c.err, true,
+                                                      warm ? nxt - first[s] : -1);
     else
       gemv_item<FMT, XK, MX, YK, QM, true, false, !MR>(a, i - first[s], smem, nullptr, 0u, c.err,
                                                        !again);
