@@ -107,6 +107,35 @@ def test_chain_dependent_stages(fmt):
     chain.close()
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_chain_waiting_second_items(fmt):
+    """A waiting product with more work items than resident workgroups
+    (19200 x 10240: 300 row groups x 2 K-slices = 600 items): the workgroups
+    that run a second item of the same K-slice warm its codes and scales
+    before their first wait.  Every output must still meet the oracle."""
+    shapes = [(640, 1024), (19200, 10240)]
+    mats, xs, ys, refs = [], [], [], []
+    for j, (N, K) in enumerate(shapes):
+        codes, scales, pc, ps = make(fmt, N, K, tid=320 + 2 * j)
+        mats.append((pc, ps))
+        xh = synth.normal_bf16(SEED, 340 + j, 1, K)
+        xs.append(dev(xh.view(np.int16)).view(torch.bfloat16)[0])
+        ys.append(torch.full((N,), float("nan"), device="cuda"))
+        refs.append(O.matmul(codes, scales, O.X_BF16, xh))
+    stages = [(fmt, N, K, mats[j][0], mats[j][1], xs[j], ys[j], 1) for j, (N, K) in enumerate(shapes)]
+    chain = lb.Chain(stages, x_dtype=lb.BF16, y_dtype=lb.F32)
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        chain.run()
+        torch.cuda.synchronize()
+        for j in range(len(shapes)):
+            yref, absY = refs[j]
+            assert_within(ys[j].cpu().numpy()[None], yref, absY, what=f"stage {j} run {rep}")
+    assert chain.failed_waits() == 0
+    chain.close()
+
+
 def test_chain_rejects_bad_stages():
     _, _, pc, ps = make(1, 64, 256, tid=300)
     x = torch.zeros(256, dtype=torch.bfloat16, device="cuda")
